@@ -1,0 +1,229 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv, paged KV-cache attention for AMD MI355X (gfx950).
+ *
+ * The operations follow the engine read in the code series "An Inference Engine
+ * in 1,500 Lines of CUDA: The Map" (jaehun.me, English page, and its Korean
+ * original): a KV cache that is one pool carved into 16-token blocks, a block
+ * table per (sequence slot, layer) whose unassigned entries hold -1 (section
+ * "The path of one inference", step (4)), Llama-3-scaled RoPE (same section,
+ * step (3)), grouped-query attention with 4 query heads per KV head and an
+ * online softmax (Korean page, table in "What is in the box"), and the paired
+ * prefill / decode kernels (section "The path of one inference", closing
+ * paragraph).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - bf16 values are stored as their 16-bit patterns (pkv_bf16).
+ *  - Pointers are DEVICE pointers unless the parameter name ends in _host.
+ *    bf16 and float device buffers must be 16-byte aligned, int32 device
+ *    arrays 4-byte aligned (PKV_ERR_MISALIGNED otherwise).
+ *  - Ownership: the caller allocates and frees every buffer. No call allocates
+ *    or frees device memory; the library keeps no state between calls.
+ *  - Layouts are row-major with head_dim innermost:
+ *      k_pool, v_pool   [num_blocks][16][n_kv_heads][head_dim]   (same block id
+ *                        for K and V; a block holds 16 tokens of one layer)
+ *      block_table      rows of int32, row s starts at s * bt_row_stride and has
+ *                        max_blocks_per_seq entries; entry j names the block that
+ *                        holds tokens 16j .. 16j+15 of that row's sequence; -1 = none.
+ *                        A caller with a [slots][layers][max_blocks] table passes a
+ *                        layer's base pointer and bt_row_stride = layers*max_blocks.
+ *      q, out           [tokens][n_q_heads][head_dim];  k_new, v_new [tokens][n_kv_heads][head_dim]
+ *  - Query head h reads KV head h / (n_q_heads / n_kv_heads) (contiguous groups).
+ *  - Compiled shapes: head_dim == 64, block size 16, n_q_heads / n_kv_heads in
+ *    {1, 2, 4, 8}; anything else returns PKV_ERR_UNSUPPORTED.
+ *  - Calls that take `stream` (a hipStream_t, NULL = default stream) only
+ *    enqueue work and return; argument errors are found on the host before any
+ *    launch, and then nothing is enqueued. A failed launch returns PKV_ERR_HIP.
+ *  - Device-side data (block ids, context lengths, positions, slot ids) is not
+ *    validated by the kernels beyond staying in bounds: a kernel never reads or
+ *    writes outside the buffers described by its size arguments, but results for
+ *    invalid data are unspecified. pkv_check_block_table validates on the host.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t pkv_bf16;
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,          /* a required pointer is NULL */
+  PKV_ERR_MISALIGNED = 2,    /* a device pointer is not suitably aligned */
+  PKV_ERR_UNSUPPORTED = 3,   /* head_dim / head ratio outside the compiled set */
+  PKV_ERR_INVALID_ARG = 4,   /* negative size, n_q % n_kv != 0, bad partition size, ... */
+  PKV_ERR_BAD_BLOCK = 5,     /* host check: -1 or out-of-range block inside a context */
+  PKV_ERR_CAPACITY = 6,      /* workspace too small, free list empty, table row too short */
+  PKV_ERR_HIP = 7            /* the HIP runtime reported an error */
+};
+
+#define PKV_BLOCK_SIZE 16
+#define PKV_HEAD_DIM 64
+
+/* Text for a status code (static storage; never NULL). */
+const char* pkv_status_str(int status);
+
+/* Version of the library ABI: (major << 16) | minor. */
+int pkv_abi_version(void);
+
+/* ------------------------------------------------------------------------ *
+ * RoPE (Llama-3 scaling).  Source: "The path of one inference", step (3): a
+ * positional-encoding table is built once from head_dim, the maximum length,
+ * base 500000 and the scaling numbers 32, 1, 4, 8192; the Korean page's table
+ * names the kernel ropeKernel_llama3.  The scaling rule is the public Llama-3
+ * one: with f_i = theta^(-2i/d) and wavelength w_i = 2 pi / f_i, pairs with
+ * w_i < original_max_pos / high_freq_factor keep f_i, pairs with
+ * w_i > original_max_pos / low_freq_factor use f_i / factor, and the rest blend
+ * the two linearly in original_max_pos / w_i.
+ * ------------------------------------------------------------------------ */
+
+/* Fill the device table cos_sin[max_pos][head_dim/2][2] (float32 cos, sin of
+ * p * f_i'), computed in double precision on the host and copied in; the call
+ * waits for the copy to finish.  Errors: NULL, max_pos < 1, odd head_dim,
+ * non-positive theta/factor, high_freq_factor <= low_freq_factor. */
+int pkv_rope_table_init(float* cos_sin, int max_pos, int head_dim, double theta, double factor,
+                        double low_freq_factor, double high_freq_factor, int original_max_pos,
+                        void* stream);
+
+/* Rotate, in place, q[num_tokens][n_q_heads][head_dim] and k[num_tokens][n_kv_heads][head_dim]
+ * of token t by position positions[t]: pair (i, i + head_dim/2) becomes
+ * (x cos - y sin, y cos + x sin), computed in float32 and rounded to bf16
+ * nearest-even.  Used for the decode step (one token per sequence) and for
+ * prefill chunks (many tokens).  k may be NULL (q only).  A position outside
+ * [0, max_pos) leaves that token unrotated. */
+int pkv_rope_decode(pkv_bf16* q, pkv_bf16* k, const int32_t* positions, int num_tokens,
+                    int n_q_heads, int n_kv_heads, int head_dim, const float* cos_sin, int max_pos,
+                    void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Paged KV cache.  Source: "The path of one inference", step (4) (pool
+ * allocated once and cut into 16-token blocks, free list, block table with -1)
+ * and the series' sixth chapter title (reading non-contiguous blocks through
+ * the block table).
+ * ------------------------------------------------------------------------ */
+
+/* For each token t: s = slot_ids[t], p = positions[t], blk = table[s][p / 16];
+ * copy the bits of k_new[t] and v_new[t] into k_pool[blk][p % 16] and
+ * v_pool[blk][p % 16].  Tokens whose slot, table entry or block id is out of
+ * range are skipped (nothing is written for them). */
+int pkv_paged_kv_append(pkv_bf16* k_pool, pkv_bf16* v_pool, int num_blocks,
+                        const pkv_bf16* k_new, const pkv_bf16* v_new,
+                        const int32_t* block_table, int64_t bt_row_stride, int num_slots,
+                        int max_blocks_per_seq, const int32_t* slot_ids, const int32_t* positions,
+                        int num_tokens, int n_kv_heads, int head_dim, void* stream);
+
+/* Diagnostic read-back through the same addressing: copy tokens
+ * 0 .. context_len-1 of table row `slot` into k_dense/v_dense
+ * [context_len][n_kv_heads][head_dim].  Rows whose block id is out of range
+ * are written as zeros. */
+int pkv_paged_gather(pkv_bf16* k_dense, pkv_bf16* v_dense, const pkv_bf16* k_pool,
+                     const pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
+                     int64_t bt_row_stride, int max_blocks_per_seq, int slot, int context_len,
+                     int n_kv_heads, int head_dim, void* stream);
+
+/* Host-side block allocation for one step ("The path of one inference",
+ * step (4): blocks come off a free list; -1 marks an unassigned entry).
+ * For every token t whose table entry bt_host[slot_ids_host[t]][positions_host[t] / 16]
+ * is -1, pop a block from the end of free_list_host (n_free is updated) and
+ * store it there; each assignment is also appended to patch_offsets_host /
+ * patch_values_host (flat index into the table, block id; room for num_tokens
+ * entries) and counted in *n_patch.  All or nothing: if the free list or a
+ * table row is too short, nothing changes and PKV_ERR_CAPACITY is returned.
+ * Pure host code; no device is touched. */
+int pkv_blocks_assign(int32_t* bt_host, int64_t bt_row_stride, int num_slots,
+                      int max_blocks_per_seq, int32_t* free_list_host, int* n_free,
+                      const int32_t* slot_ids_host, const int32_t* positions_host, int num_tokens,
+                      int32_t* patch_offsets_host, int32_t* patch_values_host, int* n_patch);
+
+/* Return every assigned block of table row `slot` to the free list (pushed at
+ * the end) and reset the row to -1; the released entries are appended to the
+ * patch arrays (room for max_blocks_per_seq entries) with value -1.
+ * PKV_ERR_CAPACITY if the free list would exceed free_capacity. Host only. */
+int pkv_blocks_release(int32_t* bt_host, int64_t bt_row_stride, int num_slots,
+                       int max_blocks_per_seq, int slot, int32_t* free_list_host, int* n_free,
+                       int free_capacity, int32_t* patch_offsets_host, int32_t* patch_values_host,
+                       int* n_patch);
+
+/* Apply host-side table changes to the device copy: bt_dev[offsets[i]] = values[i]
+ * for i < n_patch.  The two arrays are HOST arrays; their contents travel in
+ * the kernel arguments, so they may be reused as soon as the call returns.
+ * Offsets outside [0, bt_elems) are skipped. */
+int pkv_block_table_patch(int32_t* bt_dev, int64_t bt_elems, const int32_t* patch_offsets_host,
+                          const int32_t* patch_values_host, int n_patch, void* stream);
+
+/* Validate tables on the host for rows slot_ids_host[0..batch) (NULL = rows
+ * 0..batch-1) and lengths context_lens_host (indexed by row): every entry
+ * covering tokens 0 .. len-1 must be in [0, num_blocks), len must fit the row,
+ * and no block may appear twice among the checked entries. Returns PKV_OK, or
+ * PKV_ERR_BAD_BLOCK with *bad_row / *bad_idx set to the first offending
+ * (batch index, table entry); bad_idx = -1 flags a length beyond the row,
+ * -2 a slot id out of range. Host only. */
+int pkv_check_block_table(const int32_t* bt_host, int64_t bt_row_stride, int num_slots,
+                          int max_blocks_per_seq, const int32_t* slot_ids_host,
+                          const int32_t* context_lens_host, int batch, int num_blocks,
+                          int* bad_row, int* bad_idx);
+
+/* ------------------------------------------------------------------------ *
+ * Decode attention.  Source: the Korean page's table ("What is in the box":
+ * online softmax and PagedAttention in pagedAttentionKernel, GQA ratio 4) and
+ * the chapter-6 title (each decode step re-reads the sequence's cached K/V
+ * through the block table).  For batch row b with s = slot_ids[b] (NULL =
+ * identity) and n = context_lens[s] (the length includes the token appended
+ * this step), query head h with KV head g:
+ *     out[b][h] = sum_j softmax_j(scale * <q[b][h], K_j,g>) V_j,g ,  j < n
+ * bf16 inputs, float32 accumulation, bf16 output (nearest-even); n == 0 gives a
+ * zero row.  Long contexts are split into partitions of partition_size tokens
+ * whose partial (max, sum, unnormalised output) are merged by a second kernel.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of workspace pkv_paged_attn_decode needs for these sizes
+ * (0 when no sequence can need more than one partition). partition_size 0 =
+ * the automatic choice, which depends only on the arguments given here. */
+size_t pkv_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                  int max_context_len, int partition_size);
+
+/* The partition size the automatic choice picks for these sizes. */
+int pkv_decode_partition_size(int batch, int n_kv_heads, int max_context_len);
+
+/* max_context_len: host-known upper bound of the lengths (sizes the grid);
+ * a longer context is still handled correctly, by the last partition, only
+ * slower. Contexts are clipped to max_blocks_per_seq * 16.
+ * partition_size: 0 = automatic, else a positive multiple of 16.
+ * workspace: device memory of at least pkv_decode_workspace_bytes(...) bytes
+ * (may be NULL when that is 0); its contents need no initialisation. */
+int pkv_paged_attn_decode(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_pool,
+                          const pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
+                          int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,
+                          const int32_t* slot_ids, const int32_t* context_lens, int batch,
+                          int max_context_len, int n_q_heads, int n_kv_heads, int head_dim,
+                          float scale, int partition_size, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Chunked causal prefill.  Source: "The path of one inference", closing
+ * paragraph (prefill pushes the whole prompt through at once, matrix x
+ * matrix) and the category page's chunked-prefill chapter title. Sequence i
+ * owns query rows cu_q_lens[i] .. cu_q_lens[i+1]-1; its first query is at
+ * absolute position q_start_pos[i]; query row at position a attends keys
+ * 0 .. a of table row slot_ids[i] (NULL = i). The chunk's own K/V must already
+ * be in the pool (pkv_paged_kv_append). QK^T and PV run on MFMA (bf16 in,
+ * float32 accumulate); out is bf16 [total_q][n_q_heads][head_dim].
+ * max_q_len: host bound on the longest query run (sizes the grid).
+ * ------------------------------------------------------------------------ */
+int pkv_paged_attn_prefill(pkv_bf16* out, const pkv_bf16* q, const int32_t* cu_q_lens,
+                           const int32_t* q_start_pos, const int32_t* slot_ids,
+                           const pkv_bf16* k_pool, const pkv_bf16* v_pool, int num_blocks,
+                           const int32_t* block_table, int64_t bt_row_stride, int num_slots,
+                           int max_blocks_per_seq, int num_seqs, int total_q, int max_q_len,
+                           int n_q_heads, int n_kv_heads, int head_dim, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

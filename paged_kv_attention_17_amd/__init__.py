@@ -1,1 +1,15 @@
-"""paged_kv_attention_17_amd -- paged KV-cache attention for MI355X (gfx950)."""
+"""paged_kv_attention_17_amd -- paged KV-cache attention for AMD MI355X (gfx950).
+
+The compute lives in libpagedkv.so (HIP kernels behind the C ABI of
+include/pagedkv.h); this package is its ctypes binding (``_abi``, re-exported
+here under the C names), the in-place build (``build``), a decode-step
+driver over the C ABI (``engine``) and seeded synthetic workloads
+(``workloads``).  Importing the package does not load the library; the first
+call does, and raises if it has not been built.
+"""
+from ._abi import (  # noqa: F401
+    PagedKVError, load, header_functions, LIB_PATH,
+    pkv_status_str, pkv_abi_version, pkv_rope_table_init, pkv_rope_decode, pkv_paged_kv_append,
+    pkv_paged_gather, pkv_blocks_assign, pkv_blocks_release, pkv_block_table_patch, pkv_check_block_table,
+    pkv_decode_workspace_bytes, pkv_decode_partition_size, pkv_paged_attn_decode, pkv_paged_attn_prefill,
+)

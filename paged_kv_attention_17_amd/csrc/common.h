@@ -1,0 +1,84 @@
+// Shared device/host helpers for the gfx950 kernels of libpagedkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+
+namespace pkv {
+
+constexpr int kBlock = PKV_BLOCK_SIZE;   // tokens per KV block
+constexpr int kHeadDim = PKV_HEAD_DIM;   // compiled head dimension
+constexpr int kWave = 64;                // CDNA wavefront width
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- device --
+
+// Widen the low / high bf16 of a packed dword to float32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+
+// Round two float32 to bf16 nearest-even and pack (lo, hi) into one dword;
+// gfx950 does this in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+}
+
+// Two-term bf16 dot product accumulated in float32: a.lo*b.lo + a.hi*b.hi + c.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                        false);
+}
+
+// DPP lane exchanges inside rows of 16 lanes (value from the partner lane).
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF,
+                                                               false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each group of 8
+constexpr int kDppRowRor8 = 0x128;    // lane i <- (i+8) mod 16 inside a row
+
+// Sum over each aligned group of 8 lanes, result in all 8 lanes.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane (self ^ mask) via ds_bpermute (any mask < 64).
+__device__ __forceinline__ float shfl_xor(float x, int mask) {
+  const int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// ------------------------------------------------------------------ host --
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+inline bool ratio_supported(int n_q, int n_kv) {
+  if (n_q <= 0 || n_kv <= 0 || n_q % n_kv) return false;
+  const int g = n_q / n_kv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+}  // namespace pkv

@@ -1,0 +1,162 @@
+// KV-cache writes and reads through the block table, for gfx950.
+//
+// Source: "An Inference Engine in 1,500 Lines of CUDA: The Map", section "The
+// path of one inference", step (4): one pool cut into 16-token blocks and a
+// block table per (slot, layer) mapping each 16-token chunk of a sequence to
+// its block (-1 = none yet); the series' sixth chapter title (reading
+// non-contiguous blocks through the table).
+//
+// Token p of table row s lives at pool[table[s][p / 16]][p % 16][head][:].
+// Each thread moves one 16-byte chunk (8 bf16) of one head's row, so a K or V
+// row of 128 bytes is eight adjacent lanes and every load/store is a full
+// dwordx4.  Every index that comes from device data is range-checked before
+// it is used as an address.
+#include "common.h"
+
+namespace pkv {
+
+constexpr int kChunks = kHeadDim * 2 / 16;   // 16-byte chunks per head row
+
+__global__ __launch_bounds__(256) void append_kernel(uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+                                                     int num_blocks, const uint4* __restrict__ k_new,
+                                                     const uint4* __restrict__ v_new,
+                                                     const int32_t* __restrict__ bt, int64_t stride,
+                                                     int num_slots, int max_blocks,
+                                                     const int32_t* __restrict__ slot_ids,
+                                                     const int32_t* __restrict__ positions, int num_tokens,
+                                                     int n_kv) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)n_kv * kChunks * 2;
+  if (gid >= (int64_t)num_tokens * per_token) return;
+  const int t = (int)(gid / per_token);
+  const int rem = (int)(gid % per_token);
+  const int which = rem / (n_kv * kChunks);            // 0 = K, 1 = V
+  const int hc = rem % (n_kv * kChunks);                // head * kChunks + chunk
+  const int s = slot_ids[t];
+  const int p = positions[t];
+  if (s < 0 || s >= num_slots || p < 0 || p / kBlock >= max_blocks) return;
+  const int blk = bt[(int64_t)s * stride + p / kBlock];
+  if (blk < 0 || blk >= num_blocks) return;
+  const int64_t dst = ((int64_t)blk * kBlock + p % kBlock) * n_kv * kChunks + hc;
+  const int64_t src = (int64_t)t * n_kv * kChunks + hc;
+  if (which == 0)
+    k_pool[dst] = k_new[src];
+  else
+    v_pool[dst] = v_new[src];
+}
+
+__global__ __launch_bounds__(256) void gather_kernel(uint4* __restrict__ k_dense, uint4* __restrict__ v_dense,
+                                                     const uint4* __restrict__ k_pool,
+                                                     const uint4* __restrict__ v_pool, int num_blocks,
+                                                     const int32_t* __restrict__ row, int context_len,
+                                                     int n_kv) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)n_kv * kChunks;
+  if (gid >= (int64_t)context_len * per_token) return;
+  const int p = (int)(gid / per_token);
+  const int hc = (int)(gid % per_token);
+  const int blk = row[p / kBlock];
+  uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
+  if (blk >= 0 && blk < num_blocks) {
+    const int64_t src = ((int64_t)blk * kBlock + p % kBlock) * per_token + hc;
+    kv = k_pool[src];
+    vv = v_pool[src];
+  }
+  k_dense[gid] = kv;
+  v_dense[gid] = vv;
+}
+
+constexpr int kPatchPerLaunch = 240;   // (offset, value) pairs carried in one kernel's arguments
+
+struct PatchArgs {
+  int32_t off[kPatchPerLaunch];
+  int32_t val[kPatchPerLaunch];
+};
+
+__global__ __launch_bounds__(256) void patch_kernel(int32_t* __restrict__ bt, int64_t elems, PatchArgs pa, int n) {
+  const int i = threadIdx.x;
+  if (i < n && pa.off[i] >= 0 && pa.off[i] < elems) bt[pa.off[i]] = pa.val[i];
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int pkv_paged_kv_append(pkv_bf16* k_pool, pkv_bf16* v_pool, int num_blocks, const pkv_bf16* k_new,
+                                   const pkv_bf16* v_new, const int32_t* block_table, int64_t bt_row_stride,
+                                   int num_slots, int max_blocks_per_seq, const int32_t* slot_ids,
+                                   const int32_t* positions, int num_tokens, int n_kv_heads, int head_dim,
+                                   void* stream) {
+  if (num_tokens < 0 || num_blocks < 0 || n_kv_heads <= 0 || num_slots < 0 || max_blocks_per_seq < 0 ||
+      bt_row_stride < max_blocks_per_seq)
+    return PKV_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !block_table || !slot_ids || !positions) return PKV_ERR_NULL;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new) ||
+      !aligned4(block_table) || !aligned4(slot_ids) || !aligned4(positions))
+    return PKV_ERR_MISALIGNED;
+  const int64_t total = (int64_t)num_tokens * n_kv_heads * kChunks * 2;
+  const int64_t grid = (total + 255) / 256;
+  if (grid > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  uint4* kp = reinterpret_cast<uint4*>(k_pool);
+  uint4* vp = reinterpret_cast<uint4*>(v_pool);
+  const uint4* kn = reinterpret_cast<const uint4*>(k_new);
+  const uint4* vn = reinterpret_cast<const uint4*>(v_new);
+  int nb = num_blocks, ns = num_slots, mb = max_blocks_per_seq, nt = num_tokens, nk = n_kv_heads;
+  int64_t st = bt_row_stride;
+  const int32_t *bt = block_table, *si = slot_ids, *po = positions;
+  void* args[] = {&kp, &vp, &nb, &kn, &vn, &bt, &st, &ns, &mb, &si, &po, &nt, &nk};
+  return launch_status(hipLaunchKernel((const void*)append_kernel, dim3((unsigned)grid), dim3(256), args, 0,
+                                       (hipStream_t)stream));
+}
+
+extern "C" int pkv_paged_gather(pkv_bf16* k_dense, pkv_bf16* v_dense, const pkv_bf16* k_pool,
+                                const pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
+                                int64_t bt_row_stride, int max_blocks_per_seq, int slot, int context_len,
+                                int n_kv_heads, int head_dim, void* stream) {
+  if (context_len < 0 || num_blocks < 0 || n_kv_heads <= 0 || slot < 0 || max_blocks_per_seq < 0 ||
+      bt_row_stride < max_blocks_per_seq)
+    return PKV_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return PKV_ERR_UNSUPPORTED;
+  if (context_len == 0) return PKV_OK;
+  if ((context_len + kBlock - 1) / kBlock > max_blocks_per_seq) return PKV_ERR_CAPACITY;
+  if (!k_dense || !v_dense || !k_pool || !v_pool || !block_table) return PKV_ERR_NULL;
+  if (!aligned16(k_dense) || !aligned16(v_dense) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PKV_ERR_MISALIGNED;
+  const int64_t total = (int64_t)context_len * n_kv_heads * kChunks;
+  const int64_t grid = (total + 255) / 256;
+  uint4* kd = reinterpret_cast<uint4*>(k_dense);
+  uint4* vd = reinterpret_cast<uint4*>(v_dense);
+  const uint4* kp = reinterpret_cast<const uint4*>(k_pool);
+  const uint4* vp = reinterpret_cast<const uint4*>(v_pool);
+  const int32_t* row = block_table + (int64_t)slot * bt_row_stride;
+  int nb = num_blocks, cl = context_len, nk = n_kv_heads;
+  void* args[] = {&kd, &vd, &kp, &vp, &nb, &row, &cl, &nk};
+  return launch_status(hipLaunchKernel((const void*)gather_kernel, dim3((unsigned)grid), dim3(256), args, 0,
+                                       (hipStream_t)stream));
+}
+
+extern "C" int pkv_block_table_patch(int32_t* bt_dev, int64_t bt_elems, const int32_t* patch_offsets_host,
+                                     const int32_t* patch_values_host, int n_patch, void* stream) {
+  if (n_patch < 0 || bt_elems < 0) return PKV_ERR_INVALID_ARG;
+  if (n_patch == 0) return PKV_OK;
+  if (!bt_dev || !patch_offsets_host || !patch_values_host) return PKV_ERR_NULL;
+  if (!aligned4(bt_dev)) return PKV_ERR_MISALIGNED;
+  for (int base = 0; base < n_patch; base += kPatchPerLaunch) {
+    PatchArgs pa;
+    const int n = n_patch - base < kPatchPerLaunch ? n_patch - base : kPatchPerLaunch;
+    for (int i = 0; i < n; ++i) {
+      pa.off[i] = patch_offsets_host[base + i];
+      pa.val[i] = patch_values_host[base + i];
+    }
+    int32_t* bt = bt_dev;
+    int64_t el = bt_elems;
+    int nn = n;
+    void* args[] = {&bt, &el, &pa, &nn};
+    const int st = launch_status(hipLaunchKernel((const void*)patch_kernel, dim3(1), dim3(256), args, 0,
+                                                 (hipStream_t)stream));
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
