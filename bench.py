@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Paged decode attention bench on one MI355X.
+
+Workload: B=64 sequences, 16 layers, contexts uniform in [512, 4096], 32 query
+/ 8 KV heads, head_dim 64, bf16 16-token blocks in a pool of 1.25x the blocks
+needed with tables interleaved round-robin over (layer, sequence).  One step
+= one decode step of all 16 layers through the native pkv_decode_step: host
+block allocation, then per layer RoPE on the new q/k, KV append and paged
+attention (split-context partitions + merge).  Inputs are seeded synthetic
+data resident in HBM before timing starts; contexts grow by one token per
+step as in a real decode loop.
+
+Prints ONE JSON line:
+  value        KV GB/s over the whole step = algorithmic KV bytes of all
+               layers / step wall time (2,048 B per context token per layer)
+  roofline     the attention kernel alone: algorithmic bytes per launch /
+               its mean launch duration (HIP events on its stream)
+  cpu_baseline the float64 CPU oracle on a bounded sample of the same step
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KV_BYTES_PER_TOKEN = 8 * 64 * 2 * 2          # per layer: 8 KV heads x 64 dims x bf16 x (K and V)
+METRIC = "paged decode attn: KV GB/s (% of HBM peak) and us/step at B=64 per layer"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "common.h"):
+        with open(os.path.join(ROOT, "paged_kv_attention_17_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(src_hash: str):
+    """HBM bytes per attention launch from the committed counter summary,
+    if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_attn_traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != src_hash:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def stream_copy_gbs(torch, nbytes=2 << 30, iters=10):
+    """Achievable bandwidth of a plain device-to-device copy (read + write)."""
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(2):
+        b.copy_(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3 / iters
+    del a, b
+    return 2 * nbytes / t / 1e9
+
+
+def cpu_baseline(eng, q_host, seconds: float):
+    """Time the float64 oracle (as it stands) on layer-by-layer samples of the
+    step: sequences are gathered into a compact host pool (not timed), then
+    oracle.attention.decode runs on them until `seconds` have passed."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    from oracle import attention
+    rng = np.random.default_rng(0)
+    done_bytes = 0
+    t_total = 0.0
+    n_rows = 0
+    with threadpool_limits(limits=1):
+        while t_total < seconds:
+            layer = int(rng.integers(eng.n_layers))
+            rows = rng.choice(eng.n_slots, size=4, replace=False).astype(np.int32)
+            ctx = eng.cached[rows].astype(np.int32)
+            nbs = [-(-int(c) // 16) for c in ctx]
+            ids = np.concatenate([eng.bt_host[r, layer, :n] for r, n in zip(rows, nbs)]).astype(np.int64)
+            idx = torch.from_numpy(ids).cuda()
+            kp = eng.k_pool.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+            vp = eng.v_pool.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+            bt = np.full((4, max(nbs)), -1, np.int32)
+            o = 0
+            for i, n in enumerate(nbs):
+                bt[i, :n] = np.arange(o, o + n)
+                o += n
+            q = q_host[layer, rows]
+            t0 = time.perf_counter()
+            attention.decode(q, kp, vp, bt, np.arange(4), ctx, eng.scale)
+            t_total += time.perf_counter() - t0
+            done_bytes += int(ctx.sum()) * KV_BYTES_PER_TOKEN
+            n_rows += 4
+    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_rows} (sequence, layer) rows of the B=64 16-layer step, float64 numpy oracle "
+                      f"(gather through the block table + two-pass softmax), BLAS limited to 1 thread, "
+                      f"{t_total:.1f} s of CPU time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--attn-iters", type=int, default=10, help="passes over the 16 layers for kernel timing")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--partition-size", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import paged_kv_attention_17_amd as pkv
+    from paged_kv_attention_17_amd import workloads as W
+    from paged_kv_attention_17_amd.engine import DecodeEngine
+
+    if not os.path.exists(pkv.LIB_PATH):
+        from paged_kv_attention_17_amd import build
+        build.build()
+    pkv.load()
+    torch.cuda.set_device(0)
+    steps_total = args.warmup + args.steps
+    log(f"building workload (B=64, 16 layers, ctx U[512,4096]) ...")
+    w = W.config3(fill_pool=False, extra_steps=steps_total + 1)
+    kp = torch.empty((w.num_blocks, 16, 8, 64), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    W.fill_pool_device(kp, 31)
+    W.fill_pool_device(vp, 32)
+    stream = torch.cuda.current_stream()
+    eng = DecodeEngine(kp, vp, w.block_table, w.context_lens - 1, w.free_list, max_pos=8192,
+                       partition_size=args.partition_size, stream=stream)
+    q = torch.from_numpy(w.q_new.view(np.int16)).cuda().view(torch.bfloat16)
+    k = torch.from_numpy(w.k_new.view(np.int16)).cuda().view(torch.bfloat16)
+    v = torch.from_numpy(w.v_new.view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty_like(q)
+    sids = np.arange(w.batch, dtype=np.int32)
+    L = w.n_layers
+    log(f"pool {w.num_blocks} blocks ({2 * kp.numel() * 2 / 1e9:.2f} GB K+V), mean ctx {w.context_lens.mean():.0f}")
+
+    for _ in range(args.warmup):
+        eng.step(sids, q, k, v, out)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole decode steps --------------------------------
+    kv_bytes = 0
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        kv_bytes += (int(eng.cached.sum()) + w.batch) * KV_BYTES_PER_TOKEN * L   # lengths after this step
+        eng.step(sids, q, k, v, out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    t_step = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    value = kv_bytes / args.steps / t_step / 1e9
+    log(f"step: {t_step * 1e6:.1f} us ({t_step * 1e6 / L:.2f} us/layer), KV {value:.0f} GB/s, "
+        f"host wall {wall / args.steps * 1e6:.1f} us/step")
+
+    # ---- dominant kernel: attention alone, events around every launch ------
+    ctx_now = eng.cached.copy()
+    bytes_per_launch = int(ctx_now.sum()) * KV_BYTES_PER_TOKEN
+    sid_dev = eng.meta[eng.n_slots + w.batch:eng.n_slots + 2 * w.batch]
+    pairs = []
+    for it in range(args.attn_iters + 1):
+        for layer in range(L):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pkv.pkv_paged_attn_decode(out[layer], q[layer], kp, vp, eng.bt_dev[:, layer, :], sid_dev, eng.ctx_dev,
+                                      eng.max_context_len, eng.scale, eng.partition_size, eng.workspace,
+                                      stream=stream)
+            e1.record(stream)
+            if it > 0:                      # first pass is a warm-up
+                pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) / 1e3 for a, b in pairs])
+    t_attn = float(durs.mean())
+    achieved = bytes_per_launch / t_attn / 1e9
+    log(f"attention: {t_attn * 1e6:.2f} us/launch (p10 {np.percentile(durs, 10) * 1e6:.2f}, "
+        f"p90 {np.percentile(durs, 90) * 1e6:.2f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of peak")
+
+    copy_gbs = stream_copy_gbs(torch)
+    log(f"plain copy kernel: {copy_gbs:.0f} GB/s (read + write)")
+
+    src_hash = decode_source_hash()
+    traffic = traffic_from_profile(src_hash)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(eng, w.q_new, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']:.3f} GB/s ({cpu['sample']})")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode step, B=64, 16 layers, ctx U[512,4096] (+1/step), 32q/8kv heads, d=64, "
+                               "bf16 16-token blocks, pool 1.25x, interleaved tables",
+                   "batch": w.batch, "layers": L, "mean_context": round(float(ctx_now.mean()), 1),
+                   "partition_size": pkv.pkv_decode_partition_size(w.batch, 8, eng.max_context_len)
+                   if args.partition_size == 0 else args.partition_size},
+        "us_per_layer": round(t_step * 1e6 / L, 3),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "pkv_paged_attn_decode", "bytes_per_launch": bytes_per_launch,
+                     "us_per_launch": round(t_attn * 1e6, 3), "source_hash": src_hash},
+        "copy_kernel_GBps": round(copy_gbs, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -222,6 +222,38 @@ int pkv_paged_attn_prefill(pkv_bf16* out, const pkv_bf16* q, const int32_t* cu_q
                            int max_blocks_per_seq, int num_seqs, int total_q, int max_q_len,
                            int n_q_heads, int n_kv_heads, int head_dim, float scale, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * One whole decode step of an n-layer engine, driven natively.  Source: "The
+ * path of one inference" (after prefill, every active slot produces one token
+ * per decode step; blocks come off the free list as sequences grow).  For each
+ * batch row b (slot s = slot_ids_host[b], new token at position
+ * p = cached_lens_host[s]):
+ *   1. host: for every layer whose table entry bt_host[s][layer][p / 16] is -1,
+ *      pop a block from free_list_host (all or nothing: PKV_ERR_CAPACITY and no
+ *      change at all if the free list is too short or p / 16 >= max_blocks);
+ *   2. cached_lens_host[s] += 1; the new table entries go to bt_dev and the
+ *      context lengths, positions and slot ids to meta_dev, carried in kernel
+ *      arguments (no host buffer is read after the call returns);
+ *   3. per layer l: pkv_rope_decode(q[l], k[l]), pkv_paged_kv_append(k[l], v[l]),
+ *      pkv_paged_attn_decode(out[l], q[l]) over the layer's table view.
+ * q, k, v, out are HOST arrays of n_layers DEVICE pointers ([batch][n_q][64],
+ * [batch][n_kv][64], [batch][n_kv][64], [batch][n_q][64]); q and k are rotated
+ * in place.  bt_host / bt_dev: [num_slots][n_layers][max_blocks_per_seq] int32,
+ * the device copy mirroring the host one.  meta_dev: device int32
+ * [num_slots + 2 * batch] = context lengths (per slot) | positions | slot ids,
+ * written by this call; its context-length part must hold cached_lens_host
+ * before the first step.  The workspace is pkv_paged_attn_decode's, for
+ * (batch, n_q_heads, n_kv_heads, head_dim, max_context_len, partition_size).
+ * All launches go to `stream`; the call returns after enqueueing them.
+ * ------------------------------------------------------------------------ */
+int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const* k, const pkv_bf16* const* v,
+                    pkv_bf16* const* out, pkv_bf16* k_pool, pkv_bf16* v_pool, int num_blocks,
+                    int32_t* bt_host, int32_t* bt_dev, int num_slots, int max_blocks_per_seq,
+                    int32_t* free_list_host, int* n_free, int32_t* cached_lens_host, int32_t* meta_dev,
+                    const int32_t* slot_ids_host, int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                    const float* cos_sin, int max_pos, float scale, int max_context_len,
+                    int partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,8 @@ SIGNATURES = {
                                    _p, _sz, _p]),
     "pkv_paged_attn_prefill": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _p, _i64, _i, _i, _i, _i, _i, _i, _i, _i,
                                     _f, _p]),
+    "pkv_decode_step": (_i, [_i, _p, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _p, _ip, _p, _p, _p, _i, _i, _i, _i,
+                             _p, _i, _f, _i, _i, _p, _sz, _p]),
 }
 
 
@@ -345,3 +347,54 @@ def pkv_paged_attn_prefill(out, q, cu_q_lens, q_start_pos, slot_ids, k_pool, v_p
         _dev_ptr(slot_ids, "slot_ids", (torch.int32,)), _dev_ptr(k_pool, "k_pool", _bf16_types()),
         _dev_ptr(v_pool, "v_pool", _bf16_types()), k_pool.shape[0], bt, stride, rows, mb, S, q.shape[0], max_q_len,
         q.shape[1], k_pool.shape[2], q.shape[2], float(scale), _stream(stream)))
+
+
+def pkv_decode_step(q, k, v, out, k_pool, v_pool, bt_host, bt_dev, free_list, n_free, cached_lens, meta_dev,
+                    slot_ids, cos_sin, scale, max_context_len, partition_size=0, workspace=None, stream=None):
+    """One decode step over all layers (see pkv_decode_step in pagedkv.h).
+
+    q/out [L, B, n_q, 64], k/v [L, B, n_kv, 64] device bf16 (or lists of L
+    such tensors); bt_host numpy int32 [slots, L, max_blocks] (updated in
+    place) with bt_dev its contiguous device copy; free_list numpy int32
+    (popped from index n_free - 1 down); cached_lens numpy int32 [slots]
+    (advanced in place); meta_dev device int32 [slots + 2B].  Returns n_free.
+    """
+    import torch
+    L = len(q)
+    B = q[0].shape[0]
+    _np_i32(bt_host, "bt_host", writable=True)
+    _np_i32(free_list, "free_list", writable=True)
+    _np_i32(cached_lens, "cached_lens", writable=True)
+    if bt_host.ndim != 3 or not bt_host.flags.c_contiguous or bt_host.shape[1] != L:
+        raise ValueError("bt_host must be a contiguous [slots, layers, max_blocks] array")
+    if not bt_dev.is_contiguous() or tuple(bt_dev.shape) != bt_host.shape or bt_dev.dtype != torch.int32:
+        raise ValueError("bt_dev must be the contiguous device copy of bt_host")
+    slots, _, mb = bt_host.shape
+    sid = np.ascontiguousarray(slot_ids, dtype=np.int32)
+    if len(sid) != B or meta_dev.numel() != slots + 2 * B or not meta_dev.is_contiguous():
+        raise ValueError("meta_dev must be int32 [slots + 2 * batch]")
+    if len(cached_lens) != slots or not 0 <= n_free <= len(free_list):
+        raise ValueError("cached_lens / n_free inconsistent")
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _contig(t, n)
+    ptrs = []
+    for arr, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if len(arr) != L:
+            raise ValueError(f"{name} needs one tensor per layer")
+        for t in arr:
+            _contig(t, name)
+        ptrs.append((C.c_void_p * L)(*[_dev_ptr(t, name, _bf16_types()) for t in arr]))
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _contig(workspace, "workspace")
+        ws_ptr = _dev_ptr(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    nf = C.c_int(n_free)
+    _check("pkv_decode_step", load().pkv_decode_step(
+        L, ptrs[0], ptrs[1], ptrs[2], ptrs[3], _dev_ptr(k_pool, "k_pool", _bf16_types()),
+        _dev_ptr(v_pool, "v_pool", _bf16_types()), k_pool.shape[0], bt_host.ctypes.data,
+        _dev_ptr(bt_dev, "bt_dev"), slots, mb, free_list.ctypes.data, C.byref(nf), cached_lens.ctypes.data,
+        _dev_ptr(meta_dev, "meta_dev", (torch.int32,)), sid.ctypes.data, B, q[0].shape[1], k_pool.shape[2],
+        q[0].shape[2], _dev_ptr(cos_sin, "cos_sin", (torch.float32,)), cos_sin.shape[0], float(scale),
+        max_context_len, partition_size, ws_ptr, ws_bytes, _stream(stream)))
+    return nf.value

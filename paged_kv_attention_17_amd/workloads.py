@@ -94,6 +94,7 @@ class DecodeWorkload:
     free_list: np.ndarray
     scale: float
     seed: int
+    n_blocks: int = 0
 
     @property
     def n_layers(self) -> int:
@@ -105,7 +106,7 @@ class DecodeWorkload:
 
     @property
     def num_blocks(self) -> int:
-        return self.k_pool.shape[0]
+        return self.n_blocks if self.k_pool is None else self.k_pool.shape[0]
 
     @property
     def max_blocks(self) -> int:
@@ -216,7 +217,7 @@ def make_decode(seed: int, context_lens, n_layers: int = 1, num_blocks: int | No
     else:
         v_new = uniform_bf16(rng, (n_layers, n_slots, n_kv, d), -1.0, 1.0)
     return DecodeWorkload(k_pool, v_pool, bt, ctx, slot_ids, q_new, k_new, v_new, free,
-                          scale=1.0 / math.sqrt(d), seed=seed)
+                          scale=1.0 / math.sqrt(d), seed=seed, n_blocks=num_blocks)
 
 
 def spike_keys(rng, k_pool, bt, n_cached, per_seq: int, factor: float):

@@ -94,7 +94,7 @@ def test_empty_context_gives_zero_row(gpu):
     rng = np.random.default_rng(3)
     q = W.randn_bf16(rng, (2, 32, 64))
     kp, vp = W.randn_bf16(rng, (4, 16, 8, 64)), W.randn_bf16(rng, (4, 16, 8, 64))
-    got = run_decode(q, kp, vp, np.array([[1, 2], [3, -1]], np.int32), None, [0, 20], max_ctx=20)
+    got = run_decode(q, kp, vp, np.array([[-1, -1], [1, 2]], np.int32), None, [0, 20], max_ctx=20)
     assert not got[0].any()
     ref = attention.decode(q[1:], kp, vp, np.array([[1, 2]], np.int32), [0], [20], 0.125)
     check_attention(got[1:], ref, "row after empty")
