@@ -6,15 +6,16 @@ Workload: B=64 sequences, 16 layers, contexts uniform in [512, 4096], 32 query
 needed with tables interleaved round-robin over (layer, sequence).  One step
 = one decode step of all 16 layers through the native pkv_decode_step: host
 block allocation, then per layer RoPE on the new q/k, KV append and paged
-attention (split-context partitions + merge).  Inputs are seeded synthetic
+attention (split-context partitions merged in the same launch), fused into
+one kernel per layer.  Inputs are seeded synthetic
 data resident in HBM before timing starts; contexts grow by one token per
 step as in a real decode loop.
 
 Prints ONE JSON line:
   value        KV GB/s over the whole step = algorithmic KV bytes of all
                layers / step wall time (2,048 B per context token per layer)
-  roofline     the attention kernel alone: algorithmic bytes per launch /
-               its mean launch duration (HIP events on its stream)
+  roofline     the per-layer decode kernel alone: algorithmic bytes per
+               launch / its mean launch duration (HIP events on its stream)
   cpu_baseline the float64 CPU oracle on a bounded sample of the same step
 """
 from __future__ import annotations
@@ -184,18 +185,19 @@ def main():
     log(f"step: {t_step * 1e6:.1f} us ({t_step * 1e6 / L:.2f} us/layer), KV {value:.0f} GB/s, "
         f"host wall {wall / args.steps * 1e6:.1f} us/step")
 
-    # ---- dominant kernel: attention alone, events around every launch ------
+    # ---- dominant kernel: the fused per-layer decode kernel alone, events ---
+    # around every launch (it re-appends the last step's token in place, so
+    # the cache does not change)
     ctx_now = eng.cached.copy()
     bytes_per_launch = int(ctx_now.sum()) * KV_BYTES_PER_TOKEN
-    sid_dev = eng.meta[eng.n_slots + w.batch:eng.n_slots + 2 * w.batch]
     pairs = []
     for it in range(args.attn_iters + 1):
         for layer in range(L):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            pkv.pkv_paged_attn_decode(out[layer], q[layer], kp, vp, eng.bt_dev[:, layer, :], sid_dev, eng.ctx_dev,
-                                      eng.max_context_len, eng.scale, eng.partition_size, eng.workspace,
-                                      stream=stream)
+            pkv.pkv_paged_decode_fused(out[layer], q[layer], k[layer], v[layer], kp, vp, eng.bt_dev[:, layer, :],
+                                       None, eng.ctx_dev, eng.max_context_len, eng.cos_sin, eng.scale,
+                                       eng.partition_size, eng.workspace, stream=stream, row_lens_host=ctx_now)
             e1.record(stream)
             if it > 0:                      # first pass is a warm-up
                 pairs.append((e0, e1))
@@ -238,7 +240,8 @@ def main():
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "pkv_paged_attn_decode", "bytes_per_launch": bytes_per_launch,
+                     "kernel": "pkv_paged_decode_fused (decode_kernel<4, fused>)",
+                     "bytes_per_launch": bytes_per_launch,
                      "us_per_launch": round(t_attn * 1e6, 3), "source_hash": src_hash},
         "copy_kernel_GBps": round(copy_gbs, 1),
         "cpu_baseline": cpu,

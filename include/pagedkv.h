@@ -176,16 +176,24 @@ int pkv_check_block_table(const int32_t* bt_host, int64_t bt_row_stride, int num
  * identity) and n = context_lens[s] (the length includes the token appended
  * this step), query head h with KV head g:
  *     out[b][h] = sum_j softmax_j(scale * <q[b][h], K_j,g>) V_j,g ,  j < n
- * bf16 inputs, float32 accumulation, bf16 output (nearest-even); n == 0 gives a
- * zero row.  Long contexts are split into partitions of partition_size tokens
- * whose partial (max, sum, unnormalised output) are merged by a second kernel.
+ * bf16 inputs, float32 accumulation (the softmax weights are rounded to bf16
+ * before they multiply V and before they are summed), bf16 output
+ * (nearest-even); n == 0 gives a zero row.  Long contexts are split into
+ * partitions of partition_size tokens whose partial (max, sum, unnormalised
+ * output) a second, small kernel merges.
+ * scale must be positive and finite.
  * ------------------------------------------------------------------------ */
 
-/* Bytes of workspace pkv_paged_attn_decode needs for these sizes
- * (0 when no sequence can need more than one partition). partition_size 0 =
- * the automatic choice, which depends only on the arguments given here. */
+/* Bytes of workspace the decode calls need for these sizes (0 when no
+ * sequence can need more than one partition). partition_size 0 = the
+ * automatic choice, which depends only on the arguments given here. */
 size_t pkv_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
                                   int max_context_len, int partition_size);
+
+/* Zero a decode workspace (a kernel on `stream`, no memset node).  Optional:
+ * the decode calls need no particular initial contents; provided so that a
+ * workspace never holds stale data from other users. */
+int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* The partition size the automatic choice picks for these sizes. */
 int pkv_decode_partition_size(int batch, int n_kv_heads, int max_context_len);
@@ -193,16 +201,43 @@ int pkv_decode_partition_size(int batch, int n_kv_heads, int max_context_len);
 /* max_context_len: host-known upper bound of the lengths (sizes the grid);
  * a longer context is still handled correctly, by the last partition, only
  * slower. Contexts are clipped to max_blocks_per_seq * 16.
+ * row_lens_host: optional HOST copy of each batch row's length
+ * (context_lens[slot_ids[b]]), batch <= 256.  When given, only the partitions
+ * that exist are launched, longest first; the kernels still take their lengths
+ * from context_lens, and the two must agree (otherwise the result is
+ * unspecified).  NULL launches the max_context_len grid.
  * partition_size: 0 = automatic, else a positive multiple of 16.
- * workspace: device memory of at least pkv_decode_workspace_bytes(...) bytes
- * (may be NULL when that is 0); its contents need no initialisation. */
+ * workspace: at least pkv_decode_workspace_bytes(...) bytes of device memory,
+ * any contents; may be NULL when that size is 0.  Calls sharing one workspace
+ * must not run concurrently. */
 int pkv_paged_attn_decode(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_pool,
                           const pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
                           int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,
-                          const int32_t* slot_ids, const int32_t* context_lens, int batch,
-                          int max_context_len, int n_q_heads, int n_kv_heads, int head_dim,
-                          float scale, int partition_size, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          const int32_t* slot_ids, const int32_t* context_lens,
+                          const int32_t* row_lens_host, int batch, int max_context_len,
+                          int n_q_heads, int n_kv_heads, int head_dim, float scale,
+                          int partition_size, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* The decode step of one layer in one launch: RoPE + KV append + attention.
+ * For batch row b (s = slot_ids[b], n = context_lens[s], new token at
+ * p = n - 1): q[b] and k_new[b] are rotated by position p exactly as
+ * pkv_rope_decode would (in registers; q and k_new are not modified), the
+ * rotated key and v_new[b] are written into pool row p of table row s (the
+ * table entry must already hold a block; pkv_blocks_assign), and out[b] is the
+ * attention of the rotated query over tokens 0 .. p, the new one included.
+ * Same cache contents (bit for bit) and, up to float32 summation order, the
+ * same outputs as pkv_rope_decode + pkv_paged_kv_append + pkv_paged_attn_decode.
+ * k_new, v_new: [batch][n_kv_heads][64]; cos_sin: pkv_rope_table_init's table. */
+int pkv_paged_decode_fused(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_new,
+                           const pkv_bf16* v_new, pkv_bf16* k_pool, pkv_bf16* v_pool,
+                           int num_blocks, const int32_t* block_table, int64_t bt_row_stride,
+                           int num_slots, int max_blocks_per_seq, const int32_t* slot_ids,
+                           const int32_t* context_lens, const int32_t* row_lens_host, int batch,
+                           int max_context_len, int n_q_heads, int n_kv_heads, int head_dim,
+                           const float* cos_sin,
+                           int max_pos, float scale, int partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * Chunked causal prefill.  Source: "The path of one inference", closing
@@ -234,11 +269,11 @@ int pkv_paged_attn_prefill(pkv_bf16* out, const pkv_bf16* q, const int32_t* cu_q
  *   2. cached_lens_host[s] += 1; the new table entries go to bt_dev and the
  *      context lengths, positions and slot ids to meta_dev, carried in kernel
  *      arguments (no host buffer is read after the call returns);
- *   3. per layer l: pkv_rope_decode(q[l], k[l]), pkv_paged_kv_append(k[l], v[l]),
- *      pkv_paged_attn_decode(out[l], q[l]) over the layer's table view.
+ *   3. per layer l: pkv_paged_decode_fused(out[l], q[l], k[l], v[l]) over the
+ *      layer's table view (one launch per layer).
  * q, k, v, out are HOST arrays of n_layers DEVICE pointers ([batch][n_q][64],
- * [batch][n_kv][64], [batch][n_kv][64], [batch][n_q][64]); q and k are rotated
- * in place.  bt_host / bt_dev: [num_slots][n_layers][max_blocks_per_seq] int32,
+ * [batch][n_kv][64], [batch][n_kv][64], [batch][n_q][64]); q and k are not
+ * modified.  bt_host / bt_dev: [num_slots][n_layers][max_blocks_per_seq] int32,
  * the device copy mirroring the host one.  meta_dev: device int32
  * [num_slots + 2 * batch] = context lengths (per slot) | positions | slot ids,
  * written by this call; its context-length part must hold cached_lens_host

@@ -48,10 +48,13 @@ SIGNATURES = {
     "pkv_check_block_table": (_i, [_p, _i64, _i, _i, _p, _p, _i, _i, _ip, _ip]),
     "pkv_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "pkv_decode_partition_size": (_i, [_i, _i, _i]),
-    "pkv_paged_attn_decode": (_i, [_p, _p, _p, _p, _i, _p, _i64, _i, _i, _p, _p, _i, _i, _i, _i, _i, _f, _i,
+    "pkv_paged_attn_decode": (_i, [_p, _p, _p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i,
                                    _p, _sz, _p]),
     "pkv_paged_attn_prefill": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _p, _i64, _i, _i, _i, _i, _i, _i, _i, _i,
                                     _f, _p]),
+    "pkv_decode_workspace_init": (_i, [_p, _sz, _p]),
+    "pkv_paged_decode_fused": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _p,
+                                    _i, _f, _i, _p, _sz, _p]),
     "pkv_decode_step": (_i, [_i, _p, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _p, _ip, _p, _p, _p, _i, _i, _i, _i,
                              _p, _i, _f, _i, _i, _p, _sz, _p]),
 }
@@ -297,10 +300,72 @@ def pkv_decode_partition_size(batch, n_kv_heads, max_context_len):
     return load().pkv_decode_partition_size(batch, n_kv_heads, max_context_len)
 
 
+def pkv_decode_workspace_init(workspace, stream=None):
+    """Zero a decode workspace (uint8 device tensor) before its first use."""
+    _contig(workspace, "workspace")
+    _check("pkv_decode_workspace_init", load().pkv_decode_workspace_init(
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def decode_workspace(batch, n_q_heads, n_kv_heads, max_context_len, partition_size=0, device="cuda", stream=None):
+    """Allocate and zero a decode workspace of the size the library asks for."""
+    import torch
+    n = pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, 64, max_context_len, partition_size)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    pkv_decode_workspace_init(ws, stream=stream)
+    return ws
+
+
+def _row_lens(row_lens_host, B):
+    if row_lens_host is None:
+        return None, None
+    a = np.ascontiguousarray(row_lens_host, dtype=np.int32)
+    if a.shape != (B,):
+        raise ValueError("row_lens_host must hold one length per batch row")
+    return a, a.ctypes.data
+
+
+def pkv_paged_decode_fused(out, q, k_new, v_new, k_pool, v_pool, block_table, slot_ids, context_lens,
+                           max_context_len, cos_sin, scale, partition_size=0, workspace=None, stream=None,
+                           row_lens_host=None):
+    """RoPE + append + attention for one layer in one launch (q, k_new, v_new not modified).
+    row_lens_host: optional numpy copy of each batch row's length (enables the compact schedule)."""
+    import torch
+    for t, n in ((out, "out"), (q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool"),
+                 (slot_ids, "slot_ids"), (context_lens, "context_lens"), (workspace, "workspace"),
+                 (cos_sin, "cos_sin")):
+        _contig(t, n)
+    B, n_q, d = q.shape
+    if out.shape != q.shape or k_pool.shape != v_pool.shape or k_new.shape != v_new.shape:
+        raise ValueError("shape mismatch")
+    if k_new.shape[0] != B or k_new.shape[1] != k_pool.shape[2]:
+        raise ValueError("k_new must be [batch, n_kv, 64]")
+    bt, stride, rows, mb = _table(block_table)
+    if context_lens.shape[0] < rows:
+        raise ValueError("context_lens must have an entry per table row")
+    if slot_ids is not None and slot_ids.shape[0] != B:
+        raise ValueError("slot_ids must have one entry per batch row")
+    if slot_ids is None and B > rows:
+        raise ValueError("batch larger than the table without slot_ids")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev_ptr(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    keep, rl = _row_lens(row_lens_host, B)
+    _check("pkv_paged_decode_fused", load().pkv_paged_decode_fused(
+        _dev_ptr(out, "out", _bf16_types()), _dev_ptr(q, "q", _bf16_types()),
+        _dev_ptr(k_new, "k_new", _bf16_types()), _dev_ptr(v_new, "v_new", _bf16_types()),
+        _dev_ptr(k_pool, "k_pool", _bf16_types()), _dev_ptr(v_pool, "v_pool", _bf16_types()), k_pool.shape[0],
+        bt, stride, rows, mb, _dev_ptr(slot_ids, "slot_ids", (torch.int32,)),
+        _dev_ptr(context_lens, "context_lens", (torch.int32,)), rl, B, max_context_len, n_q, k_pool.shape[2], d,
+        _dev_ptr(cos_sin, "cos_sin", (torch.float32,)), cos_sin.shape[0], float(scale), partition_size, ws_ptr,
+        ws_bytes, _stream(stream)))
+
+
 def pkv_paged_attn_decode(out, q, k_pool, v_pool, block_table, slot_ids, context_lens, max_context_len,
-                          scale, partition_size=0, workspace=None, stream=None):
+                          scale, partition_size=0, workspace=None, stream=None, row_lens_host=None):
     """out/q [B, n_q, 64]; pools [NB, 16, n_kv, 64]; block_table [rows, max_blocks] (row-strided view ok);
-    slot_ids [B] int32 or None; context_lens [rows] int32; workspace: uint8 tensor or None."""
+    slot_ids [B] int32 or None; context_lens [rows] int32; workspace: zeroed uint8 tensor or None."""
     import torch
     for t, n in ((out, "out"), (q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool"), (slot_ids, "slot_ids"),
                  (context_lens, "context_lens"), (workspace, "workspace")):
@@ -320,11 +385,12 @@ def pkv_paged_attn_decode(out, q, k_pool, v_pool, block_table, slot_ids, context
     if workspace is not None:
         ws_ptr = _dev_ptr(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
+    keep, rl = _row_lens(row_lens_host, B)
     _check("pkv_paged_attn_decode", load().pkv_paged_attn_decode(
         _dev_ptr(out, "out", _bf16_types()), _dev_ptr(q, "q", _bf16_types()),
         _dev_ptr(k_pool, "k_pool", _bf16_types()), _dev_ptr(v_pool, "v_pool", _bf16_types()), k_pool.shape[0],
         bt, stride, rows, mb, _dev_ptr(slot_ids, "slot_ids", (torch.int32,)),
-        _dev_ptr(context_lens, "context_lens", (torch.int32,)), B, max_context_len, n_q, k_pool.shape[2], d,
+        _dev_ptr(context_lens, "context_lens", (torch.int32,)), rl, B, max_context_len, n_q, k_pool.shape[2], d,
         float(scale), partition_size, ws_ptr, ws_bytes, _stream(stream)))
 
 

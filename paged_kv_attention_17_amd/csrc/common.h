@@ -68,6 +68,33 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Raw buffer access: a scalar descriptor (base, size) and a per-lane 32-bit
+// byte offset, so address arithmetic stays on the scalar unit.  Offsets at or
+// beyond `bytes` read as zero instead of touching memory.  Word 3 is the gfx9
+// family value for untyped dword access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
+// Byte permute: result byte k = byte sel[k] of the 8-byte value (hi:lo).
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// (lo.bf16[0], hi.bf16[0]) and (lo.bf16[1], hi.bf16[1]) of two packed dwords.
+__device__ __forceinline__ uint32_t pack_lo_halves(uint32_t lo, uint32_t hi) { return perm_b32(hi, lo, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi_halves(uint32_t lo, uint32_t hi) { return perm_b32(hi, lo, 0x07060302u); }
+
+// The two halves of a RoPE rotation of the pair (x, y) = (dim i, dim i + d/2)
+// by an angle with cosine c and sine s.  Written with explicit fused
+// multiply-adds so every kernel that rotates rounds identically.
+__device__ __forceinline__ float rope_first(float x, float y, float c, float s) { return __builtin_fmaf(x, c, -(y * s)); }
+__device__ __forceinline__ float rope_second(float x, float y, float c, float s) { return __builtin_fmaf(y, c, x * s); }
+
 // ------------------------------------------------------------------ host --
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -1,5 +1,5 @@
-// Paged single-query (decode) attention for gfx950: split-context partitions
-// plus a merge kernel.
+// Paged single-query (decode) attention for gfx950, optionally fused with the
+// step's RoPE and KV append.
 //
 // Source: the Korean page of "An Inference Engine in 1,500 Lines of CUDA: The
 // Map" ("What is in the box" table: online softmax and PagedAttention inside
@@ -9,247 +9,431 @@
 // title (each decode step re-reads every cached K/V of the sequence through the
 // block table).
 //
-// What one workgroup does.  A workgroup of kWaves wave64s owns one
-// (sequence, KV head, context partition) and serves all G query heads that
-// share the KV head, so each K/V byte is fetched from HBM once for G queries.
-// The waves take the partition's 16-token blocks round-robin.  Inside a wave,
-// lane = 8 * r + c: c picks 8 of the 64 dims (one 16-byte chunk), r picks rows
-// r and r + 8 of the block, so one dwordx4 load per lane covers 8 token rows of
-// 128 contiguous bytes (the pool layout [block][16][kv head][64] keeps a head's
-// row contiguous).  Scores use the bf16 dot2 instruction (no widening of K);
-// the 8 partial dots of a row are summed with three DPP steps.  Every lane
-// keeps its own running (max, sum, 8 output dims) per query head over the rows
-// it saw; rows are merged at the end: across r with lane exchanges, across
-// waves through LDS.  Scores are kept in log2 units (scale * log2 e folded in)
-// so the exponentials are single v_exp_f32.  Masked rows (past the context) are
-// removed by selects, never by multiplying, so NaN in unused slots cannot leak.
+// Work split.  A workgroup of 4 wave64s owns one (sequence, KV head, context
+// partition) and serves all G query heads that share the KV head, so each K/V
+// byte leaves HBM once for G queries.  The workgroups of one (sequence,
+// partition) are placed on one XCD (see decode_item).  The waves take the partition's 16-token
+// blocks round-robin, two blocks in flight per wave (unconditional, clamped
+// loads into two register sets, so the compiler can wait for exactly the older
+// set).  A partition's block ids are read once into a VGPR (lane i = block i)
+// and picked with v_readlane, so no scalar load sits in the loop.
 //
-// A sequence whose context fits one partition is finished in place (output
-// written as bf16); otherwise each partition leaves (max, sum, unnormalised
-// output) in the workspace and decode_merge_kernel combines them.
+// Lane layout inside a wave: lane = 8 r + c.  c picks dims 8c..8c+7 (one
+// 16-byte chunk), r picks rows r and r + 8 of the block.  One dwordx4 load per
+// lane covers rows r of all lanes = 8 contiguous 128-byte head rows of the pool
+// layout [block][16][kv head][64].
+//   scores   s = q . k with v_dot2_f32_bf16 (bf16 pairs, float32 sum): 4 per
+//            (row, head), then a 3-step DPP sum over the 8 lanes of the row;
+//   softmax  one running max per head shared by the whole wave, raised only
+//            when some score exceeds it by more than 8 (log2 units), so the
+//            rescale of the accumulators is rare; p = 2^(s*scale*log2e - m);
+//   p . V    p of rows r and r+8 packed as a bf16 pair, V of the same rows
+//            packed per dim with v_perm_b32, one v_dot2_f32_bf16 per
+//            (head, dim): float32 accumulation of bf16 products;
+//   sum      l accumulates the same bf16 p values as the numerator (dot2 with
+//            (1, 1)), so numerator and denominator see identical weights.
+// Rows past the context (or in a block whose id is out of range) are removed
+// by selects on the scores and on V, never by multiplying, so NaN in unused
+// pool slots cannot reach the output.
+//
+// Merge.  The 8 row groups of a wave are summed pairwise with DPP and the rest
+// through LDS together with the other waves (each wave carries its own max).
+// A context that fits one partition is finished in place.  Otherwise every
+// partition stores (max, sum, unnormalised output) in the workspace and a
+// second, small kernel merges them (the kernel boundary orders the memory
+// traffic; merging inside the first kernel would need an agent-scope release
+// per workgroup, an L2 write-back on this chip, which costs far more).
+//
+// Fused variant (the decode step).  The query and the new token's key are
+// rotated in registers from the RoPE table (same arithmetic as the RoPE
+// kernel), the new token (position context_len - 1) takes part in the
+// attention from registers, and the workgroup of the last partition writes the
+// rotated key and the value into their pool row at the end of the kernel.
 #include "common.h"
 
 namespace pkv {
 
 constexpr int kWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;   // running-max start value (finite: no inf - inf)
+constexpr float kNegBig = -1.0e30f;   // running-max start (finite, so no inf - inf)
+constexpr float kTau = 8.0f;          // lazy rescale threshold, log2 units
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
+constexpr int kMaxPlanSeqs = 256;     // batch rows a host schedule can describe
 
 struct DecodeArgs {
   uint16_t* out;
   const uint16_t* q;
-  const uint16_t* k_pool;
-  const uint16_t* v_pool;
+  const uint16_t* k_new;       // fused: new keys (before RoPE) [B][n_kv][64]
+  const uint16_t* v_new;       // fused: new values [B][n_kv][64]
+  uint16_t* k_pool;
+  uint16_t* v_pool;
   const int32_t* bt;
   const int32_t* slot_ids;
   const int32_t* ctx_lens;
-  float* ws_ml;   // [B][n_q][P][2]  running max (log2 units) and sum per partition
-  float* ws_o;    // [B][n_q][P][64] unnormalised output per partition
+  const float2* rope;          // fused: cos/sin table [max_pos][32]
+  float* ws_o;                 // [B][n_kv][P][G][64] unnormalised partial outputs
+  float* ws_ml;                // [B][n_kv][P][G][2]  partial (max, sum)
   int64_t bt_stride;
   int num_blocks;
   int num_slots;
   int max_blocks;
   int n_q;
   int n_kv;
-  int P;          // partitions in the grid
-  int ps;         // tokens per partition (multiple of 16)
+  int P;                       // partitions in the grid
+  int ps;                      // tokens per partition (multiple of 16)
+  int max_pos;
+  int batch;
   float scale_log2e;
+  // Host schedule (plan_seqs > 0): items [0, full_items) are the partitions
+  // that are not a sequence's last one, row b owning items plan_pre[b] ..
+  // plan_pre[b+1]-1 (partition = item - plan_pre[b]); items full_items + j are
+  // the last partitions, longest first: plan_last[j] = (partition << 16) | row.
+  int plan_seqs;
+  int full_items;
+  int n_items;
+  int32_t plan_pre[kMaxPlanSeqs + 1];
+  int32_t plan_last[kMaxPlanSeqs];
 };
 
-// Context length of batch row b after clipping to the table, and the number of
-// partitions that hold tokens of it (the last one runs to the end).
 __device__ __forceinline__ void seq_extent(const DecodeArgs& a, int b, int& slot, int& n, int& nparts) {
   slot = a.slot_ids ? a.slot_ids[b] : b;
   n = 0;
-  if (slot >= 0 && slot < a.num_slots) {
+  if (slot >= 0 && slot < a.num_slots && a.num_blocks > 0) {
     n = a.ctx_lens[slot];
     n = n < 0 ? 0 : n;
     n = n > a.max_blocks * kBlock ? a.max_blocks * kBlock : n;
+  } else {
+    slot = 0;
   }
   nparts = (n + a.ps - 1) / a.ps;
   nparts = nparts > a.P ? a.P : nparts;
 }
 
-template <int G>
-__global__ __launch_bounds__(kWaves * kWave) void decode_partition_kernel(DecodeArgs a) {
-  const int kvh = blockIdx.x;
-  const int part = blockIdx.y;
-  const int b = blockIdx.z;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = wave_uniform(threadIdx.x >> 6);
+struct KVRegs {
+  uint4 k0, k1, v0, v1;        // rows r and r + 8 of one block, this lane's 8 dims
+};
+
+// Element-wise select (keeps the four dwords in registers).
+__device__ __forceinline__ uint4 sel4(bool t, uint4 a, uint4 b) {
+  return make_uint4(t ? a.x : b.x, t ? a.y : b.y, t ? a.z : b.z, t ? a.w : b.w);
+}
+
+// Maximum over the wave; rows repeat across the 8 lanes of a row group.
+__device__ __forceinline__ float wave_max_rows(float x) {
+  x = fmaxf(x, dpp<kDppRowRor8>(x));
+  x = fmaxf(x, shfl_xor(x, 16));
+  x = fmaxf(x, shfl_xor(x, 32));
+  return x;
+}
+
+// Rotate this lane's 8 dims (chunk c) of a 64-dim head vector in place.  The
+// pair partner of dim i < 32 is dim i + 32, held by lane c ^ 4 of the row group.
+__device__ __forceinline__ uint4 rope_chunk(uint4 v, const float2* cs, int c) {
+  uint4 pv;
+  pv.x = (uint32_t)__builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 4) << 2, (int)v.x);
+  pv.y = (uint32_t)__builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 4) << 2, (int)v.y);
+  pv.z = (uint32_t)__builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 4) << 2, (int)v.z);
+  pv.w = (uint32_t)__builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 4) << 2, (int)v.w);
+  const uint32_t own[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t oth[4] = {pv.x, pv.y, pv.z, pv.w};
+  uint32_t res[4];
+  const bool first_half = c < 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float r[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float mine = e ? bf16_hi(own[j]) : bf16_lo(own[j]);
+      const float other = e ? bf16_hi(oth[j]) : bf16_lo(oth[j]);
+      const float2 t = cs[2 * j + e];
+      r[e] = first_half ? rope_first(mine, other, t.x, t.y) : rope_second(other, mine, t.x, t.y);
+    }
+    res[j] = pack_bf16x2(r[0], r[1]);
+  }
+  return make_uint4(res[0], res[1], res[2], res[3]);
+}
+
+// Workgroup id -> (KV head, partition, sequence).  Workgroups are handed to the
+// 8 XCDs round-robin by linear id, so ids are arranged in groups of 8 items
+// (item = sequence * P + partition) x n_kv heads with the item's low 3 bits in
+// the id's low 3 bits: all KV heads of an item run on the same XCD at about the
+// same time and fetch the 128-byte head rows of each 1 KB token row together.
+// (One XCD per head instead costs about 15% of HBM bandwidth on this layout.)
+// Without a host schedule, item = sequence * P + partition over the grid that
+// max_context_len implies (items past a sequence's length exit at once); with
+// one, only real partitions are launched, longest first.
+__device__ __forceinline__ bool decode_item(const DecodeArgs& a, int batch, int& kvh, int& part, int& b) {
+  const int id = blockIdx.x;
+  const int grp = id / (8 * a.n_kv);
+  const int in = id - grp * 8 * a.n_kv;
+  kvh = in >> 3;
+  const int item = grp * 8 + (in & 7);
+  if (a.plan_seqs > 0) {
+    if (item >= a.n_items) return false;
+    if (item < a.full_items) {
+      int lo = 0, hi = a.plan_seqs;            // plan_pre[lo] <= item < plan_pre[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.plan_pre[mid] <= item) lo = mid; else hi = mid;
+      }
+      b = lo;
+      part = item - a.plan_pre[lo];
+    } else {
+      const int packed = a.plan_last[item - a.full_items];
+      b = packed & 0xffff;
+      part = packed >> 16;
+    }
+    return b < batch;
+  }
+  b = item / a.P;
+  part = item - b * a.P;
+  return b < batch;
+}
+
+template <int G, bool FUSED>
+__global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
+  int kvh, part, b;
+  if (!decode_item(a, a.batch, kvh, part, b)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = wave_uniform(tid >> 6);
   const int c = lane & 7;
   const int r = lane >> 3;
 
-  int slot, n, nparts;
-  seq_extent(a, b, slot, n, nparts);
+  // Prologue.  The table slice of this partition is fetched in parallel with
+  // the context length (both need only the slot) so that the first K/V loads
+  // wait for two memory round trips, not three.
+  int slot = a.slot_ids ? a.slot_ids[b] : b;
+  const bool slot_ok = slot >= 0 && slot < a.num_slots && a.num_blocks > 0;
+  slot = slot_ok ? slot : 0;
+  const int32_t* btrow = a.bt + (int64_t)slot * a.bt_stride;
+  const int jb_begin = part * (a.ps / kBlock);
+  const int spec_idx = jb_begin + lane;
+  int tab0 = spec_idx < a.max_blocks ? btrow[spec_idx] : -1;
+  int n = slot_ok ? a.ctx_lens[slot] : 0;
+  n = n < 0 ? 0 : (n > a.max_blocks * kBlock ? a.max_blocks * kBlock : n);
+  int nparts = (n + a.ps - 1) / a.ps;
+  nparts = nparts > a.P ? a.P : nparts;
   if (part >= (nparts > 0 ? nparts : 1)) return;   // partition 0 always runs (zero row for n == 0)
   const int t_begin = part * a.ps;
   const int t_end = (part == nparts - 1) ? n : (nparts == 0 ? 0 : t_begin + a.ps);
+  const int64_t row_elems = (int64_t)a.n_kv * kHeadDim;
 
-  // q chunk for each of the G heads: 8 bf16 = 4 packed dwords.
+  // This lane's chunk of the G query heads (rotated here when fused).
   uint4 qv[G];
 #pragma unroll
   for (int h = 0; h < G; ++h)
     qv[h] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.n_q + kvh * G + h) * kHeadDim + c * 8);
+  const int pos_new = n - 1;              // the token appended this step (fused)
+  uint4 knew = make_uint4(0, 0, 0, 0), vnew = knew;
+  if constexpr (FUSED) {
+    if (n > 0) {
+      knew = *reinterpret_cast<const uint4*>(a.k_new + ((int64_t)b * a.n_kv + kvh) * kHeadDim + c * 8);
+      vnew = *reinterpret_cast<const uint4*>(a.v_new + ((int64_t)b * a.n_kv + kvh) * kHeadDim + c * 8);
+      if (pos_new < a.max_pos) {
+        float2 cs[8];
+        const float2* trow = a.rope + (int64_t)pos_new * (kHeadDim / 2) + (c & 3) * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cs[j] = trow[j];
+#pragma unroll
+        for (int h = 0; h < G; ++h) qv[h] = rope_chunk(qv[h], cs, c);
+        knew = rope_chunk(knew, cs, c);
+      }
+    }
+  }
 
-  float m[G], l[G], o[G][8];
+  float m[G], thr[G], l[G], o[G][8];
+  const float C = a.scale_log2e;
+  const float invC = 1.0f / C;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = kNegBig;
+    thr[h] = -INFINITY;        // raw-score level above which m must be raised
     l[h] = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
   }
 
-  const int jb_begin = t_begin / kBlock;
-  const int jb_end = (t_end + kBlock - 1) / kBlock;
-  const int64_t row_elems = (int64_t)a.n_kv * kHeadDim;          // elements between token rows
-  const int32_t* btrow = a.bt + (int64_t)slot * a.bt_stride;
-  const int64_t lane_off = (int64_t)r * row_elems + kvh * kHeadDim + c * 8;
-  const int64_t block_elems = (int64_t)kBlock * row_elems;
-
-  auto block_base = [&](int jb) -> int64_t {
-    int blk = wave_uniform(btrow[jb]);
-    blk = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
-    return blk < 0 ? -1 : (int64_t)blk * block_elems;
-  };
-
-  int jb = jb_begin + w;
-  uint4 k0 = make_uint4(0, 0, 0, 0), k1 = k0, v0 = k0, v1 = k0;
-  int64_t base = -1;
-  if (jb < jb_end) {
-    base = block_base(jb);
-    if (base >= 0) {
-      const uint16_t* kp = a.k_pool + base + lane_off;
-      const uint16_t* vp = a.v_pool + base + lane_off;
-      k0 = *reinterpret_cast<const uint4*>(kp);
-      k1 = *reinterpret_cast<const uint4*>(kp + 8 * row_elems);
-      v0 = *reinterpret_cast<const uint4*>(vp);
-      v1 = *reinterpret_cast<const uint4*>(vp + 8 * row_elems);
-    }
-  }
-
-  for (; jb < jb_end; jb += kWaves) {
-    // Issue the next block's loads before working on this one.
-    const int jn = jb + kWaves;
-    uint4 nk0 = make_uint4(0, 0, 0, 0), nk1 = nk0, nv0 = nk0, nv1 = nk0;
-    int64_t nbase = -1;
-    if (jn < jb_end) {
-      nbase = block_base(jn);
-      if (nbase >= 0) {
-        const uint16_t* kp = a.k_pool + nbase + lane_off;
-        const uint16_t* vp = a.v_pool + nbase + lane_off;
-        nk0 = *reinterpret_cast<const uint4*>(kp);
-        nk1 = *reinterpret_cast<const uint4*>(kp + 8 * row_elems);
-        nv0 = *reinterpret_cast<const uint4*>(vp);
-        nv1 = *reinterpret_cast<const uint4*>(vp + 8 * row_elems);
+  // Raise the wave's running max to cover raw scores s0/s1 (rare: only when
+  // some score exceeds the current max by more than kTau in log2 units).
+  auto rescale_if_needed = [&](const float (&s0)[G], const float (&s1)[G]) {
+    bool need = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) need |= (s0[h] > thr[h]) | (s1[h] > thr[h]);
+    if (__any(need)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mx = fmaxf(s0[h], s1[h]) * C;
+        const float mn = fmaxf(m[h], wave_max_rows(mx));
+        const float alpha = fast_exp2(m[h] - mn);
+        l[h] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[h][j] *= alpha;
+        m[h] = mn;
+        thr[h] = (mn + kTau) * invC;
       }
     }
+  };
 
-    if (base >= 0) {
-      const int tok0 = jb * kBlock + r;
-      const bool ok0 = tok0 < t_end;
-      const bool ok1 = tok0 + 8 < t_end;
+  // In the fused step the new token's pool row is not read: it joins from
+  // registers after the loop.
+  const int t_loop_end = (FUSED && part == nparts - 1 && n > 0) ? n - 1 : t_end;
+  const int nb = (t_loop_end + kBlock - 1) / kBlock - jb_begin;
+  const uint32_t block_bytes = (uint32_t)(kBlock * row_elems * 2);
+  const uint32_t lane_off = (uint32_t)(((int64_t)r * row_elems + kvh * kHeadDim + c * 8) * 2);
+  const uint32_t lane_off8 = lane_off + (uint32_t)(8 * row_elems * 2);   // row r + 8
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+
+  for (int cb = 0; cb < nb; cb += kWave) {
+    const int ncb = min(kWave, nb - cb);
+    int tab = cb == 0 ? tab0 : btrow[jb_begin + cb + min(lane, ncb - 1)];
+    tab = (tab >= 0 && tab < a.num_blocks && lane < ncb) ? tab : -1;
+    if (w >= ncb) continue;
+
+    auto issue = [&](KVRegs& R, int i) {
+      int blk = __builtin_amdgcn_readlane(tab, min(i, ncb - 1));
+      blk = blk < 0 ? 0 : blk;
+      const auto rk = buf_rsrc(kbase + (size_t)blk * block_bytes, block_bytes);
+      const auto rv = buf_rsrc(vbase + (size_t)blk * block_bytes, block_bytes);
+      R.k0 = buf_load16(rk, lane_off);
+      R.k1 = buf_load16(rk, lane_off8);
+      R.v0 = buf_load16(rv, lane_off);
+      R.v1 = buf_load16(rv, lane_off8);
+    };
+
+    // One block: branch-free apart from the rare rescale.  Rows past the
+    // context and rows of an unusable block are removed by selects.
+    auto process = [&](const KVRegs& R, int i) {
+      const bool blk_ok = __builtin_amdgcn_readlane(tab, i) >= 0;
+      const int tok0 = (jb_begin + cb + i) * kBlock + r;
+      const bool ok0 = blk_ok && tok0 < t_loop_end;
+      const bool ok1 = blk_ok && tok0 + 8 < t_loop_end;
       float s0[G], s1[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float d0 = dot2_bf16(qv[h].x, k0.x, 0.f);
-        float d1 = dot2_bf16(qv[h].x, k1.x, 0.f);
-        d0 = dot2_bf16(qv[h].y, k0.y, d0);
-        d1 = dot2_bf16(qv[h].y, k1.y, d1);
-        d0 = dot2_bf16(qv[h].z, k0.z, d0);
-        d1 = dot2_bf16(qv[h].z, k1.z, d1);
-        d0 = dot2_bf16(qv[h].w, k0.w, d0);
-        d1 = dot2_bf16(qv[h].w, k1.w, d1);
-        s0[h] = ok0 ? sum8(d0) * a.scale_log2e : -INFINITY;
-        s1[h] = ok1 ? sum8(d1) * a.scale_log2e : -INFINITY;
+        float d0 = dot2_bf16(qv[h].x, R.k0.x, 0.f);
+        float d1 = dot2_bf16(qv[h].x, R.k1.x, 0.f);
+        d0 = dot2_bf16(qv[h].y, R.k0.y, d0);
+        d1 = dot2_bf16(qv[h].y, R.k1.y, d1);
+        d0 = dot2_bf16(qv[h].z, R.k0.z, d0);
+        d1 = dot2_bf16(qv[h].z, R.k1.z, d1);
+        d0 = dot2_bf16(qv[h].w, R.k0.w, d0);
+        d1 = dot2_bf16(qv[h].w, R.k1.w, d1);
+        d0 = sum8(d0);
+        d1 = sum8(d1);
+        // keep the score computation unconditional (no branch around it)
+        __asm__ volatile("" : "+v"(d0), "+v"(d1));
+        s0[h] = ok0 ? d0 : -INFINITY;
+        s1[h] = ok1 ? d1 : -INFINITY;
       }
+      rescale_if_needed(s0, s1);
       const uint4 z = make_uint4(0, 0, 0, 0);
-      const uint4 va = ok0 ? v0 : z;
-      const uint4 vb = ok1 ? v1 : z;
-      float fa[8] = {bf16_lo(va.x), bf16_hi(va.x), bf16_lo(va.y), bf16_hi(va.y),
-                     bf16_lo(va.z), bf16_hi(va.z), bf16_lo(va.w), bf16_hi(va.w)};
-      float fb[8] = {bf16_lo(vb.x), bf16_hi(vb.x), bf16_lo(vb.y), bf16_hi(vb.y),
-                     bf16_lo(vb.z), bf16_hi(vb.z), bf16_lo(vb.w), bf16_hi(vb.w)};
+      const uint4 v0 = sel4(ok0, R.v0, z);
+      const uint4 v1 = sel4(ok1, R.v1, z);
+      const uint32_t vlo[4] = {pack_lo_halves(v0.x, v1.x), pack_lo_halves(v0.y, v1.y),
+                               pack_lo_halves(v0.z, v1.z), pack_lo_halves(v0.w, v1.w)};
+      const uint32_t vhi[4] = {pack_hi_halves(v0.x, v1.x), pack_hi_halves(v0.y, v1.y),
+                               pack_hi_halves(v0.z, v1.z), pack_hi_halves(v0.w, v1.w)};
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float mx = fmaxf(s0[h], s1[h]);
-        const float mn = fmaxf(m[h], mx);
-        const float alpha = fast_exp2(m[h] - mn);
-        const float p0 = fast_exp2(s0[h] - mn);
-        const float p1 = fast_exp2(s1[h] - mn);
-        l[h] = l[h] * alpha + p0 + p1;
+        const float p0 = fast_exp2(__builtin_fmaf(s0[h], C, -m[h]));
+        const float p1 = fast_exp2(__builtin_fmaf(s1[h], C, -m[h]));
+        const uint32_t pp = pack_bf16x2(p0, p1);
+        l[h] = dot2_bf16(pp, kOnesBf16x2, l[h]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[h][i] = o[h][i] * alpha + p0 * fa[i] + p1 * fb[i];
-        m[h] = mn;
+        for (int j = 0; j < 4; ++j) {
+          o[h][2 * j] = dot2_bf16(pp, vlo[j], o[h][2 * j]);
+          o[h][2 * j + 1] = dot2_bf16(pp, vhi[j], o[h][2 * j + 1]);
+        }
       }
-    }
-    k0 = nk0;
-    k1 = nk1;
-    v0 = nv0;
-    v1 = nv1;
-    base = nbase;
-  }
+    };
 
-  // Merge the 8 row groups of the wave (lane bits 3..5).
-#pragma unroll
-  for (int step = 0; step < 3; ++step) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float m2, l2;
-      if (step == 0) {
-        m2 = dpp<kDppRowRor8>(m[h]);
-        l2 = dpp<kDppRowRor8>(l[h]);
-      } else {
-        m2 = shfl_xor(m[h], 8 << step);
-        l2 = shfl_xor(l[h], 8 << step);
-      }
-      const float mm = fmaxf(m[h], m2);
-      const float a1 = fast_exp2(m[h] - mm);
-      const float a2 = fast_exp2(m2 - mm);
-      l[h] = l[h] * a1 + l2 * a2;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float o2 = step == 0 ? dpp<kDppRowRor8>(o[h][i]) : shfl_xor(o[h][i], 8 << step);
-        o[h][i] = o[h][i] * a1 + o2 * a2;
-      }
-      m[h] = mm;
+    KVRegs X, Y;
+    issue(X, w);
+    issue(Y, w + kWaves);
+    for (int i = w;; i += 2 * kWaves) {
+      process(X, i);
+      issue(X, i + 2 * kWaves);
+      if (i + kWaves >= ncb) break;
+      process(Y, i + kWaves);
+      issue(Y, i + 3 * kWaves);
+      if (i + 2 * kWaves >= ncb) break;
     }
   }
 
-  // Merge the waves through LDS.
-  __shared__ float sm_ml[kWaves][G][2];
-  __shared__ float sm_o[kWaves][G][kHeadDim];
-  if (r == 0) {
+  if constexpr (FUSED) {
+    // The new token, from registers, counted once (row group 0 of wave 0).
+    if (part == nparts - 1 && n > 0 && w == 0) {
+      float s0[G], s1[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+      for (int h = 0; h < G; ++h) {
+        float d = dot2_bf16(qv[h].x, knew.x, 0.f);
+        d = dot2_bf16(qv[h].y, knew.y, d);
+        d = dot2_bf16(qv[h].z, knew.z, d);
+        d = dot2_bf16(qv[h].w, knew.w, d);
+        s0[h] = r == 0 ? sum8(d) : -INFINITY;
+        s1[h] = -INFINITY;
+      }
+      rescale_if_needed(s0, s1);
+      const uint4 v0 = sel4(r == 0, vnew, make_uint4(0, 0, 0, 0));
+      const uint32_t vv[4] = {v0.x, v0.y, v0.z, v0.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sm_o[w][h][c * 8 + i] = o[h][i];
-      if (c == 0) {
-        sm_ml[w][h][0] = m[h];
-        sm_ml[w][h][1] = l[h];
+      for (int h = 0; h < G; ++h) {
+        const uint32_t pp = pack_bf16x2(fast_exp2(__builtin_fmaf(s0[h], C, -m[h])), 0.f);
+        l[h] = dot2_bf16(pp, kOnesBf16x2, l[h]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[h][2 * j] = dot2_bf16(pp, vv[j] & 0xffffu, o[h][2 * j]);
+          o[h][2 * j + 1] = dot2_bf16(pp, vv[j] >> 16, o[h][2 * j + 1]);
+        }
       }
     }
+  }
+
+  // ---- merge: row-group pairs by DPP, the rest through LDS ----------------
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    l[h] += dpp<kDppRowRor8>(l[h]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[h][j] += dpp<kDppRowRor8>(o[h][j]);
+  }
+  __shared__ float sm_o[kWaves][4][G][kHeadDim];
+  __shared__ float sm_l[kWaves][4][G];
+  __shared__ float sm_m[kWaves][G];
+  if ((r & 1) == 0) {
+    const int grp = r >> 1;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      *reinterpret_cast<float4*>(&sm_o[w][grp][h][c * 8]) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+      *reinterpret_cast<float4*>(&sm_o[w][grp][h][c * 8 + 4]) = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+      if (c == 0) sm_l[w][grp][h] = l[h];
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) sm_m[w][h] = m[h];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < G * kHeadDim; e += kWaves * kWave) {
+
+  const int64_t grp_row = (int64_t)b * a.n_kv + kvh;          // (sequence, kv head)
+  for (int e = tid; e < G * kHeadDim; e += kWaves * kWave) {
     const int h = e / kHeadDim;
     const int d = e % kHeadDim;
-    float mm = sm_ml[0][h][0];
+    float mm = sm_m[0][h];
 #pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) mm = fmaxf(mm, sm_ml[ww][h][0]);
+    for (int ww = 1; ww < kWaves; ++ww) mm = fmaxf(mm, sm_m[ww][h]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = fast_exp2(sm_ml[ww][h][0] - mm);
-      L += sm_ml[ww][h][1] * f;
-      O += sm_o[ww][h][d] * f;
+      const float f = fast_exp2(sm_m[ww][h] - mm);
+      L += f * (sm_l[ww][0][h] + sm_l[ww][1][h] + sm_l[ww][2][h] + sm_l[ww][3][h]);
+      O += f * (sm_o[ww][0][h][d] + sm_o[ww][1][h][d] + sm_o[ww][2][h][d] + sm_o[ww][3][h][d]);
     }
-    const int64_t row = (int64_t)b * a.n_q + kvh * G + h;
     if (nparts <= 1) {
-      a.out[row * kHeadDim + d] = to_bf16(L > 0.f ? O / L : 0.f);
+      a.out[((int64_t)b * a.n_q + kvh * G + h) * kHeadDim + d] = to_bf16(L > 0.f ? O / L : 0.f);
     } else {
-      const int64_t pr = row * a.P + part;
+      const int64_t pr = (grp_row * a.P + part) * G + h;
       a.ws_o[pr * kHeadDim + d] = O;
       if (d == 0) {
         a.ws_ml[pr * 2 + 0] = mm;
@@ -257,42 +441,157 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_partition_kernel(Decode
       }
     }
   }
+
+  if constexpr (FUSED) {
+    // Append the rotated key and the value of the new token (one 128-byte row
+    // each); no workgroup reads this row during the call.
+    if (part == nparts - 1 && n > 0 && tid < 8) {
+      const int blk = btrow[pos_new / kBlock];
+      if (blk >= 0 && blk < a.num_blocks) {
+        const int64_t off = ((int64_t)blk * kBlock + pos_new % kBlock) * row_elems + kvh * kHeadDim + tid * 8;
+        *reinterpret_cast<uint4*>(a.k_pool + off) = knew;
+        *reinterpret_cast<uint4*>(a.v_pool + off) = vnew;
+      }
+    }
+  }
 }
 
-// One wave per (batch row, query head); lane = output dim.
+// Split-context merge: one workgroup per (sequence, KV head), thread = (head,
+// dim).  M = max_p m_p, L = sum_p 2^(m_p - M) l_p, out = sum_p 2^(m_p - M) o_p / L.
+template <int G>
 __global__ __launch_bounds__(kWaves * kWave) void decode_merge_kernel(DecodeArgs a) {
-  const int w = threadIdx.x >> 6;
-  const int d = threadIdx.x & (kWave - 1);
-  const int h = blockIdx.x * kWaves + w;
+  const int kvh = blockIdx.x;
   const int b = blockIdx.y;
-  if (h >= a.n_q) return;
   int slot, n, nparts;
   seq_extent(a, b, slot, n, nparts);
-  if (nparts <= 1) return;   // finished by the partition kernel
-  const int64_t row = (int64_t)b * a.n_q + h;
-  const float* ml = a.ws_ml + row * a.P * 2;
-  const float* op = a.ws_o + row * a.P * kHeadDim + d;
-  float mm = ml[0];
-  for (int p = 1; p < nparts; ++p) mm = fmaxf(mm, ml[2 * p]);
-  float L = 0.f, O = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float f = fast_exp2(ml[2 * p] - mm);
-    L += ml[2 * p + 1] * f;
-    O += op[(int64_t)p * kHeadDim] * f;
+  if (nparts <= 1) return;            // finished by the partition kernel
+  const int64_t grp_row = (int64_t)b * a.n_kv + kvh;
+  for (int e = threadIdx.x; e < G * kHeadDim; e += kWaves * kWave) {
+    const int h = e / kHeadDim;
+    const int d = e % kHeadDim;
+    const int64_t base = grp_row * a.P * G + h;
+    float mm = a.ws_ml[base * 2];
+    for (int p = 1; p < nparts; ++p) mm = fmaxf(mm, a.ws_ml[(base + (int64_t)p * G) * 2]);
+    float L = 0.f, O = 0.f;
+    for (int p = 0; p < nparts; ++p) {
+      const int64_t pr = base + (int64_t)p * G;
+      const float f = fast_exp2(a.ws_ml[pr * 2] - mm);
+      L += f * a.ws_ml[pr * 2 + 1];
+      O += f * a.ws_o[pr * kHeadDim + d];
+    }
+    a.out[((int64_t)b * a.n_q + kvh * G + h) * kHeadDim + d] = to_bf16(L > 0.f ? O / L : 0.f);
   }
-  a.out[row * kHeadDim + d] = to_bf16(L > 0.f ? O / L : 0.f);
 }
 
 static int auto_partition(int batch, int n_kv, int max_ctx) {
   // Largest partition that still gives the grid about 16 workgroups per CU
-  // (256 CUs); never below one block per wave.
+  // (256 CUs); never below two blocks per wave.
   const int target = 4096;
-  const int cands[] = {1024, 512, 256, 128};
+  const int cands[] = {1024, 512, 256};
   for (int ps : cands) {
     const int64_t parts = ((int64_t)max_ctx + ps - 1) / ps;
     if ((int64_t)batch * n_kv * (parts > 0 ? parts : 1) >= target) return ps;
   }
-  return kBlock * kWaves;
+  return 2 * kBlock * kWaves;
+}
+
+static int64_t decode_parts(int max_context_len, int ps) {
+  const int64_t p = ((int64_t)max_context_len + ps - 1) / ps;
+  return p > 0 ? p : 1;
+}
+
+struct WsLayout {
+  size_t o_bytes, ml_bytes, total;
+};
+
+static WsLayout ws_layout(int batch, int n_q, int n_kv, int64_t P) {
+  WsLayout L;
+  if (P <= 1) {
+    L.o_bytes = L.ml_bytes = L.total = 0;
+    return L;
+  }
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  L.o_bytes = up((size_t)batch * n_q * P * kHeadDim * sizeof(float));
+  L.ml_bytes = up((size_t)batch * n_q * P * 2 * sizeof(float));
+  L.total = L.o_bytes + L.ml_bytes;
+  return L;
+}
+
+template <bool FUSED>
+static const void* pick_kernel(int G) {
+  return G == 1 ? (const void*)decode_kernel<1, FUSED>
+       : G == 2 ? (const void*)decode_kernel<2, FUSED>
+       : G == 4 ? (const void*)decode_kernel<4, FUSED>
+                : (const void*)decode_kernel<8, FUSED>;
+}
+
+// Longest-first schedule from host-known row lengths: every non-last
+// partition (full length) first, then each row's last partition by decreasing
+// length, so the dispatcher's in-order hand-out fills the tail with the short
+// pieces.  Rows of length 0 still get their partition 0 (a zero row).
+static void build_plan(DecodeArgs& a, const int32_t* row_lens_host, int batch) {
+  a.plan_pre[0] = 0;
+  int tmp_len[kMaxPlanSeqs];
+  int order[kMaxPlanSeqs];
+  for (int b = 0; b < batch; ++b) {
+    int n = row_lens_host[b];
+    n = n < 0 ? 0 : (n > a.max_blocks * kBlock ? a.max_blocks * kBlock : n);
+    int np = (n + a.ps - 1) / a.ps;
+    np = np > a.P ? a.P : np;
+    const int full = np > 1 ? np - 1 : 0;
+    a.plan_pre[b + 1] = a.plan_pre[b] + full;
+    const int last = np > 0 ? np - 1 : 0;
+    tmp_len[b] = n - last * a.ps;
+    a.plan_last[b] = (last << 16) | b;
+    order[b] = b;
+  }
+  // stable sort of the last partitions by decreasing length
+  for (int i = 1; i < batch; ++i) {
+    const int o = order[i];
+    int j = i;
+    while (j > 0 && tmp_len[order[j - 1]] < tmp_len[o]) { order[j] = order[j - 1]; --j; }
+    order[j] = o;
+  }
+  int32_t sorted[kMaxPlanSeqs];
+  for (int i = 0; i < batch; ++i) sorted[i] = a.plan_last[order[i]];
+  for (int i = 0; i < batch; ++i) a.plan_last[i] = sorted[i];
+  a.plan_seqs = batch;
+  a.full_items = a.plan_pre[batch];
+  a.n_items = a.full_items + batch;
+}
+
+static int decode_launch(bool fused, DecodeArgs& a, int batch, int max_context_len, int partition_size,
+                         const int32_t* row_lens_host, void* workspace, size_t workspace_bytes, hipStream_t st) {
+  a.ps = partition_size > 0 ? partition_size : auto_partition(batch, a.n_kv, max_context_len);
+  const int64_t P = decode_parts(max_context_len, a.ps);
+  if (P > 65535) return PKV_ERR_INVALID_ARG;
+  a.P = (int)P;
+  const WsLayout L = ws_layout(batch, a.n_q, a.n_kv, P);
+  if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return PKV_ERR_CAPACITY;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = L.total ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_ml = L.total ? reinterpret_cast<float*>(ws + L.o_bytes) : nullptr;
+  const int G = a.n_q / a.n_kv;
+  a.batch = batch;
+  a.plan_seqs = 0;
+  if (row_lens_host && batch <= kMaxPlanSeqs && a.P <= 0x7fff) build_plan(a, row_lens_host, batch);
+  const int64_t items = a.plan_seqs > 0 ? (int64_t)a.n_items : (int64_t)batch * a.P;
+  const int64_t grid = (items + 7) / 8 * 8 * a.n_kv;
+  if (grid > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  const void* fn = fused ? pick_kernel<true>(G) : pick_kernel<false>(G);
+  void* args[] = {&a};
+  const int rc = launch_status(hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kWaves * kWave), args, 0, st));
+  if (rc != PKV_OK || P <= 1) return rc;
+  const void* mg = G == 1 ? (const void*)decode_merge_kernel<1>
+                 : G == 2 ? (const void*)decode_merge_kernel<2>
+                 : G == 4 ? (const void*)decode_merge_kernel<4>
+                          : (const void*)decode_merge_kernel<8>;
+  return launch_status(hipLaunchKernel(mg, dim3(a.n_kv, batch), dim3(kWaves * kWave), args, 0, st));
+}
+
+__global__ void zero_kernel(uint32_t* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 }  // namespace pkv
@@ -304,46 +603,60 @@ extern "C" int pkv_decode_partition_size(int batch, int n_kv_heads, int max_cont
   return auto_partition(batch, n_kv_heads, max_context_len);
 }
 
-static int64_t decode_parts(int max_context_len, int ps) {
-  const int64_t p = ((int64_t)max_context_len + ps - 1) / ps;
-  return p > 0 ? p : 1;
-}
-
 extern "C" size_t pkv_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
                                              int max_context_len, int partition_size) {
-  if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim != kHeadDim || max_context_len < 0)
+  if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim != kHeadDim || max_context_len < 0 ||
+      partition_size < 0)
     return 0;
   const int ps = partition_size > 0 ? partition_size : auto_partition(batch, n_kv_heads, max_context_len);
-  const int64_t P = decode_parts(max_context_len, ps);
-  if (P <= 1) return 0;
-  return (size_t)batch * n_q_heads * P * (2 + kHeadDim) * sizeof(float);
+  return ws_layout(batch, n_q_heads, n_kv_heads, decode_parts(max_context_len, ps)).total;
 }
 
-extern "C" int pkv_paged_attn_decode(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_pool,
-                                     const pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
-                                     int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,
-                                     const int32_t* slot_ids, const int32_t* context_lens, int batch,
-                                     int max_context_len, int n_q_heads, int n_kv_heads, int head_dim,
-                                     float scale, int partition_size, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+extern "C" int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return PKV_OK;
+  if (!workspace) return PKV_ERR_NULL;
+  if (!aligned16(workspace)) return PKV_ERR_MISALIGNED;
+  uint32_t* p = static_cast<uint32_t*>(workspace);
+  size_t n = workspace_bytes / 4;
+  const size_t grid = (n + 255) / 256;
+  if (grid > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  void* args[] = {&p, &n};
+  return launch_status(hipLaunchKernel((const void*)zero_kernel, dim3((unsigned)grid), dim3(256), args, 0,
+                                       (hipStream_t)stream));
+}
+
+static int decode_common_checks(const pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_pool,
+                                const pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
+                                int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,
+                                const int32_t* slot_ids, const int32_t* context_lens, int batch,
+                                int max_context_len, int n_q_heads, int n_kv_heads, int head_dim, float scale,
+                                int partition_size, void* workspace) {
   if (batch < 0 || num_blocks < 0 || num_slots < 0 || max_blocks_per_seq < 0 ||
       bt_row_stride < max_blocks_per_seq || max_context_len < 0 || partition_size < 0 ||
-      partition_size % kBlock || !(scale == scale))
+      partition_size % kBlock || !(scale > 0.f && scale < 3.0e38f))
     return PKV_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads) return PKV_ERR_INVALID_ARG;
   if (head_dim != kHeadDim || !ratio_supported(n_q_heads, n_kv_heads)) return PKV_ERR_UNSUPPORTED;
-  if (batch == 0) return PKV_OK;
+  if (batch == 0) return -1;   // nothing to do
   if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens) return PKV_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned4(block_table) ||
       !aligned4(context_lens) || (slot_ids && !aligned4(slot_ids)) || (workspace && !aligned16(workspace)))
     return PKV_ERR_MISALIGNED;
-  if (batch > 65535) return PKV_ERR_INVALID_ARG;
+  if (batch > 65535 || n_kv_heads > 65535) return PKV_ERR_INVALID_ARG;
+  if ((int64_t)kBlock * n_kv_heads * kHeadDim * 2 * (int64_t)num_blocks <= 0 && num_blocks > 0)
+    return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
 
-  DecodeArgs a;
+static DecodeArgs base_args(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_pool, const pkv_bf16* v_pool,
+                            int num_blocks, const int32_t* block_table, int64_t bt_row_stride, int num_slots,
+                            int max_blocks_per_seq, const int32_t* slot_ids, const int32_t* context_lens,
+                            int n_q_heads, int n_kv_heads, float scale) {
+  DecodeArgs a{};
   a.out = out;
   a.q = q;
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
+  a.k_pool = const_cast<uint16_t*>(k_pool);
+  a.v_pool = const_cast<uint16_t*>(v_pool);
   a.bt = block_table;
   a.slot_ids = slot_ids;
   a.ctx_lens = context_lens;
@@ -353,27 +666,48 @@ extern "C" int pkv_paged_attn_decode(pkv_bf16* out, const pkv_bf16* q, const pkv
   a.max_blocks = max_blocks_per_seq;
   a.n_q = n_q_heads;
   a.n_kv = n_kv_heads;
-  a.ps = partition_size > 0 ? partition_size : auto_partition(batch, n_kv_heads, max_context_len);
-  const int64_t P = decode_parts(max_context_len, a.ps);
-  if (P > 65535) return PKV_ERR_INVALID_ARG;
-  a.P = (int)P;
   a.scale_log2e = scale * kLog2e;
-  const size_t need = pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_context_len,
-                                                 a.ps);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_CAPACITY;
-  a.ws_ml = static_cast<float*>(workspace);
-  a.ws_o = need > 0 ? a.ws_ml + (size_t)batch * n_q_heads * P * 2 : nullptr;
+  return a;
+}
 
-  const int G = n_q_heads / n_kv_heads;
-  const void* fn = G == 1 ? (const void*)decode_partition_kernel<1>
-                 : G == 2 ? (const void*)decode_partition_kernel<2>
-                 : G == 4 ? (const void*)decode_partition_kernel<4>
-                          : (const void*)decode_partition_kernel<8>;
-  void* args[] = {&a};
-  hipStream_t st = (hipStream_t)stream;
-  int rc = launch_status(hipLaunchKernel(fn, dim3(n_kv_heads, a.P, batch), dim3(kWaves * kWave), args, 0, st));
-  if (rc != PKV_OK || P <= 1) return rc;
-  return launch_status(hipLaunchKernel((const void*)decode_merge_kernel,
-                                       dim3((n_q_heads + kWaves - 1) / kWaves, batch), dim3(kWaves * kWave), args,
-                                       0, st));
+extern "C" int pkv_paged_attn_decode(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_pool,
+                                     const pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
+                                     int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,
+                                     const int32_t* slot_ids, const int32_t* context_lens,
+                                     const int32_t* row_lens_host, int batch, int max_context_len, int n_q_heads,
+                                     int n_kv_heads, int head_dim, float scale, int partition_size,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = decode_common_checks(out, q, k_pool, v_pool, num_blocks, block_table, bt_row_stride, num_slots,
+                                      max_blocks_per_seq, slot_ids, context_lens, batch, max_context_len,
+                                      n_q_heads, n_kv_heads, head_dim, scale, partition_size, workspace);
+  if (rc != PKV_OK) return rc < 0 ? PKV_OK : rc;
+  DecodeArgs a = base_args(out, q, k_pool, v_pool, num_blocks, block_table, bt_row_stride, num_slots,
+                           max_blocks_per_seq, slot_ids, context_lens, n_q_heads, n_kv_heads, scale);
+  return decode_launch(false, a, batch, max_context_len, partition_size, row_lens_host, workspace,
+                       workspace_bytes, (hipStream_t)stream);
+}
+
+extern "C" int pkv_paged_decode_fused(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_new,
+                                      const pkv_bf16* v_new, pkv_bf16* k_pool, pkv_bf16* v_pool, int num_blocks,
+                                      const int32_t* block_table, int64_t bt_row_stride, int num_slots,
+                                      int max_blocks_per_seq, const int32_t* slot_ids, const int32_t* context_lens,
+                                      const int32_t* row_lens_host, int batch, int max_context_len, int n_q_heads,
+                                      int n_kv_heads, int head_dim,
+                                      const float* cos_sin, int max_pos, float scale, int partition_size,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = decode_common_checks(out, q, k_pool, v_pool, num_blocks, block_table, bt_row_stride, num_slots,
+                                      max_blocks_per_seq, slot_ids, context_lens, batch, max_context_len,
+                                      n_q_heads, n_kv_heads, head_dim, scale, partition_size, workspace);
+  if (rc != PKV_OK) return rc < 0 ? PKV_OK : rc;
+  if (max_pos < 1) return PKV_ERR_INVALID_ARG;
+  if (!k_new || !v_new || !cos_sin) return PKV_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(cos_sin)) return PKV_ERR_MISALIGNED;
+  DecodeArgs a = base_args(out, q, k_pool, v_pool, num_blocks, block_table, bt_row_stride, num_slots,
+                           max_blocks_per_seq, slot_ids, context_lens, n_q_heads, n_kv_heads, scale);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.rope = reinterpret_cast<const float2*>(cos_sin);
+  a.max_pos = max_pos;
+  return decode_launch(true, a, batch, max_context_len, partition_size, row_lens_host, workspace,
+                       workspace_bytes, (hipStream_t)stream);
 }

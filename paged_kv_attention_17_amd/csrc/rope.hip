@@ -39,8 +39,8 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ q, uin
   const float2 cs = table[(int64_t)pos * kHalf + i];
   const float x = __builtin_bit_cast(float, (uint32_t)row[i] << 16);
   const float y = __builtin_bit_cast(float, (uint32_t)row[i + kHalf] << 16);
-  const float xr = x * cs.x - y * cs.y;
-  const float yr = y * cs.x + x * cs.y;
+  const float xr = rope_first(x, y, cs.x, cs.y);
+  const float yr = rope_second(x, y, cs.x, cs.y);
   const uint32_t packed = pack_bf16x2(xr, yr);
   row[i] = (uint16_t)(packed & 0xffffu);
   row[i + kHalf] = (uint16_t)(packed >> 16);

@@ -5,8 +5,9 @@
 // token; a block leaves the free list when a sequence's new token opens a
 // 16-token chunk; the block table maps chunks to blocks per (slot, layer).
 // The per-layer work is RoPE on the new q/k, the append of k/v into the cache
-// and paged attention, all through the library's own entry points, so the
-// whole step is one call from the host language and ~3 launches per layer.
+// and paged attention, fused into one kernel (pkv_paged_decode_fused), so the
+// whole step is one call from the host language and one launch per layer
+// (plus the metadata patches).
 #include <cstdint>
 #include <vector>
 
@@ -80,20 +81,22 @@ extern "C" int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const
   rc = pkv_block_table_patch(meta_dev, meta_elems, m_off.data(), m_val.data(), (int)m_off.size(), stream);
   if (rc != PKV_OK) return rc;
 
-  // 3. Per layer: RoPE, append, attention.
+  // 3. Per layer: RoPE, append and attention in one launch.  An identity
+  // batch (row b = slot b) passes no slot ids, which saves the kernels one
+  // dependent memory read before their first K/V load.
+  bool identity = batch <= num_slots;
+  for (int b = 0; b < batch && identity; ++b) identity = slot_ids_host[b] == b;
+  thread_local std::vector<int32_t> row_lens;
+  row_lens.resize(batch);
+  for (int b = 0; b < batch; ++b) row_lens[b] = cached_lens_host[slot_ids_host[b]];
   const int32_t* ctx_dev = meta_dev;
-  const int32_t* pos_dev = meta_dev + num_slots;
-  const int32_t* sid_dev = meta_dev + num_slots + batch;
+  const int32_t* sid_dev = identity ? nullptr : meta_dev + num_slots + batch;
   for (int l = 0; l < n_layers; ++l) {
     const int32_t* bt_l = bt_dev + l * layer_stride;
-    rc = pkv_rope_decode(q[l], k[l], pos_dev, batch, n_q_heads, n_kv_heads, head_dim, cos_sin, max_pos, stream);
-    if (rc != PKV_OK) return rc;
-    rc = pkv_paged_kv_append(k_pool, v_pool, num_blocks, k[l], v[l], bt_l, row_stride, num_slots,
-                             max_blocks_per_seq, sid_dev, pos_dev, batch, n_kv_heads, head_dim, stream);
-    if (rc != PKV_OK) return rc;
-    rc = pkv_paged_attn_decode(out[l], q[l], k_pool, v_pool, num_blocks, bt_l, row_stride, num_slots,
-                               max_blocks_per_seq, sid_dev, ctx_dev, batch, max_context_len, n_q_heads, n_kv_heads,
-                               head_dim, scale, partition_size, workspace, workspace_bytes, stream);
+    rc = pkv_paged_decode_fused(out[l], q[l], k[l], v[l], k_pool, v_pool, num_blocks, bt_l, row_stride, num_slots,
+                                max_blocks_per_seq, sid_dev, ctx_dev, row_lens.data(), batch, max_context_len, n_q_heads,
+                                n_kv_heads, head_dim, cos_sin, max_pos, scale, partition_size, workspace,
+                                workspace_bytes, stream);
     if (rc != PKV_OK) return rc;
   }
   return PKV_OK;

@@ -16,6 +16,8 @@ one call of the native ``pkv_decode_step``:
   a2  append of the rotated k and of v into the token's block row
   a3+a4 paged attention over the whole context (split into partitions and
       merged when long)
+  (a1-a4 are one launch per layer: pkv_paged_decode_fused; q and k keep their
+  unrotated values)
 
 The engine owns no arithmetic and allocates every buffer once, here.
 """
@@ -60,9 +62,8 @@ class DecodeEngine:
         self.meta = torch.from_numpy(np.concatenate([self.cached, np.zeros(2 * ns, np.int32)])).to(self.dev)
         self.cos_sin = torch.empty((max_pos, self.d // 2, 2), dtype=torch.float32, device=self.dev)
         abi.pkv_rope_table_init(self.cos_sin, head_dim=self.d, stream=stream)
-        ws = abi.pkv_decode_workspace_bytes(self.n_slots, self.n_q, self.n_kv, self.d, self.max_context_len,
-                                           partition_size)
-        self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=self.dev)
+        self.workspace = abi.decode_workspace(self.n_slots, self.n_q, self.n_kv, self.max_context_len,
+                                              partition_size, device=self.dev, stream=stream)
 
     @property
     def ctx_dev(self):
@@ -72,8 +73,8 @@ class DecodeEngine:
         return self.meta[:self.n_slots + 2 * batch]
 
     def step(self, slot_ids, q, k, v, out):
-        """q/out [L, B, n_q, 64], k/v [L, B, n_kv, 64] device bf16 (q and k are
-        rotated in place).  Batch row b is slot slot_ids[b]."""
+        """q/out [L, B, n_q, 64], k/v [L, B, n_kv, 64] device bf16 (q, k, v are
+        read only).  Batch row b is slot slot_ids[b]."""
         slot_ids = np.asarray(slot_ids, dtype=np.int32)
         self.n_free = abi.pkv_decode_step(
             q, k, v, out, self.k_pool, self.v_pool, self.bt_host, self.bt_dev, self.free, self.n_free,

@@ -43,3 +43,20 @@ def ulp_diff(a_bits, b_bits):
     a = np.where(a & 0x8000, -(a & 0x7FFF), a)
     b = np.where(b & 0x8000, -(b & 0x7FFF), b)
     return np.abs(a - b)
+
+
+# Two correct float32 evaluations of the same attention may differ: the
+# softmax weights are rounded to bf16 (relative error <= 2^-9 each) after
+# subtracting a running max whose value depends on the evaluation order, so
+# each weight can round differently; the output moves by at most about
+# 2 * 2^-9 * max|V| plus one bf16 output ulp (2^-8 relative).
+CROSS_MAX = 2.0 ** -7 * 2      # |V| <= ~4 in the tests' data
+CROSS_MEAN = 2e-4
+
+
+def check_close_evaluations(a_bits, b_bits, what=""):
+    a, b = f64(a_bits), f64(b_bits)
+    d = np.abs(a - b)
+    print(f"{what}: cross max {d.max():.3e} mean {d.mean():.3e}", flush=True)
+    assert d.max() <= CROSS_MAX, f"{what}: evaluations differ by {d.max():.3e}"
+    assert d.mean() <= CROSS_MEAN, f"{what}: evaluations differ on average by {d.mean():.3e}"

@@ -40,8 +40,13 @@ def test_workspace_and_partition_sizes(lib):
     ps = pkv.pkv_decode_partition_size(64, 8, 4096)
     assert ps % 16 == 0 and ps >= 64
     P = -(-4096 // ps)
-    assert pkv.pkv_decode_workspace_bytes(64, 32, 8, 64, 4096, 0) == 64 * 32 * P * 66 * 4
-    assert pkv.pkv_decode_workspace_bytes(2, 32, 8, 64, 100, 16) == 2 * 32 * 7 * 66 * 4
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+
+    def expect(B, nq, nkv, P):
+        # partial outputs and partial (max, sum)
+        return up(B * nq * P * 64 * 4) + up(B * nq * P * 2 * 4)
+    assert pkv.pkv_decode_workspace_bytes(64, 32, 8, 64, 4096, 0) == expect(64, 32, 8, P)
+    assert pkv.pkv_decode_workspace_bytes(2, 32, 8, 64, 100, 16) == expect(2, 32, 8, 7)
     assert pkv.pkv_decode_workspace_bytes(2, 32, 8, 32, 100, 16) == 0       # unsupported head_dim
 
 
@@ -53,7 +58,7 @@ def _decode(lib, **kw):
              batch=1, maxctx=17, nq=32, nkv=8, d=64, scale=0.125, ps=0, ws=None, wsb=0)
     a.update(kw)
     return lib.pkv_paged_attn_decode(a["out"], a["q"], a["k"], a["v"], a["nb"], a["bt"], a["stride"], a["rows"],
-                                     a["mb"], a["sid"], a["ctx"], a["batch"], a["maxctx"], a["nq"], a["nkv"],
+                                     a["mb"], a["sid"], a["ctx"], None, a["batch"], a["maxctx"], a["nq"], a["nkv"],
                                      a["d"], a["scale"], a["ps"], a["ws"], a["wsb"], None)
 
 
@@ -68,6 +73,8 @@ def test_decode_argument_errors_before_launch(lib):
     assert _decode(lib, stride=2) == _abi.PKV_ERR_INVALID_ARG            # row stride shorter than the row
     assert _decode(lib, batch=-1) == _abi.PKV_ERR_INVALID_ARG
     assert _decode(lib, scale=float("nan")) == _abi.PKV_ERR_INVALID_ARG
+    assert _decode(lib, scale=0.0) == _abi.PKV_ERR_INVALID_ARG
+    assert _decode(lib, scale=-0.125) == _abi.PKV_ERR_INVALID_ARG
     assert _decode(lib, batch=0) == _abi.PKV_OK                          # empty batch: nothing to do
     # a context needing 2 partitions of 16 with no workspace
     assert _decode(lib, ps=16, maxctx=17) == _abi.PKV_ERR_CAPACITY
@@ -92,6 +99,16 @@ def test_other_entry_points_argument_errors(lib):
                                       32, 8, 48, 0.125, None) == E.PKV_ERR_UNSUPPORTED
     assert lib.pkv_paged_attn_prefill(FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 8, FAKE, 4, 1, 4, 1, 10, 10,
                                       32, 8, 64, 0.125, None) == E.PKV_ERR_NULL
+    # fused decode: same checks plus its own inputs
+    assert lib.pkv_paged_decode_fused(FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None, 1, 17,
+                                      32, 8, 64, FAKE, 100, 0.125, 0, None, 0, None) == E.PKV_ERR_NULL
+    assert lib.pkv_paged_decode_fused(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None, 1, 17,
+                                      32, 8, 64, FAKE, 0, 0.125, 0, None, 0, None) == E.PKV_ERR_INVALID_ARG
+    assert lib.pkv_paged_decode_fused(FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None, 1,
+                                      17, 32, 8, 64, FAKE, 100, 0.125, 0, None, 0, None) == E.PKV_ERR_MISALIGNED
+    assert lib.pkv_decode_workspace_init(FAKE + 4, 64, None) == E.PKV_ERR_MISALIGNED
+    assert lib.pkv_decode_workspace_init(None, 64, None) == E.PKV_ERR_NULL
+    assert lib.pkv_decode_workspace_init(None, 0, None) == E.PKV_OK
     offs = np.array([0], np.int32)
     assert lib.pkv_block_table_patch(FAKE + 2, 10, offs.ctypes.data, offs.ctypes.data, 1, None) \
         == E.PKV_ERR_MISALIGNED
