@@ -84,30 +84,26 @@ struct DecodeArgs {
   int max_pos;
   int batch;
   float scale_log2e;
-  // Host schedule (plan_seqs > 0): items [0, full_items) are the partitions
-  // that are not a sequence's last one, row b owning items plan_pre[b] ..
-  // plan_pre[b+1]-1 (partition = item - plan_pre[b]); items full_items + j are
-  // the last partitions, longest first: plan_last[j] = (partition << 16) | row.
+  // Host schedule (plan_seqs > 0), built from host-known row lengths.  Row b
+  // has length plan_n[b] and is cut into partitions of plan_ps[b] * 16
+  // tokens (only its last one shorter).  Items [0, full_items) are the
+  // partitions that are not a row's last one, row b owning items plan_pre[b]
+  // .. plan_pre[b+1]-1; item full_items + j is the last partition of row
+  // plan_last[j], longest first.
   int plan_seqs;
   int full_items;
   int n_items;
   int32_t plan_pre[kMaxPlanSeqs + 1];
-  int32_t plan_last[kMaxPlanSeqs];
+  int32_t plan_n[kMaxPlanSeqs];
+  uint16_t plan_ps[kMaxPlanSeqs];
+  uint16_t plan_last[kMaxPlanSeqs];
 };
 
-__device__ __forceinline__ void seq_extent(const DecodeArgs& a, int b, int& slot, int& n, int& nparts) {
-  slot = a.slot_ids ? a.slot_ids[b] : b;
-  n = 0;
-  if (slot >= 0 && slot < a.num_slots && a.num_blocks > 0) {
-    n = a.ctx_lens[slot];
-    n = n < 0 ? 0 : n;
-    n = n > a.max_blocks * kBlock ? a.max_blocks * kBlock : n;
-  } else {
-    slot = 0;
-  }
-  nparts = (n + a.ps - 1) / a.ps;
-  nparts = nparts > a.P ? a.P : nparts;
-}
+// One workgroup's share: row b (table row `slot`), KV head kvh, partition
+// `part` of `nparts` covering tokens [t_begin, t_end) of the n in context.
+struct Item {
+  int b, kvh, part, slot, n, nparts, t_begin, t_end;
+};
 
 struct KVRegs {
   uint4 k0, k1, v0, v1;        // rows r and r + 8 of one block, this lane's 8 dims
@@ -162,61 +158,80 @@ __device__ __forceinline__ uint4 rope_chunk(uint4 v, const float2* cs, int c) {
 // Without a host schedule, item = sequence * P + partition over the grid that
 // max_context_len implies (items past a sequence's length exit at once); with
 // one, only real partitions are launched, longest first.
-__device__ __forceinline__ bool decode_item(const DecodeArgs& a, int batch, int& kvh, int& part, int& b) {
+__device__ __forceinline__ int clip_len(const DecodeArgs& a, int n) {
+  return n < 0 ? 0 : (n > a.max_blocks * kBlock ? a.max_blocks * kBlock : n);
+}
+
+// Row b's extent from the host schedule (no memory access) or, without one,
+// from context_lens on the device with the uniform partition size.
+__device__ __forceinline__ void row_extent(const DecodeArgs& a, int b, int& slot, int& n, int& nparts, int& ps) {
+  slot = a.slot_ids ? a.slot_ids[b] : b;
+  const bool slot_ok = slot >= 0 && slot < a.num_slots && a.num_blocks > 0;
+  slot = slot_ok ? slot : 0;
+  if (a.plan_seqs > 0) {
+    n = slot_ok ? a.plan_n[b] : 0;
+    nparts = n > 0 ? a.plan_pre[b + 1] - a.plan_pre[b] + 1 : 0;
+    ps = a.plan_ps[b] * kBlock;
+  } else {
+    n = slot_ok ? clip_len(a, a.ctx_lens[slot]) : 0;
+    nparts = (n + a.ps - 1) / a.ps;
+    nparts = nparts > a.P ? a.P : nparts;
+    ps = a.ps;
+  }
+}
+
+__device__ __forceinline__ bool decode_item(const DecodeArgs& a, Item& it) {
   const int id = blockIdx.x;
   const int grp = id / (8 * a.n_kv);
   const int in = id - grp * 8 * a.n_kv;
-  kvh = in >> 3;
+  it.kvh = in >> 3;
   const int item = grp * 8 + (in & 7);
+  int ps;
   if (a.plan_seqs > 0) {
     if (item >= a.n_items) return false;
+    bool last;
     if (item < a.full_items) {
       int lo = 0, hi = a.plan_seqs;            // plan_pre[lo] <= item < plan_pre[hi]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (a.plan_pre[mid] <= item) lo = mid; else hi = mid;
       }
-      b = lo;
-      part = item - a.plan_pre[lo];
+      it.b = lo;
+      it.part = item - a.plan_pre[lo];
+      last = false;
     } else {
-      const int packed = a.plan_last[item - a.full_items];
-      b = packed & 0xffff;
-      part = packed >> 16;
+      it.b = a.plan_last[item - a.full_items];
+      last = true;
     }
-    return b < batch;
+    if (it.b >= a.batch) return false;
+    row_extent(a, it.b, it.slot, it.n, it.nparts, ps);
+    if (last) it.part = it.nparts > 0 ? it.nparts - 1 : 0;
+  } else {
+    it.b = item / a.P;
+    it.part = item - it.b * a.P;
+    if (it.b >= a.batch) return false;
+    row_extent(a, it.b, it.slot, it.n, it.nparts, ps);
+    // partition 0 always runs (it writes the zero row of an empty context)
+    if (it.part >= (it.nparts > 0 ? it.nparts : 1)) return false;
   }
-  b = item / a.P;
-  part = item - b * a.P;
-  return b < batch;
+  it.t_begin = it.part * ps;
+  it.t_end = (it.part == it.nparts - 1) ? it.n : (it.nparts == 0 ? 0 : it.t_begin + ps);
+  return true;
 }
 
 template <int G, bool FUSED>
 __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
-  int kvh, part, b;
-  if (!decode_item(a, a.batch, kvh, part, b)) return;
+  Item it;
+  if (!decode_item(a, it)) return;
+  const int kvh = it.kvh, part = it.part, b = it.b, slot = it.slot, n = it.n, nparts = it.nparts;
+  const int t_begin = it.t_begin, t_end = it.t_end;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = wave_uniform(tid >> 6);
   const int c = lane & 7;
   const int r = lane >> 3;
-
-  // Prologue.  The table slice of this partition is fetched in parallel with
-  // the context length (both need only the slot) so that the first K/V loads
-  // wait for two memory round trips, not three.
-  int slot = a.slot_ids ? a.slot_ids[b] : b;
-  const bool slot_ok = slot >= 0 && slot < a.num_slots && a.num_blocks > 0;
-  slot = slot_ok ? slot : 0;
   const int32_t* btrow = a.bt + (int64_t)slot * a.bt_stride;
-  const int jb_begin = part * (a.ps / kBlock);
-  const int spec_idx = jb_begin + lane;
-  int tab0 = spec_idx < a.max_blocks ? btrow[spec_idx] : -1;
-  int n = slot_ok ? a.ctx_lens[slot] : 0;
-  n = n < 0 ? 0 : (n > a.max_blocks * kBlock ? a.max_blocks * kBlock : n);
-  int nparts = (n + a.ps - 1) / a.ps;
-  nparts = nparts > a.P ? a.P : nparts;
-  if (part >= (nparts > 0 ? nparts : 1)) return;   // partition 0 always runs (zero row for n == 0)
-  const int t_begin = part * a.ps;
-  const int t_end = (part == nparts - 1) ? n : (nparts == 0 ? 0 : t_begin + a.ps);
+  const int jb_begin = t_begin / kBlock;
   const int64_t row_elems = (int64_t)a.n_kv * kHeadDim;
 
   // This lane's chunk of the G query heads (rotated here when fused).
@@ -287,7 +302,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
 
   for (int cb = 0; cb < nb; cb += kWave) {
     const int ncb = min(kWave, nb - cb);
-    int tab = cb == 0 ? tab0 : btrow[jb_begin + cb + min(lane, ncb - 1)];
+    int tab = btrow[jb_begin + cb + min(lane, ncb - 1)];
     tab = (tab >= 0 && tab < a.num_blocks && lane < ncb) ? tab : -1;
     if (w >= ncb) continue;
 
@@ -457,27 +472,44 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
 }
 
 // Split-context merge: one workgroup per (sequence, KV head), thread = (head,
-// dim).  M = max_p m_p, L = sum_p 2^(m_p - M) l_p, out = sum_p 2^(m_p - M) o_p / L.
+// dim).  M = max_p m_p, L = sum_p 2^(m_p - M) l_p, out = sum_p 2^(m_p - M) o_p / L,
+// taken eight partitions at a time (independent loads) with a running merge.
 template <int G>
 __global__ __launch_bounds__(kWaves * kWave) void decode_merge_kernel(DecodeArgs a) {
   const int kvh = blockIdx.x;
   const int b = blockIdx.y;
-  int slot, n, nparts;
-  seq_extent(a, b, slot, n, nparts);
+  int slot, n, nparts, ps;
+  row_extent(a, b, slot, n, nparts, ps);
   if (nparts <= 1) return;            // finished by the partition kernel
   const int64_t grp_row = (int64_t)b * a.n_kv + kvh;
   for (int e = threadIdx.x; e < G * kHeadDim; e += kWaves * kWave) {
     const int h = e / kHeadDim;
     const int d = e % kHeadDim;
     const int64_t base = grp_row * a.P * G + h;
-    float mm = a.ws_ml[base * 2];
-    for (int p = 1; p < nparts; ++p) mm = fmaxf(mm, a.ws_ml[(base + (int64_t)p * G) * 2]);
-    float L = 0.f, O = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-      const int64_t pr = base + (int64_t)p * G;
-      const float f = fast_exp2(a.ws_ml[pr * 2] - mm);
-      L += f * a.ws_ml[pr * 2 + 1];
-      O += f * a.ws_o[pr * kHeadDim + d];
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int p0 = 0; p0 < nparts; p0 += 8) {
+      float mv[8], lv[8], ov[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool in = p0 + j < nparts;
+        const int64_t pr = base + (int64_t)(in ? p0 + j : p0) * G;
+        mv[j] = in ? a.ws_ml[pr * 2] : -INFINITY;
+        lv[j] = a.ws_ml[pr * 2 + 1];
+        ov[j] = a.ws_o[pr * kHeadDim + d];
+      }
+      float mm = M;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mm = fmaxf(mm, mv[j]);
+      const float f0 = M == -INFINITY ? 0.f : fast_exp2(M - mm);
+      L *= f0;
+      O *= f0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float f = mv[j] == -INFINITY ? 0.f : fast_exp2(mv[j] - mm);
+        L += f * lv[j];
+        O += f * ov[j];
+      }
+      M = mm;
     }
     a.out[((int64_t)b * a.n_q + kvh * G + h) * kHeadDim + d] = to_bf16(L > 0.f ? O / L : 0.f);
   }
@@ -525,36 +557,37 @@ static const void* pick_kernel(int G) {
                 : (const void*)decode_kernel<8, FUSED>;
 }
 
-// Longest-first schedule from host-known row lengths: every non-last
-// partition (full length) first, then each row's last partition by decreasing
-// length, so the dispatcher's in-order hand-out fills the tail with the short
-// pieces.  Rows of length 0 still get their partition 0 (a zero row).
+// Longest-first schedule from host-known row lengths.  Row b (n tokens) is
+// cut into round(n / ps) partitions of equal, block-aligned size (so no
+// partition is a sliver), at most P of them.  Every non-last partition comes
+// first, then each row's last partition by decreasing length, so the in-order
+// hardware dispatcher acts as a longest-first list scheduler.  Rows of length
+// 0 keep their partition 0 (the zero row).
 static void build_plan(DecodeArgs& a, const int32_t* row_lens_host, int batch) {
   a.plan_pre[0] = 0;
-  int tmp_len[kMaxPlanSeqs];
-  int order[kMaxPlanSeqs];
+  int last_len[kMaxPlanSeqs];
+  uint16_t order[kMaxPlanSeqs];
   for (int b = 0; b < batch; ++b) {
     int n = row_lens_host[b];
     n = n < 0 ? 0 : (n > a.max_blocks * kBlock ? a.max_blocks * kBlock : n);
-    int np = (n + a.ps - 1) / a.ps;
+    int np = n > 0 ? (n + a.ps / 2) / a.ps : 0;
+    np = n > 0 && np < 1 ? 1 : np;
     np = np > a.P ? a.P : np;
-    const int full = np > 1 ? np - 1 : 0;
-    a.plan_pre[b + 1] = a.plan_pre[b] + full;
-    const int last = np > 0 ? np - 1 : 0;
-    tmp_len[b] = n - last * a.ps;
-    a.plan_last[b] = (last << 16) | b;
-    order[b] = b;
+    int ps_b = np > 0 ? ((n + np - 1) / np + kBlock - 1) / kBlock * kBlock : a.ps;
+    np = n > 0 ? (n + ps_b - 1) / ps_b : 0;
+    a.plan_n[b] = n;
+    a.plan_ps[b] = (uint16_t)(ps_b / kBlock);
+    a.plan_pre[b + 1] = a.plan_pre[b] + (np > 1 ? np - 1 : 0);
+    last_len[b] = np > 0 ? n - (np - 1) * ps_b : 0;
+    order[b] = (uint16_t)b;
   }
-  // stable sort of the last partitions by decreasing length
-  for (int i = 1; i < batch; ++i) {
-    const int o = order[i];
+  for (int i = 1; i < batch; ++i) {     // stable, by decreasing last-partition length
+    const uint16_t o = order[i];
     int j = i;
-    while (j > 0 && tmp_len[order[j - 1]] < tmp_len[o]) { order[j] = order[j - 1]; --j; }
+    while (j > 0 && last_len[order[j - 1]] < last_len[o]) { order[j] = order[j - 1]; --j; }
     order[j] = o;
   }
-  int32_t sorted[kMaxPlanSeqs];
-  for (int i = 0; i < batch; ++i) sorted[i] = a.plan_last[order[i]];
-  for (int i = 0; i < batch; ++i) a.plan_last[i] = sorted[i];
+  for (int i = 0; i < batch; ++i) a.plan_last[i] = order[i];
   a.plan_seqs = batch;
   a.full_items = a.plan_pre[batch];
   a.n_items = a.full_items + batch;
@@ -574,7 +607,7 @@ static int decode_launch(bool fused, DecodeArgs& a, int batch, int max_context_l
   const int G = a.n_q / a.n_kv;
   a.batch = batch;
   a.plan_seqs = 0;
-  if (row_lens_host && batch <= kMaxPlanSeqs && a.P <= 0x7fff) build_plan(a, row_lens_host, batch);
+  if (row_lens_host && batch <= kMaxPlanSeqs && a.max_blocks <= 0xffff) build_plan(a, row_lens_host, batch);
   const int64_t items = a.plan_seqs > 0 ? (int64_t)a.n_items : (int64_t)batch * a.P;
   const int64_t grid = (items + 7) / 8 * 8 * a.n_kv;
   if (grid > 0x7fffffff) return PKV_ERR_INVALID_ARG;

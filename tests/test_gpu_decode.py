@@ -373,3 +373,41 @@ def test_workspace_reuse_across_calls(gpu):
         torch.cuda.synchronize()
         ref = attention.decode(q, kp, vp, bt, np.arange(B), lens, 0.125)
         check_attention(bits(out), ref, f"reuse {trial}")
+
+
+# ---------------------------------------------------- host schedule path ----
+
+@pytest.mark.parametrize("ps", [0, 128, 512])
+def test_host_schedule_matches_oracle(gpu, ps):
+    """With row lengths on the host the grid holds only real partitions
+    (per-row sizes, longest first); results must not change."""
+    rng = np.random.default_rng(31 + ps)
+    lens = np.array([0, 1, 15, 16, 17, 300, 511, 512, 513, 1030, 2500, 4097, 64, 999], np.int32)
+    B = len(lens)
+    q = W.randn_bf16(rng, (B, 32, 64))
+    nb = sum(W.blocks_for(n) for n in lens) + 5
+    kp = np.full((nb, 16, 8, 64), W.BF16_POISON, np.uint16)
+    vp = kp.copy()
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((B, 300), -1, np.int32)
+    k = 0
+    for s_, n in enumerate(lens):
+        m = W.blocks_for(n)
+        bt[s_, :m] = perm[k:k + m]
+        k += m
+        for p in range(n):
+            kp[bt[s_, p // 16], p % 16] = W.randn_bf16(rng, (8, 64))
+            vp[bt[s_, p // 16], p % 16] = W.randn_bf16(rng, (8, 64))
+    mx = int(lens.max())
+    ws = pkv.decode_workspace(B, 32, 8, mx, ps)
+    outs = []
+    for plan in (None, lens):
+        out = torch.empty((B, 32, 64), dtype=torch.bfloat16, device="cuda")
+        pkv.pkv_paged_attn_decode(out, dev_bf16(q), dev_bf16(kp), dev_bf16(vp), dev_i32(bt), None, dev_i32(lens),
+                                  mx, 0.125, ps, ws, row_lens_host=plan)
+        torch.cuda.synchronize()
+        outs.append(bits(out))
+    ref = attention.decode(q, kp, vp, bt, np.arange(B), lens, 0.125)
+    check_attention(outs[1], ref, f"host schedule ps={ps}")
+    assert not outs[1][0].any()                      # empty context: zero row
+    check_close_evaluations(outs[0], outs[1], f"schedule vs grid ps={ps}")
