@@ -9,32 +9,21 @@
 // title (each decode step re-reads every cached K/V of the sequence through the
 // block table).
 //
+// With host-known row lengths the call goes to the streaming kernel
+// (decode_stream.hip: one workgroup per CU over an equal share of all blocks);
+// this file's kernels serve the other cases (lengths only on the device,
+// shapes the streaming kernel does not cover).
+//
 // Work split.  A workgroup of 4 wave64s owns one (sequence, KV head, context
 // partition) and serves all G query heads that share the KV head, so each K/V
 // byte leaves HBM once for G queries.  The workgroups of one (sequence,
-// partition) are placed on one XCD (see decode_item).  The waves take the partition's 16-token
-// blocks round-robin, two blocks in flight per wave (unconditional, clamped
-// loads into two register sets, so the compiler can wait for exactly the older
-// set).  A partition's block ids are read once into a VGPR (lane i = block i)
-// and picked with v_readlane, so no scalar load sits in the loop.
-//
-// Lane layout inside a wave: lane = 8 r + c.  c picks dims 8c..8c+7 (one
-// 16-byte chunk), r picks rows r and r + 8 of the block.  One dwordx4 load per
-// lane covers rows r of all lanes = 8 contiguous 128-byte head rows of the pool
-// layout [block][16][kv head][64].
-//   scores   s = q . k with v_dot2_f32_bf16 (bf16 pairs, float32 sum): 4 per
-//            (row, head), then a 3-step DPP sum over the 8 lanes of the row;
-//   softmax  one running max per head shared by the whole wave, raised only
-//            when some score exceeds it by more than 8 (log2 units), so the
-//            rescale of the accumulators is rare; p = 2^(s*scale*log2e - m);
-//   p . V    p of rows r and r+8 packed as a bf16 pair, V of the same rows
-//            packed per dim with v_perm_b32, one v_dot2_f32_bf16 per
-//            (head, dim): float32 accumulation of bf16 products;
-//   sum      l accumulates the same bf16 p values as the numerator (dot2 with
-//            (1, 1)), so numerator and denominator see identical weights.
-// Rows past the context (or in a block whose id is out of range) are removed
-// by selects on the scores and on V, never by multiplying, so NaN in unused
-// pool slots cannot reach the output.
+// partition) are placed on one XCD (see decode_item).  The waves take the
+// partition's 16-token blocks round-robin, two blocks in flight per wave
+// (unconditional, clamped loads into two register sets, so the compiler can
+// wait for exactly the older set).  A partition's block ids are read once into
+// a VGPR (lane i = block i) and picked with v_readlane, so no scalar load sits
+// in the loop.  The per-block arithmetic (scores, lazy-rescaled online
+// softmax, p . V, masking by selects) is attn_block.h's.
 //
 // Merge.  The 8 row groups of a wave are summed pairwise with DPP and the rest
 // through LDS together with the other waves (each wave carries its own max).
@@ -49,15 +38,14 @@
 // kernel), the new token (position context_len - 1) takes part in the
 // attention from registers, and the workgroup of the last partition writes the
 // rotated key and the value into their pool row at the end of the kernel.
-#include "common.h"
+#include "attn_block.h"
+#include "decode_stream.h"
+
+#include <algorithm>
 
 namespace pkv {
 
 constexpr int kWaves = 4;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;   // running-max start (finite, so no inf - inf)
-constexpr float kTau = 8.0f;          // lazy rescale threshold, log2 units
-constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 constexpr int kMaxPlanSeqs = 256;     // batch rows a host schedule can describe
 
 struct DecodeArgs {
@@ -104,50 +92,6 @@ struct DecodeArgs {
 struct Item {
   int b, kvh, part, slot, n, nparts, t_begin, t_end;
 };
-
-struct KVRegs {
-  uint4 k0, k1, v0, v1;        // rows r and r + 8 of one block, this lane's 8 dims
-};
-
-// Element-wise select (keeps the four dwords in registers).
-__device__ __forceinline__ uint4 sel4(bool t, uint4 a, uint4 b) {
-  return make_uint4(t ? a.x : b.x, t ? a.y : b.y, t ? a.z : b.z, t ? a.w : b.w);
-}
-
-// Maximum over the wave; rows repeat across the 8 lanes of a row group.
-__device__ __forceinline__ float wave_max_rows(float x) {
-  x = fmaxf(x, dpp<kDppRowRor8>(x));
-  x = fmaxf(x, shfl_xor(x, 16));
-  x = fmaxf(x, shfl_xor(x, 32));
-  return x;
-}
-
-// Rotate this lane's 8 dims (chunk c) of a 64-dim head vector in place.  The
-// pair partner of dim i < 32 is dim i + 32, held by lane c ^ 4 of the row group.
-__device__ __forceinline__ uint4 rope_chunk(uint4 v, const float2* cs, int c) {
-  uint4 pv;
-  pv.x = (uint32_t)__builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 4) << 2, (int)v.x);
-  pv.y = (uint32_t)__builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 4) << 2, (int)v.y);
-  pv.z = (uint32_t)__builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 4) << 2, (int)v.z);
-  pv.w = (uint32_t)__builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 4) << 2, (int)v.w);
-  const uint32_t own[4] = {v.x, v.y, v.z, v.w};
-  const uint32_t oth[4] = {pv.x, pv.y, pv.z, pv.w};
-  uint32_t res[4];
-  const bool first_half = c < 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float r[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float mine = e ? bf16_hi(own[j]) : bf16_lo(own[j]);
-      const float other = e ? bf16_hi(oth[j]) : bf16_lo(oth[j]);
-      const float2 t = cs[2 * j + e];
-      r[e] = first_half ? rope_first(mine, other, t.x, t.y) : rope_second(other, mine, t.x, t.y);
-    }
-    res[j] = pack_bf16x2(r[0], r[1]);
-  }
-  return make_uint4(res[0], res[1], res[2], res[3]);
-}
 
 // Workgroup id -> (KV head, partition, sequence).  Workgroups are handed to the
 // 8 XCDs round-robin by linear id, so ids are arranged in groups of 8 items
@@ -257,38 +201,10 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  float m[G], thr[G], l[G], o[G][8];
+  OnlineSoftmax<G> acc;
+  acc.reset();
   const float C = a.scale_log2e;
   const float invC = 1.0f / C;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegBig;
-    thr[h] = -INFINITY;        // raw-score level above which m must be raised
-    l[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
-  }
-
-  // Raise the wave's running max to cover raw scores s0/s1 (rare: only when
-  // some score exceeds the current max by more than kTau in log2 units).
-  auto rescale_if_needed = [&](const float (&s0)[G], const float (&s1)[G]) {
-    bool need = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) need |= (s0[h] > thr[h]) | (s1[h] > thr[h]);
-    if (__any(need)) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float mx = fmaxf(s0[h], s1[h]) * C;
-        const float mn = fmaxf(m[h], wave_max_rows(mx));
-        const float alpha = fast_exp2(m[h] - mn);
-        l[h] *= alpha;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[h][j] *= alpha;
-        m[h] = mn;
-        thr[h] = (mn + kTau) * invC;
-      }
-    }
-  };
 
   // In the fused step the new token's pool row is not read: it joins from
   // registers after the loop.
@@ -322,46 +238,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
     auto process = [&](const KVRegs& R, int i) {
       const bool blk_ok = __builtin_amdgcn_readlane(tab, i) >= 0;
       const int tok0 = (jb_begin + cb + i) * kBlock + r;
-      const bool ok0 = blk_ok && tok0 < t_loop_end;
-      const bool ok1 = blk_ok && tok0 + 8 < t_loop_end;
-      float s0[G], s1[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d0 = dot2_bf16(qv[h].x, R.k0.x, 0.f);
-        float d1 = dot2_bf16(qv[h].x, R.k1.x, 0.f);
-        d0 = dot2_bf16(qv[h].y, R.k0.y, d0);
-        d1 = dot2_bf16(qv[h].y, R.k1.y, d1);
-        d0 = dot2_bf16(qv[h].z, R.k0.z, d0);
-        d1 = dot2_bf16(qv[h].z, R.k1.z, d1);
-        d0 = dot2_bf16(qv[h].w, R.k0.w, d0);
-        d1 = dot2_bf16(qv[h].w, R.k1.w, d1);
-        d0 = sum8(d0);
-        d1 = sum8(d1);
-        // keep the score computation unconditional (no branch around it)
-        __asm__ volatile("" : "+v"(d0), "+v"(d1));
-        s0[h] = ok0 ? d0 : -INFINITY;
-        s1[h] = ok1 ? d1 : -INFINITY;
-      }
-      rescale_if_needed(s0, s1);
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      const uint4 v0 = sel4(ok0, R.v0, z);
-      const uint4 v1 = sel4(ok1, R.v1, z);
-      const uint32_t vlo[4] = {pack_lo_halves(v0.x, v1.x), pack_lo_halves(v0.y, v1.y),
-                               pack_lo_halves(v0.z, v1.z), pack_lo_halves(v0.w, v1.w)};
-      const uint32_t vhi[4] = {pack_hi_halves(v0.x, v1.x), pack_hi_halves(v0.y, v1.y),
-                               pack_hi_halves(v0.z, v1.z), pack_hi_halves(v0.w, v1.w)};
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p0 = fast_exp2(__builtin_fmaf(s0[h], C, -m[h]));
-        const float p1 = fast_exp2(__builtin_fmaf(s1[h], C, -m[h]));
-        const uint32_t pp = pack_bf16x2(p0, p1);
-        l[h] = dot2_bf16(pp, kOnesBf16x2, l[h]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o[h][2 * j] = dot2_bf16(pp, vlo[j], o[h][2 * j]);
-          o[h][2 * j + 1] = dot2_bf16(pp, vhi[j], o[h][2 * j + 1]);
-        }
-      }
+      acc.block(qv, R, blk_ok && tok0 < t_loop_end, blk_ok && tok0 + 8 < t_loop_end, C, invC);
     };
 
     KVRegs X, Y;
@@ -379,39 +256,15 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
 
   if constexpr (FUSED) {
     // The new token, from registers, counted once (row group 0 of wave 0).
-    if (part == nparts - 1 && n > 0 && w == 0) {
-      float s0[G], s1[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d = dot2_bf16(qv[h].x, knew.x, 0.f);
-        d = dot2_bf16(qv[h].y, knew.y, d);
-        d = dot2_bf16(qv[h].z, knew.z, d);
-        d = dot2_bf16(qv[h].w, knew.w, d);
-        s0[h] = r == 0 ? sum8(d) : -INFINITY;
-        s1[h] = -INFINITY;
-      }
-      rescale_if_needed(s0, s1);
-      const uint4 v0 = sel4(r == 0, vnew, make_uint4(0, 0, 0, 0));
-      const uint32_t vv[4] = {v0.x, v0.y, v0.z, v0.w};
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint32_t pp = pack_bf16x2(fast_exp2(__builtin_fmaf(s0[h], C, -m[h])), 0.f);
-        l[h] = dot2_bf16(pp, kOnesBf16x2, l[h]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o[h][2 * j] = dot2_bf16(pp, vv[j] & 0xffffu, o[h][2 * j]);
-          o[h][2 * j + 1] = dot2_bf16(pp, vv[j] >> 16, o[h][2 * j + 1]);
-        }
-      }
-    }
+    if (part == nparts - 1 && n > 0 && w == 0) acc.token(qv, knew, vnew, r == 0, C, invC);
   }
 
   // ---- merge: row-group pairs by DPP, the rest through LDS ----------------
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    l[h] += dpp<kDppRowRor8>(l[h]);
+    acc.l[h] += dpp<kDppRowRor8>(acc.l[h]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[h][j] += dpp<kDppRowRor8>(o[h][j]);
+    for (int j = 0; j < 8; ++j) acc.o[h][j] += dpp<kDppRowRor8>(acc.o[h][j]);
   }
   __shared__ float sm_o[kWaves][4][G][kHeadDim];
   __shared__ float sm_l[kWaves][4][G];
@@ -420,14 +273,16 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
     const int grp = r >> 1;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      *reinterpret_cast<float4*>(&sm_o[w][grp][h][c * 8]) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-      *reinterpret_cast<float4*>(&sm_o[w][grp][h][c * 8 + 4]) = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
-      if (c == 0) sm_l[w][grp][h] = l[h];
+      *reinterpret_cast<float4*>(&sm_o[w][grp][h][c * 8]) =
+          make_float4(acc.o[h][0], acc.o[h][1], acc.o[h][2], acc.o[h][3]);
+      *reinterpret_cast<float4*>(&sm_o[w][grp][h][c * 8 + 4]) =
+          make_float4(acc.o[h][4], acc.o[h][5], acc.o[h][6], acc.o[h][7]);
+      if (c == 0) sm_l[w][grp][h] = acc.l[h];
     }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) sm_m[w][h] = m[h];
+    for (int h = 0; h < G; ++h) sm_m[w][h] = acc.m[h];
   }
   __syncthreads();
 
@@ -593,8 +448,36 @@ static void build_plan(DecodeArgs& a, const int32_t* row_lens_host, int batch) {
   a.n_items = a.full_items + batch;
 }
 
-static int decode_launch(bool fused, DecodeArgs& a, int batch, int max_context_len, int partition_size,
-                         const int32_t* row_lens_host, void* workspace, size_t workspace_bytes, hipStream_t st) {
+static int decode_launch(bool fused, DecodeArgs& a, float scale, int batch, int max_context_len,
+                         int partition_size, const int32_t* row_lens_host, void* workspace,
+                         size_t workspace_bytes, hipStream_t st) {
+  if (row_lens_host) {
+    StreamCall sc{};
+    sc.out = a.out;
+    sc.q = a.q;
+    sc.k_new = a.k_new;
+    sc.v_new = a.v_new;
+    sc.k_pool = a.k_pool;
+    sc.v_pool = a.v_pool;
+    sc.num_blocks = a.num_blocks;
+    sc.block_table = a.bt;
+    sc.bt_row_stride = a.bt_stride;
+    sc.num_slots = a.num_slots;
+    sc.max_blocks = a.max_blocks;
+    sc.slot_ids = a.slot_ids;
+    sc.row_lens_host = row_lens_host;
+    sc.batch = batch;
+    sc.n_q = a.n_q;
+    sc.n_kv = a.n_kv;
+    sc.cos_sin = reinterpret_cast<const float*>(a.rope);
+    sc.max_pos = a.max_pos;
+    sc.scale = scale;
+    sc.workspace = workspace;
+    sc.workspace_bytes = workspace_bytes;
+    sc.stream = st;
+    const int rc = stream_decode(fused, sc);
+    if (rc != -1) return rc;
+  }
   a.ps = partition_size > 0 ? partition_size : auto_partition(batch, a.n_kv, max_context_len);
   const int64_t P = decode_parts(max_context_len, a.ps);
   if (P > 65535) return PKV_ERR_INVALID_ARG;
@@ -642,7 +525,8 @@ extern "C" size_t pkv_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_
       partition_size < 0)
     return 0;
   const int ps = partition_size > 0 ? partition_size : auto_partition(batch, n_kv_heads, max_context_len);
-  return ws_layout(batch, n_q_heads, n_kv_heads, decode_parts(max_context_len, ps)).total;
+  return std::max(ws_layout(batch, n_q_heads, n_kv_heads, decode_parts(max_context_len, ps)).total,
+                  stream_workspace_bytes(n_q_heads, n_kv_heads));
 }
 
 extern "C" int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -716,7 +600,7 @@ extern "C" int pkv_paged_attn_decode(pkv_bf16* out, const pkv_bf16* q, const pkv
   if (rc != PKV_OK) return rc < 0 ? PKV_OK : rc;
   DecodeArgs a = base_args(out, q, k_pool, v_pool, num_blocks, block_table, bt_row_stride, num_slots,
                            max_blocks_per_seq, slot_ids, context_lens, n_q_heads, n_kv_heads, scale);
-  return decode_launch(false, a, batch, max_context_len, partition_size, row_lens_host, workspace,
+  return decode_launch(false, a, scale, batch, max_context_len, partition_size, row_lens_host, workspace,
                        workspace_bytes, (hipStream_t)stream);
 }
 
@@ -741,6 +625,6 @@ extern "C" int pkv_paged_decode_fused(pkv_bf16* out, const pkv_bf16* q, const pk
   a.v_new = v_new;
   a.rope = reinterpret_cast<const float2*>(cos_sin);
   a.max_pos = max_pos;
-  return decode_launch(true, a, batch, max_context_len, partition_size, row_lens_host, workspace,
+  return decode_launch(true, a, scale, batch, max_context_len, partition_size, row_lens_host, workspace,
                        workspace_bytes, (hipStream_t)stream);
 }

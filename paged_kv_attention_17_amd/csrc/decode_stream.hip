@@ -1,0 +1,495 @@
+// Streaming decode attention for gfx950: one 1024-thread workgroup per CU,
+// each taking an equal, contiguous share of all 16-token blocks of the batch.
+//
+// Source: the Korean page of "An Inference Engine in 1,500 Lines of CUDA: The
+// Map" ("What is in the box" table: online softmax and PagedAttention, four
+// query heads per KV head) and the sixth chapter's title (each decode step
+// re-reads every cached K/V of the sequence through the block table).  The
+// split of the work across the chip is this library's own.
+//
+// Why.  Decode attention reads every cached block once, so the step is an HBM
+// stream of about 2 KB per token and layer.  With one workgroup per
+// (sequence, KV head, partition) the launch has a long ramp and tail: each
+// workgroup first waits for its table slice and its first blocks, workgroups
+// on one CU progress at very different speeds, and the last ones run alone.
+// Here the batch's blocks are laid end to end (row by row, the block stream)
+// and cut into equal shares, one per CU; every block is read whole (all KV
+// heads, 16 KB of K and V each), so a CU streams contiguous 1 KB token rows.
+//
+// Work inside a workgroup.  16 waves = n_kv heads x (16 / n_kv) lanes of
+// blocks: wave w serves KV head w % n_kv and takes every (16 / n_kv)-th block
+// of the share, with two blocks in flight (the per-block arithmetic is
+// attn_block.h's).  The rows the share touches (at most kMaxRows) have their
+// queries staged in LDS, rotated when fused.  When a wave's next block belongs
+// to another row it folds its state for the finished row (DPP and lane
+// shuffles over the 8 row groups) into that row's LDS slot, without waiting
+// for the other waves.  After the last block one barrier, then the waves of
+// each KV head are merged per row: a row that lies inside the share is
+// finished in place, a row cut by the share's ends leaves (max, sum,
+// unnormalised output) in one of the share's two workspace records, and a
+// small kernel merges those records.
+//
+// Fused variant.  The workgroup holding a row's last block rotates the row's
+// new key, keeps key and value in LDS and writes them into the pool (position
+// context_len - 1).  Pool reads of that block stop before the new token, which
+// joins the attention from LDS in the wave that processes the block, so no
+// read waits for the write.
+#include "attn_block.h"
+#include "decode_stream.h"
+
+#include <algorithm>
+#include <atomic>
+
+namespace pkv {
+
+namespace {
+
+constexpr int kWaves = 16;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kMaxRows = 4;           // rows one share may touch
+constexpr int kMaxSeqs = 256;         // batch rows described in the arguments
+constexpr int kMaxQ = 32;             // query heads staged per row
+constexpr int kMaxGrid = 512;         // workgroups (one per CU)
+constexpr int kRec = kHeadDim + 2;    // partial record per query head: o[64], max, sum
+
+struct StreamArgs {
+  uint16_t* out;
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  const int32_t* bt;
+  const int32_t* slot_ids;
+  const float2* rope;
+  float* ws;                   // records [2 * grid][n_q][kRec]
+  int64_t bt_stride;
+  int num_blocks;
+  int num_slots;
+  int max_blocks;
+  int n_q;
+  int n_kv;
+  int max_pos;
+  int batch;
+  float scale_log2e;
+  int share;                   // blocks per workgroup
+  int total;                   // blocks in the stream
+  int32_t row_start[kMaxSeqs + 1];   // first stream block of each row
+  int32_t row_n[kMaxSeqs];           // tokens of each row
+};
+static_assert(sizeof(StreamArgs) <= 4096, "kernel argument block");
+
+__device__ __forceinline__ int row_slot(const StreamArgs& a, int b) {
+  const int s = a.slot_ids ? a.slot_ids[b] : b;
+  return (s >= 0 && s < a.num_slots) ? s : -1;
+}
+
+// Row holding stream block p (the last row whose start is <= p; empty rows
+// share their start with the next row and are passed over).
+__device__ __forceinline__ int stream_row(const StreamArgs& a, int p) {
+  int lo = 0, hi = a.batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.row_start[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Rotate chunk `own` (8 dims starting at 8 * ch) against its pair partner
+// chunk (ch ^ 4) with the position's cos/sin row.
+__device__ __forceinline__ uint4 rope_own_chunk(uint4 own, uint4 oth, const float2* trow, int ch) {
+  const uint32_t o[4] = {own.x, own.y, own.z, own.w};
+  const uint32_t p[4] = {oth.x, oth.y, oth.z, oth.w};
+  uint32_t res[4];
+  const bool first_half = ch < 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float r[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float mine = e ? bf16_hi(o[j]) : bf16_lo(o[j]);
+      const float other = e ? bf16_hi(p[j]) : bf16_lo(p[j]);
+      const float2 t = trow[(ch & 3) * 8 + 2 * j + e];
+      r[e] = first_half ? rope_first(mine, other, t.x, t.y) : rope_second(other, mine, t.x, t.y);
+    }
+    res[j] = pack_bf16x2(r[0], r[1]);
+  }
+  return make_uint4(res[0], res[1], res[2], res[3]);
+}
+
+template <int G, bool FUSED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void stream_kernel(StreamArgs a) {
+  const int B0 = blockIdx.x * a.share;
+  const int B1 = min(B0 + a.share, a.total);
+  if (B0 >= B1) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = wave_uniform(tid >> 6);
+  const int c = lane & 7;
+  const int r = lane >> 3;
+  const int n_kv = a.n_kv;
+  const int S = kWaves / n_kv;           // waves per KV head
+  const int h = w % n_kv;                // this wave's KV head
+  const int s = w / n_kv;                // and its lane of blocks
+  const int bf = stream_row(a, B0);
+  const int nrows = stream_row(a, B1 - 1) - bf + 1;
+  const int64_t row_elems = (int64_t)n_kv * kHeadDim;
+  const float C = a.scale_log2e;
+  const float invC = 1.0f / C;
+
+  __shared__ uint4 sq[kMaxRows][kMaxQ * 8];                 // queries: [row][head][chunk]
+  __shared__ uint4 snew[kMaxRows][2][kWaves * 8];           // fused: new key / value [row][k|v][head][chunk]
+  __shared__ float sp[kMaxRows][kWaves][G][kRec];           // per-wave partials of each row
+  __shared__ int srow_ok[kMaxRows];                         // the row's table slot is valid
+
+  // ---- this wave's blocks ----------------------------------------------------
+  const int len = B1 - B0;
+  const int n_w = len > s ? (len - s + S - 1) / S : 0;       // blocks of this wave
+  const uint32_t block_bytes = (uint32_t)(kBlock * row_elems * 2);
+  const uint32_t lane_off = (uint32_t)(((int64_t)r * row_elems + h * kHeadDim + c * 8) * 2);
+  const uint32_t lane_off8 = lane_off + (uint32_t)(8 * row_elems * 2);
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+
+  // lane i: this wave's block cb + i -> pool block id and (row << 8 | tokens
+  // to read from the pool; the fused step's new token is not among them)
+  auto block_info = [&](int cb, int ncb, int& tab, int& meta) {
+    const int p = B0 + s + S * (cb + min(lane, ncb - 1));
+    int ri = 0;
+    for (int i = 1; i < nrows; ++i) ri = p >= a.row_start[bf + i] ? i : ri;
+    int start = a.row_start[bf], n = a.row_n[bf];
+    for (int i = 1; i < nrows; ++i) {
+      start = i == ri ? a.row_start[bf + i] : start;
+      n = i == ri ? a.row_n[bf + i] : n;
+    }
+    const int j = p - start;
+    const int slot = row_slot(a, bf + ri);
+    int valid = (FUSED ? n - 1 : n) - j * kBlock;
+    valid = valid > kBlock ? kBlock : (valid < 0 ? 0 : valid);
+    tab = -1;
+    if (slot >= 0 && j < a.max_blocks && valid > 0) {
+      const int blk = a.bt[(int64_t)slot * a.bt_stride + j];
+      tab = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+    }
+    meta = (ri << 8) | valid;
+  };
+  auto issue = [&](KVRegs& R, int tab, int ncb, int i) {
+    int blk = __builtin_amdgcn_readlane(tab, min(i, ncb - 1));
+    blk = blk < 0 ? 0 : blk;
+    const auto rk = buf_rsrc(kbase + (size_t)blk * block_bytes, block_bytes);
+    const auto rv = buf_rsrc(vbase + (size_t)blk * block_bytes, block_bytes);
+    R.k0 = buf_load16(rk, lane_off);
+    R.k1 = buf_load16(rk, lane_off8);
+    R.v0 = buf_load16(rv, lane_off);
+    R.v1 = buf_load16(rv, lane_off8);
+  };
+  // the first table slice is requested before the staging below waits
+  int ncb = min(kWave, n_w);
+  int tab = -1, meta = 0;
+  if (n_w > 0) block_info(0, ncb, tab, meta);
+
+  // ---- queries of the share's rows (rotated by position n - 1 when fused) ----
+  for (int e = tid; e < nrows * a.n_q * 8; e += kThreads) {
+    const int i = e / (a.n_q * 8);
+    const int rem = e - i * a.n_q * 8;
+    const int ch = rem & 7;
+    const int b = bf + i;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (rem >> 3)) * kHeadDim;
+    uint4 v = *reinterpret_cast<const uint4*>(qrow + ch * 8);
+    if constexpr (FUSED) {
+      const int pos = a.row_n[b] - 1;
+      if (pos >= 0 && pos < a.max_pos) {
+        const uint4 p = *reinterpret_cast<const uint4*>(qrow + (ch ^ 4) * 8);
+        v = rope_own_chunk(v, p, a.rope + (int64_t)pos * (kHeadDim / 2), ch);
+      }
+    }
+    sq[i][rem] = v;
+  }
+  // ---- fused: the new token of every row whose last block is here: rotated
+  // key and value into LDS (it joins the attention from there) and into the
+  // pool (no workgroup reads that pool row in this launch) ---------------------
+  if constexpr (FUSED) {
+    if (tid < nrows) srow_ok[tid] = row_slot(a, bf + tid) >= 0;
+    for (int e = tid; e < nrows * n_kv * 8; e += kThreads) {
+      const int i = e / (n_kv * 8);
+      const int rem = e - i * n_kv * 8;
+      const int ch = rem & 7;
+      const int kvh = rem >> 3;
+      const int b = bf + i;
+      const int n = a.row_n[b];
+      const int last = a.row_start[b + 1] - 1;
+      if (n <= 0 || last < B0 || last >= B1) continue;
+      const int pos = n - 1;
+      const uint16_t* krow = a.k_new + ((int64_t)b * n_kv + kvh) * kHeadDim;
+      uint4 k = *reinterpret_cast<const uint4*>(krow + ch * 8);
+      if (pos < a.max_pos) {
+        const uint4 p = *reinterpret_cast<const uint4*>(krow + (ch ^ 4) * 8);
+        k = rope_own_chunk(k, p, a.rope + (int64_t)pos * (kHeadDim / 2), ch);
+      }
+      const uint4 v = *reinterpret_cast<const uint4*>(a.v_new + ((int64_t)b * n_kv + kvh) * kHeadDim + ch * 8);
+      snew[i][0][rem] = k;
+      snew[i][1][rem] = v;
+      const int slot = row_slot(a, b);
+      if (slot < 0) continue;
+      const int blk = a.bt[(int64_t)slot * a.bt_stride + pos / kBlock];
+      if (blk < 0 || blk >= a.num_blocks) continue;
+      const int64_t off = ((int64_t)blk * kBlock + pos % kBlock) * row_elems + kvh * kHeadDim + ch * 8;
+      *reinterpret_cast<uint4*>(a.k_pool + off) = k;
+      *reinterpret_cast<uint4*>(a.v_pool + off) = v;
+    }
+  }
+  __syncthreads();
+
+  OnlineSoftmax<G> acc;
+  acc.reset();
+  uint4 qv[G];
+  int cur = 0;                            // row of the share being accumulated
+  auto load_q = [&]() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) qv[g] = sq[cur][(h * G + g) * 8 + c];
+  };
+  load_q();
+
+  // Fold the wave's state for row `cur` (sum over the 8 row groups) into its
+  // LDS slot and move on to the next row.
+  auto flush = [&]() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float l = acc.l[g];
+      l += dpp<kDppRowRor8>(l);
+      l += shfl_xor(l, 16);
+      l += shfl_xor(l, 32);
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float x = acc.o[g][j];
+        x += dpp<kDppRowRor8>(x);
+        x += shfl_xor(x, 16);
+        x += shfl_xor(x, 32);
+        o[j] = x;
+      }
+      if (r == 0) {
+        *reinterpret_cast<float4*>(&sp[cur][w][g][c * 8]) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4*>(&sp[cur][w][g][c * 8 + 4]) = make_float4(o[4], o[5], o[6], o[7]);
+        if (c == 0) {
+          sp[cur][w][g][kHeadDim] = acc.m[g];
+          sp[cur][w][g][kHeadDim + 1] = l;
+        }
+      }
+    }
+    ++cur;
+    acc.reset();
+    if (cur < nrows) load_q();
+  };
+
+  for (int cb = 0; cb < n_w; cb += kWave) {
+    if (cb > 0) {
+      ncb = min(kWave, n_w - cb);
+      block_info(cb, ncb, tab, meta);
+    }
+    KVRegs X, Y;
+    issue(X, tab, ncb, 0);
+    issue(Y, tab, ncb, 1);
+    auto step = [&](const KVRegs& R, int i) {
+      const int mt = __builtin_amdgcn_readlane(meta, i);
+      while (cur < (mt >> 8)) flush();
+      const bool blk_ok = __builtin_amdgcn_readlane(tab, i) >= 0;
+      const int valid = mt & 0xff;
+      acc.block(qv, R, blk_ok && r < valid, blk_ok && r + 8 < valid, C, invC);
+      if constexpr (FUSED) {
+        // the row's last block: add the new token from LDS
+        const int b = bf + cur;
+        if (B0 + s + S * (cb + i) == a.row_start[b + 1] - 1 && a.row_n[b] > 0 && srow_ok[cur])
+          acc.token(qv, snew[cur][0][h * 8 + c], snew[cur][1][h * 8 + c], r == 0, C, invC);
+      }
+    };
+    for (int i = 0;; i += 2) {
+      step(X, i);
+      issue(X, tab, ncb, i + 2);
+      if (i + 1 >= ncb) break;
+      step(Y, i + 1);
+      issue(Y, tab, ncb, i + 3);
+      if (i + 2 >= ncb) break;
+    }
+  }
+  while (cur < nrows) flush();
+  __syncthreads();
+
+  // ---- merge the KV heads' waves per row: finish rows inside the share,
+  // leave records for rows cut by its ends ------------------------------------
+  for (int e = tid; e < nrows * a.n_q * kHeadDim; e += kThreads) {
+    const int i = e / (a.n_q * kHeadDim);
+    const int rem = e - i * a.n_q * kHeadDim;
+    const int b = bf + i;
+    if (a.row_n[b] <= 0) continue;
+    const int qh = rem / kHeadDim;
+    const int d = rem % kHeadDim;
+    const int hh = qh / G;
+    const int g = qh % G;
+    float M = sp[i][hh][g][kHeadDim];
+    for (int t = 1; t < S; ++t) M = fmaxf(M, sp[i][hh + t * n_kv][g][kHeadDim]);
+    float L = 0.f, O = 0.f;
+    for (int t = 0; t < S; ++t) {
+      const float* src = sp[i][hh + t * n_kv][g];
+      const float f = fast_exp2(src[kHeadDim] - M);
+      L += f * src[kHeadDim + 1];
+      O += f * src[d];
+    }
+    if (a.row_start[b] >= B0 && a.row_start[b + 1] <= B1) {
+      a.out[((int64_t)b * a.n_q + qh) * kHeadDim + d] = to_bf16(L > 0.f ? O / L : 0.f);
+    } else {
+      const int rec = 2 * (int)blockIdx.x + (i == 0 ? 0 : 1);
+      float* dst = a.ws + ((int64_t)rec * a.n_q + qh) * kRec;
+      dst[d] = O;
+      if (d == 0) {
+        dst[kHeadDim] = M;
+        dst[kHeadDim + 1] = L;
+      }
+    }
+  }
+}
+
+// Merge of the records of rows cut by share ends: one workgroup per (row, KV
+// head), thread = (query head, dim).  Share w holds the row in record 2w when
+// the row contains the share's first block, else in record 2w + 1.  Empty
+// rows get zeros; rows inside one share were finished there.
+template <int G>
+__global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs a) {
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int n = a.row_n[b];
+  const int64_t obase = ((int64_t)b * a.n_q + kvh * G) * kHeadDim;
+  if (n <= 0) {
+    for (int e = threadIdx.x; e < G * kHeadDim; e += blockDim.x) a.out[obase + e] = 0;
+    return;
+  }
+  const int start = a.row_start[b];
+  const int w0 = start / a.share;
+  const int w1 = (a.row_start[b + 1] - 1) / a.share;
+  if (w0 == w1) return;
+  for (int e = threadIdx.x; e < G * kHeadDim; e += blockDim.x) {
+    const int qh = kvh * G + e / kHeadDim;
+    const int d = e % kHeadDim;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int w = w0; w <= w1; w += 8) {
+      float mv[8], lv[8], ov[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ww = w + j <= w1 ? w + j : w1;
+        const int rec = 2 * ww + ((ww > w0 || start == w0 * a.share) ? 0 : 1);
+        const float* src = a.ws + ((int64_t)rec * a.n_q + qh) * kRec;
+        mv[j] = w + j <= w1 ? src[kHeadDim] : -INFINITY;
+        lv[j] = src[kHeadDim + 1];
+        ov[j] = src[d];
+      }
+      float mm = M;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mm = fmaxf(mm, mv[j]);
+      const float f0 = M == -INFINITY ? 0.f : fast_exp2(M - mm);
+      L *= f0;
+      O *= f0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float f = mv[j] == -INFINITY ? 0.f : fast_exp2(mv[j] - mm);
+        L += f * lv[j];
+        O += f * ov[j];
+      }
+      M = mm;
+    }
+    a.out[obase + e] = to_bf16(L > 0.f ? O / L : 0.f);
+  }
+}
+
+int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cus[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <bool FUSED>
+const void* pick_stream(int G) {
+  return G == 1 ? (const void*)stream_kernel<1, FUSED>
+       : G == 2 ? (const void*)stream_kernel<2, FUSED>
+                : (const void*)stream_kernel<4, FUSED>;
+}
+
+}  // namespace
+
+size_t stream_workspace_bytes(int n_q, int n_kv) {
+  (void)n_kv;
+  return (size_t)2 * kMaxGrid * n_q * kRec * sizeof(float);
+}
+
+int stream_decode(bool fused, const StreamCall& c) {
+  const int G = c.n_kv > 0 ? c.n_q / c.n_kv : 0;
+  if (!c.row_lens_host || c.batch <= 0 || c.batch > kMaxSeqs || G > 4 || c.n_q > kMaxQ ||
+      c.n_kv > kWaves || kWaves % c.n_kv || !c.workspace)
+    return -1;
+  StreamArgs a{};
+  a.out = c.out;
+  a.q = c.q;
+  a.k_new = c.k_new;
+  a.v_new = c.v_new;
+  a.k_pool = c.k_pool;
+  a.v_pool = c.v_pool;
+  a.bt = c.block_table;
+  a.slot_ids = c.slot_ids;
+  a.rope = reinterpret_cast<const float2*>(c.cos_sin);
+  a.bt_stride = c.bt_row_stride;
+  a.num_blocks = c.num_blocks;
+  a.num_slots = c.num_slots;
+  a.max_blocks = c.max_blocks;
+  a.n_q = c.n_q;
+  a.n_kv = c.n_kv;
+  a.max_pos = c.max_pos;
+  a.batch = c.batch;
+  a.scale_log2e = c.scale * kLog2e;
+  // the block stream: rows end to end, each ceil(n / 16) blocks
+  int64_t total = 0;
+  a.row_start[0] = 0;
+  for (int b = 0; b < c.batch; ++b) {
+    int n = c.row_lens_host[b];
+    n = n < 0 ? 0 : (n > c.max_blocks * kBlock ? c.max_blocks * kBlock : n);
+    a.row_n[b] = n;
+    total += (n + kBlock - 1) / kBlock;
+    if (total > 0x3fffffff) return -1;
+    a.row_start[b + 1] = (int32_t)total;
+  }
+  if (total == 0) return -1;
+  const int cus = device_cus();
+  if (cus <= 0) return -1;
+  int grid = std::min(cus, kMaxGrid);
+  a.share = (int)((total + grid - 1) / grid);
+  grid = (int)((total + a.share - 1) / a.share);
+  a.total = (int)total;
+  if (c.workspace_bytes < (size_t)2 * grid * c.n_q * kRec * sizeof(float)) return -1;
+  a.ws = static_cast<float*>(c.workspace);
+  // every share must touch at most kMaxRows rows (empty rows in between count)
+  for (int g = 0, b = 0; g < grid; ++g) {
+    const int p0 = g * a.share;
+    const int p1 = std::min(p0 + a.share, a.total) - 1;
+    while (b + 1 < c.batch && a.row_start[b + 1] <= p0) ++b;
+    int e = b;
+    while (e + 1 < c.batch && a.row_start[e + 1] <= p1) ++e;
+    if (e - b + 1 > kMaxRows) return -1;
+  }
+  void* args[] = {&a};
+  hipStream_t st = static_cast<hipStream_t>(c.stream);
+  const void* fn = fused ? pick_stream<true>(G) : pick_stream<false>(G);
+  int rc = launch_status(hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st));
+  if (rc != PKV_OK) return rc;
+  const void* mg = G == 1 ? (const void*)stream_merge_kernel<1>
+                 : G == 2 ? (const void*)stream_merge_kernel<2>
+                          : (const void*)stream_merge_kernel<4>;
+  return launch_status(hipLaunchKernel(mg, dim3(c.n_kv, c.batch), dim3(256), args, 0, st));
+}
+
+}  // namespace pkv

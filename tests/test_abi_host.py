@@ -36,15 +36,16 @@ def test_status_strings(lib):
 
 
 def test_workspace_and_partition_sizes(lib):
-    assert pkv.pkv_decode_workspace_bytes(1, 32, 8, 64, 17, 0) == 0        # one partition: none needed
+    stream = 2 * 512 * 32 * 66 * 4      # streaming kernel: two records per CU (at most 512 CUs)
+    assert pkv.pkv_decode_workspace_bytes(1, 32, 8, 64, 17, 0) == stream
     ps = pkv.pkv_decode_partition_size(64, 8, 4096)
     assert ps % 16 == 0 and ps >= 64
     P = -(-4096 // ps)
     up = lambda x: -(-x // 256) * 256  # noqa: E731
 
     def expect(B, nq, nkv, P):
-        # partial outputs and partial (max, sum)
-        return up(B * nq * P * 64 * 4) + up(B * nq * P * 2 * 4)
+        # the larger of: per-partition outputs + (max, sum), and the streaming records
+        return max(up(B * nq * P * 64 * 4) + up(B * nq * P * 2 * 4), 2 * 512 * nq * 66 * 4)
     assert pkv.pkv_decode_workspace_bytes(64, 32, 8, 64, 4096, 0) == expect(64, 32, 8, P)
     assert pkv.pkv_decode_workspace_bytes(2, 32, 8, 64, 100, 16) == expect(2, 32, 8, 7)
     assert pkv.pkv_decode_workspace_bytes(2, 32, 8, 32, 100, 16) == 0       # unsupported head_dim
