@@ -6,16 +6,18 @@ Workload: B=64 sequences, 16 layers, contexts uniform in [512, 4096], 32 query
 needed with tables interleaved round-robin over (layer, sequence).  One step
 = one decode step of all 16 layers through the native pkv_decode_step: host
 block allocation, then per layer RoPE on the new q/k, KV append and paged
-attention (split-context partitions merged in the same launch), fused into
-one kernel per layer.  Inputs are seeded synthetic
+attention fused into one call: the streaming kernel (one workgroup per CU
+over an equal share of all blocks) plus a small kernel that merges the rows
+cut by share ends.  Inputs are seeded synthetic
 data resident in HBM before timing starts; contexts grow by one token per
 step as in a real decode loop.
 
 Prints ONE JSON line:
   value        KV GB/s over the whole step = algorithmic KV bytes of all
                layers / step wall time (2,048 B per context token per layer)
-  roofline     the per-layer decode kernel alone: algorithmic bytes per
-               launch / its mean launch duration (HIP events on its stream)
+  roofline     the per-layer decode call alone (streaming kernel + its
+               merge kernel, timed together): algorithmic bytes per call /
+               its mean duration (HIP events on its stream)
   cpu_baseline the float64 CPU oracle on a bounded sample of the same step
 """
 from __future__ import annotations
@@ -42,7 +44,7 @@ def log(*a):
 
 def decode_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("decode.hip", "common.h"):
+    for f in ("decode_stream.hip", "decode.hip", "attn_block.h", "common.h"):
         with open(os.path.join(ROOT, "paged_kv_attention_17_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -185,9 +187,9 @@ def main():
     log(f"step: {t_step * 1e6:.1f} us ({t_step * 1e6 / L:.2f} us/layer), KV {value:.0f} GB/s, "
         f"host wall {wall / args.steps * 1e6:.1f} us/step")
 
-    # ---- dominant kernel: the fused per-layer decode kernel alone, events ---
-    # around every launch (it re-appends the last step's token in place, so
-    # the cache does not change)
+    # ---- dominant kernel: the fused per-layer decode call alone, events ----
+    # around every call (it re-appends the last step's token in place, so the
+    # cache does not change)
     ctx_now = eng.cached.copy()
     bytes_per_launch = int(ctx_now.sum()) * KV_BYTES_PER_TOKEN
     pairs = []
@@ -240,7 +242,7 @@ def main():
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "pkv_paged_decode_fused (decode_kernel<4, fused>)",
+                     "kernel": "pkv_paged_decode_fused call: stream_kernel<4, fused> + stream_merge_kernel<4>",
                      "bytes_per_launch": bytes_per_launch,
                      "us_per_launch": round(t_attn * 1e6, 3), "source_hash": src_hash},
         "copy_kernel_GBps": round(copy_gbs, 1),

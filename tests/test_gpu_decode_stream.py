@@ -209,6 +209,30 @@ def test_stream_fused_step_equals_separate_calls(gpu):
     check_attention(bits(out1), ref, "stream fused")
 
 
+def test_stream_workspace_garbage_and_reuse(gpu):
+    """The workspace holds no state between calls: refilled with all-ones
+    bits (NaN as float) before every call, and calls of different batches
+    follow each other, including one whose rows span many shares."""
+    rng = np.random.default_rng(16)
+    cases = [np.array([4096, 3000, 17, 2500, 1, 4000, 999], np.int32),
+             np.array([70000 // 16 * 16, 33], np.int32),
+             np.array([1500] * 40, np.int32)]
+    ws = pkv.decode_workspace(64, 32, 8, 70000)
+    for trial in range(3):
+        for lens in cases:
+            kp, vp, bt = _batch(rng, lens, 8)
+            q = W.randn_bf16(rng, (len(lens), 32, 64))
+            ws.fill_(0xFF)
+            qd = dev_bf16(q)
+            out = torch.empty_like(qd)
+            mx = int(lens.max())
+            pkv.pkv_paged_attn_decode(out, qd, dev_bf16(kp), dev_bf16(vp), dev_i32(bt), None, dev_i32(lens), mx,
+                                      0.125, 0, ws, row_lens_host=lens)
+            torch.cuda.synchronize()
+            ref = attention.decode(q, kp, vp, bt, np.arange(len(lens)), lens, 0.125)
+            check_attention(bits(out), ref, f"garbage workspace trial {trial} B={len(lens)}")
+
+
 @pytest.mark.slow
 def test_stream_long_rows_several_table_slices(gpu):
     """Nine rows of 65536 tokens (36864 blocks): each wave's part of a share
