@@ -122,6 +122,66 @@ def cpu_baseline(eng, q_host, seconds: float):
                       f"{t_total:.1f} s of CPU time"}
 
 
+def prefill_leg(torch, np, pkv, W, iters: int = 5):
+    """Chunked causal prefill of the 8-prompt workload (lengths U[256, 2048],
+    512-token chunks): every chunk's K/V is appended, then all sequences' i-th
+    chunks go through one pkv_paged_attn_prefill call.  Returns the mean time
+    of the prefill kernel calls per pass and the causal-triangle flops."""
+    w = W.config5(extra_tokens=32)
+    lens = [int(n) for n in w.prompt_lens]
+    kp = torch.zeros((w.num_blocks, 16, 8, 64), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    btd = torch.from_numpy(w.block_table[:, 0, :].copy()).cuda()
+    qd = torch.from_numpy(w.q.view(np.int16)).cuda().view(torch.bfloat16)
+    kd = torch.from_numpy(w.k.view(np.int16)).cuda().view(torch.bfloat16)
+    vd = torch.from_numpy(w.v.view(np.int16)).cuda().view(torch.bfloat16)
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    chunk = 512
+    calls = []
+    for c in range(max(-(-n // chunk) for n in lens)):
+        rows, sid, pos, cu, qs, seqs = [], [], [], [0], [], []
+        for s, n in enumerate(lens):
+            a, b = c * chunk, min(n, (c + 1) * chunk)
+            if a >= b:
+                continue
+            r = np.arange(starts[s] + a, starts[s] + b)
+            rows.append(r)
+            sid += [s] * len(r)
+            pos += list(range(a, b))
+            cu.append(cu[-1] + len(r))
+            qs.append(a)
+            seqs.append(s)
+        r = torch.from_numpy(np.concatenate(rows)).cuda()
+        i32 = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")  # noqa: E731
+        calls.append(dict(q=qd[r].contiguous(), k=kd[r].contiguous(), v=vd[r].contiguous(), sid=i32(sid),
+                          pos=i32(pos), cu=i32(cu), qs=i32(qs), seqs=i32(seqs), mq=int(np.diff(cu).max())))
+    stream = torch.cuda.current_stream()
+    times = []
+    for it in range(iters + 1):
+        t = 0.0
+        for cl in calls:
+            pkv.pkv_paged_kv_append(kp, vp, cl["k"], cl["v"], btd, cl["sid"], cl["pos"])
+            out = torch.empty_like(cl["q"])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pkv.pkv_paged_attn_prefill(out, cl["q"], cl["cu"], cl["qs"], cl["seqs"], kp, vp, btd, cl["mq"], w.scale)
+            e1.record(stream)
+            e1.synchronize()
+            t += e0.elapsed_time(e1) / 1e3
+        if it > 0:
+            times.append(t)
+    pairs = sum(n * (n + 1) // 2 for n in lens)
+    flops = pairs * 32 * 64 * 2 * 2          # QK and PV, multiply-add = 2 flops
+    t = float(np.median(times))
+    del kp, vp
+    return {"workload": "chunked causal prefill, 8 prompts U[256,2048] (sum %d tokens), 512-token chunks, "
+                        "32q/8kv heads, d=64, bf16" % sum(lens),
+            "calls": len(calls), "us_per_pass": round(t * 1e6, 2), "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(flops / t / 1e12, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                         "frac": round(flops / t / 1e12 / 2500.0, 4), "traffic": None,
+                         "kernel": "pkv_paged_attn_prefill (prefill_kernel<4>)"}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,8 +267,13 @@ def main():
     durs = np.array([a.elapsed_time(b) / 1e3 for a, b in pairs])
     t_attn = float(durs.mean())
     achieved = bytes_per_launch / t_attn / 1e9
-    log(f"attention: {t_attn * 1e6:.2f} us/launch (p10 {np.percentile(durs, 10) * 1e6:.2f}, "
+    log(f"attention: {t_attn * 1e6:.2f} us/launch (median {np.median(durs) * 1e6:.2f}, "
+        f"p10 {np.percentile(durs, 10) * 1e6:.2f}, "
         f"p90 {np.percentile(durs, 90) * 1e6:.2f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of peak")
+
+    pre = prefill_leg(torch, np, pkv, W)
+    log(f"prefill: {pre['us_per_pass']:.1f} us per pass over {pre['calls']} chunk calls, "
+        f"{pre['roofline']['achieved']:.1f} TFLOP/s = {pre['roofline']['frac']:.2%} of bf16 MFMA peak")
 
     copy_gbs = stream_copy_gbs(torch)
     log(f"plain copy kernel: {copy_gbs:.0f} GB/s (read + write)")
@@ -246,6 +311,7 @@ def main():
                      "bytes_per_launch": bytes_per_launch,
                      "us_per_launch": round(t_attn * 1e6, 3), "source_hash": src_hash},
         "copy_kernel_GBps": round(copy_gbs, 1),
+        "prefill": pre,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
