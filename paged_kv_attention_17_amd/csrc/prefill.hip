@@ -6,9 +6,10 @@
 // and the category page's chapter title on chunked prefill (a prompt may arrive
 // in chunks; a chunk's queries also see the keys of earlier chunks).
 //
-// Tiling.  A workgroup of 4 wave64s owns (sequence, KV head, 32 query tokens).
-// Wave w computes query head g*G + w (looping when G > 4) for those 32 tokens,
-// so the 4 GQA heads share every K/V tile staged in LDS.  Per 32-key tile:
+// Tiling.  A workgroup of 8 wave64s owns (sequence, KV head, 256 / G query
+// tokens): wave w computes query head g*G + w % G for the 32 tokens of query
+// subtile w / G, so every K/V tile staged in LDS serves all G heads of the
+// group and 256 / G queries.  Per 64-key tile (two 32-key halves) and wave:
 //   S^T[key][query] = K . Q^T   four v_mfma_f32_32x32x16_bf16 over the 64 dims
 //   online softmax per query    (a lane owns one query column: its 16 keys are
 //                                in-lane, the other 16 in lane ^ 32)
@@ -17,22 +18,40 @@
 // lane.  MFMA contracts A's k slots against B's k slots of the same lane group,
 // so any consistent assignment of dims (or keys) to k slots is correct; the key
 // assignment used for P^T is the one the S^T accumulator layout already has
-// (keys 8*(i/4) + 4*(lane/32) + i%4 for accumulator i), and V^T is read from a
-// transposed LDS copy with the same assignment.  Keys past the sequence's cached
-// length get V = 0 in LDS and scores of -inf by select, so NaN in unused pool
-// slots never reaches the output; causal masking is a select as well.
+// (keys 8*(i/4) + 4*(lane/32) + i%4 for accumulator i).  V stays row-major in
+// LDS and the V^T operand is read with the gfx950 transpose load
+// (ds_read_b64_tr_b16): within each 16-lane group, lane i's element j comes
+// from element i % 4 of the 64-bit word addressed by lane 4j + i / 4, so lanes
+// address 4-dim pieces of the keys that the P^T slots hold (see vt_addr).  V
+// rows are rotated by 16 dims per key (mod 4) so those reads and the 16-byte
+// row writes hit distinct banks.
+//
+// Pipeline.  The next tile's K and V rows are loaded into registers while the
+// current tile is computed, then written to the other half of a double-buffered
+// LDS area: one barrier per tile.  The running max is shared by a lane and
+// lane ^ 32 (both hold the same query) and raised only when a score exceeds it
+// by more than 8 (log2 units), so the accumulator rescale and the cross-lane
+// exchange are rare; the sum stays per lane until the end.  Masks (causal, and
+// keys past the sequence's cached length, which also get V = 0 in LDS) are
+// selects applied only on tiles that need them, so NaN in unused pool slots
+// never reaches the output.
 #include "common.h"
 
 namespace pkv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kQTile = 32;            // query tokens per workgroup
-constexpr int kKTile = 32;            // keys per step
-constexpr int kPfWaves = 4;
+constexpr int kKTile = 64;            // keys per step (two 32-key MFMA blocks)
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kKsStride = kHeadDim + 8;   // padded LDS row (bf16) for K tiles
-constexpr int kVtStride = kKTile + 8;     // padded LDS row (bf16) for transposed V tiles
+constexpr int kVsStride = kHeadDim;       // LDS row (bf16) of a V tile, rotated per key
+constexpr float kPfTau = 8.0f;            // lazy rescale threshold, log2 units
+
+// Query tokens per workgroup for G query heads per KV head.
+__host__ __device__ constexpr int pf_qtile(int G) { return 32 * (kPfWaves / G); }
 
 struct PrefillArgs {
   uint16_t* out;
@@ -59,8 +78,20 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
                                                   0, 0, 0);
 }
 
+// Element (key, dim) of a V tile in LDS: rows of 64 dims, rotated by 16 dims
+// for every key mod 4 (8-dim row pieces and 4-dim read pieces stay contiguous).
+__device__ __forceinline__ int vs_index(int key, int dim) { return key * kVsStride + ((dim + 16 * (key & 3)) & 63); }
+
+// Transpose load of 4 bf16 (see the header) from an LDS address.
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
+
 template <int G>
-__global__ __launch_bounds__(kPfWaves * kWave) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void prefill_kernel(PrefillArgs a) {
+  constexpr int kQTile = pf_qtile(G);
   const int tile = a.q_tiles - 1 - (int)blockIdx.x;   // heavy (late) tiles first
   const int g = blockIdx.y;
   const int seq = blockIdx.z;
@@ -86,126 +117,168 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_kernel(PrefillArgs a
   const int32_t* btrow = a.bt + (int64_t)slot * a.bt_stride;
   const int64_t row_elems = (int64_t)a.n_kv * kHeadDim;
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kKTile * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKTile * kKsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kKTile * kVsStride];
 
-  // This lane's query: column col of the tile.
-  const int my_q = tok0 + col;                     // chunk-relative token
-  const bool q_ok = col < n_q_tile;
+  // This wave: head hh of the group, query subtile sub; this lane: one query.
+  const int hh = w % G;
+  const int sub = w / G;
+  const int h = g * G + hh;
+  const int sub0 = tok0 + sub * 32;                // first query of the subtile (chunk-relative)
+  const int my_q = sub0 + col;
+  const bool q_ok = my_q < tok0 + n_q_tile;
   const int my_pos = start + my_q;
+  const int sub_last_pos = start + min(sub0 + 31, tok0 + n_q_tile - 1);   // wave-uniform
+  const bool sub_live = sub0 < tok0 + n_q_tile;
+  const int sub_key_end = min(sub_last_pos + 1, n_keys);                  // keys this subtile sees
 
-  // Loader role: thread -> (key row, 16-byte chunk).
+  // Loader role: thread -> (key, 16-byte chunk) of the K and the V tile.
   const int ld_key = tid >> 3;
   const int ld_chunk = tid & 7;
-
-  for (int hh = w; hh < (G > kPfWaves ? G : kPfWaves); hh += kPfWaves) {
-    const bool head_active = hh < G;
-    const int h = g * G + (head_active ? hh : 0);
-    // Q^T operand: 4 k-steps of 8 dims each.
-    uint4 qb[4];
-#pragma unroll
-    for (int ks_ = 0; ks_ < 4; ++ks_) {
-      qb[ks_] = make_uint4(0, 0, 0, 0);
-      if (q_ok && head_active)
-        qb[ks_] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)(q0 + my_q) * a.n_q + h) * kHeadDim + ks_ * 16 +
-                                                  half * 8);
+  struct KV { uint4 k, v; };
+  auto fetch = [&](int kt) -> KV {
+    const int kk = kt * kKTile + ld_key;
+    KV x{make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    if (kk < n_keys) {
+      const int blk = btrow[kk / kBlock];
+      if (blk >= 0 && blk < a.num_blocks) {
+        const int64_t off = ((int64_t)blk * kBlock + kk % kBlock) * row_elems + g * kHeadDim + ld_chunk * 8;
+        x.k = *reinterpret_cast<const uint4*>(a.k_pool + off);
+        x.v = *reinterpret_cast<const uint4*>(a.v_pool + off);
+      }
     }
-    f32x16 o0 = {}, o1 = {};
-    float m = -1.0e30f, l = 0.f;
+    return x;
+  };
+  auto stage = [&](int buf, const KV& x) {
+    *reinterpret_cast<uint4*>(&ks[buf][ld_key * kKsStride + ld_chunk * 8]) = x.k;
+    *reinterpret_cast<uint4*>(&vs[buf][vs_index(ld_key, ld_chunk * 8)]) = x.v;
+  };
 
-    for (int kt = 0; kt < n_ktiles; ++kt) {
-      const int kbase = kt * kKTile;
-      // Stage the K tile (row-major) and the V tile (transposed) in LDS.
-      {
-        const int kk = kbase + ld_key;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
-        if (kk < n_keys) {
-          const int blk = btrow[kk / kBlock];
-          if (blk >= 0 && blk < a.num_blocks) {
-            const int64_t off = ((int64_t)blk * kBlock + kk % kBlock) * row_elems + g * kHeadDim + ld_chunk * 8;
-            kv = *reinterpret_cast<const uint4*>(a.k_pool + off);
-            vv = *reinterpret_cast<const uint4*>(a.v_pool + off);
+  // Q^T operand: 4 k-steps of 8 dims each.
+  uint4 qb[4];
+#pragma unroll
+  for (int ks_ = 0; ks_ < 4; ++ks_) {
+    qb[ks_] = make_uint4(0, 0, 0, 0);
+    if (q_ok)
+      qb[ks_] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)(q0 + my_q) * a.n_q + h) * kHeadDim + ks_ * 16 +
+                                                half * 8);
+  }
+  // This lane's V^T read offsets inside a 32-key group (key 4 half + kl, dims
+  // 16 (g % 2) + 4 (lane % 4) of each dim half; the rotation only depends on kl).
+  const int kl = (lane >> 2) & 3;
+  const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int vt_off0 = vs_index(4 * half + kl, vdim);
+  const int vt_off1 = vs_index(4 * half + kl, vdim + 32);
+  const float C = a.scale_log2e;
+  const float invC = 1.0f / C;
+  f32x16 o0 = {}, o1 = {};
+  float m = -1.0e30f;              // shared by lane and lane ^ 32 (same query)
+  float thr = -INFINITY;           // raw-score level above which m must be raised
+  float l = 0.f;                   // this lane's half of the sum
+
+  stage(0, fetch(0));
+  __syncthreads();
+  for (int kt = 0; kt < n_ktiles; ++kt) {
+    const int buf = kt & 1;
+    const int kbase = kt * kKTile;
+    const bool more = kt + 1 < n_ktiles;
+    KV nxt{make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    if (more) nxt = fetch(kt + 1);
+
+    if (sub_live && kbase < sub_key_end) {
+      // S^T = K . Q^T for the tile's two 32-key halves (rows: keys, cols: queries)
+      f32x16 s[2] = {};
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+        for (int ks_ = 0; ks_ < 4; ++ks_) {
+          const uint4 ka =
+              *reinterpret_cast<const uint4*>(&ks[buf][(kh * 32 + col) * kKsStride + ks_ * 16 + half * 8]);
+          s[kh] = mfma32(ka, qb[ks_], s[kh]);
+        }
+      }
+      // masks only where a key of the tile can lie past a query or the cache
+      const bool need_mask = kbase + kKTile - 1 > sub_last_pos - 31 || kbase + kKTile > n_keys;
+      if (need_mask) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kbase + kh * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+            const bool ok = q_ok && key <= my_pos && key < n_keys;
+            s[kh][i] = ok ? s[kh][i] : -INFINITY;
           }
         }
-        __syncthreads();   // previous tile fully consumed
-        *reinterpret_cast<uint4*>(&ks[ld_key * kKsStride + ld_chunk * 8]) = kv;
-        const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+      }
+      float tmax = s[0][0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vt[(ld_chunk * 8 + 2 * j) * kVtStride + ld_key] = (uint16_t)(vw[j] & 0xffffu);
-          vt[(ld_chunk * 8 + 2 * j + 1) * kVtStride + ld_key] = (uint16_t)(vw[j] >> 16);
+      for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s[0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[1][i]);
+      if (__any(tmax > thr)) {
+        // raise the shared max of this lane's query (rare)
+        const float tm = fmaxf(tmax, shfl_xor(tmax, 32)) * C;
+        const float mn = fmaxf(m, tm);
+        const float alpha = fast_exp2(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          o0[i] *= alpha;
+          o1[i] *= alpha;
         }
-        __syncthreads();
+        m = mn;
+        thr = (mn + kPfTau) * invC;
       }
-      if (!head_active) continue;
-
-      // S^T = K . Q^T  (rows: keys of the tile, cols: queries)
-      f32x16 s = {};
 #pragma unroll
-      for (int ks_ = 0; ks_ < 4; ++ks_) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(&ks[col * kKsStride + ks_ * 16 + half * 8]);
-        s = mfma32(ka, qb[ks_], s);
-      }
-      // Mask and running max for this lane's query.
-      float tmax = -INFINITY;
+      for (int kh = 0; kh < 2; ++kh) {
+        float p[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kbase + 8 * (i / 4) + 4 * half + (i % 4);
-        const bool ok = q_ok && key <= my_pos && key < n_keys;
-        s[i] = ok ? s[i] * a.scale_log2e : -INFINITY;
-        tmax = fmaxf(tmax, s[i]);
-      }
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      const float mn = fmaxf(m, tmax);
-      const float alpha = fast_exp2(m - mn);
-      float psum = 0.f;
-      float p[16];
+        for (int i = 0; i < 16; ++i) {
+          p[i] = fast_exp2(__builtin_fmaf(s[kh][i], C, -m));
+          l += p[i];
+        }
+        // P^T operands: k-step 0 = accumulators 0..7, k-step 1 = 8..15.
+        uint4 pb[2];
+        pb[0] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                           pack_bf16x2(p[6], p[7]));
+        pb[1] = make_uint4(pack_bf16x2(p[8], p[9]), pack_bf16x2(p[10], p[11]), pack_bf16x2(p[12], p[13]),
+                           pack_bf16x2(p[14], p[15]));
+        // O^T += V^T . P^T: slot 4u + j of lane (dim, half) must hold key
+        // 16 kstep + 8u + 4 half + j (the P^T slot's key), so the addressing
+        // lane 16 g + s supplies key ... + 4 (g / 2) + s / 4 and dims
+        // 16 (g % 2) + 4 (s % 4) .. + 3 of its dim half.
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = fast_exp2(s[i] - mn);
-        psum += p[i];
-      }
-      psum += shfl_xor(psum, 32);
-      l = l * alpha + psum;
-      m = mn;
+        for (int kstep = 0; kstep < 2; ++kstep) {
+          uint2 r[2][2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        o0[i] *= alpha;
-        o1[i] *= alpha;
-      }
-      // P^T operands: k-step 0 = accumulators 0..7, k-step 1 = 8..15.
-      uint4 pb[2];
-      pb[0] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                         pack_bf16x2(p[6], p[7]));
-      pb[1] = make_uint4(pack_bf16x2(p[8], p[9]), pack_bf16x2(p[10], p[11]), pack_bf16x2(p[12], p[13]),
-                         pack_bf16x2(p[14], p[15]));
-      // O^T += V^T . P^T ; V^T rows are dims, k slots the same keys as P^T.
-#pragma unroll
-      for (int kstep = 0; kstep < 2; ++kstep) {
-        const int key_a = kstep * 16 + 4 * half;   // keys key_a..+3 and key_a+8..+11
-        const uint2 a0lo = *reinterpret_cast<const uint2*>(&vt[col * kVtStride + key_a]);
-        const uint2 a0hi = *reinterpret_cast<const uint2*>(&vt[col * kVtStride + key_a + 8]);
-        const uint2 a1lo = *reinterpret_cast<const uint2*>(&vt[(col + 32) * kVtStride + key_a]);
-        const uint2 a1hi = *reinterpret_cast<const uint2*>(&vt[(col + 32) * kVtStride + key_a + 8]);
-        o0 = mfma32(make_uint4(a0lo.x, a0lo.y, a0hi.x, a0hi.y), pb[kstep], o0);
-        o1 = mfma32(make_uint4(a1lo.x, a1lo.y, a1hi.x, a1hi.y), pb[kstep], o1);
+          for (int u = 0; u < 2; ++u) {
+            const uint16_t* row = &vs[buf][(kh * 32 + kstep * 16 + 8 * u) * kVsStride];
+            r[0][u] = lds_tr16(row + vt_off0);
+            r[1][u] = lds_tr16(row + vt_off1);
+          }
+          o0 = mfma32(make_uint4(r[0][0].x, r[0][0].y, r[0][1].x, r[0][1].y), pb[kstep], o0);
+          o1 = mfma32(make_uint4(r[1][0].x, r[1][0].y, r[1][1].x, r[1][1].y), pb[kstep], o1);
+        }
       }
     }
-    if (!head_active || !q_ok) continue;
-    // O^T accumulator i holds dim 8*(i/4) + 4*half + i%4 (+32 for o1) of this lane's query.
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* orow = a.out + ((int64_t)(q0 + my_q) * a.n_q + h) * kHeadDim;
+    if (more) stage(buf ^ 1, nxt);
+    __syncthreads();
+  }
+  l += shfl_xor(l, 32);
+  if (!q_ok) return;
+  // O^T accumulator i holds dim 8*(i/4) + 4*half + i%4 (+32 for o1) of this lane's query.
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* orow = a.out + ((int64_t)(q0 + my_q) * a.n_q + h) * kHeadDim;
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const int d = 8 * grp + 4 * half;
-      uint2 v0, v1;
-      v0.x = pack_bf16x2(o0[4 * grp + 0] * inv, o0[4 * grp + 1] * inv);
-      v0.y = pack_bf16x2(o0[4 * grp + 2] * inv, o0[4 * grp + 3] * inv);
-      v1.x = pack_bf16x2(o1[4 * grp + 0] * inv, o1[4 * grp + 1] * inv);
-      v1.y = pack_bf16x2(o1[4 * grp + 2] * inv, o1[4 * grp + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + d) = v0;
-      *reinterpret_cast<uint2*>(orow + 32 + d) = v1;
-    }
+  for (int grp = 0; grp < 4; ++grp) {
+    const int d = 8 * grp + 4 * half;
+    uint2 v0, v1;
+    v0.x = pack_bf16x2(o0[4 * grp + 0] * inv, o0[4 * grp + 1] * inv);
+    v0.y = pack_bf16x2(o0[4 * grp + 2] * inv, o0[4 * grp + 3] * inv);
+    v1.x = pack_bf16x2(o1[4 * grp + 0] * inv, o1[4 * grp + 1] * inv);
+    v1.y = pack_bf16x2(o1[4 * grp + 2] * inv, o1[4 * grp + 3] * inv);
+    *reinterpret_cast<uint2*>(orow + d) = v0;
+    *reinterpret_cast<uint2*>(orow + 32 + d) = v1;
   }
 }
 
@@ -245,15 +318,15 @@ extern "C" int pkv_paged_attn_prefill(pkv_bf16* out, const pkv_bf16* q, const in
   a.max_blocks = max_blocks_per_seq;
   a.n_q = n_q_heads;
   a.n_kv = n_kv_heads;
-  a.q_tiles = (max_q_len + kQTile - 1) / kQTile;
+  const int G = n_q_heads / n_kv_heads;
+  a.q_tiles = (max_q_len + pf_qtile(G) - 1) / pf_qtile(G);
   a.total_q = total_q;
   a.scale_log2e = scale * 1.4426950408889634f;
-  const int G = n_q_heads / n_kv_heads;
   const void* fn = G == 1 ? (const void*)prefill_kernel<1>
                  : G == 2 ? (const void*)prefill_kernel<2>
                  : G == 4 ? (const void*)prefill_kernel<4>
                           : (const void*)prefill_kernel<8>;
   void* args[] = {&a};
-  return launch_status(hipLaunchKernel(fn, dim3(a.q_tiles, n_kv_heads, num_seqs), dim3(kPfWaves * kWave), args, 0,
+  return launch_status(hipLaunchKernel(fn, dim3(a.q_tiles, n_kv_heads, num_seqs), dim3(kPfThreads), args, 0,
                                        (hipStream_t)stream));
 }
