@@ -96,6 +96,21 @@ def test_prefill_gqa_ratios(gpu, n_q, n_kv):
     check_attention(got, ref, f"prefill gqa {n_q}/{n_kv}")
 
 
+@pytest.mark.parametrize("n_q,n_kv", [(8, 8), (16, 8), (64, 8), (16, 4)])
+def test_prefill_gqa_long_chunked(gpu, n_q, n_kv):
+    """Several query tiles per prompt for every GQA ratio (the workgroup holds
+    256 / G queries: 8 query subtiles of one head at G = 1, one subtile of 8
+    heads at G = 8), chunked at 160 tokens (chunk starts off the tile grid)
+    bit-identical to whole prompts, and the oracle."""
+    lens = [700, 300, 1]
+    q, kn, vn, kp, vp, bt, _ = _setup(lens, n_q=n_q, n_kv=n_kv, seed=n_q + 7 * n_kv)
+    whole, _, _ = _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk=4096)
+    part, _, _ = _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk=160)
+    np.testing.assert_array_equal(part, whole)
+    ref, _, _ = _oracle(q, kn, vn, kp, vp, bt, lens)
+    check_attention(whole, ref, f"prefill long gqa {n_q}/{n_kv}")
+
+
 def test_chunked_equals_whole_bit_identical(gpu):
     lens = [300, 129, 64]
     q, kn, vn, kp, vp, bt, _ = _setup(lens, seed=9)
