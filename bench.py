@@ -83,6 +83,59 @@ def stream_copy_gbs(torch, nbytes=2 << 30, iters=10):
     return 2 * nbytes / t / 1e9
 
 
+def stream_read_gbs(torch, pkv, nbytes=4 << 30, iters=10):
+    """Achievable HBM read rate: the library's grid-stride read probe over a
+    buffer 16x the 256 MB last-level cache, read once per iteration."""
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        pkv.pkv_hbm_read_probe(a, sink)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        pkv.pkv_hbm_read_probe(a, sink)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3 / iters
+    del a, sink
+    return nbytes / t / 1e9
+
+
+def unfused_layer_us(torch, np, pkv, eng, q, k, v, out, stream, iters=3):
+    """The unfused decode of one layer at the same point: RoPE kernel, append
+    kernel and attention call, each timed with HIP events (mean over the 16
+    layers x iters).  Works on copies of q/k so the step's inputs stay as they
+    are, and re-appends the tokens of the last step (the cache is unchanged)."""
+    L = q.shape[0]
+    B = q.shape[1]
+    pos = torch.from_numpy((eng.cached[:B] - 1).astype(np.int32)).cuda()
+    sid = torch.arange(B, dtype=torch.int32, device="cuda")
+    ctx_now = eng.cached.copy()
+    t = {"rope": [], "append": [], "attention": []}
+    for it in range(iters + 1):
+        for layer in range(L):
+            qc, kc = q[layer].clone(), k[layer].clone()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record(stream)
+            pkv.pkv_rope_decode(qc, kc, pos, eng.cos_sin, stream=stream)
+            ev[1].record(stream)
+            pkv.pkv_paged_kv_append(eng.k_pool, eng.v_pool, kc, v[layer], eng.bt_dev[:, layer, :], sid, pos,
+                                    stream=stream)
+            ev[2].record(stream)
+            pkv.pkv_paged_attn_decode(out[layer], qc, eng.k_pool, eng.v_pool, eng.bt_dev[:, layer, :], None,
+                                      eng.ctx_dev, eng.max_context_len, eng.scale, eng.partition_size,
+                                      eng.workspace, stream=stream, row_lens_host=ctx_now)
+            ev[3].record(stream)
+            if it > 0:
+                t["rope"].append(ev[:2])
+                t["append"].append(ev[1:3])
+                t["attention"].append(ev[2:4])
+    torch.cuda.synchronize()
+    return {kname: round(float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3, 2)
+            for kname, pairs in t.items()}
+
+
 def cpu_baseline(eng, q_host, seconds: float):
     """Time the float64 oracle (as it stands) on layer-by-layer samples of the
     step: sequences are gathered into a compact host pool (not timed), then
@@ -271,12 +324,17 @@ def main():
         f"p10 {np.percentile(durs, 10) * 1e6:.2f}, "
         f"p90 {np.percentile(durs, 90) * 1e6:.2f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of peak")
 
+    unf = unfused_layer_us(torch, np, pkv, eng, q, k, v, out, stream)
+    log(f"unfused layer: rope {unf['rope']:.2f} us, append {unf['append']:.2f} us, "
+        f"attention {unf['attention']:.2f} us (fused call: {t_attn * 1e6:.2f} us)")
+
     pre = prefill_leg(torch, np, pkv, W)
     log(f"prefill: {pre['us_per_pass']:.1f} us per pass over {pre['calls']} chunk calls, "
         f"{pre['roofline']['achieved']:.1f} TFLOP/s = {pre['roofline']['frac']:.2%} of bf16 MFMA peak")
 
     copy_gbs = stream_copy_gbs(torch)
-    log(f"plain copy kernel: {copy_gbs:.0f} GB/s (read + write)")
+    read_gbs = stream_read_gbs(torch, pkv)
+    log(f"plain copy kernel: {copy_gbs:.0f} GB/s (read + write); streaming read of 4 GiB: {read_gbs:.0f} GB/s")
 
     src_hash = decode_source_hash()
     traffic = traffic_from_profile(src_hash)
@@ -311,6 +369,8 @@ def main():
                      "bytes_per_launch": bytes_per_launch,
                      "us_per_launch": round(t_attn * 1e6, 3), "source_hash": src_hash},
         "copy_kernel_GBps": round(copy_gbs, 1),
+        "read_kernel_GBps": round(read_gbs, 1),
+        "unfused_layer_us": unf,
         "prefill": pre,
         "cpu_baseline": cpu,
     }

@@ -126,6 +126,13 @@ int pkv_paged_gather(pkv_bf16* k_dense, pkv_bf16* v_dense, const pkv_bf16* k_poo
                      int64_t bt_row_stride, int max_blocks_per_seq, int slot, int context_len,
                      int n_kv_heads, int head_dim, void* stream);
 
+/* Diagnostic, off the attention path: read `bytes` bytes of device memory
+ * (16-byte aligned, bytes a multiple of 16) once with wide loads spread over
+ * the whole chip, as a reference for the HBM read rate the decode kernels are
+ * measured against.  `sink` (device, 4 bytes) is written only when the data
+ * XOR to a fixed pattern, so the reads cannot be optimised away. */
+int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Host-side block allocation for one step ("The path of one inference",
  * step (4): blocks come off a free list; -1 marks an unassigned entry).
  * For every token t whose table entry bt_host[slot_ids_host[t]][positions_host[t] / 16]

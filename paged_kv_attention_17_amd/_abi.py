@@ -42,6 +42,7 @@ SIGNATURES = {
     "pkv_rope_decode": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _i, _p]),
     "pkv_paged_kv_append": (_i, [_p, _p, _i, _p, _p, _p, _i64, _i, _i, _p, _p, _i, _i, _i, _p]),
     "pkv_paged_gather": (_i, [_p, _p, _p, _p, _i, _p, _i64, _i, _i, _i, _i, _i, _p]),
+    "pkv_hbm_read_probe": (_i, [_p, _sz, _p, _p]),
     "pkv_blocks_assign": (_i, [_p, _i64, _i, _i, _p, _ip, _p, _p, _i, _p, _p, _ip]),
     "pkv_blocks_release": (_i, [_p, _i64, _i, _i, _i, _p, _ip, _i, _p, _p, _ip]),
     "pkv_block_table_patch": (_i, [_p, _i64, _p, _p, _i, _p]),
@@ -223,6 +224,14 @@ def pkv_paged_gather(k_dense, v_dense, k_pool, v_pool, block_table, slot, contex
         _dev_ptr(k_dense, "k_dense", _bf16_types()), _dev_ptr(v_dense, "v_dense", _bf16_types()),
         _dev_ptr(k_pool, "k_pool", _bf16_types()), _dev_ptr(v_pool, "v_pool", _bf16_types()), k_pool.shape[0],
         bt + 0, stride, mb, slot, context_len, k_pool.shape[2], k_pool.shape[3], _stream(stream)))
+
+
+def pkv_hbm_read_probe(buf, sink, stream=None):
+    """Read the whole of device tensor `buf` once (diagnostic HBM read rate);
+    `sink` is a device int32/uint32 tensor of at least one element."""
+    _contig(buf, "buf")
+    _check("pkv_hbm_read_probe", load().pkv_hbm_read_probe(
+        _dev_ptr(buf, "buf"), buf.numel() * buf.element_size(), _dev_ptr(sink, "sink"), _stream(stream)))
 
 
 def pkv_blocks_assign(bt_host, free_list, n_free, slot_ids, positions):

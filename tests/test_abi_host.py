@@ -197,3 +197,12 @@ def test_check_block_table_reports_first_problem(lib):
     bt3 = np.full((3, 2, 4), -1, np.int32)
     bt3[:, 1, :] = bt
     assert pkv.pkv_check_block_table(bt3[:, 1, :], None, ctx, 8)[0] == 0
+
+
+def test_read_probe_argument_errors(lib):
+    E = _abi
+    assert lib.pkv_hbm_read_probe(None, 0, None, None) == E.PKV_OK
+    assert lib.pkv_hbm_read_probe(None, 64, FAKE, None) == E.PKV_ERR_NULL
+    assert lib.pkv_hbm_read_probe(FAKE, 64, None, None) == E.PKV_ERR_NULL
+    assert lib.pkv_hbm_read_probe(FAKE + 4, 64, FAKE, None) == E.PKV_ERR_MISALIGNED
+    assert lib.pkv_hbm_read_probe(FAKE, 60, FAKE, None) == E.PKV_ERR_MISALIGNED
