@@ -1,6 +1,6 @@
-// Per-block arithmetic of paged single-query attention, shared by the decode
-// kernels (one workgroup per partition, and one workgroup per CU streaming a
-// share of all blocks).
+// Per-block arithmetic of paged single-query attention on the vector ALU, used
+// by the per-partition decode kernel (the streaming kernel shares the
+// constants and register types and does its arithmetic on the matrix cores).
 //
 // Source: the Korean page of "An Inference Engine in 1,500 Lines of CUDA: The
 // Map" ("What is in the box" table: online softmax inside the PagedAttention

@@ -18,8 +18,12 @@
 //
 // Work inside a workgroup.  16 waves = n_kv heads x (16 / n_kv) lanes of
 // blocks: wave w serves KV head w % n_kv and takes every (16 / n_kv)-th block
-// of the share, with two blocks in flight (the per-block arithmetic is
-// attn_block.h's).  The rows the share touches (at most kMaxRows) have their
+// of the share, with two blocks in flight.  The block's arithmetic runs on the
+// matrix cores: scores S^T = K . Q^T (two 16x16x32 products, K straight from
+// its loads, the G query heads as columns), then O^T += V^T . P^T (four
+// 16x16x16 products, V transposed through a per-wave LDS tile), so the vector
+// ALU is left with the masks, the exponentials and the rare rescale.  The rows
+// the share touches (at most kMaxRows) have their
 // queries staged in LDS, rotated when fused.  When a wave's next block belongs
 // to another row it folds its state for the finished row (DPP and lane
 // shuffles over the 8 row groups) into that row's LDS slot, without waiting
@@ -117,6 +121,110 @@ __device__ __forceinline__ uint4 rope_own_chunk(uint4 own, uint4 oth, const floa
   return make_uint4(res[0], res[1], res[2], res[3]);
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Element (token, dim) of a wave's 16 x 64 V tile in LDS: rows of 64 dims,
+// rotated by 16 dims for every token mod 4, so that the row-wise 16-byte
+// writes and the transposed 8-byte reads both spread over the banks.
+__device__ __forceinline__ int vt_index(int token, int dim) {
+  return token * kHeadDim + ((dim + 16 * (token & 3)) & (kHeadDim - 1));
+}
+
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives as its
+// element j the (i % 4)-th bf16 of the 8-byte word that lane 4 j + i / 4 of the
+// group addresses.
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Scores S^T[token][col] += K[token][k] . Q^T[k][col] over 32 dims: lane l
+// brings K row l % 16 and Q column l % 16, 8 dims each from group l / 16, and
+// receives S^T rows 4 (l / 16) .. + 3 of column l % 16.
+__device__ __forceinline__ f32x4 mfma_qk(uint4 k, uint4 q, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), __builtin_bit_cast(bf16x8, q), c,
+                                                  0, 0, 0);
+}
+// O^T[dim][col] += V^T[dim][token] . P^T[token][col] over the 16 tokens of a
+// block: lane l brings V^T row l % 16 and P^T column l % 16 for tokens
+// 4 (l / 16) .. + 3 and keeps O^T rows 4 (l / 16) .. + 3 of column l % 16.
+__device__ __forceinline__ f32x4 mfma_pv(uint2 vt, uint2 p, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vt), __builtin_bit_cast(i16x4, p), c,
+                                                    0, 0, 0);
+}
+
+// Online-softmax state of one wave on the matrix cores.  Column l % 16 of
+// every MFMA tile is one query head of the wave's KV head (columns >= G carry
+// zero queries and are never written out).  Lane l keeps, for its column, the
+// running max m (log2 units, equal in the four lane groups), the raw-score
+// level thr above which m must be raised, its share l of the sum (tokens
+// 4 (l / 16) .. + 3 of every block) and O^T dims 16 t + 4 (l / 16) .. + 3.
+struct MfmaAcc {
+  float m, thr, l;
+  f32x4 o[4];
+
+  __device__ __forceinline__ void reset() {
+    m = kNegBig;
+    thr = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One 16-token block: V rows go through the wave's LDS tile (rows past the
+  // context, or of a block whose id is out of range, are zeroed there so NaN
+  // in unused pool slots cannot reach the output); scores of such tokens are
+  // replaced by -inf (a select, never a product).  `extra` is a token slot
+  // that takes part whatever the block (the fused step's new token), or -1.
+  __device__ __forceinline__ void block(uint4 qb0, uint4 qb1, const KVRegs& R, uint16_t* vtile, int wr0, int wr1,
+                                        const int (&rd)[4], int r, int q4, bool blk_ok, int valid, int extra,
+                                        float C, float invC) {
+    const bool full = blk_ok && valid == kBlock;
+    uint4 v0 = R.v0, v1 = R.v1;
+    if (!full) {
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      v0 = sel4((blk_ok && r < valid) || r == extra, v0, z);
+      v1 = sel4((blk_ok && r + 8 < valid) || r + 8 == extra, v1, z);
+    }
+    *reinterpret_cast<uint4*>(vtile + wr0) = v0;
+    *reinterpret_cast<uint4*>(vtile + wr1) = v1;
+
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+    sc = mfma_qk(R.k0, qb0, sc);
+    sc = mfma_qk(R.k1, qb1, sc);
+    float sv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * q4 + j;
+      sv[j] = (full || (blk_ok && t < valid) || t == extra) ? sc[j] : -INFINITY;
+    }
+    const bool need = (sv[0] > thr) | (sv[1] > thr) | (sv[2] > thr) | (sv[3] > thr);
+    if (__any(need)) {
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])) * C;
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t] *= alpha;
+      m = mn;
+      thr = (mn + kTau) * invC;
+    }
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = fast_exp2(__builtin_fmaf(sv[j], C, -m));
+    const uint2 pp = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    l = dot2_bf16(pp.x, kOnesBf16x2, l);
+    l = dot2_bf16(pp.y, kOnesBf16x2, l);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[t] = mfma_pv(lds_tr16(vtile + rd[t]), pp, o[t]);
+  }
+};
+
 template <int G, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void stream_kernel(StreamArgs a) {
@@ -142,6 +250,7 @@ void stream_kernel(StreamArgs a) {
   __shared__ uint4 snew[kMaxRows][2][kWaves * 8];           // fused: new key / value [row][k|v][head][chunk]
   __shared__ float sp[kMaxRows][kWaves][G][kRec];           // per-wave partials of each row
   __shared__ int srow_ok[kMaxRows];                         // the row's table slot is valid
+  __shared__ uint16_t svt[kWaves][kBlock * kHeadDim];       // per-wave V tile (transposed reads)
 
   // ---- this wave's blocks ----------------------------------------------------
   const int len = B1 - B0;
@@ -149,6 +258,9 @@ void stream_kernel(StreamArgs a) {
   const uint32_t block_bytes = (uint32_t)(kBlock * row_elems * 2);
   const uint32_t lane_off = (uint32_t)(((int64_t)r * row_elems + h * kHeadDim + c * 8) * 2);
   const uint32_t lane_off8 = lane_off + (uint32_t)(8 * row_elems * 2);
+  // K in the MFMA operand layout: token lane % 16, dims 8 (lane / 16) .. + 7
+  // (and the same 32 dims further on for the second operand)
+  const uint32_t k_off = (uint32_t)(((int64_t)(lane & 15) * row_elems + h * kHeadDim + 8 * (lane >> 4)) * 2);
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
 
@@ -179,8 +291,8 @@ void stream_kernel(StreamArgs a) {
     blk = blk < 0 ? 0 : blk;
     const auto rk = buf_rsrc(kbase + (size_t)blk * block_bytes, block_bytes);
     const auto rv = buf_rsrc(vbase + (size_t)blk * block_bytes, block_bytes);
-    R.k0 = buf_load16(rk, lane_off);
-    R.k1 = buf_load16(rk, lane_off8);
+    R.k0 = buf_load16(rk, k_off);
+    R.k1 = buf_load16(rk, k_off + 64);
     R.v0 = buf_load16(rv, lane_off);
     R.v1 = buf_load16(rv, lane_off8);
   };
@@ -241,47 +353,47 @@ void stream_kernel(StreamArgs a) {
   }
   __syncthreads();
 
-  OnlineSoftmax<G> acc;
+  MfmaAcc acc;
   acc.reset();
-  uint4 qv[G];
-  int cur = 0;                            // row of the share being accumulated
+  const int col = lane & 15;             // MFMA column: query head of the KV head's group
+  const int q4 = lane >> 4;              // MFMA lane group
+  uint4 qb0, qb1;                        // Q^T operands: dims 8 q4 .. and 32 + 8 q4 ..
+  int cur = 0;                           // row of the share being accumulated
   auto load_q = [&]() {
-#pragma unroll
-    for (int g = 0; g < G; ++g) qv[g] = sq[cur][(h * G + g) * 8 + c];
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    qb0 = col < G ? sq[cur][(h * G + col) * 8 + q4] : z;
+    qb1 = col < G ? sq[cur][(h * G + col) * 8 + q4 + 4] : z;
   };
   load_q();
 
-  // Fold the wave's state for row `cur` (sum over the 8 row groups) into its
-  // LDS slot and move on to the next row.
+  // Fold the wave's state for row `cur` into its LDS slot (the four lane
+  // groups hold different tokens' shares of the sum) and move on.
   auto flush = [&]() {
+    float l = acc.l;
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    if (col < G) {
+      float* dst = sp[cur][w][col];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float l = acc.l[g];
-      l += dpp<kDppRowRor8>(l);
-      l += shfl_xor(l, 16);
-      l += shfl_xor(l, 32);
-      float o[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float x = acc.o[g][j];
-        x += dpp<kDppRowRor8>(x);
-        x += shfl_xor(x, 16);
-        x += shfl_xor(x, 32);
-        o[j] = x;
-      }
-      if (r == 0) {
-        *reinterpret_cast<float4*>(&sp[cur][w][g][c * 8]) = make_float4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<float4*>(&sp[cur][w][g][c * 8 + 4]) = make_float4(o[4], o[5], o[6], o[7]);
-        if (c == 0) {
-          sp[cur][w][g][kHeadDim] = acc.m[g];
-          sp[cur][w][g][kHeadDim + 1] = l;
-        }
+      for (int t = 0; t < 4; ++t)
+        *reinterpret_cast<float4*>(dst + 16 * t + 4 * q4) = make_float4(acc.o[t][0], acc.o[t][1], acc.o[t][2], acc.o[t][3]);
+      if (q4 == 0) {
+        dst[kHeadDim] = acc.m;
+        dst[kHeadDim + 1] = l;
       }
     }
     ++cur;
     acc.reset();
     if (cur < nrows) load_q();
   };
+
+  // this wave's V tile in LDS: written row-wise, read transposed
+  uint16_t* vtile = svt[w];
+  const int v_wr0 = vt_index(r, 8 * c);
+  const int v_wr1 = vt_index(r + 8, 8 * c);
+  int v_rd[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v_rd[t] = vt_index(lane >> 2, 16 * t + 4 * (lane & 3));
 
   for (int cb = 0; cb < n_w; cb += kWave) {
     if (cb > 0) {
@@ -291,18 +403,26 @@ void stream_kernel(StreamArgs a) {
     KVRegs X, Y;
     issue(X, tab, ncb, 0);
     issue(Y, tab, ncb, 1);
-    auto step = [&](const KVRegs& R, int i) {
+    auto step = [&](KVRegs R, int i) {
       const int mt = __builtin_amdgcn_readlane(meta, i);
       while (cur < (mt >> 8)) flush();
       const bool blk_ok = __builtin_amdgcn_readlane(tab, i) >= 0;
-      const int valid = mt & 0xff;
-      acc.block(qv, R, blk_ok && r < valid, blk_ok && r + 8 < valid, C, invC);
+      const int valid = mt & 0xff;       // tokens read from the pool
+      int extra = -1;                    // fused: slot of the new token in this block
       if constexpr (FUSED) {
-        // the row's last block: add the new token from LDS
+        // the row's last block: the new token (rotated key, value) from LDS
         const int b = bf + cur;
-        if (B0 + s + S * (cb + i) == a.row_start[b + 1] - 1 && a.row_n[b] > 0 && srow_ok[cur])
-          acc.token(qv, snew[cur][0][h * 8 + c], snew[cur][1][h * 8 + c], r == 0, C, invC);
+        if (B0 + s + S * (cb + i) == a.row_start[b + 1] - 1 && a.row_n[b] > 0 && srow_ok[cur]) {
+          extra = valid;
+          if (col == extra) {
+            R.k0 = snew[cur][0][h * 8 + q4];
+            R.k1 = snew[cur][0][h * 8 + q4 + 4];
+          }
+          if (r == extra) R.v0 = snew[cur][1][h * 8 + c];
+          if (r + 8 == extra) R.v1 = snew[cur][1][h * 8 + c];
+        }
       }
+      acc.block(qb0, qb1, R, vtile, v_wr0, v_wr1, v_rd, r, q4, blk_ok, valid, extra, C, invC);
     };
     for (int i = 0;; i += 2) {
       step(X, i);
