@@ -80,23 +80,13 @@ struct StreamArgs {
   int total;                   // blocks in the stream
   int32_t row_start[kMaxSeqs + 1];   // first stream block of each row
   int32_t row_n[kMaxSeqs];           // tokens of each row
+  uint16_t wg_rows[kMaxGrid];        // per workgroup: first row << 3 | rows touched
 };
 static_assert(sizeof(StreamArgs) <= 4096, "kernel argument block");
 
 __device__ __forceinline__ int row_slot(const StreamArgs& a, int b) {
   const int s = a.slot_ids ? a.slot_ids[b] : b;
   return (s >= 0 && s < a.num_slots) ? s : -1;
-}
-
-// Row holding stream block p (the last row whose start is <= p; empty rows
-// share their start with the next row and are passed over).
-__device__ __forceinline__ int stream_row(const StreamArgs& a, int p) {
-  int lo = 0, hi = a.batch;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.row_start[mid] <= p) lo = mid; else hi = mid;
-  }
-  return lo;
 }
 
 // Rotate chunk `own` (8 dims starting at 8 * ch) against its pair partner
@@ -240,8 +230,9 @@ void stream_kernel(StreamArgs a) {
   const int S = kWaves / n_kv;           // waves per KV head
   const int h = w % n_kv;                // this wave's KV head
   const int s = w / n_kv;                // and its lane of blocks
-  const int bf = stream_row(a, B0);
-  const int nrows = stream_row(a, B1 - 1) - bf + 1;
+  const int wr = a.wg_rows[blockIdx.x];
+  const int bf = wr >> 3;                // first row of the share
+  const int nrows = wr & 7;              // rows it touches
   const int64_t row_elems = (int64_t)n_kv * kHeadDim;
   const float C = a.scale_log2e;
   const float invC = 1.0f / C;
@@ -592,7 +583,10 @@ int stream_decode(bool fused, const StreamCall& c) {
   a.total = (int)total;
   if (c.workspace_bytes < (size_t)2 * grid * c.n_q * kRec * sizeof(float)) return -1;
   a.ws = static_cast<float*>(c.workspace);
-  // every share must touch at most kMaxRows rows (empty rows in between count)
+  // rows of each share (the row of a block is the last row whose start is at
+  // or before it: empty rows share their start with the next row and are
+  // passed over); every share must touch at most kMaxRows rows, empty rows in
+  // between included
   for (int g = 0, b = 0; g < grid; ++g) {
     const int p0 = g * a.share;
     const int p1 = std::min(p0 + a.share, a.total) - 1;
@@ -600,6 +594,7 @@ int stream_decode(bool fused, const StreamCall& c) {
     int e = b;
     while (e + 1 < c.batch && a.row_start[e + 1] <= p1) ++e;
     if (e - b + 1 > kMaxRows) return -1;
+    a.wg_rows[g] = (uint16_t)(b << 3 | (e - b + 1));
   }
   void* args[] = {&a};
   hipStream_t st = static_cast<hipStream_t>(c.stream);
