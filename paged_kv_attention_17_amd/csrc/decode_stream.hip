@@ -310,36 +310,34 @@ void stream_kernel(StreamArgs a) {
     sq[i][rem] = v;
   }
   // ---- fused: the new token of every row whose last block is here: rotated
-  // key and value into LDS (it joins the attention from there) and into the
-  // pool (no workgroup reads that pool row in this launch) ---------------------
+  // key and value into LDS (it joins the attention from there).  Its pool
+  // write waits for the end of the workgroup's stream (no workgroup reads that
+  // pool row in this launch), which keeps the table lookup it needs off the
+  // start-up path.  nrows * n_kv * 8 <= kMaxRows * kWaves * 8 <= kThreads: one
+  // 8-dim chunk per thread.
+  int app_blk = -1;                      // pool block of this thread's new-token chunk
   if constexpr (FUSED) {
     if (tid < nrows) srow_ok[tid] = row_slot(a, bf + tid) >= 0;
-    for (int e = tid; e < nrows * n_kv * 8; e += kThreads) {
-      const int i = e / (n_kv * 8);
-      const int rem = e - i * n_kv * 8;
+    if (tid < nrows * n_kv * 8) {
+      const int i = tid / (n_kv * 8);
+      const int rem = tid - i * n_kv * 8;
       const int ch = rem & 7;
       const int kvh = rem >> 3;
       const int b = bf + i;
       const int n = a.row_n[b];
       const int last = a.row_start[b + 1] - 1;
-      if (n <= 0 || last < B0 || last >= B1) continue;
-      const int pos = n - 1;
-      const uint16_t* krow = a.k_new + ((int64_t)b * n_kv + kvh) * kHeadDim;
-      uint4 k = *reinterpret_cast<const uint4*>(krow + ch * 8);
-      if (pos < a.max_pos) {
+      if (n > 0 && last >= B0 && last < B1) {
+        const int pos = n - 1;
+        const uint16_t* krow = a.k_new + ((int64_t)b * n_kv + kvh) * kHeadDim;
+        uint4 k = *reinterpret_cast<const uint4*>(krow + ch * 8);
         const uint4 p = *reinterpret_cast<const uint4*>(krow + (ch ^ 4) * 8);
-        k = rope_own_chunk(k, p, a.rope + (int64_t)pos * (kHeadDim / 2), ch);
+        const uint4 v = *reinterpret_cast<const uint4*>(a.v_new + ((int64_t)b * n_kv + kvh) * kHeadDim + ch * 8);
+        const int slot = row_slot(a, b);
+        if (slot >= 0) app_blk = a.bt[(int64_t)slot * a.bt_stride + pos / kBlock];
+        if (pos < a.max_pos) k = rope_own_chunk(k, p, a.rope + (int64_t)pos * (kHeadDim / 2), ch);
+        snew[i][0][rem] = k;
+        snew[i][1][rem] = v;
       }
-      const uint4 v = *reinterpret_cast<const uint4*>(a.v_new + ((int64_t)b * n_kv + kvh) * kHeadDim + ch * 8);
-      snew[i][0][rem] = k;
-      snew[i][1][rem] = v;
-      const int slot = row_slot(a, b);
-      if (slot < 0) continue;
-      const int blk = a.bt[(int64_t)slot * a.bt_stride + pos / kBlock];
-      if (blk < 0 || blk >= a.num_blocks) continue;
-      const int64_t off = ((int64_t)blk * kBlock + pos % kBlock) * row_elems + kvh * kHeadDim + ch * 8;
-      *reinterpret_cast<uint4*>(a.k_pool + off) = k;
-      *reinterpret_cast<uint4*>(a.v_pool + off) = v;
     }
   }
   __syncthreads();
@@ -350,10 +348,15 @@ void stream_kernel(StreamArgs a) {
   const int q4 = lane >> 4;              // MFMA lane group
   uint4 qb0, qb1;                        // Q^T operands: dims 8 q4 .. and 32 + 8 q4 ..
   int cur = 0;                           // row of the share being accumulated
+  int row_last = -1;                     // fused: stream block holding the row's new token, or -1
   auto load_q = [&]() {
     const uint4 z = make_uint4(0, 0, 0, 0);
     qb0 = col < G ? sq[cur][(h * G + col) * 8 + q4] : z;
     qb1 = col < G ? sq[cur][(h * G + col) * 8 + q4 + 4] : z;
+    if constexpr (FUSED) {
+      const int b = bf + cur;
+      row_last = wave_uniform(a.row_n[b] > 0 && srow_ok[cur] ? a.row_start[b + 1] - 1 : -1);
+    }
   };
   load_q();
 
@@ -402,8 +405,7 @@ void stream_kernel(StreamArgs a) {
       int extra = -1;                    // fused: slot of the new token in this block
       if constexpr (FUSED) {
         // the row's last block: the new token (rotated key, value) from LDS
-        const int b = bf + cur;
-        if (B0 + s + S * (cb + i) == a.row_start[b + 1] - 1 && a.row_n[b] > 0 && srow_ok[cur]) {
+        if (B0 + s + S * (cb + i) == row_last) {
           extra = valid;
           if (col == extra) {
             R.k0 = snew[cur][0][h * 8 + q4];
@@ -425,6 +427,17 @@ void stream_kernel(StreamArgs a) {
     }
   }
   while (cur < nrows) flush();
+  if constexpr (FUSED) {
+    // the new token into the pool (position context_len - 1 of its row)
+    if (app_blk >= 0 && app_blk < a.num_blocks) {
+      const int i = tid / (n_kv * 8);
+      const int rem = tid - i * n_kv * 8;
+      const int pos = a.row_n[bf + i] - 1;
+      const int64_t off = ((int64_t)app_blk * kBlock + pos % kBlock) * row_elems + (rem >> 3) * kHeadDim + (rem & 7) * 8;
+      *reinterpret_cast<uint4*>(a.k_pool + off) = snew[i][0][rem];
+      *reinterpret_cast<uint4*>(a.v_pool + off) = snew[i][1][rem];
+    }
+  }
   __syncthreads();
 
   // ---- merge the KV heads' waves per row: finish rows inside the share,
