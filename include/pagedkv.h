@@ -191,9 +191,13 @@ int pkv_check_block_table(const int32_t* bt_host, int64_t bt_row_stride, int num
  * scale must be positive and finite.
  * ------------------------------------------------------------------------ */
 
-/* Bytes of workspace the decode calls need for these sizes (0 when no
- * sequence can need more than one partition). partition_size 0 = the
- * automatic choice, which depends only on the arguments given here. */
+/* Bytes of workspace the decode calls need for these sizes: the larger of
+ * the per-partition kernels' partials (batch x n_q_heads x partitions records)
+ * and the streaming kernel's records (two per workgroup, at most 512
+ * workgroups), each record 66 floats per query head (output, max, sum).
+ * Returns 0 for invalid arguments.  partition_size 0 = the automatic choice,
+ * which depends only on the arguments given here.  A call given less than the
+ * streaming kernel's share of this size uses the per-partition kernels. */
 size_t pkv_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
                                   int max_context_len, int partition_size);
 
@@ -215,8 +219,10 @@ int pkv_decode_partition_size(int batch, int n_kv_heads, int max_context_len);
  * unspecified).  NULL launches the max_context_len grid.
  * partition_size: 0 = automatic, else a positive multiple of 16.
  * workspace: at least pkv_decode_workspace_bytes(...) bytes of device memory,
- * any contents; may be NULL when that size is 0.  Calls sharing one workspace
- * must not run concurrently. */
+ * 16-byte aligned, any contents (every value read is written first in the same
+ * call); NULL is accepted when no sequence needs more than one partition (the
+ * call then uses the per-partition kernels).  Calls sharing one workspace must
+ * not run concurrently. */
 int pkv_paged_attn_decode(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_pool,
                           const pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
                           int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,
