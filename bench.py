@@ -207,22 +207,29 @@ def prefill_leg(torch, np, pkv, W, iters: int = 5):
         r = torch.from_numpy(np.concatenate(rows)).cuda()
         i32 = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")  # noqa: E731
         calls.append(dict(q=qd[r].contiguous(), k=kd[r].contiguous(), v=vd[r].contiguous(), sid=i32(sid),
-                          pos=i32(pos), cu=i32(cu), qs=i32(qs), seqs=i32(seqs), mq=int(np.diff(cu).max())))
+                          pos=i32(pos), cu=i32(cu), qs=i32(qs), seqs=i32(seqs), mq=int(np.diff(cu).max()),
+                          cu_h=np.array(cu, np.int32), qs_h=np.array(qs, np.int32)))
     stream = torch.cuda.current_stream()
+    outs = [torch.empty_like(cl["q"]) for cl in calls]
     times = []
     for it in range(iters + 1):
-        t = 0.0
-        for cl in calls:
+        # a short device-side wait first, so that every call of the pass is
+        # already queued when its events run (the events then time the
+        # kernels, not the host's launch latency)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(200000)
+        ev = []
+        for cl, out in zip(calls, outs):
             pkv.pkv_paged_kv_append(kp, vp, cl["k"], cl["v"], btd, cl["sid"], cl["pos"])
-            out = torch.empty_like(cl["q"])
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            pkv.pkv_paged_attn_prefill(out, cl["q"], cl["cu"], cl["qs"], cl["seqs"], kp, vp, btd, cl["mq"], w.scale)
+            pkv.pkv_paged_attn_prefill(out, cl["q"], cl["cu"], cl["qs"], cl["seqs"], kp, vp, btd, cl["mq"], w.scale,
+                                       cu_q_lens_host=cl["cu_h"], q_start_host=cl["qs_h"])
             e1.record(stream)
-            e1.synchronize()
-            t += e0.elapsed_time(e1) / 1e3
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
         if it > 0:
-            times.append(t)
+            times.append(sum(e0.elapsed_time(e1) for e0, e1 in ev) / 1e3)
     pairs = sum(n * (n + 1) // 2 for n in lens)
     flops = pairs * 32 * 64 * 2 * 2          # QK and PV, multiply-add = 2 flops
     t = float(np.median(times))

@@ -262,13 +262,20 @@ int pkv_paged_decode_fused(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_n
  * be in the pool (pkv_paged_kv_append). QK^T and PV run on MFMA (bf16 in,
  * float32 accumulate); out is bf16 [total_q][n_q_heads][head_dim].
  * max_q_len: host bound on the longest query run (sizes the grid).
+ * cu_q_lens_host, q_start_host: optional HOST copies of cu_q_lens and
+ * q_start_pos (both or neither).  When given (and the call has at most 768
+ * (sequence, query tile) pairs), only real work is launched, the tiles that
+ * see the most keys first; the kernels still read the device arrays, and the
+ * two must agree (otherwise the result is unspecified).  NULL launches the
+ * max_q_len grid.  Either way the output is the same, bit for bit.
  * ------------------------------------------------------------------------ */
 int pkv_paged_attn_prefill(pkv_bf16* out, const pkv_bf16* q, const int32_t* cu_q_lens,
                            const int32_t* q_start_pos, const int32_t* slot_ids,
                            const pkv_bf16* k_pool, const pkv_bf16* v_pool, int num_blocks,
                            const int32_t* block_table, int64_t bt_row_stride, int num_slots,
                            int max_blocks_per_seq, int num_seqs, int total_q, int max_q_len,
-                           int n_q_heads, int n_kv_heads, int head_dim, float scale, void* stream);
+                           int n_q_heads, int n_kv_heads, int head_dim, float scale,
+                           const int32_t* cu_q_lens_host, const int32_t* q_start_host, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * One whole decode step of an n-layer engine, driven natively.  Source: "The

@@ -52,7 +52,7 @@ SIGNATURES = {
     "pkv_paged_attn_decode": (_i, [_p, _p, _p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i,
                                    _p, _sz, _p]),
     "pkv_paged_attn_prefill": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _p, _i64, _i, _i, _i, _i, _i, _i, _i, _i,
-                                    _f, _p]),
+                                    _f, _p, _p, _p]),
     "pkv_decode_workspace_init": (_i, [_p, _sz, _p]),
     "pkv_paged_decode_fused": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _p,
                                     _i, _f, _i, _p, _sz, _p]),
@@ -404,8 +404,10 @@ def pkv_paged_attn_decode(out, q, k_pool, v_pool, block_table, slot_ids, context
 
 
 def pkv_paged_attn_prefill(out, q, cu_q_lens, q_start_pos, slot_ids, k_pool, v_pool, block_table, max_q_len,
-                           scale, stream=None):
-    """q/out [total_q, n_q, 64]; cu_q_lens [S+1]; q_start_pos [S]; slot_ids [S] or None."""
+                           scale, stream=None, cu_q_lens_host=None, q_start_host=None):
+    """q/out [total_q, n_q, 64]; cu_q_lens [S+1]; q_start_pos [S]; slot_ids [S] or None.
+    cu_q_lens_host / q_start_host: optional numpy copies (both or neither) that
+    let the library launch only real work, heaviest first."""
     import torch
     for t, n in ((out, "out"), (q, "q"), (cu_q_lens, "cu_q_lens"), (q_start_pos, "q_start_pos"),
                  (slot_ids, "slot_ids"), (k_pool, "k_pool"), (v_pool, "v_pool")):
@@ -416,12 +418,21 @@ def pkv_paged_attn_prefill(out, q, cu_q_lens, q_start_pos, slot_ids, k_pool, v_p
     if cu_q_lens.shape[0] != S + 1 or (slot_ids is not None and slot_ids.shape[0] != S):
         raise ValueError("per-sequence arrays disagree")
     bt, stride, rows, mb = _table(block_table)
+    if (cu_q_lens_host is None) != (q_start_host is None):
+        raise ValueError("cu_q_lens_host and q_start_host go together")
+    cuh = qsh = None
+    if cu_q_lens_host is not None:
+        cuh = np.ascontiguousarray(cu_q_lens_host, dtype=np.int32)
+        qsh = np.ascontiguousarray(q_start_host, dtype=np.int32)
+        if cuh.shape != (S + 1,) or qsh.shape != (S,):
+            raise ValueError("host copies must match cu_q_lens / q_start_pos")
     _check("pkv_paged_attn_prefill", load().pkv_paged_attn_prefill(
         _dev_ptr(out, "out", _bf16_types()), _dev_ptr(q, "q", _bf16_types()),
         _dev_ptr(cu_q_lens, "cu_q_lens", (torch.int32,)), _dev_ptr(q_start_pos, "q_start_pos", (torch.int32,)),
         _dev_ptr(slot_ids, "slot_ids", (torch.int32,)), _dev_ptr(k_pool, "k_pool", _bf16_types()),
         _dev_ptr(v_pool, "v_pool", _bf16_types()), k_pool.shape[0], bt, stride, rows, mb, S, q.shape[0], max_q_len,
-        q.shape[1], k_pool.shape[2], q.shape[2], float(scale), _stream(stream)))
+        q.shape[1], k_pool.shape[2], q.shape[2], float(scale), None if cuh is None else cuh.ctypes.data,
+        None if qsh is None else qsh.ctypes.data, _stream(stream)))
 
 
 def pkv_decode_step(q, k, v, out, k_pool, v_pool, bt_host, bt_dev, free_list, n_free, cached_lens, meta_dev,

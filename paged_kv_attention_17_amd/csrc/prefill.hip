@@ -37,6 +37,10 @@
 // never reaches the output.
 #include "common.h"
 
+#include <algorithm>
+#include <utility>
+#include <vector>
+
 namespace pkv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -49,6 +53,7 @@ constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kKsStride = kHeadDim + 8;   // padded LDS row (bf16) for K tiles
 constexpr int kVsStride = kHeadDim;       // LDS row (bf16) of a V tile, rotated per key
 constexpr float kPfTau = 8.0f;            // lazy rescale threshold, log2 units
+constexpr int kPfMaxItems = 768;          // host-ordered work items carried in the kernel arguments
 
 // Query tokens per workgroup for G query heads per KV head.
 __host__ __device__ constexpr int pf_qtile(int G) { return 32 * (kPfWaves / G); }
@@ -68,9 +73,11 @@ struct PrefillArgs {
   int max_blocks;
   int n_q;
   int n_kv;
-  int q_tiles;        // tiles in the grid's x dimension
+  int q_tiles;        // query tiles per sequence in the grid (fallback order)
   int total_q;
   float scale_log2e;
+  int n_items;        // > 0: the grid is n_items x n_kv workgroups taking items[id / n_kv]
+  uint32_t items[kPfMaxItems];   // (sequence << 12 | query tile), most key tiles first
 };
 
 __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
@@ -92,9 +99,21 @@ __device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
 template <int G>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void prefill_kernel(PrefillArgs a) {
   constexpr int kQTile = pf_qtile(G);
-  const int tile = a.q_tiles - 1 - (int)blockIdx.x;   // heavy (late) tiles first
-  const int g = blockIdx.y;
-  const int seq = blockIdx.z;
+  // Which (sequence, KV head, query tile): from the host's list (most key
+  // tiles first, KV heads of one item on consecutive workgroups, hence on
+  // different XCDs), else late (heavy) tiles first over all sequences.
+  int tile, g, seq;
+  if (a.n_items > 0) {
+    const int id = blockIdx.x;
+    const uint32_t it = a.items[id / a.n_kv];
+    g = id % a.n_kv;
+    seq = (int)(it >> 12);
+    tile = (int)(it & 0xfff);
+  } else {
+    g = blockIdx.x;
+    seq = blockIdx.y;
+    tile = a.q_tiles - 1 - (int)blockIdx.z;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = wave_uniform(tid >> 6);
@@ -291,7 +310,8 @@ extern "C" int pkv_paged_attn_prefill(pkv_bf16* out, const pkv_bf16* q, const in
                                       const pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
                                       int64_t bt_row_stride, int num_slots, int max_blocks_per_seq, int num_seqs,
                                       int total_q, int max_q_len, int n_q_heads, int n_kv_heads, int head_dim,
-                                      float scale, void* stream) {
+                                      float scale, const int32_t* cu_q_lens_host, const int32_t* q_start_host,
+                                      void* stream) {
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || num_slots < 0 ||
       max_blocks_per_seq < 0 || bt_row_stride < max_blocks_per_seq || !(scale == scale))
     return PKV_ERR_INVALID_ARG;
@@ -303,6 +323,7 @@ extern "C" int pkv_paged_attn_prefill(pkv_bf16* out, const pkv_bf16* q, const in
       !aligned4(cu_q_lens) || !aligned4(q_start_pos) || (slot_ids && !aligned4(slot_ids)))
     return PKV_ERR_MISALIGNED;
   if (num_seqs > 65535 || n_kv_heads > 65535) return PKV_ERR_INVALID_ARG;
+  static_assert(sizeof(PrefillArgs) <= 4096, "kernel argument block");
   PrefillArgs a;
   a.out = out;
   a.q = q;
@@ -326,7 +347,33 @@ extern "C" int pkv_paged_attn_prefill(pkv_bf16* out, const pkv_bf16* q, const in
                  : G == 2 ? (const void*)prefill_kernel<2>
                  : G == 4 ? (const void*)prefill_kernel<4>
                           : (const void*)prefill_kernel<8>;
+  // With the lengths on the host: one workgroup per real (sequence, query
+  // tile, KV head), most key tiles first.  The hardware hands workgroups out
+  // in id order and places them by id, so a list sorted by work keeps every
+  // XCD and shader engine busy to the end (the fallback grid holds empty
+  // workgroups for short sequences and groups work by sequence).
+  a.n_items = 0;
+  if (cu_q_lens_host && q_start_host) {
+    const int qt = pf_qtile(G);
+    std::vector<std::pair<int, uint32_t>> items;
+    bool fits = true;
+    for (int s = 0; s < num_seqs && fits; ++s) {
+      const int ql = cu_q_lens_host[s + 1] - cu_q_lens_host[s];
+      for (int t = 0; t * qt < ql && fits; ++t) {
+        const int64_t last = (int64_t)q_start_host[s] + std::min((t + 1) * qt, ql);   // keys seen, at most
+        const int nk = (int)std::min<int64_t>((last + kKTile - 1) / kKTile, 1 << 30);
+        items.push_back({nk, (uint32_t)s << 12 | (uint32_t)t});
+        fits = (int)items.size() <= kPfMaxItems && t < 4096 && s < (1 << 20);
+      }
+    }
+    if (fits && !items.empty()) {
+      std::stable_sort(items.begin(), items.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+      for (size_t i = 0; i < items.size(); ++i) a.items[i] = items[i].second;
+      a.n_items = (int)items.size();
+    }
+  }
   void* args[] = {&a};
-  return launch_status(hipLaunchKernel(fn, dim3(a.q_tiles, n_kv_heads, num_seqs), dim3(kPfThreads), args, 0,
-                                       (hipStream_t)stream));
+  const dim3 grid = a.n_items > 0 ? dim3((unsigned)(a.n_items * n_kv_heads)) : dim3(n_kv_heads, num_seqs, a.q_tiles);
+  if (a.n_items == 0 && a.q_tiles > 65535) return PKV_ERR_INVALID_ARG;
+  return launch_status(hipLaunchKernel(fn, grid, dim3(kPfThreads), args, 0, (hipStream_t)stream));
 }

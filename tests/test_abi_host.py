@@ -97,9 +97,9 @@ def test_other_entry_points_argument_errors(lib):
         == E.PKV_ERR_MISALIGNED
     assert lib.pkv_paged_gather(FAKE, FAKE, FAKE, FAKE, 8, FAKE, 4, 4, 0, 65, 8, 64, None) == E.PKV_ERR_CAPACITY
     assert lib.pkv_paged_attn_prefill(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 8, FAKE, 4, 1, 4, 1, 10, 10,
-                                      32, 8, 48, 0.125, None) == E.PKV_ERR_UNSUPPORTED
+                                      32, 8, 48, 0.125, None, None, None) == E.PKV_ERR_UNSUPPORTED
     assert lib.pkv_paged_attn_prefill(FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 8, FAKE, 4, 1, 4, 1, 10, 10,
-                                      32, 8, 64, 0.125, None) == E.PKV_ERR_NULL
+                                      32, 8, 64, 0.125, None, None, None) == E.PKV_ERR_NULL
     # fused decode: same checks plus its own inputs
     assert lib.pkv_paged_decode_fused(FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None, 1, 17,
                                       32, 8, 64, FAKE, 100, 0.125, 0, None, 0, None) == E.PKV_ERR_NULL

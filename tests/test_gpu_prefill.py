@@ -36,9 +36,11 @@ def _setup(lens, n_q=32, n_kv=8, seed=0, poison=True, extra=0):
     return q, kn, vn, kp, vp, bt, perm[k:]
 
 
-def _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk):
+def _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk, host=False):
     """Append and prefill every sequence chunk by chunk (all sequences'
-    i-th chunks in one call).  Returns output bits and the device pools."""
+    i-th chunks in one call); host=True also hands the library host copies of
+    the chunk layout (the launch then holds only real work, heaviest first).
+    Returns output bits and the device pools."""
     kpd, vpd, btd = dev_bf16(kp), dev_bf16(vp), dev_i32(bt)
     out = torch.zeros((q.shape[0],) + q.shape[1:], dtype=torch.bfloat16, device="cuda")
     qd, knd, vnd = dev_bf16(q), dev_bf16(kn), dev_bf16(vn)
@@ -61,8 +63,9 @@ def _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk):
         kc, vc, qc = knd[r].contiguous(), vnd[r].contiguous(), qd[r].contiguous()
         pkv.pkv_paged_kv_append(kpd, vpd, kc, vc, btd, dev_i32(sid), dev_i32(pos))
         oc = torch.empty_like(qc)
+        extra = dict(cu_q_lens_host=np.array(cu, np.int32), q_start_host=np.array(qs, np.int32)) if host else {}
         pkv.pkv_paged_attn_prefill(oc, qc, dev_i32(cu), dev_i32(qs), dev_i32(seqs), kpd, vpd, btd,
-                                   int(np.diff(cu).max()), 0.125)
+                                   int(np.diff(cu).max()), 0.125, **extra)
         out[r] = oc
     torch.cuda.synchronize()
     return bits(out), kpd, vpd
@@ -107,6 +110,9 @@ def test_prefill_gqa_long_chunked(gpu, n_q, n_kv):
     whole, _, _ = _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk=4096)
     part, _, _ = _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk=160)
     np.testing.assert_array_equal(part, whole)
+    for chunk in (160, 4096):
+        sched, _, _ = _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk=chunk, host=True)
+        np.testing.assert_array_equal(sched, whole)
     ref, _, _ = _oracle(q, kn, vn, kp, vp, bt, lens)
     check_attention(whole, ref, f"prefill long gqa {n_q}/{n_kv}")
 
@@ -118,8 +124,28 @@ def test_chunked_equals_whole_bit_identical(gpu):
     for chunk in (16, 64, 100):
         part, _, _ = _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk=chunk)
         np.testing.assert_array_equal(part, whole)
+        part, _, _ = _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk=chunk, host=True)
+        np.testing.assert_array_equal(part, whole)
     ref, _, _ = _oracle(q, kn, vn, kp, vp, bt, lens)
     check_attention(whole, ref, "chunked")
+
+
+def test_prefill_host_schedule_many_items(gpu):
+    """More (sequence, query tile) pairs than the kernel arguments carry: the
+    host copies are then ignored and the full grid runs; both agree with the
+    oracle and, bit for bit, with each other."""
+    lens = [1, 3] * 400 + [70, 200]
+    q, kn, vn, kp, vp, bt, _ = _setup(lens, seed=11)
+    grid, _, _ = _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk=4096)
+    sched, _, _ = _gpu_chunked(q, kn, vn, kp, vp, bt, lens, chunk=4096, host=True)
+    np.testing.assert_array_equal(sched, grid)
+    few = [70, 200, 1, 3]
+    q2, kn2, vn2, kp2, vp2, bt2, _ = _setup(few, seed=12)
+    a, _, _ = _gpu_chunked(q2, kn2, vn2, kp2, vp2, bt2, few, chunk=64)
+    b, _, _ = _gpu_chunked(q2, kn2, vn2, kp2, vp2, bt2, few, chunk=64, host=True)
+    np.testing.assert_array_equal(a, b)
+    ref, _, _ = _oracle(q, kn, vn, kp, vp, bt, lens)
+    check_attention(grid, ref, "prefill many sequences")
 
 
 @pytest.mark.slow
