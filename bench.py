@@ -242,6 +242,44 @@ def prefill_leg(torch, np, pkv, W, iters: int = 5):
                          "kernel": "pkv_paged_attn_prefill (prefill_kernel<4>)"}}
 
 
+def long_context_leg(torch, np, pkv, W, iters: int = 10):
+    """Split-context decode at B=256 with 8,192 tokens each (4.29 GB of K/V,
+    one layer, more than 16x the last-level cache): the streaming kernel and
+    its merge (host lengths given) and the per-partition kernels (lengths on
+    the device only), each timed with HIP events around back-to-back calls."""
+    w = W.config4(fill_pool=False)
+    kp = torch.empty((w.num_blocks, 16, 8, 64), dtype=torch.bfloat16, device="cuda").normal_()
+    vp = torch.empty_like(kp).uniform_(-1, 1)
+    bt = torch.from_numpy(w.block_table[:, 0, :].copy()).cuda()
+    ctx = w.context_lens.astype(np.int32)
+    ctxd = torch.from_numpy(ctx).cuda()
+    q = torch.from_numpy(w.q_new[0].view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty_like(q)
+    B, mx = q.shape[0], int(ctx.max())
+    ws = torch.empty(pkv.pkv_decode_workspace_bytes(B, 32, 8, 64, mx, 0) // 4 + 64, dtype=torch.int32, device="cuda")
+    nbytes = int(ctx.sum()) * KV_BYTES_PER_TOKEN
+    res = {"workload": "decode attention, B=256, context 8192 each, 32q/8kv heads, d=64, bf16 16-token blocks, "
+                       "one layer", "bytes_per_call": nbytes}
+    for name, rl in (("stream", ctx), ("partitions", None)):
+        run = lambda: pkv.pkv_paged_attn_decode(out, q, kp, vp, bt, None, ctxd, mx, w.scale, 0, ws,  # noqa: E731
+                                                row_lens_host=rl)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            run()
+        e1.record()
+        e1.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / iters
+        res[name] = {"us_per_call": round(t * 1e6, 1), "GBps": round(nbytes / t / 1e9, 1),
+                     "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del kp, vp
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,6 +377,11 @@ def main():
     log(f"prefill: {pre['us_per_pass']:.1f} us per pass over {pre['calls']} chunk calls, "
         f"{pre['roofline']['achieved']:.1f} TFLOP/s = {pre['roofline']['frac']:.2%} of bf16 MFMA peak")
 
+    lc = long_context_leg(torch, np, pkv, W)
+    log(f"long context (B=256 x 8192): stream {lc['stream']['us_per_call']:.1f} us = {lc['stream']['GBps']:.0f} GB/s "
+        f"({lc['stream']['frac']:.1%}); per-partition {lc['partitions']['us_per_call']:.1f} us = "
+        f"{lc['partitions']['GBps']:.0f} GB/s ({lc['partitions']['frac']:.1%})")
+
     copy_gbs = stream_copy_gbs(torch)
     read_gbs = stream_read_gbs(torch, pkv)
     log(f"plain copy kernel: {copy_gbs:.0f} GB/s (read + write); streaming read of 4 GiB: {read_gbs:.0f} GB/s")
@@ -379,6 +422,7 @@ def main():
         "read_kernel_GBps": round(read_gbs, 1),
         "unfused_layer_us": unf,
         "prefill": pre,
+        "long_context": lc,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
