@@ -25,6 +25,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import math
 import os
 import sys
@@ -43,10 +44,16 @@ def log(*a):
 
 
 def decode_source_hash() -> str:
+    """Hash of the decode kernels' sources with comments and whitespace
+    removed, so that a counter summary stays valid across comment edits and
+    only a code change invalidates it."""
     h = hashlib.sha256()
     for f in ("decode_stream.hip", "decode.hip", "attn_block.h", "common.h"):
-        with open(os.path.join(ROOT, "paged_kv_attention_17_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_attention_17_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -34,10 +34,12 @@
 // small kernel merges those records.
 //
 // Fused variant.  The workgroup holding a row's last block rotates the row's
-// new key, keeps key and value in LDS and writes them into the pool (position
-// context_len - 1).  Pool reads of that block stop before the new token, which
-// joins the attention from LDS in the wave that processes the block, so no
-// read waits for the write.
+// new key and keeps key and value in LDS.  Pool reads of that block stop
+// before the new token; the wave that processes the block puts the token into
+// its K and V registers at the token's slot, so it joins the same products and
+// no read waits for a write.  The workgroup writes the token into the pool
+// (position context_len - 1) after its stream, which keeps the table lookup
+// for that write off the start-up path.
 #include "attn_block.h"
 #include "decode_stream.h"
 
