@@ -31,7 +31,8 @@
 // LDS area: one barrier per tile.  The running max is shared by a lane and
 // lane ^ 32 (both hold the same query) and raised only when a score exceeds it
 // by more than 8 (log2 units), so the accumulator rescale and the cross-lane
-// exchange are rare; the sum stays per lane until the end.  Masks (causal, and
+// exchange are rare; the sum (of the same bf16 weights that multiply V) stays
+// per lane until the end.  Masks (causal, and
 // keys past the sequence's cached length, which also get V = 0 in LDS) are
 // selects applied only on tiles that need them, so NaN in unused pool slots
 // never reaches the output.
@@ -54,6 +55,7 @@ constexpr int kKsStride = kHeadDim + 8;   // padded LDS row (bf16) for K tiles
 constexpr int kVsStride = kHeadDim;       // LDS row (bf16) of a V tile, rotated per key
 constexpr float kPfTau = 8.0f;            // lazy rescale threshold, log2 units
 constexpr int kPfMaxItems = 768;          // host-ordered work items carried in the kernel arguments
+constexpr uint32_t kOnesBf16 = 0x3F803F80u;  // (1, 1) as a bf16 pair
 
 // Query tokens per workgroup for G query heads per KV head.
 __host__ __device__ constexpr int pf_qtile(int G) { return 32 * (kPfWaves / G); }
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
     const int buf = kt & 1;
     const int kbase = kt * kKTile;
     const bool more = kt + 1 < n_ktiles;
-    KV nxt{make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    KV nxt;
     if (more) nxt = fetch(kt + 1);
 
     if (sub_live && kbase < sub_key_end) {
@@ -252,16 +254,21 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
       for (int kh = 0; kh < 2; ++kh) {
         float p[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = fast_exp2(__builtin_fmaf(s[kh][i], C, -m));
-          l += p[i];
-        }
+        for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(s[kh][i], C, -m));
         // P^T operands: k-step 0 = accumulators 0..7, k-step 1 = 8..15.
         uint4 pb[2];
         pb[0] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                            pack_bf16x2(p[6], p[7]));
         pb[1] = make_uint4(pack_bf16x2(p[8], p[9]), pack_bf16x2(p[10], p[11]), pack_bf16x2(p[12], p[13]),
                            pack_bf16x2(p[14], p[15]));
+        // the sum takes the same bf16 weights as the numerator (dot2 with (1, 1))
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          l = dot2_bf16(pb[u].x, kOnesBf16, l);
+          l = dot2_bf16(pb[u].y, kOnesBf16, l);
+          l = dot2_bf16(pb[u].z, kOnesBf16, l);
+          l = dot2_bf16(pb[u].w, kOnesBf16, l);
+        }
         // O^T += V^T . P^T: slot 4u + j of lane (dim, half) must hold key
         // 16 kstep + 8u + 4 half + j (the P^T slot's key), so the addressing
         // lane 16 g + s supplies key ... + 4 (g / 2) + s / 4 and dims
