@@ -424,7 +424,10 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "pkv_paged_decode_fused call: stream_kernel<4, fused> + stream_merge_kernel<4>",
                      "bytes_per_launch": bytes_per_launch,
-                     "us_per_launch": round(t_attn * 1e6, 3), "source_hash": src_hash},
+                     "touched_bytes_per_launch": int(((ctx_now + 15) // 16).sum()) * 16 * KV_BYTES_PER_TOKEN,
+                     "us_per_launch": round(t_attn * 1e6, 3), "us_median": round(float(np.median(durs)) * 1e6, 3),
+                     "us_p10": round(float(np.percentile(durs, 10)) * 1e6, 3),
+                     "us_p90": round(float(np.percentile(durs, 90)) * 1e6, 3), "source_hash": src_hash},
         "copy_kernel_GBps": round(copy_gbs, 1),
         "read_kernel_GBps": round(read_gbs, 1),
         "unfused_layer_us": unf,
