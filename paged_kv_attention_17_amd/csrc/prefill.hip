@@ -22,13 +22,17 @@
 // LDS and the V^T operand is read with the gfx950 transpose load
 // (ds_read_b64_tr_b16): within each 16-lane group, lane i's element j comes
 // from element i % 4 of the 64-bit word addressed by lane 4j + i / 4, so lanes
-// address 4-dim pieces of the keys that the P^T slots hold (see vt_addr).  V
-// rows are rotated by 16 dims per key (mod 4) so those reads and the 16-byte
-// row writes hit distinct banks.
+// address 4-dim pieces of the keys that the P^T slots hold (the vt_off
+// offsets).  V rows are rotated by 16 dims per key (mod 4) and K rows have
+// their 16-byte pieces permuted by key (mod 8), so the operand reads hit
+// distinct banks without padding.
 //
-// Pipeline.  The next tile's K and V rows are loaded into registers while the
-// current tile is computed, then written to the other half of a double-buffered
-// LDS area: one barrier per tile.  The running max is shared by a lane and
+// Pipeline.  K and V tiles travel from the pool straight into a three-stage
+// LDS ring by buffer loads that write LDS (no registers, no LDS stores): tile
+// kt + 2 is requested while tile kt is computed, each wave waits for its own
+// loads of tile kt (s_waitcnt vmcnt) and one barrier per tile publishes them.
+// Block ids come from a per-wave table slice (lane j: tile tb + j) read with
+// v_readlane.  The running max is shared by a lane and
 // lane ^ 32 (both hold the same query) and raised only when a score exceeds it
 // by more than 8 (log2 units), so the accumulator rescale and the cross-lane
 // exchange are rare; the sum (of the same bf16 weights that multiply V) stays
@@ -51,8 +55,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kKTile = 64;            // keys per step (two 32-key MFMA blocks)
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kKsStride = kHeadDim + 8;   // padded LDS row (bf16) for K tiles
 constexpr int kVsStride = kHeadDim;       // LDS row (bf16) of a V tile, rotated per key
+constexpr int kPfStages = 3;              // K/V tiles in flight per workgroup (LDS ring)
 constexpr float kPfTau = 8.0f;            // lazy rescale threshold, log2 units
 constexpr int kPfMaxItems = 768;          // host-ordered work items carried in the kernel arguments
 constexpr uint32_t kOnesBf16 = 0x3F803F80u;  // (1, 1) as a bf16 pair
@@ -98,6 +102,28 @@ __device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor words (base, size; gfx9 untyped dword access).
+__device__ __forceinline__ v4u rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4u{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+// Byte address of a shared-memory location.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+// Buffer load of 16 bytes per lane written straight to LDS: lane i's bytes
+// land at lds + 16 i; offsets at or past the descriptor's size read zeros.
+// Written as assembly so that the compiler neither tracks nor waits for these
+// loads: the kernel waits for them itself (s_waitcnt vmcnt, then a barrier).
+__device__ __forceinline__ void lds_dma16(v4u rsrc, uint32_t voff, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(voff), "s"(rsrc), "s"(lds)
+                   : "memory", "m0");
+}
+
 template <int G>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void prefill_kernel(PrefillArgs a) {
   constexpr int kQTile = pf_qtile(G);
@@ -138,8 +164,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
   const int32_t* btrow = a.bt + (int64_t)slot * a.bt_stride;
   const int64_t row_elems = (int64_t)a.n_kv * kHeadDim;
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKTile * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kKTile * kVsStride];
+  // Three stages of one 64-key K tile and one V tile (8 KB each), filled by
+  // buffer loads that write LDS directly: slot s (16 bytes) of K row `key`
+  // holds dims 8 (s ^ (key & 7)) .. + 7, slot s of V row `key` holds dims
+  // 8 ((s - 2 (key & 3)) & 7) .. + 7 (V element (key, d) sits at
+  // vs_index(key, d)); both keep the MFMA-operand reads conflict-free.
+  __shared__ __attribute__((aligned(16))) uint16_t kvs[kPfStages][2][kKTile * kHeadDim];
 
   // This wave: head hh of the group, query subtile sub; this lane: one query.
   const int hh = w % G;
@@ -153,26 +183,42 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
   const bool sub_live = sub0 < tok0 + n_q_tile;
   const int sub_key_end = min(sub_last_pos + 1, n_keys);                  // keys this subtile sees
 
-  // Loader role: thread -> (key, 16-byte chunk) of the K and the V tile.
-  const int ld_key = tid >> 3;
-  const int ld_chunk = tid & 7;
-  struct KV { uint4 k, v; };
-  auto fetch = [&](int kt) -> KV {
-    const int kk = kt * kKTile + ld_key;
-    KV x{make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-    if (kk < n_keys) {
-      const int blk = btrow[kk / kBlock];
-      if (blk >= 0 && blk < a.num_blocks) {
-        const int64_t off = ((int64_t)blk * kBlock + kk % kBlock) * row_elems + g * kHeadDim + ld_chunk * 8;
-        x.k = *reinterpret_cast<const uint4*>(a.k_pool + off);
-        x.v = *reinterpret_cast<const uint4*>(a.v_pool + off);
-      }
-    }
-    return x;
+  // Loader role: wave w brings keys 8 w .. 8 w + 7 of every tile (half of one
+  // 16-token block), lane i key 8 w + i / 8 into LDS slot i % 8.  Keys past
+  // the cache, and blocks whose id is out of range, read as zeros (offsets
+  // beyond the buffer's size), so no NaN from an unused pool slot reaches a
+  // product.
+  const int ld_row = 8 * (w & 1) + (lane >> 3);              // row inside the block
+  const int ld_kx = (lane >> 3) & 7;                         // key & 7
+  const uint32_t block_bytes = (uint32_t)(kBlock * row_elems * 2);
+  const uint32_t ld_base = (uint32_t)((ld_row * row_elems + g * kHeadDim) * 2);
+  const uint32_t ld_koff = ld_base + 16u * (uint32_t)((lane & 7) ^ ld_kx);
+  const uint32_t ld_voff = ld_base + 16u * (uint32_t)(((lane & 7) - 2 * (ld_kx & 3)) & 7);
+  const char* kpool = reinterpret_cast<const char*>(a.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(a.v_pool);
+  // block ids of this wave's half-blocks for tiles tb .. tb + 63 (lane j: tile tb + j)
+  int tb = 0, tabv = -1;
+  auto load_table = [&](int t0) {
+    tb = t0;
+    const int bi = (t0 + lane) * (kKTile / kBlock) + (w >> 1);
+    tabv = (t0 + lane) * kKTile < n_keys && bi < a.max_blocks ? btrow[bi] : -1;
+    // wait here (vmcnt 0; expcnt and lgkmcnt fields at their maximum), where
+    // the compiler sees it, so that no wait for this load is placed on the
+    // path every tile takes
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   };
-  auto stage = [&](int buf, const KV& x) {
-    *reinterpret_cast<uint4*>(&ks[buf][ld_key * kKsStride + ld_chunk * 8]) = x.k;
-    *reinterpret_cast<uint4*>(&vs[buf][vs_index(ld_key, ld_chunk * 8)]) = x.v;
+  const uint32_t lds_base = lds_addr(&kvs[0][0][8 * w * kHeadDim]);   // this wave's rows, stage 0
+  auto issue = [&](int kt, int stage) {
+    if (kt - tb >= kWave) load_table(kt);
+    const int blk = __builtin_amdgcn_readlane(tabv, kt - tb);
+    const bool ok = blk >= 0 && blk < a.num_blocks;
+    const int key = kt * kKTile + 8 * w + (lane >> 3);
+    const uint32_t past = key < n_keys ? 0u : 0x80000000u;
+    const int64_t boff = (int64_t)(ok ? blk : 0) * block_bytes;
+    const uint32_t nrec = ok ? block_bytes : 0u;
+    const uint32_t dst = lds_base + (uint32_t)stage * (2 * kKTile * kHeadDim * 2);
+    lds_dma16(rsrc_words(kpool + boff, nrec), ld_koff | past, dst);
+    lds_dma16(rsrc_words(vpool + boff, nrec), ld_voff | past, dst + kKTile * kHeadDim * 2);
   };
 
   // Q^T operand: 4 k-steps of 8 dims each.
@@ -197,14 +243,31 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
   float thr = -INFINITY;           // raw-score level above which m must be raised
   float l = 0.f;                   // this lane's half of the sum
 
-  stage(0, fetch(0));
-  __syncthreads();
+  // This lane's K-operand slots: row `col` of each 32-key half, dims
+  // 16 ks + 8 half .. + 7, i.e. chunk 2 ks + half at slot (2 ks + half) ^ (col & 7)
+  // = 2 (ks ^ kc) + (half ^ (col & 1)) with kc = (col >> 1) & 3.
+  const int k_base = col * kHeadDim + 8 * (half ^ (col & 1));
+  const int kc = (col >> 1) & 3;
+
+  // Pipeline: tile kt + 2 is requested while tile kt is computed.  Each wave
+  // waits for its own loads of tile kt (two per tile, counted in order), then
+  // the barrier makes every wave's part visible and frees the stage that tile
+  // kt + 2 overwrites (its previous tile, kt - 1, is done everywhere).
+  load_table(0);
+  issue(0, 0);
+  if (n_ktiles > 1) issue(1, 1);
+  int st = 0;                                      // stage of tile kt
   for (int kt = 0; kt < n_ktiles; ++kt) {
-    const int buf = kt & 1;
     const int kbase = kt * kKTile;
-    const bool more = kt + 1 < n_ktiles;
-    KV nxt;
-    if (more) nxt = fetch(kt + 1);
+    if (kt + 1 < n_ktiles)
+      __asm__ volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 2 < n_ktiles) issue(kt + 2, st == 0 ? 2 : st - 1);
+    const uint16_t* ks = kvs[st][0];
+    const uint16_t* vs = kvs[st][1];
+    st = st == kPfStages - 1 ? 0 : st + 1;
 
     if (sub_live && kbase < sub_key_end) {
       // S^T = K . Q^T for the tile's two 32-key halves (rows: keys, cols: queries)
@@ -213,8 +276,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
       for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
         for (int ks_ = 0; ks_ < 4; ++ks_) {
-          const uint4 ka =
-              *reinterpret_cast<const uint4*>(&ks[buf][(kh * 32 + col) * kKsStride + ks_ * 16 + half * 8]);
+          const uint4 ka = *reinterpret_cast<const uint4*>(ks + kh * 32 * kHeadDim + k_base + 16 * (ks_ ^ kc));
           s[kh] = mfma32(ka, qb[ks_], s[kh]);
         }
       }
@@ -278,7 +340,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
           uint2 r[2][2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const uint16_t* row = &vs[buf][(kh * 32 + kstep * 16 + 8 * u) * kVsStride];
+            const uint16_t* row = vs + (kh * 32 + kstep * 16 + 8 * u) * kVsStride;
             r[0][u] = lds_tr16(row + vt_off0);
             r[1][u] = lds_tr16(row + vt_off1);
           }
@@ -287,8 +349,6 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
         }
       }
     }
-    if (more) stage(buf ^ 1, nxt);
-    __syncthreads();
   }
   l += shfl_xor(l, 32);
   if (!q_ok) return;
