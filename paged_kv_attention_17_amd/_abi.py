@@ -85,6 +85,12 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with paged_kv_attention_17_amd.build")
+    # torch bundles its own libamdhip64 and finds it as "libamdhip64.so"; this
+    # library asks for the soname "libamdhip64.so.7".  Loaded first, it would
+    # pull in the system runtime and torch would then load a second one, whose
+    # streams and allocations this library's kernels cannot use.  Importing
+    # torch first makes its runtime the one both resolve to.
+    import torch  # noqa: F401
     lib = C.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -206,3 +206,24 @@ def test_read_probe_argument_errors(lib):
     assert lib.pkv_hbm_read_probe(FAKE, 64, None, None) == E.PKV_ERR_NULL
     assert lib.pkv_hbm_read_probe(FAKE + 4, 64, FAKE, None) == E.PKV_ERR_MISALIGNED
     assert lib.pkv_hbm_read_probe(FAKE, 60, FAKE, None) == E.PKV_ERR_MISALIGNED
+
+
+def test_load_shares_torch_hip_runtime():
+    """Loaded before anything imports torch, the library must still end up on
+    the HIP runtime torch brings (one libamdhip64 in the process): with two,
+    torch's streams and allocations are foreign to this library's kernels."""
+    import subprocess
+    import sys
+    code = (
+        "import sys, paged_kv_attention_17_amd as p\n"
+        "assert 'torch' not in sys.modules\n"
+        "p.load()\n"
+        "import torch\n"
+        "maps = open('/proc/self/maps').read().split('\\n')\n"
+        "libs = sorted({l.split()[-1] for l in maps if 'libamdhip64' in l})\n"
+        "print(libs)\n"
+        "assert len(libs) == 1, libs\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
