@@ -289,6 +289,89 @@ def long_context_leg(torch, np, pkv, W, iters: int = 10):
     return res
 
 
+def prefix_sharing_leg(torch, np, pkv, W, iters: int = 10):
+    """Decode attention where the 64 rows continue 4 shared 2,048-token
+    prompts with private tails U[64, 1024] (16 layers, each with its own
+    blocks; the rows of one prompt list the same prompt blocks), timed like
+    the main step's attention (16 layers back to back, host lengths given).
+    Beside it: the same rows with every block private (no sharing), and the
+    copy on write of every row's last block in all 16 layers
+    (pkv_blocks_copy, 1,024 block pairs)."""
+    L = 16
+    w = W.shared_prefix(n_layers=L, fill_pool=False)
+    B = len(w.context_lens)
+    ctx = w.context_lens.astype(np.int32)
+    ctxd = torch.from_numpy(ctx).cuda()
+    q = torch.from_numpy(w.q.view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty_like(q)
+    mx = int(ctx.max())
+    ws = torch.empty(pkv.pkv_decode_workspace_bytes(B, 32, 8, 64, mx, 0) // 4 + 64, dtype=torch.int32, device="cuda")
+    logical = int(ctx.sum()) * KV_BYTES_PER_TOKEN
+    tails = ctx - w.prompt_len
+    unique = (w.n_prompts * w.prompt_len + int(tails.sum())) * KV_BYTES_PER_TOKEN
+    res = {"workload": "decode attention, B=64 rows over 4 shared 2048-token prompts + private tails U[64,1024], "
+                       "16 layers, 32q/8kv heads, d=64, bf16 16-token blocks",
+           "mean_context": round(float(ctx.mean()), 1), "logical_bytes_per_layer": logical,
+           "unique_bytes_per_layer": unique}
+
+    def timed(kp, vp, bts):
+        run = lambda: [pkv.pkv_paged_attn_decode(out, q, kp, vp, bt, None, ctxd, mx, 0.125, 0, ws,  # noqa: E731
+                                                 row_lens_host=ctx) for bt in bts]
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            run()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / (iters * L)
+
+    extra = B * L                       # destination blocks of the copy-on-write leg
+    kp = torch.empty((w.num_blocks + extra, 16, 8, 64), dtype=torch.bfloat16, device="cuda").normal_()
+    vp = torch.empty_like(kp).normal_()
+    bts = [torch.from_numpy(np.ascontiguousarray(w.block_table[:, l, :])).cuda() for l in range(L)]
+    t = timed(kp, vp, bts)
+    res["shared"] = {"us_per_layer": round(t * 1e6, 2), "logical_GBps": round(logical / t / 1e9, 1),
+                     "unique_GBps": round(unique / t / 1e9, 1), "unique_frac": round(unique / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+    last = (ctx + 15) // 16 - 1
+    src = np.concatenate([w.block_table[np.arange(B), l, last] for l in range(L)]).astype(np.int32)
+    dst = np.arange(w.num_blocks, w.num_blocks + extra, dtype=np.int32)
+    pkv.pkv_blocks_copy(kp, vp, src, dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        pkv.pkv_blocks_copy(kp, vp, src, dst)
+    e1.record()
+    e1.synchronize()
+    tc = e0.elapsed_time(e1) / 1e3 / iters
+    moved = 2 * extra * 2 * 16 * 8 * 64 * 2     # read + write, K and V
+    res["copy_on_write"] = {"pairs": extra, "us": round(tc * 1e6, 2), "GBps": round(moved / tc / 1e9, 1)}
+    del kp, vp, bts
+
+    # the same rows with private blocks only
+    nbp = int(((ctx + 15) // 16).sum())
+    perm = np.random.Generator(np.random.PCG64(w.seed)).permutation(nbp * L).astype(np.int32)
+    kp = torch.empty((nbp * L, 16, 8, 64), dtype=torch.bfloat16, device="cuda").normal_()
+    vp = torch.empty_like(kp).normal_()
+    bts, k = [], 0
+    for _ in range(L):
+        bt = np.full(w.block_table.shape[::2], -1, np.int32)
+        for b in range(B):
+            n = int((ctx[b] + 15) // 16)
+            bt[b, :n] = perm[k:k + n]
+            k += n
+        bts.append(torch.from_numpy(bt).cuda())
+    t = timed(kp, vp, bts)
+    res["private"] = {"us_per_layer": round(t * 1e6, 2), "GBps": round(logical / t / 1e9, 1),
+                      "frac": round(logical / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del kp, vp, bts
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,6 +474,12 @@ def main():
         f"({lc['stream']['frac']:.1%}); per-partition {lc['partitions']['us_per_call']:.1f} us = "
         f"{lc['partitions']['GBps']:.0f} GB/s ({lc['partitions']['frac']:.1%})")
 
+    ps = prefix_sharing_leg(torch, np, pkv, W)
+    log(f"prefix sharing (B=64 over 4 shared 2048-token prompts): {ps['shared']['us_per_layer']:.1f} us/layer "
+        f"({ps['shared']['logical_GBps']:.0f} GB/s of rows' K/V, {ps['shared']['unique_GBps']:.0f} GB/s of distinct "
+        f"blocks) vs {ps['private']['us_per_layer']:.1f} us/layer with private blocks; copy on write of "
+        f"{ps['copy_on_write']['pairs']} blocks {ps['copy_on_write']['us']:.1f} us = {ps['copy_on_write']['GBps']:.0f} GB/s")
+
     copy_gbs = stream_copy_gbs(torch)
     read_gbs = stream_read_gbs(torch, pkv)
     log(f"plain copy kernel: {copy_gbs:.0f} GB/s (read + write); streaming read of 4 GiB: {read_gbs:.0f} GB/s")
@@ -435,6 +524,7 @@ def main():
         "unfused_layer_us": unf,
         "prefill": pre,
         "long_context": lc,
+        "prefix_sharing": ps,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -163,6 +163,63 @@ int pkv_blocks_release(int32_t* bt_host, int64_t bt_row_stride, int num_slots,
 int pkv_block_table_patch(int32_t* bt_dev, int64_t bt_elems, const int32_t* patch_offsets_host,
                           const int32_t* patch_values_host, int n_patch, void* stream);
 
+/* Prefix sharing (host).  Source: the category page "code-series", whose
+ * mini-sglang series has a chapter on a radix cache: requests that open with
+ * the same prompt reuse that prefix's cached K/V rather than computing it
+ * again.  The pages give no mechanism; the one here: a block may be listed by
+ * several table entries, refcount_host[b] (one int32 per pool block, kept by
+ * the caller, 0 for a free block) counts the entries that list b, and a block
+ * is written only through an entry that lists it alone.
+ *
+ * pkv_blocks_share: row dst_slot takes row src_slot's entries for tokens
+ * 0 .. n_tokens-1 (entries 0 .. ceil(n_tokens/16)-1), the same block ids, and
+ * each listed block's count grows by one.  Those entries of dst_slot must be
+ * -1 and the source's must hold counted blocks of the pool; otherwise nothing
+ * changes and PKV_ERR_INVALID_ARG / PKV_ERR_BAD_BLOCK is returned
+ * (PKV_ERR_CAPACITY if the row is too short).  Changes are appended to the
+ * patch arrays (room for ceil(n_tokens/16) entries). */
+int pkv_blocks_share(int32_t* bt_host, int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,
+                     int src_slot, int dst_slot, int n_tokens, int32_t* refcount_host, int num_blocks,
+                     int32_t* patch_offsets_host, int32_t* patch_values_host, int* n_patch);
+
+/* pkv_blocks_assign with shared blocks.  For every entry that a token
+ * (slot_ids_host[t], positions_host[t]) writes into, in token order:
+ *   - entry -1: a block is popped from the end of free_list_host, count 1;
+ *   - entry listing a block whose count (after the moves earlier in this
+ *     call) exceeds 1: copy on write -- a block is popped (count 1), the entry
+ *     points to it, the old block's count drops by one and the pair (old, new)
+ *     is appended to copy_src_host / copy_dst_host (room for num_tokens pairs;
+ *     *n_copy);
+ *   - otherwise the entry stays.
+ * Every changed entry goes to the patch arrays (room for num_tokens).  The
+ * caller copies the listed blocks (pkv_blocks_copy) before the append that
+ * writes them.  Popped blocks must have count 0.  All or nothing. Host only. */
+int pkv_blocks_assign_shared(int32_t* bt_host, int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,
+                             int32_t* free_list_host, int* n_free, int32_t* refcount_host, int num_blocks,
+                             const int32_t* slot_ids_host, const int32_t* positions_host, int num_tokens,
+                             int32_t* patch_offsets_host, int32_t* patch_values_host, int* n_patch,
+                             int32_t* copy_src_host, int32_t* copy_dst_host, int* n_copy);
+
+/* pkv_blocks_release with shared blocks: every assigned entry of row `slot`
+ * drops its block's count by one and becomes -1; a block whose count reaches 0
+ * is pushed onto the free list.  PKV_ERR_CAPACITY if the free list would
+ * exceed free_capacity, PKV_ERR_INVALID_ARG if a count would go negative; a
+ * failure changes nothing.  Patch arrays: room for max_blocks_per_seq. */
+int pkv_blocks_release_shared(int32_t* bt_host, int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,
+                              int slot, int32_t* free_list_host, int* n_free, int free_capacity,
+                              int32_t* refcount_host, int num_blocks, int32_t* patch_offsets_host,
+                              int32_t* patch_values_host, int* n_patch);
+
+/* Device half of copy on write: for i < n_copy, block dst_host[i] of both
+ * pools takes the 16 rows (all KV heads) of block src_host[i].  The id arrays
+ * are HOST arrays carried in the kernel arguments (reusable when the call
+ * returns).  Every copy reads the pools as they were before the call: ids must
+ * lie in [0, num_blocks) (else PKV_ERR_BAD_BLOCK), no block may be written
+ * twice or be both written and read (PKV_ERR_INVALID_ARG), checked on the
+ * host before anything is enqueued. */
+int pkv_blocks_copy(pkv_bf16* k_pool, pkv_bf16* v_pool, int num_blocks, int n_kv_heads, int head_dim,
+                    const int32_t* src_host, const int32_t* dst_host, int n_copy, void* stream);
+
 /* Validate tables on the host for rows slot_ids_host[0..batch) (NULL = rows
  * 0..batch-1) and lengths context_lens_host (indexed by row): every entry
  * covering tokens 0 .. len-1 must be in [0, num_blocks), len must fit the row,

@@ -99,3 +99,58 @@ def allocation_problems(bt_before, bt_after, free_before, free_after, slot_ids, 
     if free_before - set(handed) != free_after:
         problems.append("free list changed by more than the handed-out blocks")
     return problems
+
+
+# ------------------------------------------------------------------ sharing --
+# Prefix reuse.  The category page "code-series" lists, in its mini-sglang
+# series, a chapter on a radix cache: when many requests open with the same
+# prompt, the cached K/V of that prefix is reused instead of being computed
+# again.  The pages give no mechanism.  Reading adopted: a block may be listed
+# by several table entries; refcount[b] is the number of entries listing b; a
+# block is only written through an entry that lists it alone, so a row that is
+# about to append into a shared block first points its entry at a private
+# copy of it (copy on write).  Sharing must not change what any sequence
+# reads: gather() of every row still returns that sequence's own tokens.
+
+
+def copy_blocks(k_pool, v_pool, src, dst):
+    """Whole-block copies, K and V: block dst[i] takes the 16 rows of block
+    src[i].  Returns new (k_pool, v_pool); inputs untouched."""
+    k_out, v_out = k_pool.copy(), v_pool.copy()
+    for a, b in zip(src, dst):
+        k_out[int(b)] = k_pool[int(a)]
+        v_out[int(b)] = v_pool[int(a)]
+    return k_out, v_out
+
+
+def refcount_problems(tables, refcount, free_list):
+    """Check the sharing bookkeeping over every table view in ``tables``
+    (each [rows][max_blocks]); return a list of problems (empty = valid):
+
+      * refcount[b] equals the number of table entries that list b;
+      * a block on the free list is listed by no entry and has count 0;
+      * no block is on the free list twice;
+      * every listed block is a block of the pool.
+    """
+    problems = []
+    nb = len(refcount)
+    counts = np.zeros(nb, np.int64)
+    for t in tables:
+        ids = np.asarray(t).ravel()
+        ids = ids[ids != UNASSIGNED]
+        bad = ids[(ids < 0) | (ids >= nb)]
+        if len(bad):
+            problems.append(f"table lists block {int(bad[0])} outside the pool")
+            ids = ids[(ids >= 0) & (ids < nb)]
+        np.add.at(counts, ids, 1)
+    wrong = np.nonzero(counts != np.asarray(refcount))[0]
+    for b in wrong[:5]:
+        problems.append(f"block {int(b)}: refcount {int(refcount[b])}, listed {int(counts[b])} times")
+    free = [int(b) for b in free_list]
+    if len(set(free)) != len(free):
+        problems.append("free list holds a block twice")
+    for b in free:
+        if counts[b] or refcount[b]:
+            problems.append(f"block {b} is free but listed {int(counts[b])} times (refcount {int(refcount[b])})")
+            break
+    return problems

@@ -46,6 +46,10 @@ SIGNATURES = {
     "pkv_blocks_assign": (_i, [_p, _i64, _i, _i, _p, _ip, _p, _p, _i, _p, _p, _ip]),
     "pkv_blocks_release": (_i, [_p, _i64, _i, _i, _i, _p, _ip, _i, _p, _p, _ip]),
     "pkv_block_table_patch": (_i, [_p, _i64, _p, _p, _i, _p]),
+    "pkv_blocks_share": (_i, [_p, _i64, _i, _i, _i, _i, _i, _p, _i, _p, _p, _ip]),
+    "pkv_blocks_assign_shared": (_i, [_p, _i64, _i, _i, _p, _ip, _p, _i, _p, _p, _i, _p, _p, _ip, _p, _p, _ip]),
+    "pkv_blocks_release_shared": (_i, [_p, _i64, _i, _i, _i, _p, _ip, _i, _p, _i, _p, _p, _ip]),
+    "pkv_blocks_copy": (_i, [_p, _p, _i, _i, _i, _p, _p, _i, _p]),
     "pkv_check_block_table": (_i, [_p, _i64, _i, _i, _p, _p, _i, _i, _ip, _ip]),
     "pkv_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "pkv_decode_partition_size": (_i, [_i, _i, _i]),
@@ -150,6 +154,8 @@ def _stream(stream):
 def _np_i32(a, name, writable=False):
     if not isinstance(a, np.ndarray) or a.dtype != np.int32:
         raise TypeError(f"{name} must be a numpy int32 array")
+    if name in ("free_list", "refcount") and (a.ndim != 1 or not a.flags.c_contiguous):
+        raise ValueError(f"{name} must be a contiguous 1-D array")
     if writable and not a.flags.writeable:
         raise ValueError(f"{name} must be writable")
     return a
@@ -275,6 +281,80 @@ def pkv_blocks_release(bt_host, slot, free_list, n_free):
         ptr, stride, rows, mb, slot, free_list.ctypes.data, C.byref(nf), len(free_list), off.ctypes.data,
         val.ctypes.data, C.byref(npch)))
     return nf.value, off[:npch.value].copy(), val[:npch.value].copy()
+
+
+def pkv_blocks_share(bt_host, src_slot, dst_slot, n_tokens, refcount):
+    """Row dst_slot lists row src_slot's blocks for tokens 0..n_tokens-1
+    (counts in `refcount` grow).  Returns (patch_offsets, patch_values)."""
+    ptr, stride, rows, mb = _np_table(bt_host)
+    _np_i32(refcount, "refcount", writable=True)
+    nb = -(-int(n_tokens) // 16)
+    off = np.zeros(max(nb, 1), np.int32)
+    val = np.zeros(max(nb, 1), np.int32)
+    npch = C.c_int(0)
+    _check("pkv_blocks_share", load().pkv_blocks_share(
+        ptr, stride, rows, mb, src_slot, dst_slot, n_tokens, refcount.ctypes.data, len(refcount),
+        off.ctypes.data, val.ctypes.data, C.byref(npch)))
+    return off[:npch.value].copy(), val[:npch.value].copy()
+
+
+def pkv_blocks_assign_shared(bt_host, free_list, n_free, refcount, slot_ids, positions):
+    """Host allocation with shared blocks (copy on write).  Returns
+    (n_free, patch_offsets, patch_values, copy_src, copy_dst)."""
+    ptr, stride, rows, mb = _np_table(bt_host)
+    _np_i32(free_list, "free_list", writable=True)
+    _np_i32(refcount, "refcount", writable=True)
+    slot_ids = np.ascontiguousarray(slot_ids, dtype=np.int32)
+    positions = np.ascontiguousarray(positions, dtype=np.int32)
+    n = len(slot_ids)
+    if len(positions) != n:
+        raise ValueError("slot_ids / positions lengths differ")
+    if not 0 <= n_free <= len(free_list):
+        raise ValueError("n_free outside the free list")
+    off, val, cs, cd = (np.zeros(max(n, 1), np.int32) for _ in range(4))
+    nf, npch, ncp = C.c_int(n_free), C.c_int(0), C.c_int(0)
+    _check("pkv_blocks_assign_shared", load().pkv_blocks_assign_shared(
+        ptr, stride, rows, mb, free_list.ctypes.data, C.byref(nf), refcount.ctypes.data, len(refcount),
+        slot_ids.ctypes.data, positions.ctypes.data, n, off.ctypes.data, val.ctypes.data, C.byref(npch),
+        cs.ctypes.data, cd.ctypes.data, C.byref(ncp)))
+    k, c = npch.value, ncp.value
+    return nf.value, off[:k].copy(), val[:k].copy(), cs[:c].copy(), cd[:c].copy()
+
+
+def pkv_blocks_release_shared(bt_host, slot, free_list, n_free, refcount):
+    """Drop row `slot`'s references; blocks whose count reaches 0 are freed.
+    Returns (n_free, patch_offsets, patch_values)."""
+    ptr, stride, rows, mb = _np_table(bt_host)
+    _np_i32(free_list, "free_list", writable=True)
+    _np_i32(refcount, "refcount", writable=True)
+    if not 0 <= n_free <= len(free_list):
+        raise ValueError("n_free outside the free list")
+    off = np.zeros(max(mb, 1), np.int32)
+    val = np.zeros(max(mb, 1), np.int32)
+    nf, npch = C.c_int(n_free), C.c_int(0)
+    _check("pkv_blocks_release_shared", load().pkv_blocks_release_shared(
+        ptr, stride, rows, mb, slot, free_list.ctypes.data, C.byref(nf), len(free_list), refcount.ctypes.data,
+        len(refcount), off.ctypes.data, val.ctypes.data, C.byref(npch)))
+    return nf.value, off[:npch.value].copy(), val[:npch.value].copy()
+
+
+def pkv_blocks_copy(k_pool, v_pool, copy_src, copy_dst, stream=None):
+    """k_pool[dst[i]] = k_pool[src[i]] and the same for v_pool, whole blocks
+    (pools [num_blocks][16][n_kv][64], bf16); id lists are host arrays."""
+    import torch
+    for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _contig(t, nm)
+        _dev_ptr(t, nm, _bf16_types())
+    if k_pool.shape != v_pool.shape or k_pool.dim() != 4 or k_pool.shape[1] != 16:
+        raise ValueError("pools must both be [num_blocks][16][n_kv][head_dim]")
+    src = np.ascontiguousarray(copy_src, dtype=np.int32)
+    dst = np.ascontiguousarray(copy_dst, dtype=np.int32)
+    if src.shape != dst.shape or src.ndim != 1:
+        raise ValueError("copy_src / copy_dst must be 1-D of one length")
+    st = _stream(stream)
+    _check("pkv_blocks_copy", load().pkv_blocks_copy(
+        k_pool.data_ptr(), v_pool.data_ptr(), k_pool.shape[0], k_pool.shape[2], k_pool.shape[3],
+        src.ctypes.data, dst.ctypes.data, len(src), st))
 
 
 def pkv_block_table_patch(bt_dev, patch_offsets, patch_values, stream=None):

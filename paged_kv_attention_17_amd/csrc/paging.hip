@@ -13,6 +13,8 @@
 // it is used as an address.
 #include "common.h"
 
+#include <vector>
+
 namespace pkv {
 
 constexpr int kChunks = kHeadDim * 2 / 16;   // 16-byte chunks per head row
@@ -135,6 +137,75 @@ extern "C" int pkv_paged_gather(pkv_bf16* k_dense, pkv_bf16* v_dense, const pkv_
   void* args[] = {&kd, &vd, &kp, &vp, &nb, &row, &cl, &nk};
   return launch_status(hipLaunchKernel((const void*)gather_kernel, dim3((unsigned)grid), dim3(256), args, 0,
                                        (hipStream_t)stream));
+}
+
+namespace pkv {
+
+// Whole-block copies for copy on write of a shared block: workgroup 2 i + w
+// copies pool w (0 = K, 1 = V) of pair i, the block's 16 rows of every head
+// (16 KB at 8 KV heads) as 16-byte words, consecutive lanes on consecutive
+// words.  The pairs travel in the kernel arguments.
+constexpr int kCopyPerLaunch = 480;
+
+struct CopyArgs {
+  int32_t src[kCopyPerLaunch];
+  int32_t dst[kCopyPerLaunch];
+};
+static_assert(sizeof(CopyArgs) + 64 <= 4096, "kernel argument block");
+
+__global__ __launch_bounds__(256) void block_copy_kernel(uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+                                                         int num_blocks, int64_t words_per_block, CopyArgs c,
+                                                         int n) {
+  const int i = blockIdx.x >> 1;
+  if (i >= n) return;
+  const int32_t a = c.src[i], b = c.dst[i];
+  if (a < 0 || a >= num_blocks || b < 0 || b >= num_blocks) return;
+  uint4* pool = (blockIdx.x & 1) ? v_pool : k_pool;
+  const uint4* from = pool + (int64_t)a * words_per_block;
+  uint4* to = pool + (int64_t)b * words_per_block;
+  for (int64_t w = threadIdx.x; w < words_per_block; w += blockDim.x) to[w] = from[w];
+}
+
+}  // namespace pkv
+
+extern "C" int pkv_blocks_copy(pkv_bf16* k_pool, pkv_bf16* v_pool, int num_blocks, int n_kv_heads, int head_dim,
+                               const int32_t* src_host, const int32_t* dst_host, int n_copy, void* stream) {
+  if (n_copy < 0 || num_blocks < 0 || n_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return PKV_ERR_UNSUPPORTED;
+  if (n_copy == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src_host || !dst_host) return PKV_ERR_NULL;
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_MISALIGNED;
+  // Every copy reads the pool as it was before the call: ids in range, no
+  // block written twice, and no block both written and read.
+  std::vector<uint8_t> role((size_t)num_blocks, 0);   // bit 0: read, bit 1: written
+  for (int i = 0; i < n_copy; ++i) {
+    const int32_t a = src_host[i], b = dst_host[i];
+    if (a < 0 || a >= num_blocks || b < 0 || b >= num_blocks) return PKV_ERR_BAD_BLOCK;
+    if (role[b] & 2) return PKV_ERR_INVALID_ARG;
+    role[a] |= 1;
+    role[b] |= 2;
+  }
+  for (int i = 0; i < n_copy; ++i)
+    if (role[src_host[i]] & 2) return PKV_ERR_INVALID_ARG;
+  const int64_t words = (int64_t)kBlock * n_kv_heads * kChunks;
+  for (int base = 0; base < n_copy; base += kCopyPerLaunch) {
+    CopyArgs c;
+    const int n = n_copy - base < kCopyPerLaunch ? n_copy - base : kCopyPerLaunch;
+    for (int i = 0; i < n; ++i) {
+      c.src[i] = src_host[base + i];
+      c.dst[i] = dst_host[base + i];
+    }
+    uint4* kp = reinterpret_cast<uint4*>(k_pool);
+    uint4* vp = reinterpret_cast<uint4*>(v_pool);
+    int nbk = num_blocks;
+    int64_t w = words;
+    int nn = n;
+    void* args[] = {&kp, &vp, &nbk, &w, &c, &nn};
+    const int st = launch_status(hipLaunchKernel((const void*)block_copy_kernel, dim3(2 * n), dim3(256), args, 0,
+                                                 (hipStream_t)stream));
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
 }
 
 extern "C" int pkv_block_table_patch(int32_t* bt_dev, int64_t bt_elems, const int32_t* patch_offsets_host,

@@ -324,6 +324,70 @@ def config5(extra_tokens: int = 32) -> PrefillWorkload:
     return make_prefill(1705, config5_prompt_lens(), extra_tokens=extra_tokens)
 
 
+@dataclasses.dataclass
+class SharedPrefixWorkload:
+    """Decode inputs where rows open with shared prompts: row b continues
+    prompt b % n_prompts (prompt_len tokens, a whole number of blocks, listed
+    by every such row) with its own tail.
+
+      k_pool, v_pool : [num_blocks, 16, n_kv, d] or None (fill on the device)
+      block_table    : int32 [batch, n_layers, max_blocks], -1 = unassigned
+      context_lens   : int32 [batch]  (prompt + tail)
+      q              : [batch, n_q, d]
+    """
+    k_pool: np.ndarray | None
+    v_pool: np.ndarray | None
+    block_table: np.ndarray
+    context_lens: np.ndarray
+    q: np.ndarray
+    num_blocks: int
+    prompt_len: int
+    n_prompts: int
+    seed: int
+
+    @property
+    def listed_blocks(self) -> int:
+        return int(np.count_nonzero(self.block_table >= 0))
+
+    @property
+    def unique_blocks(self) -> int:
+        return int(len(np.unique(self.block_table[self.block_table >= 0])))
+
+
+def shared_prefix(seed: int = 1706, batch: int = 64, n_prompts: int = 4, prompt_len: int = 2048,
+                  tail_lo: int = 64, tail_hi: int = 1024, n_layers: int = 1, fill_pool: bool = True,
+                  n_q: int = N_Q_HEADS, n_kv: int = N_KV_HEADS, d: int = HEAD_DIM) -> SharedPrefixWorkload:
+    """B rows over a few common prompts (many requests with one system
+    prompt), tails uniform in [tail_lo, tail_hi]; each layer's blocks come
+    off one shuffled free list, prompts first."""
+    if prompt_len % BLOCK_SIZE:
+        raise ValueError("prompt_len must be a whole number of blocks")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    tails = rng.integers(tail_lo, tail_hi, size=batch, endpoint=True).astype(np.int32)
+    ctx = (prompt_len + tails).astype(np.int32)
+    pb = prompt_len // BLOCK_SIZE
+    max_blocks = blocks_for(int(ctx.max()))
+    per_layer = n_prompts * pb + sum(blocks_for(int(t)) for t in tails)
+    num_blocks = per_layer * n_layers
+    free = rng.permutation(num_blocks).astype(np.int32)
+    bt = np.full((batch, n_layers, max_blocks), UNASSIGNED, np.int32)
+    k = 0
+    for layer in range(n_layers):
+        prompts = free[k:k + n_prompts * pb].reshape(n_prompts, pb)
+        k += n_prompts * pb
+        for b in range(batch):
+            bt[b, layer, :pb] = prompts[b % n_prompts]
+            nt = blocks_for(int(tails[b]))
+            bt[b, layer, pb:pb + nt] = free[k:k + nt]
+            k += nt
+    q = randn_bf16(rng, (batch, n_q, d))
+    kp = vp = None
+    if fill_pool:
+        kp = randn_bf16(rng, (num_blocks, BLOCK_SIZE, n_kv, d))
+        vp = randn_bf16(rng, (num_blocks, BLOCK_SIZE, n_kv, d))
+    return SharedPrefixWorkload(kp, vp, bt, ctx, q, num_blocks, prompt_len, n_prompts, seed)
+
+
 def fill_pool_device(pool, seed: int, kind: str = "normal", lo: float = -1.0, hi: float = 1.0,
                      chunk_blocks: int = 8192):
     """Fill a device bf16 tensor [NB, 16, H, D] in place from a seeded torch
