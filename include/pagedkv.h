@@ -159,7 +159,9 @@ int pkv_blocks_release(int32_t* bt_host, int64_t bt_row_stride, int num_slots,
 /* Apply host-side table changes to the device copy: bt_dev[offsets[i]] = values[i]
  * for i < n_patch.  The two arrays are HOST arrays; their contents travel in
  * the kernel arguments, so they may be reused as soon as the call returns.
- * Offsets outside [0, bt_elems) are skipped. */
+ * The pairs take effect in list order: when an offset appears more than once
+ * the last pair wins (a release followed by a reuse of the same entry may be
+ * sent as one list).  Offsets outside [0, bt_elems) are skipped. */
 int pkv_block_table_patch(int32_t* bt_dev, int64_t bt_elems, const int32_t* patch_offsets_host,
                           const int32_t* patch_values_host, int n_patch, void* stream);
 

@@ -13,6 +13,8 @@
 // it is used as an address.
 #include "common.h"
 
+#include <algorithm>
+#include <unordered_set>
 #include <vector>
 
 namespace pkv {
@@ -214,12 +216,26 @@ extern "C" int pkv_block_table_patch(int32_t* bt_dev, int64_t bt_elems, const in
   if (n_patch == 0) return PKV_OK;
   if (!bt_dev || !patch_offsets_host || !patch_values_host) return PKV_ERR_NULL;
   if (!aligned4(bt_dev)) return PKV_ERR_MISALIGNED;
-  for (int base = 0; base < n_patch; base += kPatchPerLaunch) {
+  // The list is applied in order: when an entry appears more than once (a row
+  // released and reused in one step) only its last pair is kept, so the pairs
+  // that reach the device name distinct entries and their order within a
+  // launch does not matter.
+  std::vector<int> keep;
+  keep.reserve(n_patch);
+  {
+    std::unordered_set<int32_t> seen;
+    seen.reserve((size_t)n_patch * 2);
+    for (int i = n_patch - 1; i >= 0; --i)
+      if (seen.insert(patch_offsets_host[i]).second) keep.push_back(i);
+    std::reverse(keep.begin(), keep.end());
+  }
+  const int n_keep = (int)keep.size();
+  for (int base = 0; base < n_keep; base += kPatchPerLaunch) {
     PatchArgs pa;
-    const int n = n_patch - base < kPatchPerLaunch ? n_patch - base : kPatchPerLaunch;
+    const int n = n_keep - base < kPatchPerLaunch ? n_keep - base : kPatchPerLaunch;
     for (int i = 0; i < n; ++i) {
-      pa.off[i] = patch_offsets_host[base + i];
-      pa.val[i] = patch_values_host[base + i];
+      pa.off[i] = patch_offsets_host[keep[base + i]];
+      pa.val[i] = patch_values_host[keep[base + i]];
     }
     int32_t* bt = bt_dev;
     int64_t el = bt_elems;

@@ -134,3 +134,11 @@ def test_block_table_patch(gpu):
     pkv.pkv_block_table_patch(e, np.arange(600, dtype=np.int32), np.arange(600, dtype=np.int32) + 1)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(e.cpu().numpy(), np.arange(600) + 1)
+    # repeated offsets take effect in list order (the last pair wins), also
+    # across the launches a long list is split into
+    f = dev_i32(np.full(8, -1, np.int32))
+    off = np.array([3, 5, 3, -1, 3, 5, 7] + [6] * 300 + [7], np.int32)
+    val = np.array([10, 11, -1, 9, 12, 13, 14] + list(range(300)) + [15], np.int32)
+    pkv.pkv_block_table_patch(f, off, val)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(f.cpu().numpy(), [-1, -1, -1, 12, -1, 13, 299, 15])
