@@ -372,6 +372,75 @@ def prefix_sharing_leg(torch, np, pkv, W, iters: int = 10):
     return res
 
 
+def serving_leg(torch, np, pkv, W, n_req: int = 128, n_slots: int = 64, budget: int = 2048, new_tokens: int = 32):
+    """Continuous batching end to end: n_req requests with prompts U[256, 2048]
+    (the chunked-prefill workload's distribution) and new_tokens tokens each,
+    all queued at the start, served by the native scheduler (pkv_sched_next)
+    and run on the device (pkv_sched_run) over 16 layers, n_slots slots and a
+    per-iteration token budget.  q/k/v are seeded device tensors reused every
+    iteration (inputs resident in HBM).  Timed with HIP events from the first
+    iteration to the last."""
+    L, NQ, NKV, D = 16, 32, 8, 64
+    rng = np.random.default_rng(1707)
+    prompts = rng.integers(256, 2049, size=n_req)
+    max_blocks = -(-int(prompts.max() + new_tokens) // 16)
+    num_blocks = n_slots * L * max_blocks
+    dev = torch.device("cuda")
+    kp = torch.zeros((num_blocks, 16, NKV, D), dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1707)
+    mk = lambda h: [torch.randn((budget, h, D), generator=g, device=dev).to(torch.bfloat16)  # noqa: E731
+                    for _ in range(L)]
+    q, k, v = mk(NQ), mk(NKV), mk(NKV)
+    out = [torch.empty_like(t) for t in q]
+    cos_sin = torch.empty((4096, D // 2, 2), dtype=torch.float32, device=dev)
+    pkv.pkv_rope_table_init(cos_sin)
+    ws = pkv.decode_workspace(n_slots, NQ, NKV, max_blocks * 16)
+    stream = torch.cuda.current_stream()
+
+    def job(lens, news):
+        s = pkv.Scheduler(n_slots, L, max_blocks, num_blocks, budget)
+        for i, (p, n) in enumerate(zip(lens, news)):
+            s.submit(i, int(p), int(n))
+        bt = torch.full((n_slots, L, max_blocks), -1, dtype=torch.int32, device=dev)
+        meta = torch.zeros(s.info()["meta_elems"], dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        iters, plan, host, dec_rows, pre_rows = 0, 0.0, 0.0, 0, 0
+        while True:
+            t0 = time.perf_counter()
+            it = s.next()
+            t1 = time.perf_counter()
+            if it["n_tokens"] == 0 and len(it["patch_off"]) == 0:
+                break
+            s.run(q, k, v, out, kp, vp, bt, meta, cos_sin, 0.125, ws, stream=stream)
+            plan += t1 - t0
+            host += time.perf_counter() - t0
+            iters += 1
+            dec_rows += it["n_decode"]
+            pre_rows += it["n_tokens"] - it["n_decode"]
+        e1.record(stream)
+        torch.cuda.synchronize()
+        s.close()
+        return e0.elapsed_time(e1) / 1e3, iters, plan, host, dec_rows, pre_rows
+
+    job([300, 40, 1000], [3, 3, 3])                      # warm-up (kernels loaded, caches touched)
+    t, iters, plan, host, dec_rows, pre_rows = job(prompts, [new_tokens] * n_req)
+    del kp, vp
+    return {"workload": f"continuous batching, {n_req} requests, prompts U[256,2048] (sum {int(prompts.sum())} "
+                        f"tokens), {new_tokens} new tokens each, {n_slots} slots, {budget}-token budget, 16 layers, "
+                        "32q/8kv heads, d=64, bf16 16-token blocks",
+            "seconds": round(t, 4), "iterations": iters,
+            "prefill_tokens": pre_rows, "decode_rows": dec_rows,
+            "tokens_per_s": round((pre_rows + dec_rows) / t, 1),
+            "output_tokens_per_s": round(n_req * new_tokens / t, 1),
+            "gpu_us_per_iteration": round(t / max(iters, 1) * 1e6, 1),
+            "plan_us_per_iteration": round(plan / max(iters, 1) * 1e6, 1),
+            "host_us_per_iteration": round(host / max(iters, 1) * 1e6, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,6 +549,12 @@ def main():
         f"blocks) vs {ps['private']['us_per_layer']:.1f} us/layer with private blocks; copy on write of "
         f"{ps['copy_on_write']['pairs']} blocks {ps['copy_on_write']['us']:.1f} us = {ps['copy_on_write']['GBps']:.0f} GB/s")
 
+    sv = serving_leg(torch, np, pkv, W)
+    log(f"serving: {sv['iterations']} iterations in {sv['seconds'] * 1e3:.1f} ms, {sv['tokens_per_s']:.0f} tokens/s "
+        f"({sv['prefill_tokens']} prompt tokens, {sv['decode_rows']} decode rows), "
+        f"{sv['output_tokens_per_s']:.0f} output tokens/s; per iteration: plan {sv['plan_us_per_iteration']:.0f} us, "
+        f"plan + enqueue {sv['host_us_per_iteration']:.0f} us (includes waits for a full launch queue)")
+
     copy_gbs = stream_copy_gbs(torch)
     read_gbs = stream_read_gbs(torch, pkv)
     log(f"plain copy kernel: {copy_gbs:.0f} GB/s (read + write); streaming read of 4 GiB: {read_gbs:.0f} GB/s")
@@ -525,6 +600,7 @@ def main():
         "prefill": pre,
         "long_context": lc,
         "prefix_sharing": ps,
+        "serving": sv,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

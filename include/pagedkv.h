@@ -368,6 +368,111 @@ int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const* k, const 
                     const float* cos_sin, int max_pos, float scale, int max_context_len,
                     int partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * Continuous batching (host scheduler + device iteration).  Source: "The path
+ * of one inference" (a fixed set of sequence slots; prompts wait in a queue;
+ * a free slot takes the next prompt, which is prefilled; a decode step gives
+ * every active slot one token; a finished slot is freed; the loop ends when no
+ * slot is active and the queue is empty) and the category page's mini-sglang
+ * chapter-3 title (a per-step token budget; long prompts prefilled in chunks).
+ *
+ * One iteration (pkv_sched_next), in this order:
+ *   1. slots whose request produced its last token in the previous iteration
+ *      are released (blocks back to the free list, table entries to -1);
+ *   2. admission, first come first served: the head of the queue takes the
+ *      lowest free slot if the blocks it can ever need, n_layers x
+ *      ceil((prompt_len + max_new_tokens - 1) / 16), are not yet reserved by
+ *      admitted requests; otherwise the queue waits (no overtaking, no
+ *      preemption: an admitted request always finds its blocks);
+ *   3. decode rows: every admitted request whose prompt is cached and that
+ *      still owes tokens caches one token (row order = admission order);
+ *   4. prefill chunks: the rest of the budget goes to requests whose prompt is
+ *      not fully cached, admission order, min(uncached tokens, budget left)
+ *      each;
+ *   5. a block leaves the free list when a token opens a 16-token chunk (the
+ *      lowest free block id first on a fresh scheduler).
+ * A request yields its first token in the iteration that caches its prompt's
+ * last chunk and one more per decode row; it is finished after max_new_tokens
+ * tokens (the last one is never cached, so at most prompt_len +
+ * max_new_tokens - 1 tokens are cached).
+ *
+ * The iteration's token rows: rows 0 .. n_decode-1 are the decode rows, rows
+ * n_decode .. n_tokens-1 the prefill tokens, chunk by chunk.  All arrays point
+ * into the scheduler and stay valid until its next pkv_sched_next/destroy.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_sched pkv_sched;
+
+typedef struct {
+  int n_tokens;                 /* n_decode + n_prefill_tokens; 0 and no patches: nothing left to do */
+  int n_decode;
+  const int32_t* decode_slots;  /* [n_decode] slot of each decode row */
+  const int32_t* decode_lens;   /* [n_decode] context length with the row's token (its position + 1) */
+  const int64_t* decode_ids;    /* [n_decode] request ids */
+  int n_chunks;
+  const int32_t* chunk_slots;   /* [n_chunks] */
+  const int32_t* chunk_start;   /* [n_chunks] position of the chunk's first token */
+  const int32_t* cu_chunk;      /* [n_chunks + 1] offsets of the chunks among the prefill tokens */
+  const int64_t* chunk_ids;     /* [n_chunks] request ids */
+  int n_prefill_tokens;
+  const int32_t* token_slots;   /* [n_prefill_tokens] */
+  const int32_t* token_pos;     /* [n_prefill_tokens] */
+  int n_patch;                  /* table changes of this iteration, in order (flat index, block or -1) */
+  const int32_t* patch_off;
+  const int32_t* patch_val;
+  int n_done;                   /* requests whose last token this iteration produces */
+  const int64_t* done_ids;
+  int n_admitted;               /* requests admitted in this iteration and their slots */
+  const int64_t* admitted_ids;
+  const int32_t* admitted_slots;
+} pkv_sched_iter;
+
+typedef struct {
+  int num_slots, n_layers, max_blocks_per_seq, num_blocks, token_budget;
+  int n_queued, n_active, n_free, n_reserved;
+  const int32_t* table;         /* host table [num_slots][n_layers][max_blocks_per_seq] */
+  const int32_t* free_list;     /* [n_free] free blocks (popped from the end) */
+  int64_t meta_elems;           /* pkv_sched_meta_elems(num_slots, token_budget) */
+} pkv_sched_state;
+
+/* A scheduler with an empty table and all num_blocks blocks free.
+ * token_budget >= num_slots (every decode row always fits).
+ * PKV_ERR_INVALID_ARG for non-positive sizes or a smaller budget. */
+int pkv_sched_create(pkv_sched** sched, int num_slots, int n_layers, int max_blocks_per_seq, int num_blocks,
+                     int token_budget);
+int pkv_sched_destroy(pkv_sched* sched);
+
+/* Queue a request (ids are the caller's; not checked for uniqueness).
+ * prompt_len >= 1, max_new_tokens >= 1.  PKV_ERR_CAPACITY if it could never
+ * be admitted (its tokens exceed a table row or its blocks the pool). */
+int pkv_sched_submit(pkv_sched* sched, int64_t request_id, int prompt_len, int max_new_tokens);
+
+/* Plan the next iteration (host only; no device is touched). */
+int pkv_sched_next(pkv_sched* sched, pkv_sched_iter* iter);
+
+/* Sizes, counters and the host table / free list. */
+int pkv_sched_info(const pkv_sched* sched, pkv_sched_state* state);
+
+/* int32 elements of the device metadata array pkv_sched_run needs. */
+int64_t pkv_sched_meta_elems(int num_slots, int token_budget);
+
+/* Run an iteration on the device: apply its table patches to bt_dev (device
+ * copy of the scheduler's table, all -1 at creation), send the row metadata
+ * to meta_dev (device int32 [pkv_sched_meta_elems]; any initial contents) in
+ * kernel arguments, then per layer l:
+ *   decode rows:    pkv_paged_decode_fused on rows 0 .. n_decode-1 (q, k not modified);
+ *   prefill tokens: pkv_rope_decode (in place on those rows of q[l] and k[l]),
+ *                   pkv_paged_kv_append, pkv_paged_attn_prefill.
+ * q, k, v, out: HOST arrays of n_layers DEVICE pointers, [n_tokens][n_q][64],
+ * [n_tokens][n_kv][64], [n_tokens][n_kv][64], [n_tokens][n_q][64] (room for
+ * token_budget rows).  Pools, RoPE table and decode workspace as in the calls
+ * above (workspace for batch = num_slots).  All launches go to `stream`.
+ * Iterations must be run in the order they were planned. */
+int pkv_sched_run(const pkv_sched* sched, const pkv_sched_iter* iter, pkv_bf16* const* q, pkv_bf16* const* k,
+                  const pkv_bf16* const* v, pkv_bf16* const* out, pkv_bf16* k_pool, pkv_bf16* v_pool,
+                  int32_t* bt_dev, int32_t* meta_dev, int n_q_heads, int n_kv_heads, int head_dim,
+                  const float* cos_sin, int max_pos, float scale, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

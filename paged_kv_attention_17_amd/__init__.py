@@ -3,7 +3,8 @@
 The compute lives in libpagedkv.so (HIP kernels behind the C ABI of
 include/pagedkv.h); this package is its ctypes binding (``_abi``, re-exported
 here under the C names), the in-place build (``build``), a decode-step
-driver over the C ABI (``engine``) and seeded synthetic workloads
+driver over the C ABI (``engine``), the continuous-batching
+scheduler handle (``Scheduler``) and seeded synthetic workloads
 (``workloads``).  Importing the package does not load the library; the first
 call does, and raises if it has not been built.
 """
@@ -13,5 +14,5 @@ from ._abi import (  # noqa: F401
     pkv_paged_gather, pkv_hbm_read_probe, pkv_blocks_assign, pkv_blocks_release, pkv_block_table_patch,
     pkv_blocks_share, pkv_blocks_assign_shared, pkv_blocks_release_shared, pkv_blocks_copy, pkv_check_block_table,
     pkv_decode_workspace_bytes, pkv_decode_partition_size, pkv_paged_attn_decode, pkv_paged_attn_prefill,
-    pkv_decode_step, pkv_decode_workspace_init, pkv_paged_decode_fused, decode_workspace,
+    pkv_decode_step, pkv_decode_workspace_init, pkv_paged_decode_fused, decode_workspace, Scheduler,
 )

@@ -62,7 +62,34 @@ SIGNATURES = {
                                     _i, _f, _i, _p, _sz, _p]),
     "pkv_decode_step": (_i, [_i, _p, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _p, _ip, _p, _p, _p, _i, _i, _i, _i,
                              _p, _i, _f, _i, _i, _p, _sz, _p]),
+    "pkv_sched_create": (_i, [C.POINTER(_p), _i, _i, _i, _i, _i]),
+    "pkv_sched_destroy": (_i, [_p]),
+    "pkv_sched_submit": (_i, [_p, _i64, _i, _i]),
+    "pkv_sched_next": (_i, [_p, _p]),
+    "pkv_sched_info": (_i, [_p, _p]),
+    "pkv_sched_meta_elems": (_i64, [_i, _i]),
+    "pkv_sched_run": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _p, _i, _f, _p, _sz, _p]),
 }
+
+_I32P = C.POINTER(C.c_int32)
+_I64P = C.POINTER(C.c_int64)
+
+
+class SchedIter(C.Structure):
+    """pkv_sched_iter (include/pagedkv.h)."""
+    _fields_ = [("n_tokens", _i), ("n_decode", _i), ("decode_slots", _I32P), ("decode_lens", _I32P),
+                ("decode_ids", _I64P), ("n_chunks", _i), ("chunk_slots", _I32P), ("chunk_start", _I32P),
+                ("cu_chunk", _I32P), ("chunk_ids", _I64P), ("n_prefill_tokens", _i), ("token_slots", _I32P),
+                ("token_pos", _I32P), ("n_patch", _i), ("patch_off", _I32P), ("patch_val", _I32P),
+                ("n_done", _i), ("done_ids", _I64P), ("n_admitted", _i), ("admitted_ids", _I64P),
+                ("admitted_slots", _I32P)]
+
+
+class SchedState(C.Structure):
+    """pkv_sched_state (include/pagedkv.h)."""
+    _fields_ = [("num_slots", _i), ("n_layers", _i), ("max_blocks_per_seq", _i), ("num_blocks", _i),
+                ("token_budget", _i), ("n_queued", _i), ("n_active", _i), ("n_free", _i), ("n_reserved", _i),
+                ("table", _I32P), ("free_list", _I32P), ("meta_elems", _i64)]
 
 
 class PagedKVError(RuntimeError):
@@ -570,3 +597,106 @@ def pkv_decode_step(q, k, v, out, k_pool, v_pool, bt_host, bt_dev, free_list, n_
         q[0].shape[2], _dev_ptr(cos_sin, "cos_sin", (torch.float32,)), cos_sin.shape[0], float(scale),
         max_context_len, partition_size, ws_ptr, ws_bytes, _stream(stream)))
     return nf.value
+
+
+# ------------------------------------------------------ continuous batching --
+
+def _arr(ptr, n, dtype):
+    """Copy n elements from a C array into a numpy array."""
+    a = np.empty(n, dtype)
+    if n:
+        C.memmove(a.ctypes.data, ptr, a.nbytes)
+    return a
+
+
+class Scheduler:
+    """Handle of a pkv_sched (continuous batching; see pkv_sched_* in
+    pagedkv.h).  ``next()`` returns the iteration as a dict of numpy copies
+    and keeps the C struct for ``run``."""
+
+    def __init__(self, num_slots, n_layers, max_blocks_per_seq, num_blocks, token_budget):
+        h = C.c_void_p()
+        _check("pkv_sched_create", load().pkv_sched_create(C.byref(h), num_slots, n_layers, max_blocks_per_seq,
+                                                           num_blocks, token_budget))
+        self._h = h
+        self._it = SchedIter()
+        self._sizes = (num_slots, n_layers, max_blocks_per_seq, num_blocks,
+                       load().pkv_sched_meta_elems(num_slots, token_budget))
+
+    def close(self):
+        if self._h:
+            load().pkv_sched_destroy(self._h)
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def submit(self, request_id, prompt_len, max_new_tokens):
+        _check("pkv_sched_submit", load().pkv_sched_submit(self._h, int(request_id), int(prompt_len),
+                                                           int(max_new_tokens)))
+
+    def next(self):
+        _check("pkv_sched_next", load().pkv_sched_next(self._h, C.byref(self._it)))
+        it = self._it
+        return dict(
+            n_tokens=it.n_tokens, n_decode=it.n_decode,
+            decode_slots=_arr(it.decode_slots, it.n_decode, np.int32),
+            decode_lens=_arr(it.decode_lens, it.n_decode, np.int32),
+            decode_ids=_arr(it.decode_ids, it.n_decode, np.int64),
+            chunk_slots=_arr(it.chunk_slots, it.n_chunks, np.int32),
+            chunk_start=_arr(it.chunk_start, it.n_chunks, np.int32),
+            cu_chunk=_arr(it.cu_chunk, it.n_chunks + 1, np.int32),
+            chunk_ids=_arr(it.chunk_ids, it.n_chunks, np.int64),
+            token_slots=_arr(it.token_slots, it.n_prefill_tokens, np.int32),
+            token_pos=_arr(it.token_pos, it.n_prefill_tokens, np.int32),
+            patch_off=_arr(it.patch_off, it.n_patch, np.int32),
+            patch_val=_arr(it.patch_val, it.n_patch, np.int32),
+            done_ids=_arr(it.done_ids, it.n_done, np.int64),
+            admitted_ids=_arr(it.admitted_ids, it.n_admitted, np.int64),
+            admitted_slots=_arr(it.admitted_slots, it.n_admitted, np.int32))
+
+    def info(self):
+        st = SchedState()
+        _check("pkv_sched_info", load().pkv_sched_info(self._h, C.byref(st)))
+        n_tab = st.num_slots * st.n_layers * st.max_blocks_per_seq
+        return dict(num_slots=st.num_slots, n_layers=st.n_layers, max_blocks_per_seq=st.max_blocks_per_seq,
+                    num_blocks=st.num_blocks, token_budget=st.token_budget, n_queued=st.n_queued,
+                    n_active=st.n_active, n_free=st.n_free, n_reserved=st.n_reserved,
+                    table=_arr(st.table, n_tab, np.int32).reshape(st.num_slots, st.n_layers,
+                                                                  st.max_blocks_per_seq),
+                    free_list=_arr(st.free_list, st.n_free, np.int32), meta_elems=st.meta_elems)
+
+    def run(self, q, k, v, out, k_pool, v_pool, bt_dev, meta_dev, cos_sin, scale, workspace, stream=None):
+        """Run the last planned iteration (pkv_sched_run).  q/k/v/out: one
+        device bf16 tensor per layer, [budget rows, heads, 64]; bt_dev:
+        contiguous device int32 [slots, layers, max_blocks]; meta_dev: device
+        int32 [meta_elems]."""
+        import torch
+        L = len(q)
+        ptrs = []
+        for arr, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+            if len(arr) != L:
+                raise ValueError(f"{name} needs one tensor per layer")
+            for t in arr:
+                _contig(t, name)
+                if t.shape[0] < self._it.n_tokens:
+                    raise ValueError(f"{name} has fewer rows than the iteration's tokens")
+            ptrs.append((C.c_void_p * L)(*[_dev_ptr(t, name, _bf16_types()) for t in arr]))
+        for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool"), (bt_dev, "bt_dev"), (meta_dev, "meta_dev"),
+                     (cos_sin, "cos_sin"), (workspace, "workspace")):
+            _contig(t, n)
+        slots, layers, mb, nb, meta_elems = self._sizes
+        if L != layers or bt_dev.numel() != slots * layers * mb or meta_dev.numel() < meta_elems:
+            raise ValueError("layers, bt_dev or meta_dev do not match the scheduler")
+        if k_pool.shape[0] != nb:
+            raise ValueError("pool size differs from the scheduler's num_blocks")
+        _check("pkv_sched_run", load().pkv_sched_run(
+            self._h, C.byref(self._it), ptrs[0], ptrs[1], ptrs[2], ptrs[3],
+            _dev_ptr(k_pool, "k_pool", _bf16_types()), _dev_ptr(v_pool, "v_pool", _bf16_types()),
+            _dev_ptr(bt_dev, "bt_dev", (torch.int32,)), _dev_ptr(meta_dev, "meta_dev", (torch.int32,)),
+            q[0].shape[1], k[0].shape[1], q[0].shape[2], _dev_ptr(cos_sin, "cos_sin", (torch.float32,)),
+            cos_sin.shape[0], float(scale), _dev_ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -70,16 +70,36 @@ __global__ __launch_bounds__(256) void gather_kernel(uint4* __restrict__ k_dense
   v_dense[gid] = vv;
 }
 
-constexpr int kPatchPerLaunch = 240;   // (offset, value) pairs carried in one kernel's arguments
+constexpr int kPatchPerLaunch = 500;   // (offset, value) pairs carried in one kernel's arguments (< 4 KB)
 
 struct PatchArgs {
   int32_t off[kPatchPerLaunch];
   int32_t val[kPatchPerLaunch];
 };
 
-__global__ __launch_bounds__(256) void patch_kernel(int32_t* __restrict__ bt, int64_t elems, PatchArgs pa, int n) {
+__global__ __launch_bounds__(512) void patch_kernel(int32_t* __restrict__ bt, int64_t elems, PatchArgs pa, int n) {
   const int i = threadIdx.x;
   if (i < n && pa.off[i] >= 0 && pa.off[i] < elems) bt[pa.off[i]] = pa.val[i];
+}
+
+// Write n (offset, value) pairs whose offsets are distinct: each launch takes
+// up to kPatchPerLaunch of them in its arguments, one thread per pair.
+int patch_distinct(int32_t* bt_dev, int64_t bt_elems, const int32_t* off, const int32_t* val, int n_patch,
+                   void* stream) {
+  for (int base = 0; base < n_patch; base += kPatchPerLaunch) {
+    PatchArgs pa;
+    const int n = n_patch - base < kPatchPerLaunch ? n_patch - base : kPatchPerLaunch;
+    std::copy(off + base, off + base + n, pa.off);
+    std::copy(val + base, val + base + n, pa.val);
+    int32_t* bt = bt_dev;
+    int64_t el = bt_elems;
+    int nn = n;
+    void* args[] = {&bt, &el, &pa, &nn};
+    const int st = launch_status(hipLaunchKernel((const void*)patch_kernel, dim3(1), dim3(512), args, 0,
+                                                 (hipStream_t)stream));
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
 }
 
 }  // namespace pkv
@@ -220,32 +240,19 @@ extern "C" int pkv_block_table_patch(int32_t* bt_dev, int64_t bt_elems, const in
   // released and reused in one step) only its last pair is kept, so the pairs
   // that reach the device name distinct entries and their order within a
   // launch does not matter.
-  std::vector<int> keep;
-  keep.reserve(n_patch);
+  thread_local std::vector<int32_t> off, val;
+  off.clear();
+  val.clear();
   {
     std::unordered_set<int32_t> seen;
     seen.reserve((size_t)n_patch * 2);
     for (int i = n_patch - 1; i >= 0; --i)
-      if (seen.insert(patch_offsets_host[i]).second) keep.push_back(i);
-    std::reverse(keep.begin(), keep.end());
+      if (seen.insert(patch_offsets_host[i]).second) {
+        off.push_back(patch_offsets_host[i]);
+        val.push_back(patch_values_host[i]);
+      }
   }
-  const int n_keep = (int)keep.size();
-  for (int base = 0; base < n_keep; base += kPatchPerLaunch) {
-    PatchArgs pa;
-    const int n = n_keep - base < kPatchPerLaunch ? n_keep - base : kPatchPerLaunch;
-    for (int i = 0; i < n; ++i) {
-      pa.off[i] = patch_offsets_host[keep[base + i]];
-      pa.val[i] = patch_values_host[keep[base + i]];
-    }
-    int32_t* bt = bt_dev;
-    int64_t el = bt_elems;
-    int nn = n;
-    void* args[] = {&bt, &el, &pa, &nn};
-    const int st = launch_status(hipLaunchKernel((const void*)patch_kernel, dim3(1), dim3(256), args, 0,
-                                                 (hipStream_t)stream));
-    if (st != PKV_OK) return st;
-  }
-  return PKV_OK;
+  return patch_distinct(bt_dev, bt_elems, off.data(), val.data(), (int)off.size(), stream);
 }
 
 namespace pkv {

@@ -130,12 +130,12 @@ def test_block_table_patch(gpu):
     ref[off] = val
     np.testing.assert_array_equal(d.cpu().numpy().ravel(), ref)
     # more pairs than one launch carries: split over several launches
-    e = dev_i32(np.zeros(600, np.int32))
-    pkv.pkv_block_table_patch(e, np.arange(600, dtype=np.int32), np.arange(600, dtype=np.int32) + 1)
+    e = dev_i32(np.zeros(1200, np.int32))
+    pkv.pkv_block_table_patch(e, np.arange(1200, dtype=np.int32), np.arange(1200, dtype=np.int32) + 1)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(e.cpu().numpy(), np.arange(600) + 1)
-    # repeated offsets take effect in list order (the last pair wins), also
-    # across the launches a long list is split into
+    np.testing.assert_array_equal(e.cpu().numpy(), np.arange(1200) + 1)
+    # repeated offsets take effect in list order (the last pair wins), however
+    # far apart they are in the list
     f = dev_i32(np.full(8, -1, np.int32))
     off = np.array([3, 5, 3, -1, 3, 5, 7] + [6] * 300 + [7], np.int32)
     val = np.array([10, 11, -1, 9, 12, 13, 14] + list(range(300)) + [15], np.int32)

@@ -1,0 +1,109 @@
+"""GPU parity for continuous batching: a seeded request mix is planned by the
+native scheduler (pkv_sched_next) and run on the device (pkv_sched_run:
+table patches, fused decode rows, RoPE + append + chunked prefill for prompt
+chunks) iteration by iteration.  Every output row, decode or prefill, is
+checked against the float64 oracle: the request's query at position p,
+rotated, attending over that request's own keys 0 .. p (rotated) and values,
+gathered from nothing but the seeded inputs.  After every iteration the device
+table equals the scheduler's, and every active request's cached values read
+back bit for bit (keys within one bf16 ulp of the oracle's rotation)."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_17_amd as pkv
+from paged_kv_attention_17_amd import workloads as W
+from oracle import attention, rope
+
+from gpu_util import bits, check_attention, dev_bf16, ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+N_Q, N_KV, D = 32, 8, 64
+
+
+def token_inputs(seed, rid, pos, layer):
+    """q [32,64], k [8,64], v [8,64] bf16 bits of token `pos` of request `rid`."""
+    rng = np.random.default_rng([seed, rid, pos, layer])
+    return W.randn_bf16(rng, (N_Q, D)), W.randn_bf16(rng, (N_KV, D)), W.randn_bf16(rng, (N_KV, D))
+
+
+@pytest.mark.parametrize("seed,n_slots,n_layers,budget,num_blocks,prompts,news", [
+    (31, 4, 2, 40, 64, [17, 14, 60, 5, 33, 1, 90], [4, 6, 3, 8, 5, 2, 3]),
+    (32, 3, 1, 3, 24, [20, 7, 16], [5, 9, 2]),          # budget = slots: one-token chunks between decodes
+])
+def test_sched_iterations_match_oracle(gpu, seed, n_slots, n_layers, budget, num_blocks, prompts, news):
+    max_blocks = -(-max(p + n for p, n in zip(prompts, news)) // 16)
+    s = pkv.Scheduler(n_slots, n_layers, max_blocks, num_blocks, budget)
+    for i, (p, n) in enumerate(zip(prompts, news)):
+        s.submit(i, p, n)
+    info = s.info()
+    dev = torch.device("cuda")
+    # unused pool rows hold NaN: masking must keep them out of every output
+    k_pool = dev_bf16(np.full((num_blocks, 16, N_KV, D), W.BF16_POISON, np.uint16)).view(torch.int16)
+    v_pool = k_pool.clone()
+    bt_dev = torch.full(info["table"].shape, -1, dtype=torch.int32, device=dev)
+    meta = torch.zeros(info["meta_elems"], dtype=torch.int32, device=dev)
+    cos_sin = torch.empty((4096, D // 2, 2), dtype=torch.float32, device=dev)
+    pkv.pkv_rope_table_init(cos_sin)
+    ws = pkv.decode_workspace(n_slots, N_Q, N_KV, max_blocks * 16)
+    q = [torch.zeros((budget, N_Q, D), dtype=torch.int16, device=dev) for _ in range(n_layers)]
+    k = [torch.zeros((budget, N_KV, D), dtype=torch.int16, device=dev) for _ in range(n_layers)]
+    v = [torch.zeros((budget, N_KV, D), dtype=torch.int16, device=dev) for _ in range(n_layers)]
+    out = [torch.zeros((budget, N_Q, D), dtype=torch.int16, device=dev) for _ in range(n_layers)]
+    hist = {}            # (request, layer) -> (rotated K rows, V rows) as lists of bf16 bits
+    slot_of = {}
+    done = set()
+    rows_checked = 0
+    for _ in range(400):
+        it = s.next()
+        for r, sl in zip(it["admitted_ids"].tolist(), it["admitted_slots"].tolist()):
+            slot_of[r] = sl
+        if it["n_tokens"] == 0 and len(it["patch_off"]) == 0:
+            break
+        # the iteration's rows: (request, position)
+        rows = list(zip(it["decode_ids"].tolist(), (it["decode_lens"] - 1).tolist()))
+        cu = it["cu_chunk"]
+        for c, r in enumerate(it["chunk_ids"].tolist()):
+            rows += [(r, int(p)) for p in it["token_pos"][cu[c]:cu[c + 1]]]
+        T = len(rows)
+        host = [[token_inputs(seed, r, p, l) for (r, p) in rows] for l in range(n_layers)]
+        for l in range(n_layers):
+            if T:
+                q[l][:T] = dev_bf16(np.stack([h[0] for h in host[l]])).view(torch.int16)
+                k[l][:T] = dev_bf16(np.stack([h[1] for h in host[l]])).view(torch.int16)
+                v[l][:T] = dev_bf16(np.stack([h[2] for h in host[l]])).view(torch.int16)
+        s.run(q, k, v, out, k_pool, v_pool, bt_dev, meta, cos_sin, 0.125, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bt_dev.cpu().numpy(), s.info()["table"])
+        for l in range(n_layers):
+            # the oracle's histories grow token by token in position order
+            for t, (r, p) in enumerate(rows):
+                K, V = hist.setdefault((r, l), ([], []))
+                assert len(K) == p
+                K.append(rope.apply(host[l][t][1][None], [p])[0])
+                V.append(host[l][t][2])
+            if T:
+                ref = np.stack([attention.dense_decode(rope.apply(host[l][t][0][None], [p])[0],
+                                                       np.stack(hist[(r, l)][0][:p + 1]),
+                                                       np.stack(hist[(r, l)][1][:p + 1]), 0.125)
+                                for t, (r, p) in enumerate(rows)])
+                check_attention(bits(out[l][:T].view(torch.bfloat16)), ref, f"iteration rows {T} layer {l}")
+                rows_checked += T
+        # the cache of every request still holding its slot reads back
+        for r, sl in slot_of.items():
+            n = len(hist.get((r, 0), ([], []))[0])
+            if r in done or n == 0:
+                continue
+            for l in range(n_layers):
+                kd = torch.zeros((n, N_KV, D), dtype=torch.bfloat16, device=dev)
+                vd = torch.zeros_like(kd)
+                pkv.pkv_paged_gather(kd, vd, k_pool.view(torch.bfloat16), v_pool.view(torch.bfloat16),
+                                     bt_dev[:, l, :], sl, n)
+                torch.cuda.synchronize()
+                np.testing.assert_array_equal(bits(vd), np.stack(hist[(r, l)][1]))
+                assert ulp_diff(bits(kd), np.stack(hist[(r, l)][0])).max() <= 1
+        done |= set(it["done_ids"].tolist())
+    assert len(done) == len(prompts)
+    assert rows_checked == n_layers * sum(p + n - 1 for p, n in zip(prompts, news))
+    assert s.info()["n_free"] == num_blocks
