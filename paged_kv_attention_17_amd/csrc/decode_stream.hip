@@ -57,6 +57,7 @@ constexpr int kMaxSeqs = 256;         // batch rows described in the arguments
 constexpr int kMaxQ = 32;             // query heads staged per row
 constexpr int kMaxGrid = 512;         // workgroups (one per CU)
 constexpr int kRec = kHeadDim + 2;    // partial record per query head: o[64], max, sum
+constexpr int kWin = kThreads;        // blocks whose table entries are staged in LDS at a time
 
 struct StreamArgs {
   uint16_t* out;
@@ -244,10 +245,19 @@ void stream_kernel(StreamArgs a) {
   __shared__ float sp[kMaxRows][kWaves][G][kRec];           // per-wave partials of each row
   __shared__ int srow_ok[kMaxRows];                         // the row's table slot is valid
   __shared__ uint16_t svt[kWaves][kBlock * kHeadDim];       // per-wave V tile (transposed reads)
+  __shared__ int s_tab[kWin];                               // window's blocks: pool block id or -1
+  __shared__ int s_meta[kWin];                              // and row << 8 | tokens read from the pool
+  __shared__ int s_next[kWaves];                            // per KV head: next unclaimed block of the window
 
-  // ---- this wave's blocks ----------------------------------------------------
+  // ---- the share's blocks -------------------------------------------------
+  // The share is walked in windows of kWin blocks.  Each window's table slice
+  // is computed into LDS (thread t: block t of the window); then the waves of
+  // each KV head claim the window's blocks one at a time from the head's LDS
+  // counter, so a wave that runs ahead takes more blocks and the waves of the
+  // workgroup finish together (with a fixed split the youngest waves of a CU
+  // ended long after the oldest).  A wave's claims increase, so it still
+  // meets the share's rows in order.
   const int len = B1 - B0;
-  const int n_w = len > s ? (len - s + S - 1) / S : 0;       // blocks of this wave
   const uint32_t block_bytes = (uint32_t)(kBlock * row_elems * 2);
   const uint32_t lane_off = (uint32_t)(((int64_t)r * row_elems + h * kHeadDim + c * 8) * 2);
   const uint32_t lane_off8 = lane_off + (uint32_t)(8 * row_elems * 2);
@@ -257,10 +267,9 @@ void stream_kernel(StreamArgs a) {
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
 
-  // lane i: this wave's block cb + i -> pool block id and (row << 8 | tokens
-  // to read from the pool; the fused step's new token is not among them)
-  auto block_info = [&](int cb, int ncb, int& tab, int& meta) {
-    const int p = B0 + s + S * (cb + min(lane, ncb - 1));
+  // stream block p -> pool block id and (row << 8 | tokens to read from the
+  // pool; the fused step's new token is not among them)
+  auto block_info = [&](int p, int& tab, int& meta) {
     int ri = 0;
     for (int i = 1; i < nrows; ++i) ri = p >= a.row_start[bf + i] ? i : ri;
     int start = a.row_start[bf], n = a.row_n[bf];
@@ -279,8 +288,7 @@ void stream_kernel(StreamArgs a) {
     }
     meta = (ri << 8) | valid;
   };
-  auto issue = [&](KVRegs& R, int tab, int ncb, int i) {
-    int blk = __builtin_amdgcn_readlane(tab, min(i, ncb - 1));
+  auto issue = [&](KVRegs& R, int blk) {
     blk = blk < 0 ? 0 : blk;
     const auto rk = buf_rsrc(kbase + (size_t)blk * block_bytes, block_bytes);
     const auto rv = buf_rsrc(vbase + (size_t)blk * block_bytes, block_bytes);
@@ -289,10 +297,10 @@ void stream_kernel(StreamArgs a) {
     R.v0 = buf_load16(rv, lane_off);
     R.v1 = buf_load16(rv, lane_off8);
   };
-  // the first table slice is requested before the staging below waits
-  int ncb = min(kWave, n_w);
+  // the first window's table slice is requested before the staging below
+  // waits (and written to LDS after it)
   int tab = -1, meta = 0;
-  if (n_w > 0) block_info(0, ncb, tab, meta);
+  if (tid < min(kWin, len)) block_info(B0 + tid, tab, meta);
 
   // ---- queries of the share's rows (rotated by position n - 1 when fused) ----
   for (int e = tid; e < nrows * a.n_q * 8; e += kThreads) {
@@ -342,6 +350,11 @@ void stream_kernel(StreamArgs a) {
       }
     }
   }
+  if (tid < min(kWin, len)) {
+    s_tab[tid] = tab;
+    s_meta[tid] = meta;
+  }
+  if (tid < kWaves) s_next[tid] = 0;
   __syncthreads();
 
   MfmaAcc acc;
@@ -391,23 +404,33 @@ void stream_kernel(StreamArgs a) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) v_rd[t] = vt_index(lane >> 2, 16 * t + 4 * (lane & 3));
 
-  for (int cb = 0; cb < n_w; cb += kWave) {
-    if (cb > 0) {
-      ncb = min(kWave, n_w - cb);
-      block_info(cb, ncb, tab, meta);
+  // the next block of this wave's KV head in the current window (wave-uniform)
+  auto claim = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&s_next[h], 1);
+    return wave_uniform(v);
+  };
+  for (int w0 = 0; w0 < len; w0 += kWin) {
+    const int wl = min(kWin, len - w0);
+    if (w0 > 0) {
+      __syncthreads();                   // every wave is done with the previous window
+      if (tid < wl) {
+        block_info(B0 + w0 + tid, tab, meta);
+        s_tab[tid] = tab;
+        s_meta[tid] = meta;
+      }
+      if (tid < kWaves) s_next[tid] = 0;
+      __syncthreads();
     }
-    KVRegs X, Y;
-    issue(X, tab, ncb, 0);
-    issue(Y, tab, ncb, 1);
     auto step = [&](KVRegs R, int i) {
-      const int mt = __builtin_amdgcn_readlane(meta, i);
+      const int mt = wave_uniform(s_meta[i]);
       while (cur < (mt >> 8)) flush();
-      const bool blk_ok = __builtin_amdgcn_readlane(tab, i) >= 0;
+      const bool blk_ok = wave_uniform(s_tab[i]) >= 0;
       const int valid = mt & 0xff;       // tokens read from the pool
       int extra = -1;                    // fused: slot of the new token in this block
       if constexpr (FUSED) {
         // the row's last block: the new token (rotated key, value) from LDS
-        if (B0 + s + S * (cb + i) == row_last) {
+        if (B0 + w0 + i == row_last) {
           extra = valid;
           if (col == extra) {
             R.k0 = snew[cur][0][h * 8 + q4];
@@ -419,13 +442,22 @@ void stream_kernel(StreamArgs a) {
       }
       acc.block(qb0, qb1, R, vtile, v_wr0, v_wr1, v_rd, r, q4, blk_ok, valid, extra, C, invC);
     };
-    for (int i = 0;; i += 2) {
-      step(X, i);
-      issue(X, tab, ncb, i + 2);
-      if (i + 1 >= ncb) break;
-      step(Y, i + 1);
-      issue(Y, tab, ncb, i + 3);
-      if (i + 2 >= ncb) break;
+    // two blocks in flight in two register sets; loads are issued for every
+    // claim (a claim past the window reloads the window's last block and is
+    // not used), so each step waits for exactly the older set
+    KVRegs X, Y;
+    int ia = claim();
+    issue(X, s_tab[min(ia, wl - 1)]);
+    int ib = claim();
+    issue(Y, s_tab[min(ib, wl - 1)]);
+    while (ia < wl) {
+      step(X, ia);
+      ia = claim();
+      issue(X, s_tab[min(ia, wl - 1)]);
+      if (ib >= wl) break;
+      step(Y, ib);
+      ib = claim();
+      issue(Y, s_tab[min(ib, wl - 1)]);
     }
   }
   while (cur < nrows) flush();
