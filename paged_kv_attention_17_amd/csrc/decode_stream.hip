@@ -559,6 +559,75 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs a) {
   }
 }
 
+// The same merge for batches whose rows span many shares (few rows, long
+// contexts): one workgroup per (row, query head), 16 groups of 64 threads
+// (thread = dim); group j takes records j, j + 16, ..., eight of them with
+// their loads in flight at once, and the groups' partial (max, sum, output)
+// are combined through LDS.  More workgroups and shorter chains of dependent
+// loads per thread than the kernel above, which leaves a batch of one row
+// on n_kv workgroups walking hundreds of records each.
+__global__ __launch_bounds__(1024) void stream_merge_wide_kernel(StreamArgs a) {
+  constexpr int kGroups = 16;
+  __shared__ float part[kGroups][kHeadDim][3];
+  const int qh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int n = a.row_n[b];
+  const int d = threadIdx.x % kHeadDim;
+  const int grp = threadIdx.x / kHeadDim;
+  const int64_t obase = ((int64_t)b * a.n_q + qh) * kHeadDim;
+  if (n <= 0) {
+    if (grp == 0) a.out[obase + d] = 0;
+    return;
+  }
+  const int start = a.row_start[b];
+  const int w0 = start / a.share;
+  const int w1 = (a.row_start[b + 1] - 1) / a.share;
+  if (w0 == w1) return;
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int w = w0 + grp; w <= w1; w += 8 * kGroups) {
+    float mv[8], lv[8], ov[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int wj = w + j * kGroups;
+      const int ww = wj <= w1 ? wj : w1;
+      const int rec = 2 * ww + ((ww > w0 || start == w0 * a.share) ? 0 : 1);
+      const float* src = a.ws + ((int64_t)rec * a.n_q + qh) * kRec;
+      mv[j] = wj <= w1 ? src[kHeadDim] : -INFINITY;
+      lv[j] = src[kHeadDim + 1];
+      ov[j] = src[d];
+    }
+    float mm = M;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mm = fmaxf(mm, mv[j]);
+    const float f0 = M == -INFINITY ? 0.f : fast_exp2(M - mm);
+    L *= f0;
+    O *= f0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = mv[j] == -INFINITY ? 0.f : fast_exp2(mv[j] - mm);
+      L += f * lv[j];
+      O += f * ov[j];
+    }
+    M = mm;
+  }
+  part[grp][d][0] = M;
+  part[grp][d][1] = L;
+  part[grp][d][2] = O;
+  __syncthreads();
+  if (grp > 0) return;
+  for (int j = 1; j < kGroups; ++j) {
+    const float m2 = part[j][d][0];
+    const float mm = fmaxf(M, m2);
+    if (mm == -INFINITY) continue;
+    const float f1 = M == -INFINITY ? 0.f : fast_exp2(M - mm);
+    const float f2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mm);
+    L = L * f1 + part[j][d][1] * f2;
+    O = O * f1 + part[j][d][2] * f2;
+    M = mm;
+  }
+  a.out[obase + d] = to_bf16(L > 0.f ? O / L : 0.f);
+}
+
 int device_cus() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cus[kMaxDev];
@@ -648,6 +717,14 @@ int stream_decode(bool fused, const StreamCall& c) {
   const void* fn = fused ? pick_stream<true>(G) : pick_stream<false>(G);
   int rc = launch_status(hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st));
   if (rc != PKV_OK) return rc;
+  // rows that span many shares (few rows) are merged per query head by 16
+  // groups of threads
+  int most = 1;
+  for (int b = 0; b < c.batch; ++b)
+    if (a.row_n[b] > 0) most = std::max(most, (a.row_start[b + 1] - 1) / a.share - a.row_start[b] / a.share + 1);
+  if (most > 32)
+    return launch_status(hipLaunchKernel((const void*)stream_merge_wide_kernel, dim3(c.n_q, c.batch), dim3(1024),
+                                         args, 0, st));
   const void* mg = G == 1 ? (const void*)stream_merge_kernel<1>
                  : G == 2 ? (const void*)stream_merge_kernel<2>
                           : (const void*)stream_merge_kernel<4>;

@@ -258,3 +258,17 @@ def test_stream_long_rows_several_table_slices(gpu):
         check_attention(got[b], ref, f"long row {b}")
     del kpd, vpd
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("lens", [[8192], [3000, 5000], [16 * 256 * 3 + 5]])
+def test_stream_few_rows_over_every_share(gpu, lens):
+    """One or two rows cut into hundreds of shares: their records are merged
+    by four groups of threads combined through LDS."""
+    rng = np.random.default_rng(300 + sum(lens))
+    lens = np.array(lens, np.int32)
+    kp, vp, bt = _batch(rng, lens, 8)
+    q = W.randn_bf16(rng, (len(lens), 32, 64))
+    got = _decode(q, kp, vp, bt, None, lens, lens)
+    ref = attention.decode(q, kp, vp, bt, np.arange(len(lens)), lens, 0.125)
+    check_attention(got, ref, f"few rows {lens.tolist()}")
+    check_close_evaluations(_decode(q, kp, vp, bt, None, lens, None), got, "few rows vs per-partition")
