@@ -8,10 +8,12 @@
 //
 // Design: the table holds float32 (cos, sin) per (position, pair), computed in
 // double on the host, so the device never reduces a large angle.  The rotation
-// kernel gives each thread one (token, head, pair): two bf16 loads, one 8-byte
-// table load, float32 math, nearest-even bf16 stores.  The work is a few
-// hundred KB per decode step, so the kernel is launch-latency bound; it is
-// kept simple and fully parallel.
+// kernel gives each thread eight pairs of one (token, head): the 16-byte chunk
+// of dims 8c .. 8c + 7, the chunk 32 dims further on that holds their
+// partners, and the pairs' 64 bytes of table, all in 16-byte accesses;
+// float32 math, nearest-even bf16 stores.  A decode step's few hundred KB are
+// launch-latency bound; a prefill chunk of a few thousand tokens moves tens
+// of MB, which the wide accesses stream.
 #include <cmath>
 #include <vector>
 
@@ -24,26 +26,37 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ q, uin
                                                    int n_q, int n_kv, const float2* __restrict__ table,
                                                    int max_pos) {
   constexpr int kHalf = kHeadDim / 2;
+  constexpr int kChunks = kHalf / 8;     // 8-pair chunks per head row
   const int heads = n_q + (k ? n_kv : 0);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)num_tokens * heads * kHalf;
+  const int64_t total = (int64_t)num_tokens * heads * kChunks;
   if (gid >= total) return;
-  const int i = (int)(gid % kHalf);
-  const int64_t th = gid / kHalf;
+  const int c = (int)(gid % kChunks);
+  const int64_t th = gid / kChunks;
   const int h = (int)(th % heads);
   const int t = (int)(th / heads);
   const int pos = positions[t];
   if (pos < 0 || pos >= max_pos) return;
   uint16_t* row = h < n_q ? q + ((int64_t)t * n_q + h) * kHeadDim
                           : k + ((int64_t)t * n_kv + (h - n_q)) * kHeadDim;
-  const float2 cs = table[(int64_t)pos * kHalf + i];
-  const float x = __builtin_bit_cast(float, (uint32_t)row[i] << 16);
-  const float y = __builtin_bit_cast(float, (uint32_t)row[i + kHalf] << 16);
-  const float xr = rope_first(x, y, cs.x, cs.y);
-  const float yr = rope_second(x, y, cs.x, cs.y);
-  const uint32_t packed = pack_bf16x2(xr, yr);
-  row[i] = (uint16_t)(packed & 0xffffu);
-  row[i + kHalf] = (uint16_t)(packed >> 16);
+  uint4* r4 = reinterpret_cast<uint4*>(row);
+  const uint4 lo = r4[c];                // dims 8c .. 8c + 7
+  const uint4 hi = r4[c + kChunks];      // their partners, 32 dims further on
+  // (cos, sin) of pairs 8c .. 8c + 7, two pairs per 16-byte load
+  const float4* tb = reinterpret_cast<const float4*>(table + (int64_t)pos * kHalf + 8 * c);
+  const uint32_t xs[4] = {lo.x, lo.y, lo.z, lo.w};
+  const uint32_t ys[4] = {hi.x, hi.y, hi.z, hi.w};
+  uint32_t out_lo[4], out_hi[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float4 cs = tb[j];
+    const float x0 = bf16_lo(xs[j]), x1 = bf16_hi(xs[j]);
+    const float y0 = bf16_lo(ys[j]), y1 = bf16_hi(ys[j]);
+    out_lo[j] = pack_bf16x2(rope_first(x0, y0, cs.x, cs.y), rope_first(x1, y1, cs.z, cs.w));
+    out_hi[j] = pack_bf16x2(rope_second(x0, y0, cs.x, cs.y), rope_second(x1, y1, cs.z, cs.w));
+  }
+  r4[c] = make_uint4(out_lo[0], out_lo[1], out_lo[2], out_lo[3]);
+  r4[c + kChunks] = make_uint4(out_hi[0], out_hi[1], out_hi[2], out_hi[3]);
 }
 
 }  // namespace pkv
@@ -98,7 +111,7 @@ extern "C" int pkv_rope_decode(pkv_bf16* q, pkv_bf16* k, const int32_t* position
   if (!aligned16(q) || (k && !aligned16(k)) || !aligned4(positions) || !aligned16(cos_sin))
     return PKV_ERR_MISALIGNED;
   const int heads = n_q_heads + (k ? n_kv_heads : 0);
-  const int64_t total = (int64_t)num_tokens * heads * (kHeadDim / 2);
+  const int64_t total = (int64_t)num_tokens * heads * (kHeadDim / 16);
   if (total == 0) return PKV_OK;
   const int64_t grid = (total + 255) / 256;
   if (grid > 0x7fffffff) return PKV_ERR_INVALID_ARG;
