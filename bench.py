@@ -383,7 +383,7 @@ def serving_leg(torch, np, pkv, W, n_req: int = 128, n_slots: int = 64, budget: 
     L, NQ, NKV, D = 16, 32, 8, 64
     rng = np.random.default_rng(1707)
     prompts = rng.integers(256, 2049, size=n_req)
-    max_blocks = -(-int(prompts.max() + new_tokens) // 16)
+    max_blocks = -(-(2048 + new_tokens) // 16)            # longest prompt of either mix + new tokens
     num_blocks = n_slots * L * max_blocks
     dev = torch.device("cuda")
     kp = torch.zeros((num_blocks, 16, NKV, D), dtype=torch.bfloat16, device=dev)
@@ -399,10 +399,10 @@ def serving_leg(torch, np, pkv, W, n_req: int = 128, n_slots: int = 64, budget: 
     ws = pkv.decode_workspace(n_slots, NQ, NKV, max_blocks * 16)
     stream = torch.cuda.current_stream()
 
-    def job(lens, news):
+    def job(lens, news, tokens=None):
         s = pkv.Scheduler(n_slots, L, max_blocks, num_blocks, budget)
         for i, (p, n) in enumerate(zip(lens, news)):
-            s.submit(i, int(p), int(n))
+            s.submit(i, int(p), int(n), tokens=None if tokens is None else tokens[i])
         bt = torch.full((n_slots, L, max_blocks), -1, dtype=torch.int32, device=dev)
         meta = torch.zeros(s.info()["meta_elems"], dtype=torch.int32, device=dev)
         torch.cuda.synchronize()
@@ -423,12 +423,32 @@ def serving_leg(torch, np, pkv, W, n_req: int = 128, n_slots: int = 64, budget: 
             pre_rows += it["n_tokens"] - it["n_decode"]
         e1.record(stream)
         torch.cuda.synchronize()
+        hits = s.info()["cache_hit_tokens"]
         s.close()
-        return e0.elapsed_time(e1) / 1e3, iters, plan, host, dec_rows, pre_rows
+        return e0.elapsed_time(e1) / 1e3, iters, plan, host, dec_rows, pre_rows, hits
 
     job([300, 40, 1000], [3, 3, 3])                      # warm-up (kernels loaded, caches touched)
-    t, iters, plan, host, dec_rows, pre_rows = job(prompts, [new_tokens] * n_req)
+    t, iters, plan, host, dec_rows, pre_rows, _ = job(prompts, [new_tokens] * n_req)
+    # the same serving run where every prompt opens with one of 4 shared
+    # 1,024-token system prompts (then a private part U[64, 1024]): with token
+    # ids (prefix cache on) and without (every prompt prefilled in full)
+    sys_prompts = rng.integers(0, 128000, size=(4, 1024)).astype(np.int32)
+    toks = [np.concatenate([sys_prompts[int(rng.integers(0, 4))],
+                            rng.integers(0, 128000, size=int(rng.integers(64, 1025)))]).astype(np.int32)
+            for _ in range(n_req)]
+    lens_sp = [len(x) for x in toks]
+    t_on, it_on, _, _, dec_on, pre_on, hits = job(lens_sp, [new_tokens] * n_req, toks)
+    t_off, it_off, _, _, dec_off, pre_off, _ = job(lens_sp, [new_tokens] * n_req)
     del kp, vp
+    shared = {"workload": f"{n_req} requests, prompts = one of 4 shared 1024-token system prompts + U[64,1024] "
+                          f"private tokens (sum {sum(lens_sp)}), {new_tokens} new tokens each, same slots, budget "
+                          "and layers",
+              "cache_on": {"seconds": round(t_on, 4), "iterations": it_on, "prefill_tokens": pre_on,
+                           "reused_prompt_tokens": int(hits),
+                           "output_tokens_per_s": round(n_req * new_tokens / t_on, 1)},
+              "cache_off": {"seconds": round(t_off, 4), "iterations": it_off, "prefill_tokens": pre_off,
+                            "output_tokens_per_s": round(n_req * new_tokens / t_off, 1)},
+              "speedup": round(t_off / t_on, 3)}
     return {"workload": f"continuous batching, {n_req} requests, prompts U[256,2048] (sum {int(prompts.sum())} "
                         f"tokens), {new_tokens} new tokens each, {n_slots} slots, {budget}-token budget, 16 layers, "
                         "32q/8kv heads, d=64, bf16 16-token blocks",
@@ -438,7 +458,8 @@ def serving_leg(torch, np, pkv, W, n_req: int = 128, n_slots: int = 64, budget: 
             "output_tokens_per_s": round(n_req * new_tokens / t, 1),
             "gpu_us_per_iteration": round(t / max(iters, 1) * 1e6, 1),
             "plan_us_per_iteration": round(plan / max(iters, 1) * 1e6, 1),
-            "host_us_per_iteration": round(host / max(iters, 1) * 1e6, 1)}
+            "host_us_per_iteration": round(host / max(iters, 1) * 1e6, 1),
+            "shared_prompts": shared}
 
 
 def main():
@@ -554,6 +575,11 @@ def main():
         f"({sv['prefill_tokens']} prompt tokens, {sv['decode_rows']} decode rows), "
         f"{sv['output_tokens_per_s']:.0f} output tokens/s; per iteration: plan {sv['plan_us_per_iteration']:.0f} us, "
         f"plan + enqueue {sv['host_us_per_iteration']:.0f} us (includes waits for a full launch queue)")
+    sp = sv["shared_prompts"]
+    log(f"serving over shared system prompts: prefix cache on {sp['cache_on']['seconds'] * 1e3:.1f} ms "
+        f"({sp['cache_on']['prefill_tokens']} prompt tokens prefilled, {sp['cache_on']['reused_prompt_tokens']} "
+        f"reused), off {sp['cache_off']['seconds'] * 1e3:.1f} ms ({sp['cache_off']['prefill_tokens']} prefilled): "
+        f"{sp['speedup']:.2f}x")
 
     copy_gbs = stream_copy_gbs(torch)
     read_gbs = stream_read_gbs(torch, pkv)

@@ -424,6 +424,7 @@ typedef struct {
   int n_admitted;               /* requests admitted in this iteration and their slots */
   const int64_t* admitted_ids;
   const int32_t* admitted_slots;
+  const int32_t* admitted_cached;  /* prompt tokens each found in the prefix cache (not prefilled) */
 } pkv_sched_iter;
 
 typedef struct {
@@ -432,6 +433,11 @@ typedef struct {
   const int32_t* table;         /* host table [num_slots][n_layers][max_blocks_per_seq] */
   const int32_t* free_list;     /* [n_free] free blocks (popped from the end) */
   int64_t meta_elems;           /* pkv_sched_meta_elems(num_slots, token_budget) */
+  int n_cache_nodes;            /* prefix cache: full prompt blocks held */
+  int n_cache_blocks;           /* their pool blocks (n_cache_nodes x n_layers) */
+  const int32_t* cache_blocks;  /* [n_cache_blocks] */
+  int n_evictable;              /* nodes no active request lists and with no cached continuation */
+  int64_t cache_hit_tokens;     /* prompt tokens taken from the cache so far */
 } pkv_sched_state;
 
 /* A scheduler with an empty table and all num_blocks blocks free.
@@ -445,6 +451,25 @@ int pkv_sched_destroy(pkv_sched* sched);
  * prompt_len >= 1, max_new_tokens >= 1.  PKV_ERR_CAPACITY if it could never
  * be admitted (its tokens exceed a table row or its blocks the pool). */
 int pkv_sched_submit(pkv_sched* sched, int64_t request_id, int prompt_len, int max_new_tokens);
+
+/* Prefix cache.  Source: the category page's mini-sglang chapter-5 title (a
+ * radix cache reuses the cached K/V of prefixes that many requests share, and
+ * evicts).  A request queued with its prompt's token ids (copied; HOST array
+ * of prompt_len ids) takes part: at admission its table row lists the blocks
+ * of the longest run of its prompt's full 16-token blocks already cached
+ * (keeping at least one prompt token to prefill), in every layer, and its
+ * prefill starts after them; when its whole prompt is cached, its full prompt
+ * blocks join the cache (a trie of 16-token keys, one node per block, each
+ * holding a pool block per layer) unless an identical block was published
+ * first.  Cached blocks are never written (writes start after the listed
+ * prefix), stay allocated after their requests finish, and are evicted least
+ * recently used first, leaves only and only when no active request lists
+ * them, when an admission needs blocks.  K/V of a token must depend only on
+ * the tokens before it and its position (true of a model; the caller's duty
+ * for synthetic inputs).  pkv_sched_submit is this call with no ids (the
+ * request neither reuses nor publishes). */
+int pkv_sched_submit_tokens(pkv_sched* sched, int64_t request_id, const int32_t* prompt_tokens_host,
+                            int prompt_len, int max_new_tokens);
 
 /* Plan the next iteration (host only; no device is touched). */
 int pkv_sched_next(pkv_sched* sched, pkv_sched_iter* iter);

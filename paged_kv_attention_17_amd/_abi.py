@@ -65,6 +65,7 @@ SIGNATURES = {
     "pkv_sched_create": (_i, [C.POINTER(_p), _i, _i, _i, _i, _i]),
     "pkv_sched_destroy": (_i, [_p]),
     "pkv_sched_submit": (_i, [_p, _i64, _i, _i]),
+    "pkv_sched_submit_tokens": (_i, [_p, _i64, _p, _i, _i]),
     "pkv_sched_next": (_i, [_p, _p]),
     "pkv_sched_info": (_i, [_p, _p]),
     "pkv_sched_meta_elems": (_i64, [_i, _i]),
@@ -82,14 +83,15 @@ class SchedIter(C.Structure):
                 ("cu_chunk", _I32P), ("chunk_ids", _I64P), ("n_prefill_tokens", _i), ("token_slots", _I32P),
                 ("token_pos", _I32P), ("n_patch", _i), ("patch_off", _I32P), ("patch_val", _I32P),
                 ("n_done", _i), ("done_ids", _I64P), ("n_admitted", _i), ("admitted_ids", _I64P),
-                ("admitted_slots", _I32P)]
+                ("admitted_slots", _I32P), ("admitted_cached", _I32P)]
 
 
 class SchedState(C.Structure):
     """pkv_sched_state (include/pagedkv.h)."""
     _fields_ = [("num_slots", _i), ("n_layers", _i), ("max_blocks_per_seq", _i), ("num_blocks", _i),
                 ("token_budget", _i), ("n_queued", _i), ("n_active", _i), ("n_free", _i), ("n_reserved", _i),
-                ("table", _I32P), ("free_list", _I32P), ("meta_elems", _i64)]
+                ("table", _I32P), ("free_list", _I32P), ("meta_elems", _i64), ("n_cache_nodes", _i),
+                ("n_cache_blocks", _i), ("cache_blocks", _I32P), ("n_evictable", _i), ("cache_hit_tokens", _i64)]
 
 
 class PagedKVError(RuntimeError):
@@ -634,9 +636,18 @@ class Scheduler:
         except Exception:
             pass
 
-    def submit(self, request_id, prompt_len, max_new_tokens):
-        _check("pkv_sched_submit", load().pkv_sched_submit(self._h, int(request_id), int(prompt_len),
-                                                           int(max_new_tokens)))
+    def submit(self, request_id, prompt_len, max_new_tokens, tokens=None):
+        """Queue a request; with `tokens` (its prompt's ids, int32) it takes
+        part in prefix caching (pkv_sched_submit_tokens)."""
+        if tokens is None:
+            _check("pkv_sched_submit", load().pkv_sched_submit(self._h, int(request_id), int(prompt_len),
+                                                               int(max_new_tokens)))
+            return
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        if t.shape != (int(prompt_len),):
+            raise ValueError("tokens must hold prompt_len ids")
+        _check("pkv_sched_submit_tokens", load().pkv_sched_submit_tokens(
+            self._h, int(request_id), t.ctypes.data, int(prompt_len), int(max_new_tokens)))
 
     def next(self):
         _check("pkv_sched_next", load().pkv_sched_next(self._h, C.byref(self._it)))
@@ -656,7 +667,8 @@ class Scheduler:
             patch_val=_arr(it.patch_val, it.n_patch, np.int32),
             done_ids=_arr(it.done_ids, it.n_done, np.int64),
             admitted_ids=_arr(it.admitted_ids, it.n_admitted, np.int64),
-            admitted_slots=_arr(it.admitted_slots, it.n_admitted, np.int32))
+            admitted_slots=_arr(it.admitted_slots, it.n_admitted, np.int32),
+            admitted_cached=_arr(it.admitted_cached, it.n_admitted, np.int32))
 
     def info(self):
         st = SchedState()
@@ -667,7 +679,9 @@ class Scheduler:
                     n_active=st.n_active, n_free=st.n_free, n_reserved=st.n_reserved,
                     table=_arr(st.table, n_tab, np.int32).reshape(st.num_slots, st.n_layers,
                                                                   st.max_blocks_per_seq),
-                    free_list=_arr(st.free_list, st.n_free, np.int32), meta_elems=st.meta_elems)
+                    free_list=_arr(st.free_list, st.n_free, np.int32), meta_elems=st.meta_elems,
+                    n_cache_nodes=st.n_cache_nodes, cache_blocks=_arr(st.cache_blocks, st.n_cache_blocks, np.int32),
+                    n_evictable=st.n_evictable, cache_hit_tokens=st.cache_hit_tokens)
 
     def run(self, q, k, v, out, k_pool, v_pool, bt_dev, meta_dev, cos_sin, scale, workspace, stream=None):
         """Run the last planned iteration (pkv_sched_run).  q/k/v/out: one

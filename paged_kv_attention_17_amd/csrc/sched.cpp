@@ -37,6 +37,9 @@
 #include <cstdint>
 #include <cstring>
 #include <deque>
+#include <set>
+#include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "../../include/pagedkv.h"
@@ -57,7 +60,32 @@ struct Request {
   int produced = 0;     // tokens produced so far
   int reserved = 0;     // blocks reserved and not yet taken from the free list
   int64_t order = 0;    // admission order
+  std::vector<int32_t> tokens;   // prompt token ids (empty: the request takes no part in prefix caching)
+  std::vector<int> path;         // prefix-cache nodes its first table entries list, in block order
 };
+
+// A node of the prefix cache: one full 16-token block of some prompt, under
+// the node of the block before it.  Its blocks (one per layer) hold the K/V of
+// those tokens after exactly that prefix, so any request whose prompt starts
+// with the same tokens can list them instead of prefilling them again.
+struct Node {
+  int parent = -1;
+  int32_t key[PKV_BLOCK_SIZE];           // the block's token ids
+  std::vector<int32_t> blocks;           // pool block per layer
+  std::unordered_map<uint64_t, int> kids;  // key hash -> child
+  int ref = 0;                           // active requests whose rows list it
+  int64_t last_use = 0;
+  bool live = false;
+};
+
+uint64_t key_hash(const int32_t* t) {
+  uint64_t h = 1469598103934665603ull;   // FNV-1a over the 16 ids
+  for (int i = 0; i < PKV_BLOCK_SIZE; ++i) {
+    h ^= (uint32_t)t[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
 
 int blocks_needed(int tokens) { return (tokens + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE; }
 
@@ -78,7 +106,17 @@ struct pkv_sched {
   std::vector<int32_t> decode_slots, decode_lens, chunk_slots, chunk_start, cu_chunk, token_slots, token_pos,
       patch_off, patch_val;
   std::vector<int64_t> decode_ids, chunk_ids, done_ids, admitted_ids;
-  std::vector<int32_t> admitted_slots;
+  std::vector<int32_t> admitted_slots, admitted_cached;
+
+  // prefix cache: node 0 is the root (no blocks); evictable = live nodes with
+  // no children that no active request lists, oldest use first
+  std::vector<Node> nodes;
+  std::vector<int> dead_nodes;
+  std::set<std::pair<int64_t, int>> evictable;
+  int64_t tick = 0;
+  int cache_nodes = 0;                 // live nodes besides the root
+  int64_t hit_tokens = 0;              // prompt tokens taken from the cache
+  std::vector<int32_t> cache_list;     // pkv_sched_info's list of the cache's blocks
 
   int64_t entry(int s, int l, int j) const { return ((int64_t)s * n_layers + l) * max_blocks + j; }
 };
@@ -103,6 +141,8 @@ extern "C" int pkv_sched_create(pkv_sched** out, int num_slots, int n_layers, in
   s->n_free = num_blocks;
   s->slot.resize(num_slots);
   s->finished.assign(num_slots, 0);
+  s->nodes.resize(1);
+  s->nodes[0].live = true;
   *out = s;
   return PKV_OK;
 }
@@ -112,7 +152,8 @@ extern "C" int pkv_sched_destroy(pkv_sched* s) {
   return PKV_OK;
 }
 
-extern "C" int pkv_sched_submit(pkv_sched* s, int64_t request_id, int prompt_len, int max_new_tokens) {
+extern "C" int pkv_sched_submit_tokens(pkv_sched* s, int64_t request_id, const int32_t* prompt_tokens_host,
+                                       int prompt_len, int max_new_tokens) {
   if (!s) return PKV_ERR_NULL;
   if (request_id < 0 || prompt_len <= 0 || max_new_tokens <= 0) return PKV_ERR_INVALID_ARG;
   const int64_t tokens = (int64_t)prompt_len + max_new_tokens - 1;
@@ -122,8 +163,13 @@ extern "C" int pkv_sched_submit(pkv_sched* s, int64_t request_id, int prompt_len
   r.id = request_id;
   r.prompt = prompt_len;
   r.max_new = max_new_tokens;
-  s->queue.push_back(r);
+  if (prompt_tokens_host) r.tokens.assign(prompt_tokens_host, prompt_tokens_host + prompt_len);
+  s->queue.push_back(std::move(r));
   return PKV_OK;
+}
+
+extern "C" int pkv_sched_submit(pkv_sched* s, int64_t request_id, int prompt_len, int max_new_tokens) {
+  return pkv_sched_submit_tokens(s, request_id, nullptr, prompt_len, max_new_tokens);
 }
 
 namespace {
@@ -145,17 +191,112 @@ void open_chunk(pkv_sched* s, int si, int pos) {
   }
 }
 
+// ---- prefix cache ----------------------------------------------------------
+
+void touch(pkv_sched* s, int n) {
+  Node& x = s->nodes[n];
+  if (x.ref == 0 && x.kids.empty()) s->evictable.erase({x.last_use, n});
+  x.last_use = ++s->tick;
+  if (x.ref == 0 && x.kids.empty()) s->evictable.insert({x.last_use, n});
+}
+
+void add_ref(pkv_sched* s, int n, int d) {
+  Node& x = s->nodes[n];
+  if (x.ref == 0 && x.kids.empty()) s->evictable.erase({x.last_use, n});
+  x.ref += d;
+  if (x.ref == 0 && x.kids.empty()) s->evictable.insert({x.last_use, n});
+}
+
+// The child of `n` whose key is tokens t[0..16), or -1.
+int find_child(const pkv_sched* s, int n, const int32_t* t) {
+  const Node& x = s->nodes[n];
+  auto it = x.kids.find(key_hash(t));
+  if (it == x.kids.end()) return -1;
+  const Node& c = s->nodes[it->second];
+  return std::equal(t, t + PKV_BLOCK_SIZE, c.key) ? it->second : -1;
+}
+
+// Longest run of the prompt's full blocks in the cache, leaving at least one
+// prompt token to prefill (its row gives the first new token).
+std::vector<int> match(const pkv_sched* s, const Request& r) {
+  std::vector<int> path;
+  if (r.tokens.empty()) return path;
+  int n = 0;
+  for (int j = 0; (j + 1) * PKV_BLOCK_SIZE < r.prompt; ++j) {
+    const int c = find_child(s, n, r.tokens.data() + j * PKV_BLOCK_SIZE);
+    if (c < 0) break;
+    path.push_back(c);
+    n = c;
+  }
+  return path;
+}
+
+// Drop the least recently used evictable node; its blocks go back to the
+// free list (no table lists them).
+void evict_one(pkv_sched* s) {
+  const int n = s->evictable.begin()->second;
+  s->evictable.erase(s->evictable.begin());
+  Node& x = s->nodes[n];
+  for (int32_t b : x.blocks) s->free_list[s->n_free++] = b;
+  Node& p = s->nodes[x.parent];
+  p.kids.erase(key_hash(x.key));
+  if (x.parent != 0 && p.ref == 0 && p.kids.empty()) s->evictable.insert({p.last_use, x.parent});
+  x = Node();
+  s->dead_nodes.push_back(n);
+  --s->cache_nodes;
+}
+
+// The request in slot si has just cached its whole prompt: publish its full
+// prompt blocks after the ones it already lists from the cache.  Stops at a
+// block another request has published meanwhile (this row keeps its own copy).
+void publish(pkv_sched* s, int si) {
+  Request& r = s->slot[si];
+  if (r.tokens.empty()) return;
+  int parent = r.path.empty() ? 0 : r.path.back();
+  for (int j = (int)r.path.size(); (j + 1) * PKV_BLOCK_SIZE <= r.prompt; ++j) {
+    const int32_t* t = r.tokens.data() + j * PKV_BLOCK_SIZE;
+    if (s->nodes[parent].kids.count(key_hash(t))) break;
+    int n;
+    if (!s->dead_nodes.empty()) {
+      n = s->dead_nodes.back();
+      s->dead_nodes.pop_back();
+    } else {
+      n = (int)s->nodes.size();
+      s->nodes.emplace_back();
+    }
+    Node& x = s->nodes[n];
+    x.live = true;
+    x.parent = parent;
+    std::copy(t, t + PKV_BLOCK_SIZE, x.key);
+    x.blocks.resize(s->n_layers);
+    for (int l = 0; l < s->n_layers; ++l) x.blocks[l] = s->table[s->entry(si, l, j)];
+    x.ref = 1;
+    x.last_use = ++s->tick;
+    Node& p = s->nodes[parent];
+    if (parent != 0 && p.ref == 0 && p.kids.empty()) s->evictable.erase({p.last_use, parent});
+    p.kids[key_hash(t)] = n;
+    r.path.push_back(n);
+    ++s->cache_nodes;
+    parent = n;
+  }
+}
+
 void release(pkv_sched* s, int si) {
   Request& r = s->slot[si];
+  const int shared = (int)r.path.size();       // entries listing cache blocks stay allocated
   for (int l = 0; l < s->n_layers; ++l)
     for (int j = 0; j < s->max_blocks; ++j) {
       const int64_t e = s->entry(si, l, j);
       if (s->table[e] == -1) continue;
-      s->free_list[s->n_free++] = s->table[e];
+      if (j >= shared) s->free_list[s->n_free++] = s->table[e];
       s->table[e] = -1;
       s->patch_off.push_back((int32_t)e);
       s->patch_val.push_back(-1);
     }
+  for (int n : r.path) {
+    touch(s, n);
+    add_ref(s, n, -1);
+  }
   s->reserved -= r.reserved;
   r = Request();
 }
@@ -171,6 +312,7 @@ extern "C" int pkv_sched_next(pkv_sched* s, pkv_sched_iter* it) {
   s->chunk_ids.clear();
   s->done_ids.clear();
   s->admitted_ids.clear();
+  s->admitted_cached.clear();
 
   // 1. release the slots finished last time
   for (int si = 0; si < s->num_slots; ++si)
@@ -178,22 +320,43 @@ extern "C" int pkv_sched_next(pkv_sched* s, pkv_sched_iter* it) {
       release(s, si);
       s->finished[si] = 0;
     }
-  // 2. admission (first come first served, no overtaking)
+  // 2. admission (first come first served, no overtaking): the prompt's
+  // longest cached prefix is listed, not prefilled; cache blocks nobody lists
+  // are evicted (least recently used first) when the free list is short
   while (!s->queue.empty()) {
     const Request& h = s->queue.front();
     int si = 0;
     while (si < s->num_slots && s->slot[si].id >= 0) ++si;
     if (si == s->num_slots) break;
-    const int need = blocks_needed(h.prompt + h.max_new - 1) * s->n_layers;
-    if (need > s->n_free - s->reserved) break;
-    Request r = h;
+    std::vector<int> path = match(s, h);
+    const int need = (blocks_needed(h.prompt + h.max_new - 1) - (int)path.size()) * s->n_layers;
+    for (int n : path) add_ref(s, n, 1);          // not evictable while admitting
+    while (need > s->n_free - s->reserved && !s->evictable.empty()) evict_one(s);
+    if (need > s->n_free - s->reserved) {
+      for (int n : path) add_ref(s, n, -1);
+      break;
+    }
+    Request r = std::move(s->queue.front());
     s->queue.pop_front();
     r.reserved = need;
     r.order = s->admissions++;
+    r.path = std::move(path);
+    r.cached = (int)r.path.size() * PKV_BLOCK_SIZE;
+    s->hit_tokens += r.cached;
+    for (int j = 0; j < (int)r.path.size(); ++j) {
+      touch(s, r.path[j]);
+      for (int l = 0; l < s->n_layers; ++l) {
+        const int64_t e = s->entry(si, l, j);
+        s->table[e] = s->nodes[r.path[j]].blocks[l];
+        s->patch_off.push_back((int32_t)e);
+        s->patch_val.push_back(s->table[e]);
+      }
+    }
     s->reserved += need;
-    s->slot[si] = r;
     s->admitted_ids.push_back(r.id);
     s->admitted_slots.push_back(si);
+    s->admitted_cached.push_back(r.cached);
+    s->slot[si] = std::move(r);
   }
   // active slots by admission order
   std::vector<int> order;
@@ -229,7 +392,10 @@ extern "C" int pkv_sched_next(pkv_sched* s, pkv_sched_iter* it) {
       s->token_pos.push_back(p);
     }
     r.cached = start + n;
-    if (r.cached == r.prompt) r.produced = 1;   // the prompt's last row gives the first token
+    if (r.cached == r.prompt) {
+      r.produced = 1;                           // the prompt's last row gives the first token
+      publish(s, si);
+    }
     s->chunk_slots.push_back(si);
     s->chunk_start.push_back(start);
     s->chunk_ids.push_back(r.id);
@@ -267,8 +433,18 @@ extern "C" int pkv_sched_next(pkv_sched* s, pkv_sched_iter* it) {
   it->n_admitted = (int)s->admitted_ids.size();
   it->admitted_ids = s->admitted_ids.data();
   it->admitted_slots = s->admitted_slots.data();
+  it->admitted_cached = s->admitted_cached.data();
   return PKV_OK;
 }
+
+namespace {
+void s_list_cache(const pkv_sched* s) {
+  auto& v = const_cast<pkv_sched*>(s)->cache_list;
+  v.clear();
+  for (size_t n = 1; n < s->nodes.size(); ++n)
+    if (s->nodes[n].live) v.insert(v.end(), s->nodes[n].blocks.begin(), s->nodes[n].blocks.end());
+}
+}  // namespace
 
 extern "C" int pkv_sched_info(const pkv_sched* s, pkv_sched_state* st) {
   if (!s || !st) return PKV_ERR_NULL;
@@ -285,6 +461,12 @@ extern "C" int pkv_sched_info(const pkv_sched* s, pkv_sched_state* st) {
   st->n_reserved = s->reserved;
   st->table = s->table.data();
   st->free_list = s->free_list.data();
+  s_list_cache(s);
+  st->n_cache_nodes = s->cache_nodes;
+  st->n_cache_blocks = (int)s->cache_list.size();
+  st->cache_blocks = s->cache_list.data();
+  st->n_evictable = (int)s->evictable.size();
+  st->cache_hit_tokens = s->hit_tokens;
   st->meta_elems = pkv_sched_meta_elems(s->num_slots, s->budget);
   return PKV_OK;
 }

@@ -22,21 +22,31 @@ pytestmark = pytest.mark.gpu
 N_Q, N_KV, D = 32, 8, 64
 
 
-def token_inputs(seed, rid, pos, layer):
-    """q [32,64], k [8,64], v [8,64] bf16 bits of token `pos` of request `rid`."""
-    rng = np.random.default_rng([seed, rid, pos, layer])
-    return W.randn_bf16(rng, (N_Q, D)), W.randn_bf16(rng, (N_KV, D)), W.randn_bf16(rng, (N_KV, D))
+def token_inputs(seed, rid, pos, layer, prompt=None):
+    """q [32,64], k [8,64], v [8,64] bf16 bits of token `pos` of request `rid`.
+    Inside a prompt given by its token ids, k and v depend only on the ids up
+    to `pos` (as a model's would), so requests that share a prefix share
+    them; q, and everything past the prompt, belong to the request alone."""
+    rq = np.random.default_rng([seed, 1, rid, pos, layer])
+    q = W.randn_bf16(rq, (N_Q, D))
+    if prompt is not None and pos < len(prompt):
+        h = 0
+        for t in prompt[:pos + 1]:
+            h = (h * 1000003 + int(t) + 1) % (1 << 61)
+        rkv = np.random.default_rng([seed, 2, h & 0xffffffff, h >> 32, pos, layer])
+    else:
+        rkv = np.random.default_rng([seed, 3, rid, pos, layer])
+    return q, W.randn_bf16(rkv, (N_KV, D)), W.randn_bf16(rkv, (N_KV, D))
 
 
-@pytest.mark.parametrize("seed,n_slots,n_layers,budget,num_blocks,prompts,news", [
-    (31, 4, 2, 40, 64, [17, 14, 60, 5, 33, 1, 90], [4, 6, 3, 8, 5, 2, 3]),
-    (32, 3, 1, 3, 24, [20, 7, 16], [5, 9, 2]),          # budget = slots: one-token chunks between decodes
-])
-def test_sched_iterations_match_oracle(gpu, seed, n_slots, n_layers, budget, num_blocks, prompts, news):
-    max_blocks = -(-max(p + n for p, n in zip(prompts, news)) // 16)
+def run_iterations(seed, n_slots, n_layers, budget, num_blocks, reqs):
+    """reqs: (prompt_len, max_new, token ids or None).  Runs the scheduler to
+    completion on the device, checking every iteration; returns the prompt
+    tokens taken from the prefix cache."""
+    max_blocks = -(-max(p + n for p, n, _ in reqs) // 16)
     s = pkv.Scheduler(n_slots, n_layers, max_blocks, num_blocks, budget)
-    for i, (p, n) in enumerate(zip(prompts, news)):
-        s.submit(i, p, n)
+    for i, (p, n, toks) in enumerate(reqs):
+        s.submit(i, p, n, tokens=toks)
     info = s.info()
     dev = torch.device("cuda")
     # unused pool rows hold NaN: masking must keep them out of every output
@@ -55,10 +65,24 @@ def test_sched_iterations_match_oracle(gpu, seed, n_slots, n_layers, budget, num
     slot_of = {}
     done = set()
     rows_checked = 0
+    reused = 0
+
+    def inputs(r, p, l):
+        return token_inputs(seed, r, p, l, reqs[r][2])
+
     for _ in range(400):
         it = s.next()
-        for r, sl in zip(it["admitted_ids"].tolist(), it["admitted_slots"].tolist()):
+        for r, sl, c in zip(it["admitted_ids"].tolist(), it["admitted_slots"].tolist(),
+                            it["admitted_cached"].tolist()):
             slot_of[r] = sl
+            reused += c
+            # the cached prefix: the request's own tokens, which the cache must hold
+            for l in range(n_layers):
+                K, V = hist.setdefault((r, l), ([], []))
+                for p in range(c):
+                    _, kk, vv = inputs(r, p, l)
+                    K.append(rope.apply(kk[None], [p])[0])
+                    V.append(vv)
         if it["n_tokens"] == 0 and len(it["patch_off"]) == 0:
             break
         # the iteration's rows: (request, position)
@@ -67,7 +91,7 @@ def test_sched_iterations_match_oracle(gpu, seed, n_slots, n_layers, budget, num
         for c, r in enumerate(it["chunk_ids"].tolist()):
             rows += [(r, int(p)) for p in it["token_pos"][cu[c]:cu[c + 1]]]
         T = len(rows)
-        host = [[token_inputs(seed, r, p, l) for (r, p) in rows] for l in range(n_layers)]
+        host = [[inputs(r, p, l) for (r, p) in rows] for l in range(n_layers)]
         for l in range(n_layers):
             if T:
                 q[l][:T] = dev_bf16(np.stack([h[0] for h in host[l]])).view(torch.int16)
@@ -104,6 +128,34 @@ def test_sched_iterations_match_oracle(gpu, seed, n_slots, n_layers, budget, num
                 np.testing.assert_array_equal(bits(vd), np.stack(hist[(r, l)][1]))
                 assert ulp_diff(bits(kd), np.stack(hist[(r, l)][0])).max() <= 1
         done |= set(it["done_ids"].tolist())
-    assert len(done) == len(prompts)
-    assert rows_checked == n_layers * sum(p + n - 1 for p, n in zip(prompts, news))
-    assert s.info()["n_free"] == num_blocks
+    assert len(done) == len(reqs)
+    assert rows_checked + n_layers * reused == n_layers * sum(p + n - 1 for p, n, _ in reqs)
+    st = s.info()
+    assert st["n_free"] + len(st["cache_blocks"]) == num_blocks
+    return reused
+
+
+@pytest.mark.parametrize("seed,n_slots,n_layers,budget,num_blocks,prompts,news", [
+    (31, 4, 2, 40, 64, [17, 14, 60, 5, 33, 1, 90], [4, 6, 3, 8, 5, 2, 3]),
+    (32, 3, 1, 3, 24, [20, 7, 16], [5, 9, 2]),          # budget = slots: one-token chunks between decodes
+])
+def test_sched_iterations_match_oracle(gpu, seed, n_slots, n_layers, budget, num_blocks, prompts, news):
+    run_iterations(seed, n_slots, n_layers, budget, num_blocks, [(p, n, None) for p, n in zip(prompts, news)])
+
+
+def test_sched_prefix_cache_matches_oracle(gpu):
+    """Requests over two shared system prompts (plus one without token ids):
+    later requests list the cached prefix blocks instead of prefilling them,
+    and a small pool makes admissions evict cached blocks."""
+    rng = np.random.default_rng(33)
+    sysa = rng.integers(0, 5000, size=70).astype(np.int32)
+    sysb = rng.integers(0, 5000, size=35).astype(np.int32)
+    reqs = []
+    for i, (base, cut, extra, new) in enumerate([(sysa, 70, 9, 3), (sysa, 70, 20, 2), (sysb, 35, 0, 4),
+                                                 (sysa, 48, 5, 2), (sysb, 35, 30, 3), (None, 0, 40, 2),
+                                                 (sysa, 70, 1, 5), (sysb, 20, 12, 2)]):
+        toks = rng.integers(0, 5000, size=extra).astype(np.int32) if base is None else \
+            np.concatenate([base[:cut], rng.integers(0, 5000, size=extra)]).astype(np.int32)
+        reqs.append((len(toks), new, None if base is None else toks))
+    reused = run_iterations(34, 2, 2, 48, 16, reqs)
+    assert reused >= 64

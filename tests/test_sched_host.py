@@ -191,3 +191,125 @@ def test_argument_errors():
     assert e.value.status == pkv._abi.PKV_ERR_CAPACITY
     assert pkv.load().pkv_sched_next(None, None) == pkv._abi.PKV_ERR_NULL
     assert pkv.load().pkv_sched_meta_elems(4, 16) == 4 + 6 * 16 + 1
+
+
+# ------------------------------------------------------------ prefix cache --
+
+def _content(tokens, p, layer):
+    """Identity of the K/V of token p after tokens[:p] (what a model's cache
+    holds there): equal exactly when the prefixes up to p are equal."""
+    return hash((tuple(int(t) for t in tokens[:p + 1]), layer))
+
+
+def run_cache_walk(seed, n_slots, n_layers, budget, num_blocks, n_req, max_new=6):
+    rng = np.random.default_rng(seed)
+    systems = [rng.integers(0, 1000, size=int(n)).astype(np.int32) for n in (40, 100, 257)]
+    reqs = []
+    for i in range(n_req):
+        if rng.random() < 0.15:
+            toks = rng.integers(0, 1000, size=int(rng.integers(1, 60))).astype(np.int32)
+            use_ids = False                          # a request that takes no part in caching
+        else:
+            sysp = systems[int(rng.integers(0, 3))]
+            cut = int(rng.integers(1, len(sysp) + 1))
+            toks = np.concatenate([sysp[:cut], rng.integers(0, 1000, size=int(rng.integers(0, 40)))]).astype(np.int32)
+            use_ids = True
+        reqs.append((toks, int(rng.integers(1, max_new + 1)), use_ids))
+    max_blocks = -(-max(len(t) + n for t, n, _ in reqs) // 16)
+    s = pkv.Scheduler(n_slots, n_layers, max_blocks, num_blocks, budget)
+    for i, (t, n, u) in enumerate(reqs):
+        s.submit(i, len(t), n, tokens=t if u else None)
+    pool = {}                                        # (block, row) -> content id
+    slot_of, cached, done, hits = {}, {}, set(), 0
+    mirror = np.full((n_slots, n_layers, max_blocks), -1, np.int32)
+    for _ in range(10000):
+        it = s.next()
+        for o, v in zip(it["patch_off"].tolist(), it["patch_val"].tolist()):
+            mirror.ravel()[o] = v
+        for r in list(slot_of):
+            if r in done:
+                del slot_of[r]
+        for r, sl, c in zip(it["admitted_ids"].tolist(), it["admitted_slots"].tolist(),
+                            it["admitted_cached"].tolist()):
+            slot_of[r], cached[r] = sl, c
+            hits += c
+            assert c % 16 == 0 and c < len(reqs[r][0])
+            if not reqs[r][2]:
+                assert c == 0
+        if it["n_tokens"] == 0 and len(it["patch_off"]) == 0:
+            break
+        # writes of this iteration: decode rows then prompt tokens
+        writes = [(r, int(n) - 1) for r, n in zip(it["decode_ids"].tolist(), it["decode_lens"].tolist())]
+        cu = it["cu_chunk"]
+        for c, (r, st) in enumerate(zip(it["chunk_ids"].tolist(), it["chunk_start"].tolist())):
+            assert st == cached[r]                   # a prefill starts after the cached prefix
+            writes += [(r, int(p)) for p in it["token_pos"][cu[c]:cu[c + 1]]]
+        for r, p in writes:
+            toks = reqs[r][0]
+            for l in range(n_layers):
+                blk = int(mirror[slot_of[r], l, p // 16])
+                assert blk >= 0
+                cid = _content(toks, p, l) if p < len(toks) else hash(("gen", r, p, l))
+                pool[(blk, p % 16)] = cid
+            cached[r] = max(cached[r], p + 1)
+        done |= set(it["done_ids"].tolist())
+        info = s.info()
+        np.testing.assert_array_equal(info["table"], mirror)
+        # every live row reads its own prefix's K/V, shared blocks included
+        for r, sl in slot_of.items():
+            toks = reqs[r][0]
+            for l in range(n_layers):
+                for p in range(cached[r]):
+                    want = _content(toks, p, l) if p < len(toks) else hash(("gen", r, p, l))
+                    assert pool.get((int(mirror[sl, l, p // 16]), p % 16)) == want, (r, l, p)
+        # every block is free, or listed and/or held by the cache; a block
+        # listed twice is a cache block
+        listed = mirror[mirror >= 0]
+        cache = set(info["cache_blocks"].tolist())
+        free = set(info["free_list"].tolist())
+        assert len(free) == len(info["free_list"]) and not (free & (set(listed.tolist()) | cache))
+        assert free | set(listed.tolist()) | cache == set(range(num_blocks))
+        vals, counts = np.unique(listed, return_counts=True)
+        assert set(vals[counts > 1].tolist()) <= cache
+        assert len(info["cache_blocks"]) == n_layers * info["n_cache_nodes"] == len(cache)
+    info = s.info()
+    assert len(done) == n_req and info["n_active"] == 0 and (info["table"] == -1).all()
+    assert info["n_free"] + len(info["cache_blocks"]) == num_blocks
+    assert info["cache_hit_tokens"] == hits
+    return hits, info
+
+
+@pytest.mark.parametrize("seed,n_slots,n_layers,budget,num_blocks,n_req", [
+    (21, 4, 2, 64, 400, 30),        # roomy pool: the cache only grows
+    (22, 6, 1, 40, 30, 40),         # tight pool: admissions evict cached blocks (25 nodes)
+    (23, 3, 3, 3, 150, 15),         # budget = slots: one-token chunks
+])
+def test_prefix_cache_walk(seed, n_slots, n_layers, budget, num_blocks, n_req):
+    hits, info = run_cache_walk(seed, n_slots, n_layers, budget, num_blocks, n_req)
+    assert hits > 0
+
+
+def test_prefix_cache_reuse_and_eviction():
+    s = pkv.Scheduler(2, 1, 12, 12, 64)
+    a = np.arange(50, dtype=np.int32)               # 3 full blocks + 2 tokens
+    s.submit(0, 50, 1, tokens=a)
+    it = s.next()                                   # prefilled whole: 3 blocks published
+    assert it["admitted_cached"].tolist() == [0] and it["done_ids"].tolist() == [0]
+    assert s.info()["n_cache_nodes"] == 3
+    s.submit(1, 40, 2, tokens=a[:40])               # 2 full blocks cached, 8 tokens to prefill
+    s.submit(2, 48, 1, tokens=a[:48])               # 3 full blocks, but one token must be prefilled: 2
+    s.submit(3, 20, 1, tokens=np.arange(100, 120, dtype=np.int32))
+    it = s.next()
+    assert it["admitted_ids"].tolist() == [1, 2] and it["admitted_cached"].tolist() == [32, 32]
+    assert it["chunk_start"].tolist() == [32, 32]
+    t = s.info()["table"]
+    assert (t[0, 0, :2] == t[1, 0, :2]).all()        # both rows list the cached blocks
+    # pool of 12: 3 cached + request 1's 1 + request 2's 1; request 3 needs 2 blocks
+    for _ in range(5):
+        it = s.next()
+    info = s.info()
+    assert info["n_active"] == 0 and info["n_free"] + len(info["cache_blocks"]) == 12
+    # a request needing almost the whole pool evicts every unused cached block
+    s.submit(4, 16 * 12 - 5, 1)
+    it = s.next()
+    assert it["admitted_ids"].tolist() == [4] and s.info()["n_cache_nodes"] == 0
