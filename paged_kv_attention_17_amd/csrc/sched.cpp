@@ -116,7 +116,7 @@ struct pkv_sched {
   int64_t tick = 0;
   int cache_nodes = 0;                 // live nodes besides the root
   int64_t hit_tokens = 0;              // prompt tokens taken from the cache
-  std::vector<int32_t> cache_list;     // pkv_sched_info's list of the cache's blocks
+  mutable std::vector<int32_t> cache_list;   // pkv_sched_info's list of the cache's blocks
 
   int64_t entry(int s, int l, int j) const { return ((int64_t)s * n_layers + l) * max_blocks + j; }
 };
@@ -439,7 +439,7 @@ extern "C" int pkv_sched_next(pkv_sched* s, pkv_sched_iter* it) {
 
 namespace {
 void s_list_cache(const pkv_sched* s) {
-  auto& v = const_cast<pkv_sched*>(s)->cache_list;
+  auto& v = s->cache_list;
   v.clear();
   for (size_t n = 1; n < s->nodes.size(); ++n)
     if (s->nodes[n].live) v.insert(v.end(), s->nodes[n].blocks.begin(), s->nodes[n].blocks.end());
