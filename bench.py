@@ -251,11 +251,14 @@ def prefill_leg(torch, np, pkv, W, iters: int = 5):
                          "kernel": "pkv_paged_attn_prefill (prefill_kernel<4>)"}}
 
 
-def long_context_leg(torch, np, pkv, W, iters: int = 10):
+def long_context_leg(torch, np, pkv, W, iters: int = 10, cpu_seconds: float = 0.0):
     """Split-context decode at B=256 with 8,192 tokens each (4.29 GB of K/V,
     one layer, more than 16x the last-level cache): the streaming kernel and
     its merge (host lengths given) and the per-partition kernels (lengths on
-    the device only), each timed with HIP events around back-to-back calls."""
+    the device only), each timed with HIP events around back-to-back calls.
+    With cpu_seconds > 0 the float64 oracle is also timed on sampled whole
+    sequences of the same call (one BLAS thread) and its rate extrapolated to
+    the call."""
     w = W.config4(fill_pool=False)
     kp = torch.empty((w.num_blocks, 16, 8, 64), dtype=torch.bfloat16, device="cuda").normal_()
     vp = torch.empty_like(kp).uniform_(-1, 1)
@@ -284,6 +287,30 @@ def long_context_leg(torch, np, pkv, W, iters: int = 10):
         t = e0.elapsed_time(e1) / 1e3 / iters
         res[name] = {"us_per_call": round(t * 1e6, 1), "GBps": round(nbytes / t / 1e9, 1),
                      "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+    if cpu_seconds > 0:
+        from threadpoolctl import threadpool_limits
+        from oracle import attention
+        rng = np.random.default_rng(4)
+        q_host = w.q_new[0]
+        t_cpu, n_seq, done = 0.0, 0, 0
+        with threadpool_limits(limits=1):
+            while t_cpu < cpu_seconds and n_seq < 64:
+                b = int(rng.integers(B))
+                n = int(ctx[b])
+                ids = torch.from_numpy(w.block_table[b, 0, :-(-n // 16)].astype(np.int64)).cuda()
+                kh = kp.index_select(0, ids).view(torch.int16).cpu().numpy().view(np.uint16)
+                vh = vp.index_select(0, ids).view(torch.int16).cpu().numpy().view(np.uint16)
+                bt1 = np.arange(len(kh), dtype=np.int32)[None]
+                t0 = time.perf_counter()
+                attention.decode(q_host[b:b + 1], kh, vh, bt1, np.zeros(1, np.int32), np.array([n], np.int32),
+                                 w.scale)
+                t_cpu += time.perf_counter() - t0
+                done += n * KV_BYTES_PER_TOKEN
+                n_seq += 1
+        res["cpu_oracle"] = {"value": round(done / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                             "sample": f"{n_seq} whole sequences of the call (8,192 tokens each), float64 numpy "
+                                       f"oracle, BLAS limited to 1 thread, {t_cpu:.1f} s of CPU time; "
+                                       f"extrapolated call time {nbytes / (done / t_cpu):.1f} s"}
     del kp, vp
     torch.cuda.empty_cache()
     return res
@@ -559,10 +586,12 @@ def main():
     log(f"prefill: {pre['us_per_pass']:.1f} us per pass over {pre['calls']} chunk calls, "
         f"{pre['roofline']['achieved']:.1f} TFLOP/s = {pre['roofline']['frac']:.2%} of bf16 MFMA peak")
 
-    lc = long_context_leg(torch, np, pkv, W)
+    lc = long_context_leg(torch, np, pkv, W, cpu_seconds=0.0 if args.no_cpu_baseline else 3.0)
     log(f"long context (B=256 x 8192): stream {lc['stream']['us_per_call']:.1f} us = {lc['stream']['GBps']:.0f} GB/s "
         f"({lc['stream']['frac']:.1%}); per-partition {lc['partitions']['us_per_call']:.1f} us = "
         f"{lc['partitions']['GBps']:.0f} GB/s ({lc['partitions']['frac']:.1%})")
+    if "cpu_oracle" in lc:
+        log(f"long context, cpu oracle: {lc['cpu_oracle']['value']:.3f} GB/s ({lc['cpu_oracle']['sample']})")
 
     ps = prefix_sharing_leg(torch, np, pkv, W)
     log(f"prefix sharing (B=64 over 4 shared 2048-token prompts): {ps['shared']['us_per_layer']:.1f} us/layer "
