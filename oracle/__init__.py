@@ -15,10 +15,13 @@ Modules:
   paging     -- append, gather and block-allocation validity through a block table
   attention  -- single-query decode attention and causal prefill attention,
                 two-pass softmax in float64
+  layer      -- the rest of a Llama decode layer around the attention:
+                RMSNorm, projections, gated SiLU MLP, residual adds
 
 Pins (tests/test_oracle_*.py) tie every function to something other than
 itself: library routines (torch's float64 scaled_dot_product_attention,
-transformers' Llama-3 RoPE parameters and rotate-half), closed forms,
+transformers' Llama-3 RoPE parameters and rotate-half, transformers' Llama
+RMSNorm, MLP and decoder layer), closed forms,
 invariants, brute force and the constants the pages print.
 """
-from . import bf16, rope, paging, attention  # noqa: F401
+from . import bf16, rope, paging, attention, layer  # noqa: F401
