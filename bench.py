@@ -489,6 +489,59 @@ def serving_leg(torch, np, pkv, W, n_req: int = 128, n_slots: int = 64, budget: 
             "shared_prompts": shared}
 
 
+def decode_layer_leg(torch, np, pkv, eng, ctx_now, stream, iters: int = 5):
+    """Whole Llama-3.2-1B decode layers (pkv_decode_layer: RMSNorm, rocBLAS
+    projections, the fused paged attention, the gated MLP) for the B=64 rows
+    of the main workload, 16 layers, synthetic bf16 weights ~ N(0, 1/fan_in)
+    on the device (121 MB per layer).  Each layer's attention re-writes the
+    last token in place, like the attention timing.  HIP events around each
+    16-layer pass."""
+    HID, INTER, NQ, NKV = 2048, 8192, 32, 8
+    L = eng.n_layers
+    B = len(ctx_now)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1708)
+
+    def mat(n, k):
+        return (torch.randn((n, k), generator=g, device="cuda") * (1.0 / math.sqrt(k))).to(torch.bfloat16)
+
+    weights = []
+    for _ in range(L):
+        weights.append({"attn_norm": torch.ones(HID, dtype=torch.bfloat16, device="cuda"),
+                        "wq": mat(NQ * 64, HID), "wk": mat(NKV * 64, HID), "wv": mat(NKV * 64, HID),
+                        "wo": mat(HID, NQ * 64), "mlp_norm": torch.ones(HID, dtype=torch.bfloat16, device="cuda"),
+                        "w_gate_up": mat(2 * INTER, HID), "w_down": mat(HID, INTER)})
+    wbytes = sum(t.numel() * 2 for t in weights[0].values())
+    h = torch.randn((B, HID), generator=g, device="cuda").to(torch.bfloat16)
+    scratch = torch.empty(pkv.pkv_decode_layer_scratch_elems(B, HID, INTER, NQ, NKV), dtype=torch.bfloat16,
+                          device="cuda")
+
+    def one_pass():
+        for layer in range(L):
+            pkv.pkv_decode_layer(h, weights[layer], scratch, eng.k_pool, eng.v_pool, eng.bt_dev[:, layer, :], None,
+                                 eng.ctx_dev, eng.max_context_len, eng.cos_sin, eng.scale, eng.workspace,
+                                 row_lens_host=ctx_now, stream=stream)
+
+    one_pass()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        one_pass()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    t = float(np.median(times))
+    del weights
+    torch.cuda.empty_cache()
+    return {"workload": f"Llama-3.2-1B decode step, B={B}, {L} layers, hidden 2048, intermediate 8192, synthetic "
+                        "bf16 weights, the main workload's paged cache (ctx U[512,4096])",
+            "ms_per_step": round(t * 1e3, 4), "us_per_layer": round(t / L * 1e6, 2),
+            "tokens_per_s": round(B / t, 1), "weight_bytes_per_layer": wbytes,
+            "kv_bytes_per_layer": int(ctx_now.sum()) * KV_BYTES_PER_TOKEN}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -578,6 +631,15 @@ def main():
         f"p10 {np.percentile(durs, 10) * 1e6:.2f}, "
         f"p90 {np.percentile(durs, 90) * 1e6:.2f}), {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of peak")
 
+    dl = decode_layer_leg(torch, np, pkv, eng, ctx_now, stream)
+    bytes_layer = dl["weight_bytes_per_layer"] + dl["kv_bytes_per_layer"]
+    dl["attention_us_per_layer"] = round(t_attn * 1e6, 2)
+    dl["rest_us_per_layer"] = round(dl["us_per_layer"] - t_attn * 1e6, 2)
+    dl["GBps"] = round(bytes_layer / (dl["us_per_layer"] * 1e-6) / 1e9, 1)
+    log(f"decode layer (B={w.batch}, weights + paged attention): {dl['us_per_layer']:.1f} us/layer "
+        f"({dl['attention_us_per_layer']:.1f} us attention, {dl['rest_us_per_layer']:.1f} us norms, projections "
+        f"and MLP), {dl['tokens_per_s']:.0f} tokens/s, {dl['GBps']:.0f} GB/s of weights + K/V")
+
     unf = unfused_layer_us(torch, np, pkv, eng, q, k, v, out, stream)
     log(f"unfused layer: rope {unf['rope']:.2f} us, append {unf['append']:.2f} us, "
         f"attention {unf['attention']:.2f} us (fused call: {t_attn * 1e6:.2f} us)")
@@ -656,6 +718,7 @@ def main():
         "long_context": lc,
         "prefix_sharing": ps,
         "serving": sv,
+        "decode_layer": dl,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -498,6 +498,69 @@ int pkv_sched_run(const pkv_sched* sched, const pkv_sched_iter* iter, pkv_bf16* 
                   const float* cos_sin, int max_pos, float scale, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * The rest of a Llama decode layer.  Source: the opening paragraph of "An
+ * Inference Engine in 1,500 Lines of CUDA: The Map" (Llama 3.2 1B; attention,
+ * RMSNorm and softmax in the engine's own kernels), the Korean page's "What
+ * is in the box" table (rmsNormKernel), the 2048-wide buf_2048_* buffers of
+ * "A function with 51 parameters" and the chapter-4 title (projections on the
+ * vendor GEMM).  Formulas: the public Llama ones.  All tensors bf16,
+ * row-major; weights in the Hugging Face layout [out_features][in_features].
+ * ------------------------------------------------------------------------ */
+
+/* out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * weight, float32 math, one
+ * nearest-even rounding per output.  dim % 8 == 0. */
+int pkv_rmsnorm(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weight, int rows, int dim, float eps,
+                void* stream);
+
+/* act[r][i] = silu(g) * u with g = gate_up[r][i], u = gate_up[r][intermediate + i]
+ * (gate_up [rows][2 * intermediate]), silu(g) = g / (1 + e^-g), float32 math.
+ * intermediate % 8 == 0. */
+int pkv_silu_mul(pkv_bf16* act, const pkv_bf16* gate_up, int rows, int intermediate, void* stream);
+
+/* out[rows][out_features] = x[rows][in_features] weight^T (+ out when
+ * accumulate != 0), float32 sums, one rounding per output: a plain rocBLAS
+ * bf16 GEMM (the library keeps one rocBLAS handle per device for the
+ * process; concurrent calls on one device from several host threads must be
+ * serialised by the caller). */
+int pkv_linear(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weight, int rows, int out_features,
+               int in_features, int accumulate, void* stream);
+
+typedef struct {
+  const pkv_bf16* attn_norm;    /* [hidden] */
+  const pkv_bf16* wq;           /* [n_q_heads * 64][hidden] */
+  const pkv_bf16* wk;           /* [n_kv_heads * 64][hidden] */
+  const pkv_bf16* wv;           /* [n_kv_heads * 64][hidden] */
+  const pkv_bf16* wo;           /* [hidden][n_q_heads * 64] */
+  const pkv_bf16* mlp_norm;     /* [hidden] */
+  const pkv_bf16* w_gate_up;    /* [2 * intermediate][hidden]: gate rows, then up rows */
+  const pkv_bf16* w_down;       /* [hidden][intermediate] */
+} pkv_layer_weights;
+
+/* bf16 elements of pkv_decode_layer's scratch: a | q | k | v | o | m |
+ * gate_up | act, each [batch][width] (widths hidden, n_q*64, n_kv*64, n_kv*64,
+ * n_q*64, hidden, 2*intermediate, intermediate), in that order; 0 for
+ * invalid sizes. */
+size_t pkv_decode_layer_scratch_elems(int batch, int hidden, int intermediate, int n_q_heads, int n_kv_heads);
+
+/* One layer's decode step for `batch` rows, in place on the residual stream
+ * h [batch][hidden]:
+ *   a = rmsnorm(h, attn_norm);  q, k, v = a Wq^T, a Wk^T, a Wv^T;
+ *   o = pkv_paged_decode_fused(q, k, v, ...)  (RoPE, append, attention; the
+ *       cache arguments as there, head_dim 64);
+ *   h += o Wo^T;  m = rmsnorm(h, mlp_norm);  gate_up = m Wgu^T;
+ *   act = silu(gate) * up;  h += act Wd^T.
+ * scratch: caller-owned device bf16, >= pkv_decode_layer_scratch_elems(...)
+ * elements, any contents (the intermediates are left there).  All launches
+ * go to `stream`. */
+int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* weights, int hidden, int intermediate,
+                     pkv_bf16* scratch, size_t scratch_elems, pkv_bf16* k_pool, pkv_bf16* v_pool,
+                     int num_blocks, const int32_t* block_table, int64_t bt_row_stride, int num_slots,
+                     int max_blocks_per_seq, const int32_t* slot_ids, const int32_t* context_lens,
+                     const int32_t* row_lens_host, int batch, int max_context_len, int n_q_heads,
+                     int n_kv_heads, const float* cos_sin, int max_pos, float scale, float eps,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -80,8 +80,9 @@ def decode_layer(h, W, hist_k, hist_v, positions, n_q, n_kv, scale=0.125, eps=EP
       [n_kv*64][D], wo [D][n_q*64], mlp_norm [D], wg and wu [I][D], wd [D][I].
     hist_k[b], hist_v[b]: float64 [positions[b]][n_kv][64], row b's cached
       (rotated) keys and values of tokens 0 .. positions[b] - 1.
-    Returns dict: h (after the layer) and the intermediate buffers a, q_rot,
-    k_rot, v, o, h_mid (after the attention residual), m, act.
+    Returns dict: h (after the layer) and the intermediate buffers a, q, k
+    (before RoPE), q_rot, k_rot, v, o, h_mid (after the attention residual),
+    m, g, u (gate and up projections), act.
     """
     rnd = rnd or _ident
     h = np.asarray(h, dtype=np.float64)
@@ -107,7 +108,7 @@ def decode_layer(h, W, hist_k, hist_v, positions, n_q, n_kv, scale=0.125, eps=EP
     u = rnd(linear(m, W["wu"]))
     act = rnd(silu(g) * u)
     h_out = rnd(h_mid + linear(act, W["wd"]))
-    return dict(h=h_out, a=a, q_rot=q_rot, k_rot=k_rot, v=v, o=o, h_mid=h_mid, m=m, act=act)
+    return dict(h=h_out, a=a, q=q, k=k, q_rot=q_rot, k_rot=k_rot, v=v, o=o, h_mid=h_mid, m=m, g=g, u=u, act=act)
 
 
 def init_scale(fan_in):

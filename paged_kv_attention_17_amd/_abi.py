@@ -69,6 +69,12 @@ SIGNATURES = {
     "pkv_sched_next": (_i, [_p, _p]),
     "pkv_sched_info": (_i, [_p, _p]),
     "pkv_sched_meta_elems": (_i64, [_i, _i]),
+    "pkv_rmsnorm": (_i, [_p, _p, _p, _i, _i, _f, _p]),
+    "pkv_silu_mul": (_i, [_p, _p, _i, _i, _p]),
+    "pkv_linear": (_i, [_p, _p, _p, _i, _i, _i, _i, _p]),
+    "pkv_decode_layer_scratch_elems": (_sz, [_i, _i, _i, _i, _i]),
+    "pkv_decode_layer": (_i, [_p, _p, _i, _i, _p, _sz, _p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _i, _i, _i, _p,
+                              _i, _f, _f, _p, _sz, _p]),
     "pkv_sched_run": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _p, _i, _f, _p, _sz, _p]),
 }
 
@@ -714,3 +720,83 @@ class Scheduler:
             q[0].shape[1], k[0].shape[1], q[0].shape[2], _dev_ptr(cos_sin, "cos_sin", (torch.float32,)),
             cos_sin.shape[0], float(scale), _dev_ptr(workspace, "workspace"),
             workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ------------------------------------------------------- rest of the layer --
+
+def pkv_rmsnorm(out, x, weight, eps=1e-5, stream=None):
+    """out[r] = rmsnorm(x[r]) * weight; x/out bf16 [rows, dim], weight [dim]."""
+    for t, n in ((out, "out"), (x, "x"), (weight, "weight")):
+        _contig(t, n)
+    rows, dim = x.shape
+    if tuple(out.shape) != (rows, dim) or weight.numel() != dim:
+        raise ValueError("out, x and weight disagree")
+    bt = _bf16_types()
+    _check("pkv_rmsnorm", load().pkv_rmsnorm(_dev_ptr(out, "out", bt), _dev_ptr(x, "x", bt),
+                                             _dev_ptr(weight, "weight", bt), rows, dim, float(eps), _stream(stream)))
+
+
+def pkv_silu_mul(act, gate_up, stream=None):
+    """act[r] = silu(gate_up[r, :I]) * gate_up[r, I:]; act [rows, I], gate_up [rows, 2I]."""
+    _contig(act, "act")
+    _contig(gate_up, "gate_up")
+    rows, inter = act.shape
+    if tuple(gate_up.shape) != (rows, 2 * inter):
+        raise ValueError("gate_up must be [rows, 2 * intermediate]")
+    bt = _bf16_types()
+    _check("pkv_silu_mul", load().pkv_silu_mul(_dev_ptr(act, "act", bt), _dev_ptr(gate_up, "gate_up", bt), rows,
+                                               inter, _stream(stream)))
+
+
+def pkv_linear(out, x, weight, accumulate=False, stream=None):
+    """out = x weight^T (+ out when accumulate); x [rows, in], weight [out, in]."""
+    for t, n in ((out, "out"), (x, "x"), (weight, "weight")):
+        _contig(t, n)
+    rows, k = x.shape
+    n_out = weight.shape[0]
+    if weight.shape[1] != k or tuple(out.shape) != (rows, n_out):
+        raise ValueError("out, x and weight disagree")
+    bt = _bf16_types()
+    _check("pkv_linear", load().pkv_linear(_dev_ptr(out, "out", bt), _dev_ptr(x, "x", bt),
+                                           _dev_ptr(weight, "weight", bt), rows, n_out, k, 1 if accumulate else 0,
+                                           _stream(stream)))
+
+
+class LayerWeights(C.Structure):
+    """pkv_layer_weights (include/pagedkv.h)."""
+    _fields_ = [(n, _p) for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate_up", "w_down")]
+
+
+def pkv_decode_layer_scratch_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads):
+    return load().pkv_decode_layer_scratch_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads)
+
+
+def pkv_decode_layer(h, weights, scratch, k_pool, v_pool, block_table, slot_ids, context_lens, max_context_len,
+                     cos_sin, scale, workspace, row_lens_host=None, eps=1e-5, n_q_heads=32, stream=None):
+    """One layer's decode step in place on h [B, hidden] (pkv_decode_layer).
+    weights: dict of device bf16 tensors attn_norm, wq, wk, wv, wo, mlp_norm,
+    w_gate_up, w_down; scratch: device bf16 with at least
+    pkv_decode_layer_scratch_elems(...) elements (intermediates left there)."""
+    import torch
+    bt16 = _bf16_types()
+    for t, n in ((h, "h"), (scratch, "scratch"), (k_pool, "k_pool"), (v_pool, "v_pool"), (cos_sin, "cos_sin"),
+                 (workspace, "workspace")):
+        _contig(t, n)
+    B, hidden = h.shape
+    inter = weights["w_down"].shape[1]
+    n_kv = k_pool.shape[2]
+    lw = LayerWeights()
+    for name in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate_up", "w_down"):
+        _contig(weights[name], name)
+        setattr(lw, name, _dev_ptr(weights[name], name, bt16))
+    if weights["wq"].shape != (n_q_heads * 64, hidden) or weights["w_gate_up"].shape != (2 * inter, hidden):
+        raise ValueError("weight shapes do not match hidden / heads / intermediate")
+    ptr, stride, rows, mb = _table(block_table)
+    rl, rl_ptr = _row_lens(row_lens_host, B)
+    _check("pkv_decode_layer", load().pkv_decode_layer(
+        _dev_ptr(h, "h", bt16), C.byref(lw), hidden, inter, _dev_ptr(scratch, "scratch", bt16), scratch.numel(),
+        _dev_ptr(k_pool, "k_pool", bt16), _dev_ptr(v_pool, "v_pool", bt16), k_pool.shape[0], ptr, stride, rows, mb,
+        _dev_ptr(slot_ids, "slot_ids", (torch.int32,)), _dev_ptr(context_lens, "context_lens", (torch.int32,)),
+        rl_ptr, B, int(max_context_len), n_q_heads, n_kv, _dev_ptr(cos_sin, "cos_sin", (torch.float32,)),
+        cos_sin.shape[0], float(scale), float(eps), _dev_ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -68,7 +68,8 @@ def build(verbose: bool = False) -> str:
                 print(r.stdout, r.stderr, file=sys.stderr)
     objs = [j[-1] for j in jobs]
     tmp = LIB + ".tmp"
-    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    # rocBLAS serves the layer's plain projections (pkv_linear)
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-lrocblas", "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

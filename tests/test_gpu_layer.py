@@ -1,0 +1,201 @@
+"""GPU parity for the rest of the Llama decode layer: RMSNorm, the gated
+SiLU product, the rocBLAS projections and pkv_decode_layer (Llama-3.2-1B
+shapes: hidden 2048, 32 / 8 heads of 64, intermediate 8192, synthetic bf16
+weights ~ N(0, 1/fan_in)) against the float64 oracle with bf16 rounding where
+the engine keeps a buffer.
+
+Tolerances, from the arithmetic.  Every buffer is one nearest-even rounding
+of a float32 (GPU) or float64 (oracle) value.  RMSNorm and the SiLU product
+have no cancellation: the two pre-rounding values agree to a few float32
+ulps, so the outputs agree within 1 bf16 ulp.  A projection's float32 sum of
+K products, in whatever order the library takes them, is within the standard
+a-priori bound K 2^-24 sum_k |x_k w_k| of the exact sum; after rounding the
+output is within that bound plus 1 ulp of the oracle (a near-cancelling sum
+has a tiny value whose ulp is below the float32 error of its large terms).
+Through the whole layer each stage's input already differs from the
+oracle's (the attention output by up to the attention bar, max-abs 2e-2 and
+mean-abs 2e-3, which it is held to), so each stage is held to what its
+measured input difference allows: a projection to |dx| |W|^T plus the
+float32 bound plus 1 ulp, RMSNorm and silu(g) * u to their first-order
+(mean-value) sensitivity to their inputs' differences plus 1 ulp.  The
+layer leaves its intermediates in the scratch buffer, so every stage but
+the attention residual (bounded through the output projection) is checked
+on the kernels' own inputs."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_17_amd as pkv
+from paged_kv_attention_17_amd import workloads as W
+from oracle import bf16, layer, paging
+
+from gpu_util import ATOL_MAX, ATOL_MEAN, bits, dev_bf16, dev_i32, f64, ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+HID, NQ, NKV, INTER = 2048, 32, 8, 8192
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 values at |x| (normal range)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 2.0 ** -126)))
+    return 2.0 ** (np.maximum(e, -126) - 7)
+
+
+def assert_within(got_bits, ref, bound, what):
+    """|got - ref| <= bound plus the two sides' roundings (half an ulp each,
+    at most one ulp of the larger of the two)."""
+    got = f64(got_bits)
+    err = np.abs(got - ref)
+    bound = bound + bf16_ulp(np.maximum(np.abs(got), np.abs(ref)))
+    bad = err > bound
+    assert not bad.any(), f"{what}: {bad.sum()} outside, worst {np.max(err - bound):.3e} over the bound"
+
+
+def _weights(rng):
+    s = layer.init_scale
+    w = {"attn_norm": W.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(HID)).astype(np.float32)),
+         "wq": W.randn_bf16(rng, (NQ * 64, HID), s(HID)), "wk": W.randn_bf16(rng, (NKV * 64, HID), s(HID)),
+         "wv": W.randn_bf16(rng, (NKV * 64, HID), s(HID)), "wo": W.randn_bf16(rng, (HID, NQ * 64), s(NQ * 64)),
+         "mlp_norm": W.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(HID)).astype(np.float32)),
+         "w_gate_up": W.randn_bf16(rng, (2 * INTER, HID), s(HID)), "w_down": W.randn_bf16(rng, (HID, INTER), s(INTER))}
+    return w
+
+
+def test_rmsnorm_within_one_ulp(gpu):
+    rng = np.random.default_rng(1)
+    x = W.randn_bf16(rng, (7, HID), 2.0)
+    w = W.f32_to_bf16_bits((1.0 + 0.3 * rng.standard_normal(HID)).astype(np.float32))
+    out = torch.empty((7, HID), dtype=torch.bfloat16, device="cuda")
+    pkv.pkv_rmsnorm(out, dev_bf16(x), dev_bf16(w))
+    torch.cuda.synchronize()
+    ref = bf16.from_f64(layer.rmsnorm(f64(x), f64(w)))
+    d = ulp_diff(bits(out), ref)
+    assert d.max() <= 1 and (d == 0).mean() > 0.95
+
+
+def test_silu_mul_within_one_ulp(gpu):
+    rng = np.random.default_rng(2)
+    gu = W.randn_bf16(rng, (5, 2 * INTER), 2.0)
+    act = torch.empty((5, INTER), dtype=torch.bfloat16, device="cuda")
+    pkv.pkv_silu_mul(act, dev_bf16(gu))
+    torch.cuda.synchronize()
+    g, u = f64(gu[:, :INTER]), f64(gu[:, INTER:])
+    ref = bf16.from_f64(layer.silu(g) * u)
+    d = ulp_diff(bits(act), ref)
+    assert d.max() <= 1 and (d == 0).mean() > 0.95
+
+
+@pytest.mark.parametrize("rows,n,k", [(64, 3072, 2048), (1, 512, 2048), (13, 2048, 8192)])
+def test_linear_within_one_ulp(gpu, rows, n, k):
+    rng = np.random.default_rng(rows + n + k)
+    x = W.randn_bf16(rng, (rows, k))
+    w = W.randn_bf16(rng, (n, k), layer.init_scale(k))
+    c0 = W.randn_bf16(rng, (rows, n))
+    out = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda")
+    pkv.pkv_linear(out, dev_bf16(x), dev_bf16(w))
+    acc = dev_bf16(c0)
+    pkv.pkv_linear(acc, dev_bf16(x), dev_bf16(w), accumulate=True)
+    torch.cuda.synchronize()
+    prod = layer.linear(f64(x), f64(w))
+    fp32_sum = k * 2.0 ** -24 * layer.linear(np.abs(f64(x)), np.abs(f64(w)))
+    assert_within(bits(out), prod, fp32_sum, "linear")
+    ref_acc = f64(c0) + prod
+    assert_within(bits(acc), ref_acc, fp32_sum, "linear, accumulate")
+    assert (ulp_diff(bits(out), bf16.from_f64(prod)) == 0).mean() > 0.95
+
+
+@pytest.mark.parametrize("host_lens", [True, False])
+def test_decode_layer_matches_oracle(gpu, host_lens):
+    rng = np.random.default_rng(5)
+    wts = _weights(rng)
+    pos = np.array([16, 1, 299, 1000], np.int32)           # new token positions (cached tokens before it)
+    B = len(pos)
+    nbs = [-(-(int(p) + 1) // 16) for p in pos]
+    nb = sum(nbs) + 3
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((B, max(nbs) + 1), -1, np.int32)
+    o_ = 0
+    for b, n in enumerate(nbs):
+        bt[b, :n] = perm[o_:o_ + n]
+        o_ += n
+    kp = np.full((nb, 16, NKV, 64), W.BF16_POISON, np.uint16)
+    vp = kp.copy()
+    hist_k, hist_v = [], []
+    for b, p in enumerate(pos):
+        K = W.randn_bf16(rng, (int(p), NKV, 64))
+        V = W.randn_bf16(rng, (int(p), NKV, 64))
+        if p:
+            kp, vp = paging.append(kp, vp, K, V, bt, np.full(int(p), b, np.int32), np.arange(int(p), dtype=np.int32))
+        hist_k.append(f64(K))
+        hist_v.append(f64(V))
+    h = W.randn_bf16(rng, (B, HID))
+    ref = layer.decode_layer(f64(h), {k: f64(v) for k, v in wts.items() if k not in ("w_gate_up", "w_down")} | {
+        "wg": f64(wts["w_gate_up"][:INTER]), "wu": f64(wts["w_gate_up"][INTER:]), "wd": f64(wts["w_down"])},
+        hist_k, hist_v, pos, NQ, NKV, scale=0.125)
+
+    dw = {k: dev_bf16(v) for k, v in wts.items()}
+    hd = dev_bf16(h)
+    kpd, vpd = dev_bf16(kp), dev_bf16(vp)
+    n_scr = pkv.pkv_decode_layer_scratch_elems(B, HID, INTER, NQ, NKV)
+    scr = torch.empty(n_scr, dtype=torch.bfloat16, device="cuda")
+    cos_sin = torch.empty((4096, 32, 2), dtype=torch.float32, device="cuda")
+    pkv.pkv_rope_table_init(cos_sin)
+    ctx = pos + 1
+    ws = pkv.decode_workspace(B, NQ, NKV, int(ctx.max()))
+    pkv.pkv_decode_layer(hd, dw, scr, kpd, vpd, dev_i32(bt), dev_i32(np.arange(B)), dev_i32(ctx), int(ctx.max()),
+                         cos_sin, 0.125, ws, row_lens_host=ctx if host_lens else None)
+    torch.cuda.synchronize()
+    s = bits(scr)
+    off = 0
+
+    def take(width):
+        nonlocal off
+        x = s[off:off + B * width].reshape(B, width)
+        off += B * width
+        return x
+
+    a, q, k, v, o, m, gu, act = (take(HID), take(NQ * 64), take(NKV * 64), take(NKV * 64), take(NQ * 64), take(HID),
+                                 take(2 * INTER), take(INTER))
+    Wf = {name: f64(wts[name]) for name in ("wq", "wk", "wv", "wo", "w_gate_up", "w_down")}
+    a_, o_, m_, gu_, act_ = f64(a), f64(o), f64(m), f64(gu), f64(act)
+
+    def lin_bound(x_gpu, x_ref, w):
+        """How far x_gpu W^T, summed in float32, can be from x_ref W^T."""
+        aw = np.abs(w).T
+        return np.abs(x_gpu - x_ref) @ aw + w.shape[1] * 2.0 ** -24 * (np.abs(x_gpu) @ aw)
+
+    assert ulp_diff(a, bf16.from_f64(ref["a"])).max() <= 1
+    for name, got, w in (("q", q, Wf["wq"]), ("k", k, Wf["wk"]), ("v", v, Wf["wv"])):
+        want = ref[name].reshape(B, -1)
+        assert_within(got, want, lin_bound(a_, ref["a"], w), name)
+    err = np.abs(o_ - ref["o"])
+    assert err.max() <= ATOL_MAX and err.mean() <= ATOL_MEAN, (err.max(), err.mean())
+    # h after the attention residual is not kept: its bound comes from o's difference
+    b_mid = lin_bound(o_, ref["o"], Wf["wo"]) + 2 * bf16_ulp(ref["h_mid"])
+    # rmsnorm: m = h w / r moves by |w| (|dh| / r + |h| |dr| / r^2), |dr| <= rms(dh)
+    r = np.sqrt(np.mean(np.square(ref["h_mid"]), axis=1, keepdims=True))
+    dr = np.sqrt(np.mean(np.square(b_mid), axis=1, keepdims=True))
+    wn = np.abs(f64(wts["mlp_norm"]))
+    assert_within(m, ref["m"], wn * (b_mid / r + np.abs(ref["h_mid"]) * dr / r ** 2) * 1.01, "m")
+    g_gpu, u_gpu = gu_[:, :INTER], gu_[:, INTER:]
+    assert_within(gu[:, :INTER], ref["g"], lin_bound(m_, ref["m"], Wf["w_gate_up"][:INTER]), "g")
+    assert_within(gu[:, INTER:], ref["u"], lin_bound(m_, ref["m"], Wf["w_gate_up"][INTER:]), "u")
+    # silu(g) u from the kernel's own g, u: |silu'| <= 1.1, so it moves by at
+    # most 1.1 |dg| |u| + |silu(g)| |du|, plus its rounding
+    dg, du = np.abs(g_gpu - ref["g"]), np.abs(u_gpu - ref["u"])
+    act_bound = 1.1 * dg * np.abs(u_gpu) + np.abs(layer.silu(ref["g"])) * du
+    assert_within(act, ref["act"], act_bound, "act")
+    assert_within(bits(hd), ref["h"], b_mid + lin_bound(act_, ref["act"], Wf["w_down"]), "h")
+    eh = np.abs(f64(bits(hd)) - ref["h"])
+    print(f"decode layer: h max-abs {eh.max():.3e} mean-abs {eh.mean():.3e}, "
+          f"bit-equal {(bits(hd) == bf16.from_f64(ref['h'])).mean():.3f}", flush=True)
+    # the new token's cache rows: the rotated k, and v exactly as the layer's v buffer
+    for b, p in enumerate(pos):
+        blk = int(bt[b, p // 16])
+        kb = (lin_bound(a_, ref["a"], Wf["wk"]) + bf16_ulp(ref["k"].reshape(B, -1)))[b].reshape(NKV, 64)
+        # the rotation mixes pairs (|cos| + |sin| <= sqrt 2) and rounds once more
+        assert_within(bits(kpd[blk, p % 16]), ref["k_rot"][b], 1.5 * (kb + np.roll(kb, 32, axis=1))
+                      , "cached k")
+        np.testing.assert_array_equal(bits(vpd[blk, p % 16]), v[b].reshape(NKV, 64))
