@@ -87,7 +87,9 @@ def test_silu_mul_within_one_ulp(gpu):
     assert d.max() <= 1 and (d == 0).mean() > 0.95
 
 
-@pytest.mark.parametrize("rows,n,k", [(64, 3072, 2048), (1, 512, 2048), (13, 2048, 8192)])
+# the projections of a decode batch, a wider batch and a ragged shape
+@pytest.mark.parametrize("rows,n,k", [(64, 3072, 2048), (1, 512, 2048), (13, 2048, 8192), (64, 16384, 2048),
+                                      (100, 512, 2048), (8, 64, 96)])
 def test_linear_within_one_ulp(gpu, rows, n, k):
     rng = np.random.default_rng(rows + n + k)
     x = W.randn_bf16(rng, (rows, k))
