@@ -490,8 +490,8 @@ def serving_leg(torch, np, pkv, W, n_req: int = 128, n_slots: int = 64, budget: 
 
 
 def decode_layer_leg(torch, np, pkv, eng, ctx_now, stream, iters: int = 5):
-    """Whole Llama-3.2-1B decode layers (pkv_decode_layer: RMSNorm, rocBLAS
-    projections, the fused paged attention, the gated MLP) for the B=64 rows
+    """Whole Llama-3.2-1B decode layers (pkv_decode_layer: RMSNorm, the
+    decode-batch projections, the fused paged attention, the gated MLP) for the B=64 rows
     of the main workload, 16 layers, synthetic bf16 weights ~ N(0, 1/fan_in)
     on the device (121 MB per layer).  Each layer's attention re-writes the
     last token in place, like the attention timing.  HIP events around each

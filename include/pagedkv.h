@@ -518,13 +518,23 @@ int pkv_rmsnorm(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weight, int ro
  * intermediate % 8 == 0. */
 int pkv_silu_mul(pkv_bf16* act, const pkv_bf16* gate_up, int rows, int intermediate, void* stream);
 
+/* Bytes of float32 partials pkv_linear needs for this shape (0: none).
+ * Nonzero only for decode-batch shapes (rows <= 64, out_features % 64 == 0,
+ * in_features % 128 == 0) where K is split across workgroups. */
+size_t pkv_linear_workspace_bytes(int rows, int out_features, int in_features);
+
 /* out[rows][out_features] = x[rows][in_features] weight^T (+ out when
- * accumulate != 0), float32 sums, one rounding per output: a plain rocBLAS
- * bf16 GEMM (the library keeps one rocBLAS handle per device for the
+ * accumulate != 0), float32 sums, one rounding per output.  Decode-batch
+ * shapes (see pkv_linear_workspace_bytes) run on the library's MFMA kernel,
+ * deterministic (partials summed in a fixed order); when that shape needs
+ * partials and `workspace` (caller-owned device memory, 16-byte aligned,
+ * contents ignored and overwritten) is null or smaller than
+ * pkv_linear_workspace_bytes(...), and for every other shape, the product
+ * is a rocBLAS bf16 GEMM (one rocBLAS handle per device, kept for the
  * process; concurrent calls on one device from several host threads must be
- * serialised by the caller). */
+ * serialised by the caller).  out must not overlap x or weight. */
 int pkv_linear(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weight, int rows, int out_features,
-               int in_features, int accumulate, void* stream);
+               int in_features, int accumulate, void* workspace, size_t workspace_bytes, void* stream);
 
 typedef struct {
   const pkv_bf16* attn_norm;    /* [hidden] */
@@ -539,8 +549,9 @@ typedef struct {
 
 /* bf16 elements of pkv_decode_layer's scratch: a | q | k | v | o | m |
  * gate_up | act, each [batch][width] (widths hidden, n_q*64, n_kv*64, n_kv*64,
- * n_q*64, hidden, 2*intermediate, intermediate), in that order; 0 for
- * invalid sizes. */
+ * n_q*64, hidden, 2*intermediate, intermediate), in that order, then room for
+ * the projections' float32 partials (the largest pkv_linear_workspace_bytes
+ * of the six); 0 for invalid sizes. */
 size_t pkv_decode_layer_scratch_elems(int batch, int hidden, int intermediate, int n_q_heads, int n_kv_heads);
 
 /* One layer's decode step for `batch` rows, in place on the residual stream

@@ -71,7 +71,8 @@ SIGNATURES = {
     "pkv_sched_meta_elems": (_i64, [_i, _i]),
     "pkv_rmsnorm": (_i, [_p, _p, _p, _i, _i, _f, _p]),
     "pkv_silu_mul": (_i, [_p, _p, _i, _i, _p]),
-    "pkv_linear": (_i, [_p, _p, _p, _i, _i, _i, _i, _p]),
+    "pkv_linear_workspace_bytes": (_sz, [_i, _i, _i]),
+    "pkv_linear": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
     "pkv_decode_layer_scratch_elems": (_sz, [_i, _i, _i, _i, _i]),
     "pkv_decode_layer": (_i, [_p, _p, _i, _i, _p, _sz, _p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _i, _i, _i, _p,
                               _i, _f, _f, _p, _sz, _p]),
@@ -748,8 +749,17 @@ def pkv_silu_mul(act, gate_up, stream=None):
                                                inter, _stream(stream)))
 
 
-def pkv_linear(out, x, weight, accumulate=False, stream=None):
-    """out = x weight^T (+ out when accumulate); x [rows, in], weight [out, in]."""
+def pkv_linear_workspace_bytes(rows, out_features, in_features):
+    return load().pkv_linear_workspace_bytes(rows, out_features, in_features)
+
+
+def pkv_linear(out, x, weight, accumulate=False, workspace=None, stream=None):
+    """out = x weight^T (+ out when accumulate); x [rows, in], weight [out, in].
+    workspace: device tensor of at least pkv_linear_workspace_bytes(...) bytes
+    for the K-split partials, allocated here when None and the shape needs
+    it; False hands the library a null workspace (such shapes then run on
+    rocBLAS)."""
+    import torch
     for t, n in ((out, "out"), (x, "x"), (weight, "weight")):
         _contig(t, n)
     rows, k = x.shape
@@ -757,9 +767,17 @@ def pkv_linear(out, x, weight, accumulate=False, stream=None):
     if weight.shape[1] != k or tuple(out.shape) != (rows, n_out):
         raise ValueError("out, x and weight disagree")
     bt = _bf16_types()
+    if workspace is None:
+        nb = pkv_linear_workspace_bytes(rows, n_out, k)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=out.device) if nb else False
+    if workspace is False:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        _contig(workspace, "workspace")
+        ws_ptr, ws_bytes = _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
     _check("pkv_linear", load().pkv_linear(_dev_ptr(out, "out", bt), _dev_ptr(x, "x", bt),
                                            _dev_ptr(weight, "weight", bt), rows, n_out, k, 1 if accumulate else 0,
-                                           _stream(stream)))
+                                           ws_ptr, ws_bytes, _stream(stream)))
 
 
 class LayerWeights(C.Structure):

@@ -1,7 +1,7 @@
 // The rest of a Llama decode layer around the paged attention, for gfx950:
-// RMSNorm and the gated-SiLU product as HIP kernels, the projections as plain
-// bf16 GEMMs from rocBLAS (float32 accumulation), and pkv_decode_layer, which
-// runs one layer's decode step.
+// RMSNorm and the gated-SiLU product as HIP kernels, the projections as bf16
+// products with float32 sums (an MFMA kernel for decode batches, rocBLAS for
+// other shapes), and pkv_decode_layer, which runs one layer's decode step.
 //
 // Source: "An Inference Engine in 1,500 Lines of CUDA: The Map" -- the engine
 // runs Llama 3.2 1B (opening paragraph), has its own RMSNorm kernel (Korean
@@ -12,17 +12,25 @@
 // MLP (silu(x W_gate^T) * (x W_up^T)) W_down^T, residual adds after the
 // attention and the MLP.
 //
-// Design.  At decode batch sizes the projections are matrix x skinny-matrix
-// products bound by reading the weights, a plain library GEMM; the row-major
-// product C[B][N] = X[B][K] W[N][K]^T is handed to the column-major library
-// as C^T = W X^T (op(W) = transpose), and the residual adds ride on the
-// GEMM's beta = 1, so h is read, summed in float32 and rounded once.  RMSNorm
+// Design.  At decode batch sizes (up to 64 rows) the projections are
+// matrix x skinny-matrix products bound by reading the weights once: one
+// workgroup per 64 output features and all 64 rows, so each weight byte is
+// fetched once and the activations (at most 64 x K, resident in L2) once per
+// 64 features; K is split over the workgroup's four waves and, where 64-wide
+// feature tiles alone would leave the chip's 256 CUs idle, over workgroups
+// too, whose float32 partials a second kernel sums in a fixed order (no
+// atomics: the result does not depend on scheduling).  Other shapes go to
+// rocBLAS: the row-major product C[B][N] = X[B][K] W[N][K]^T is handed to the
+// column-major library as C^T = W X^T (op(W) = transpose).  Either way the
+// residual adds are folded in (beta = 1), so h is read, summed in float32
+// and rounded once.  RMSNorm
 // is one workgroup per row: 16-byte loads, a float32 sum of squares reduced
 // across the workgroup, one rounding per output.
 #include "common.h"
 
 #include <rocblas/rocblas.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -116,10 +124,392 @@ rocblas_handle blas_handle() {
   return h;
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDbWaves = 4;     // waves per workgroup, each a quarter of the workgroup's K range
+constexpr int kDbN = 64;        // output features per workgroup (four MFMA row blocks)
+constexpr int kDbRows = 64;     // decode rows (four MFMA column blocks)
+constexpr int kDbStage = 32;    // K per MFMA step
+constexpr int kDbTilesPerWave = 16 / kDbWaves;
+constexpr int kMaxSeg = 3;
+
+// One product of a launch: C[rows][n] (+)= X[rows][k] W[n][k]^T.  Several
+// products sharing X and k (the query, key and value projections) go in one
+// launch, their 64-feature tiles numbered one after the other.
+struct GemmSeg {
+  const uint16_t* w;
+  uint16_t* c;
+  float* part;        // [splits][rows][n] float32 partials when K is split
+  int n;              // output features, a multiple of 64
+  int tile_begin;     // first tile of this product
+  int tile_end;       // one past its last tile
+};
+
+struct DecodeGemmArgs {
+  GemmSeg seg[kMaxSeg];
+  const uint16_t* x;
+  int nseg, rows, k, kchunk, accumulate;
+  int inter;          // gated mode: W = [gate; up] of 2 inter rows, C = silu(gate) * up [rows][inter]
+};
+
+// Decode-batch projection, one workgroup per (64 features, K range).  Each
+// of its four waves multiplies a quarter of the range into all 4 x 4 tiles
+// of C^T[64 n][64 b] with v_mfma_f32_16x16x32_bf16 (A = 16 rows of W, B = 16
+// rows of X, 8 k per lane from group lane / 16, 16-byte loads; a lane keeps
+// C^T rows 4 (lane / 16) .. + 3 of column lane % 16 of each tile), so each
+// weight byte is read once and each X byte once per 64 features.  The
+// waves' tiles are summed through LDS in two halves (32 KB), wave w
+// finishing column block w % 4, row blocks w / 4 + (waves / 4) q.  One K
+// range: the sums (plus C when accumulating) are rounded to bf16 into C;
+// several: they go as float32 to the product's partials for
+// decode_reduce_kernel.  Gated mode (kGlu): tile t takes gate rows
+// 32 t .. + 31 (row blocks 0, 1) and the matching up rows (row blocks 2, 3),
+// and writes silu(bf16(gate)) * bf16(up) for features 32 t .. + 31.
+template <bool kGlu>
+__global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGemmArgs args) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = blockIdx.x;
+  int si = 0;
+  while (si + 1 < args.nseg && t >= args.seg[si].tile_end) ++si;
+  const uint16_t* __restrict__ w = args.seg[si].w;
+  const int n = args.seg[si].n;
+  const int n0 = (t - args.seg[si].tile_begin) * kDbN;
+  const int k = args.k, rows = args.rows;
+  const int split = blockIdx.y;
+  const int kq = args.kchunk / kDbWaves;          // a multiple of kDbStage (checked on the host)
+  const int kbeg = split * args.kchunk + wv * kq;
+  const int r16 = lane & 15;
+  const int kg = 8 * (lane >> 4);
+  const uint16_t* wrow[4];
+  const uint16_t* xrow[4];
+  bool xok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int wr = kGlu ? (i < 2 ? 0 : args.inter) + 32 * t + 16 * (i & 1) + r16 : n0 + 16 * i + r16;
+    wrow[i] = w + (int64_t)wr * k + kbeg + kg;
+    const int b = 16 * i + r16;
+    xok[i] = b < rows;
+    xrow[i] = args.x + (int64_t)(xok[i] ? b : 0) * k + kbeg + kg;
+  }
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int kk = 0; kk < kq; kk += kDbStage) {
+    uint4 a[4], bx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = *reinterpret_cast<const uint4*>(wrow[i] + kk);
+      bx[i] = *reinterpret_cast<const uint4*>(xrow[i] + kk);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)   // rows past the batch read row 0 and are zeroed, dword by dword
+      bx[j] = make_uint4(xok[j] ? bx[j].x : 0u, xok[j] ? bx[j].y : 0u, xok[j] ? bx[j].z : 0u,
+                         xok[j] ? bx[j].w : 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                            __builtin_bit_cast(bf16x8, bx[j]), acc[i][j], 0, 0, 0);
+  }
+
+  // the second half of the waves hands its tiles to the first half, which
+  // adds them and publishes the result; every wave then sums its share of
+  // the tiles over the published copies
+  __shared__ f32x4 red[kDbWaves / 2][16][kWave];
+  if (wv >= kDbWaves / 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[wv - kDbWaves / 2][4 * i + j][lane] = acc[i][j];
+  }
+  __syncthreads();
+  if (wv < kDbWaves / 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += red[wv][4 * i + j][lane];
+  }
+  __syncthreads();
+  if (wv < kDbWaves / 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[wv][4 * i + j][lane] = acc[i][j];
+  }
+  __syncthreads();
+  // wave w finishes column block w % 4, row blocks w / 4 + (kDbWaves / 4) q
+  const int j = wv & 3;
+  const int b = 16 * j + r16;
+  f32x4 sum[kDbTilesPerWave];
+#pragma unroll
+  for (int q = 0; q < kDbTilesPerWave; ++q) {
+    const int tile = 4 * ((wv >> 2) + (kDbWaves / 4) * q) + j;
+    sum[q] = red[0][tile][lane];
+#pragma unroll
+    for (int u = 1; u < kDbWaves / 2; ++u) sum[q] += red[u][tile][lane];
+  }
+  if (b >= rows) return;
+  if (kGlu) {   // gate tiles are the first half of the wave's row blocks (0, 1), up tiles the second (2, 3)
+#pragma unroll
+    for (int q = 0; q < kDbTilesPerWave / 2; ++q) {
+      uint32_t o[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        float r[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const float g = bf16_lo(pack_bf16x2(sum[q][2 * e + f], 0.f));
+          const float u = bf16_lo(pack_bf16x2(sum[q + kDbTilesPerWave / 2][2 * e + f], 0.f));
+          r[f] = g / (1.0f + expf(-g)) * u;
+        }
+        o[e] = pack_bf16x2(r[0], r[1]);
+      }
+      const int f0 = 32 * t + 16 * ((wv >> 2) + (kDbWaves / 4) * q) + 4 * (lane >> 4);
+      *reinterpret_cast<uint2*>(args.seg[0].c + (int64_t)b * args.inter + f0) = make_uint2(o[0], o[1]);
+    }
+    return;
+  }
+#pragma unroll
+  for (int q = 0; q < kDbTilesPerWave; ++q) {
+    const int nn = n0 + 16 * ((wv >> 2) + (kDbWaves / 4) * q) + 4 * (lane >> 4);   // C^T rows nn .. nn + 3 of column b
+    if (gridDim.y == 1) {
+      uint16_t* crow = args.seg[si].c + (int64_t)b * n + nn;
+      float v[4] = {sum[q][0], sum[q][1], sum[q][2], sum[q][3]};
+      if (args.accumulate) {
+        const uint2 old = *reinterpret_cast<const uint2*>(crow);
+        v[0] += bf16_lo(old.x);
+        v[1] += bf16_hi(old.x);
+        v[2] += bf16_lo(old.y);
+        v[3] += bf16_hi(old.y);
+      }
+      *reinterpret_cast<uint2*>(crow) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    } else {
+      *reinterpret_cast<f32x4*>(args.seg[si].part + ((int64_t)split * rows + b) * n + nn) = sum[q];
+    }
+  }
+}
+
+struct ReduceSeg {
+  uint16_t* c;
+  const float* part;
+  int n;
+  int end;            // one past the last eight-column group of this product, over all products' groups
+};
+
+struct ReduceArgs {
+  ReduceSeg seg[kMaxSeg];
+  int nseg, rows, splits, accumulate;
+};
+
+// C[b][8 g .. + 7] = bf16(sum over splits of part[s][b][..] (+ C)), in split
+// order; one thread per (row, eight columns), products one after the other.
+__global__ __launch_bounds__(256) void decode_reduce_kernel(ReduceArgs args) {
+  int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  int si = 0;
+  while (si + 1 < args.nseg && gid >= args.seg[si].end) ++si;
+  if (gid >= args.seg[si].end) return;
+  if (si) gid -= args.seg[si - 1].end;
+  const int n = args.seg[si].n;
+  const int64_t e = (int64_t)gid * 8;           // row gid / (n / 8), columns 8 (gid % (n / 8)) .. + 7
+  const int64_t plane = (int64_t)args.rows * n;
+  const float* p = args.seg[si].part + e;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = 0; s < args.splits; ++s) {
+    const float4 a = reinterpret_cast<const float4*>(p + s * plane)[0];
+    const float4 c = reinterpret_cast<const float4*>(p + s * plane)[1];
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    v[4] += c.x; v[5] += c.y; v[6] += c.z; v[7] += c.w;
+  }
+  uint4* out = reinterpret_cast<uint4*>(args.seg[si].c + e);
+  if (args.accumulate) {
+    const uint4 old = *out;
+    const uint32_t o[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] += bf16_lo(o[q]);
+      v[2 * q + 1] += bf16_hi(o[q]);
+    }
+  }
+  *out = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7]));
+}
+
+// The attention output projection's finish, one workgroup per row:
+// h[b] = bf16(h[b] + sum over splits of part[s][b]) and, from that rounded
+// h, m[b] = rmsnorm(h[b]) * w (as rmsnorm_kernel).
+__global__ __launch_bounds__(kNormThreads) void reduce_residual_norm_kernel(uint16_t* __restrict__ h,
+                                                                           uint16_t* __restrict__ m,
+                                                                           const float* __restrict__ part,
+                                                                           const uint16_t* __restrict__ nw, int rows,
+                                                                           int dim, int splits, float eps) {
+  const int r = blockIdx.x;
+  const int n8 = dim / 8;
+  const int64_t plane = (int64_t)rows * dim;
+  uint4* hr = reinterpret_cast<uint4*>(h + (int64_t)r * dim);
+  float ss = 0.f;
+  for (int g = threadIdx.x; g < n8; g += kNormThreads) {
+    const float* p = part + (int64_t)r * dim + 8 * g;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = 0; s < splits; ++s) {
+      const float4 a = reinterpret_cast<const float4*>(p + s * plane)[0];
+      const float4 c = reinterpret_cast<const float4*>(p + s * plane)[1];
+      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+      v[4] += c.x; v[5] += c.y; v[6] += c.z; v[7] += c.w;
+    }
+    const uint4 old = hr[g];
+    const uint32_t o[4] = {old.x, old.y, old.z, old.w};
+    uint32_t res[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      res[q] = pack_bf16x2(v[2 * q] + bf16_lo(o[q]), v[2 * q + 1] + bf16_hi(o[q]));
+      const float x0 = bf16_lo(res[q]), x1 = bf16_hi(res[q]);
+      ss = __builtin_fmaf(x0, x0, ss);
+      ss = __builtin_fmaf(x1, x1, ss);
+    }
+    hr[g] = make_uint4(res[0], res[1], res[2], res[3]);
+  }
+  __shared__ float sh[kNormThreads / kWave];
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) ss += shfl_xor(ss, off);
+  if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormThreads / kWave; ++i) tot += sh[i];
+  const float inv = 1.0f / sqrtf(tot / (float)dim + eps);
+  const uint4* w4 = reinterpret_cast<const uint4*>(nw);
+  uint4* mr = reinterpret_cast<uint4*>(m + (int64_t)r * dim);
+  for (int g = threadIdx.x; g < n8; g += kNormThreads) {   // each thread re-reads what it wrote
+    const uint4 v = hr[g];
+    const uint4 gw = w4[g];
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t ww[4] = {gw.x, gw.y, gw.z, gw.w};
+    uint32_t res[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      res[q] = pack_bf16x2(bf16_lo(u[q]) * inv * bf16_lo(ww[q]), bf16_hi(u[q]) * inv * bf16_hi(ww[q]));
+    mr[g] = make_uint4(res[0], res[1], res[2], res[3]);
+  }
+}
+
+// K splits for a decode-batch launch of `tiles` 64-feature tiles: the fewest
+// that give >= 256 workgroups (the chip's CUs), each wave keeping whole
+// stages; 0 if the shape does not fit the kernel.
+int decode_gemm_splits(int rows, int tiles, int k) {
+  if (rows <= 0 || rows > kDbRows || tiles <= 0 || k % (kDbStage * kDbWaves)) return 0;
+  int s = 1;
+  while (tiles * s < 256 && k % (kDbStage * kDbWaves * s * 2) == 0) s *= 2;
+  return s;
+}
+
 }  // namespace
 
-// C[rows][n] = beta * C + X[rows][k] W[n][k]^T, bf16 in and out, float32 sums.
-int gemm_xwt(uint16_t* c, const uint16_t* x, const uint16_t* w, int rows, int n, int k, float beta, void* stream) {
+size_t decode_gemm_workspace_bytes(int rows, int n, int k) {
+  if (n % kDbN) return 0;
+  const int s = decode_gemm_splits(rows, n / kDbN, k);
+  return s > 1 ? (size_t)s * rows * n * sizeof(float) : 0;
+}
+
+// Products sharing X [rows][k] (1 to kMaxSeg of them: w[i] [n[i]][k] into
+// c[i] [rows][n[i]]) on the decode-batch kernel, K-split partials in
+// `part` (part_bytes) when needed.  Returns PKV_ERR_INVALID_ARG (nothing
+// launched) when the shape does not fit the kernel or the partials do not
+// fit `part`; the caller then takes another route.
+// With reduce == false and K split the partials are left for the caller
+// (the number of splits goes to *splits_out when not null).
+int decode_gemm(int nseg, uint16_t* const* c, const uint16_t* const* w, const int* n, const uint16_t* x, int rows,
+                int k, bool accumulate, void* part, size_t part_bytes, hipStream_t stream, bool reduce = true,
+                int* splits_out = nullptr) {
+  if (nseg < 1 || nseg > kMaxSeg) return PKV_ERR_INVALID_ARG;
+  int tiles = 0, ntot = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (n[i] <= 0 || n[i] % kDbN) return PKV_ERR_INVALID_ARG;
+    tiles += n[i] / kDbN;
+    ntot += n[i];
+  }
+  const int splits = decode_gemm_splits(rows, tiles, k);
+  if (splits == 0) return PKV_ERR_INVALID_ARG;
+  if (splits > 1 && (!part || part_bytes < (size_t)splits * rows * ntot * sizeof(float))) return PKV_ERR_INVALID_ARG;
+  if (splits_out) *splits_out = splits;
+  DecodeGemmArgs a{};
+  ReduceArgs ra{};
+  int t0 = 0;
+  size_t poff = 0;
+  int gend = 0;
+  for (int i = 0; i < nseg; ++i) {
+    float* pp = splits > 1 ? static_cast<float*>(part) + poff : nullptr;
+    a.seg[i] = GemmSeg{w[i], c[i], pp, n[i], t0, t0 + n[i] / kDbN};
+    t0 += n[i] / kDbN;
+    poff += (size_t)splits * rows * n[i];
+    gend += rows * (n[i] / 8);
+    ra.seg[i] = ReduceSeg{c[i], pp, n[i], gend};
+  }
+  a.x = x;
+  a.nseg = nseg;
+  a.rows = rows;
+  a.k = k;
+  a.kchunk = k / splits;
+  a.accumulate = accumulate ? 1 : 0;
+  void* args[] = {&a};
+  int rc = launch_status(hipLaunchKernel((const void*)decode_gemm_kernel<false>, dim3(tiles, splits),
+                                         dim3(kDbWaves * kWave), args, 0, stream));
+  if (rc != PKV_OK || splits == 1 || !reduce) return rc;
+  ra.nseg = nseg;
+  ra.rows = rows;
+  ra.splits = splits;
+  ra.accumulate = a.accumulate;
+  void* rargs[] = {&ra};
+  return launch_status(hipLaunchKernel((const void*)decode_reduce_kernel, dim3((gend + 255) / 256), dim3(256), rargs,
+                                       0, stream));
+}
+
+// act[rows][inter] = silu(bf16(X Wg^T)) * bf16(X Wu^T) for W = [Wg; Wu]
+// [2 inter][k], on the decode-batch kernel in gated mode (K never split).
+// PKV_ERR_INVALID_ARG (nothing launched) when the shape does not fit.
+int decode_gemm_glu(uint16_t* act, const uint16_t* x, const uint16_t* w, int rows, int inter, int k,
+                    hipStream_t stream) {
+  if (rows <= 0 || rows > kDbRows || inter <= 0 || inter % 32 || k % (kDbStage * kDbWaves)) return PKV_ERR_INVALID_ARG;
+  DecodeGemmArgs a{};
+  a.seg[0] = GemmSeg{w, act, nullptr, 2 * inter, 0, inter / 32};
+  a.x = x;
+  a.nseg = 1;
+  a.rows = rows;
+  a.k = k;
+  a.kchunk = k;
+  a.inter = inter;
+  void* args[] = {&a};
+  return launch_status(hipLaunchKernel((const void*)decode_gemm_kernel<true>, dim3(inter / 32, 1),
+                                       dim3(kDbWaves * kWave), args, 0, stream));
+}
+
+// h = bf16(h + sum of the output projection's partials), m = rmsnorm(h) * w.
+int reduce_residual_norm(uint16_t* h, uint16_t* m, const float* part, const uint16_t* w, int rows, int dim,
+                         int splits, float eps, hipStream_t stream) {
+  void* args[] = {&h, &m, &part, &w, &rows, &dim, &splits, &eps};
+  return launch_status(hipLaunchKernel((const void*)reduce_residual_norm_kernel, dim3(rows), dim3(kNormThreads),
+                                       args, 0, stream));
+}
+
+// C[rows][n] = beta * C + X[rows][k] W[n][k]^T, bf16 in and out, float32 sums:
+// the decode-batch kernel where the shape fits it, else rocBLAS.
+int gemm_xwt(uint16_t* c, const uint16_t* x, const uint16_t* w, int rows, int n, int k, float beta, void* stream,
+             void* workspace, size_t workspace_bytes) {
+  if (beta == 0.0f || beta == 1.0f) {
+    uint16_t* cc[1] = {c};
+    const uint16_t* ww[1] = {w};
+    const int nn[1] = {n};
+    const int rc = decode_gemm(1, cc, ww, nn, x, rows, k, beta == 1.0f, workspace, workspace_bytes,
+                               static_cast<hipStream_t>(stream));
+    if (rc != PKV_ERR_INVALID_ARG) return rc;
+  }
   rocblas_handle h = blas_handle();
   if (!h) return PKV_ERR_HIP;
   if (rocblas_set_stream(h, static_cast<hipStream_t>(stream)) != rocblas_status_success) return PKV_ERR_HIP;
@@ -167,21 +557,47 @@ extern "C" int pkv_silu_mul(pkv_bf16* act, const pkv_bf16* gate_up, int rows, in
                                        args, 0, (hipStream_t)stream));
 }
 
+extern "C" size_t pkv_linear_workspace_bytes(int rows, int out_features, int in_features) {
+  return decode_gemm_workspace_bytes(rows, out_features, in_features);
+}
+
 extern "C" int pkv_linear(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weight, int rows, int out_features,
-                          int in_features, int accumulate, void* stream) {
+                          int in_features, int accumulate, void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 0 || out_features <= 0 || in_features <= 0) return PKV_ERR_INVALID_ARG;
   if (rows == 0) return PKV_OK;
   if (!out || !x || !weight) return PKV_ERR_NULL;
-  if (!aligned16(out) || !aligned16(x) || !aligned16(weight)) return PKV_ERR_MISALIGNED;
-  return gemm_xwt(out, x, weight, rows, out_features, in_features, accumulate ? 1.0f : 0.0f, stream);
+  if (!aligned16(out) || !aligned16(x) || !aligned16(weight) || (workspace && !aligned16(workspace)))
+    return PKV_ERR_MISALIGNED;
+  return gemm_xwt(out, x, weight, rows, out_features, in_features, accumulate ? 1.0f : 0.0f, stream, workspace,
+                  workspace_bytes);
 }
+
+namespace {
+
+// bf16 elements of the float32 K-split partials the layer's projections need
+// (the largest over its launches, fallbacks included), placed after the
+// activations.
+size_t layer_partial_elems(int batch, int hidden, int intermediate, int n_q_heads, int n_kv_heads) {
+  const int qd = n_q_heads * kHeadDim, kvd = n_kv_heads * kHeadDim;
+  const size_t sizes[] = {decode_gemm_workspace_bytes(batch, qd + 2 * kvd, hidden),
+                          decode_gemm_workspace_bytes(batch, qd, hidden), decode_gemm_workspace_bytes(batch, kvd, hidden),
+                          decode_gemm_workspace_bytes(batch, hidden, qd),
+                          decode_gemm_workspace_bytes(batch, 2 * intermediate, hidden),
+                          decode_gemm_workspace_bytes(batch, hidden, intermediate)};
+  size_t most = 0;
+  for (size_t b : sizes) most = std::max(most, b);
+  return (most + 15) / 16 * 8;
+}
+
+}  // namespace
 
 extern "C" size_t pkv_decode_layer_scratch_elems(int batch, int hidden, int intermediate, int n_q_heads,
                                                  int n_kv_heads) {
   if (batch <= 0 || hidden <= 0 || intermediate <= 0 || n_q_heads <= 0 || n_kv_heads <= 0) return 0;
   const size_t qd = (size_t)n_q_heads * kHeadDim, kvd = (size_t)n_kv_heads * kHeadDim;
-  // a | q | k | v | o | m | gate_up | act, each row-major [batch][width]
-  return (size_t)batch * ((size_t)hidden * 2 + qd * 2 + kvd * 2 + (size_t)intermediate * 3);
+  // a | q | k | v | o | m | gate_up | act, each row-major [batch][width], then the projections' partials
+  return (size_t)batch * ((size_t)hidden * 2 + qd * 2 + kvd * 2 + (size_t)intermediate * 3) +
+         layer_partial_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads);
 }
 
 extern "C" int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int intermediate,
@@ -209,19 +625,53 @@ extern "C" int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* w, int hid
   pkv_bf16* m = o + (size_t)batch * qd;
   pkv_bf16* gu = m + (size_t)batch * hidden;
   pkv_bf16* act = gu + (size_t)batch * 2 * intermediate;
+  void* part = act + (size_t)batch * intermediate;   // 16-byte aligned: every region is a multiple of 8 elements
+  const size_t part_bytes = 2 * layer_partial_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   int rc;
   if ((rc = pkv_rmsnorm(a, h, w->attn_norm, batch, hidden, eps, stream)) != PKV_OK) return rc;
-  if ((rc = pkv_linear(q, a, w->wq, batch, qd, hidden, 0, stream)) != PKV_OK) return rc;
-  if ((rc = pkv_linear(k, a, w->wk, batch, kvd, hidden, 0, stream)) != PKV_OK) return rc;
-  if ((rc = pkv_linear(v, a, w->wv, batch, kvd, hidden, 0, stream)) != PKV_OK) return rc;
+  // q, k and v in one launch where the decode-batch kernel takes the shape
+  {
+    uint16_t* cs[3] = {q, k, v};
+    const uint16_t* ws[3] = {w->wq, w->wk, w->wv};
+    const int ns[3] = {qd, kvd, kvd};
+    rc = decode_gemm(3, cs, ws, ns, a, batch, hidden, false, part, part_bytes, st);
+  }
+  if (rc == PKV_ERR_INVALID_ARG) {
+    if ((rc = pkv_linear(q, a, w->wq, batch, qd, hidden, 0, part, part_bytes, stream)) != PKV_OK) return rc;
+    if ((rc = pkv_linear(k, a, w->wk, batch, kvd, hidden, 0, part, part_bytes, stream)) != PKV_OK) return rc;
+    rc = pkv_linear(v, a, w->wv, batch, kvd, hidden, 0, part, part_bytes, stream);
+  }
+  if (rc != PKV_OK) return rc;
   if ((rc = pkv_paged_decode_fused(o, q, k, v, k_pool, v_pool, num_blocks, block_table, bt_row_stride, num_slots,
                                    max_blocks_per_seq, slot_ids, context_lens, row_lens_host, batch, max_context_len,
                                    n_q_heads, n_kv_heads, kHeadDim, cos_sin, max_pos, scale, 0, workspace,
                                    workspace_bytes, stream)) != PKV_OK)
     return rc;
-  if ((rc = pkv_linear(h, o, w->wo, batch, hidden, qd, 1, stream)) != PKV_OK) return rc;
-  if ((rc = pkv_rmsnorm(m, h, w->mlp_norm, batch, hidden, eps, stream)) != PKV_OK) return rc;
-  if ((rc = pkv_linear(gu, m, w->w_gate_up, batch, 2 * intermediate, hidden, 0, stream)) != PKV_OK) return rc;
-  if ((rc = pkv_silu_mul(act, gu, batch, intermediate, stream)) != PKV_OK) return rc;
-  return pkv_linear(h, act, w->w_down, batch, hidden, intermediate, 1, stream);
+  // h += o Wo^T; with K split, the partials' sum, the residual add and the
+  // MLP's RMSNorm are one kernel
+  {
+    uint16_t* cs[1] = {h};
+    const uint16_t* ws[1] = {w->wo};
+    const int ns[1] = {hidden};
+    int splits = 0;
+    rc = decode_gemm(1, cs, ws, ns, o, batch, qd, true, part, part_bytes, st, false, &splits);
+    if (rc == PKV_OK && splits > 1) {
+      rc = reduce_residual_norm(h, m, static_cast<const float*>(part), w->mlp_norm, batch, hidden, splits, eps, st);
+    } else {
+      if (rc == PKV_ERR_INVALID_ARG) rc = pkv_linear(h, o, w->wo, batch, hidden, qd, 1, part, part_bytes, stream);
+      if (rc == PKV_OK) rc = pkv_rmsnorm(m, h, w->mlp_norm, batch, hidden, eps, stream);
+    }
+    if (rc != PKV_OK) return rc;
+  }
+  // act = silu(m Wg^T) * (m Wu^T): one gated launch where it fits, else the
+  // product into gate_up and the SiLU kernel
+  rc = decode_gemm_glu(act, m, w->w_gate_up, batch, intermediate, hidden, st);
+  if (rc == PKV_ERR_INVALID_ARG) {
+    if ((rc = pkv_linear(gu, m, w->w_gate_up, batch, 2 * intermediate, hidden, 0, part, part_bytes, stream)) != PKV_OK)
+      return rc;
+    rc = pkv_silu_mul(act, gu, batch, intermediate, stream);
+  }
+  if (rc != PKV_OK) return rc;
+  return pkv_linear(h, act, w->w_down, batch, hidden, intermediate, 1, part, part_bytes, stream);
 }

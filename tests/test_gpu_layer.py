@@ -1,5 +1,6 @@
 """GPU parity for the rest of the Llama decode layer: RMSNorm, the gated
-SiLU product, the rocBLAS projections and pkv_decode_layer (Llama-3.2-1B
+SiLU product, the projections (decode-batch MFMA kernel, rocBLAS for other
+shapes) and pkv_decode_layer (Llama-3.2-1B
 shapes: hidden 2048, 32 / 8 heads of 64, intermediate 8192, synthetic bf16
 weights ~ N(0, 1/fan_in)) against the float64 oracle with bf16 rounding where
 the engine keeps a buffer.
@@ -87,18 +88,22 @@ def test_silu_mul_within_one_ulp(gpu):
     assert d.max() <= 1 and (d == 0).mean() > 0.95
 
 
-# the projections of a decode batch, a wider batch and a ragged shape
-@pytest.mark.parametrize("rows,n,k", [(64, 3072, 2048), (1, 512, 2048), (13, 2048, 8192), (64, 16384, 2048),
-                                      (100, 512, 2048), (8, 64, 96)])
-def test_linear_within_one_ulp(gpu, rows, n, k):
+# the projections of a decode batch (K split over 1 to 16 workgroups), a
+# wider batch and ragged shapes (both on rocBLAS), and a split shape handed a
+# null workspace (rocBLAS too)
+@pytest.mark.parametrize("rows,n,k,ws", [(64, 3072, 2048, None), (1, 512, 2048, None), (13, 2048, 8192, None),
+                                         (64, 16384, 2048, None), (64, 2048, 2048, None), (64, 2048, 8192, None),
+                                         (37, 192, 384, None), (100, 512, 2048, None), (8, 64, 96, None),
+                                         (64, 2048, 8192, False)])
+def test_linear_within_one_ulp(gpu, rows, n, k, ws):
     rng = np.random.default_rng(rows + n + k)
     x = W.randn_bf16(rng, (rows, k))
     w = W.randn_bf16(rng, (n, k), layer.init_scale(k))
     c0 = W.randn_bf16(rng, (rows, n))
     out = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda")
-    pkv.pkv_linear(out, dev_bf16(x), dev_bf16(w))
+    pkv.pkv_linear(out, dev_bf16(x), dev_bf16(w), workspace=ws)
     acc = dev_bf16(c0)
-    pkv.pkv_linear(acc, dev_bf16(x), dev_bf16(w), accumulate=True)
+    pkv.pkv_linear(acc, dev_bf16(x), dev_bf16(w), accumulate=True, workspace=ws)
     torch.cuda.synchronize()
     prod = layer.linear(f64(x), f64(w))
     fp32_sum = k * 2.0 ** -24 * layer.linear(np.abs(f64(x)), np.abs(f64(w)))
@@ -108,11 +113,35 @@ def test_linear_within_one_ulp(gpu, rows, n, k):
     assert (ulp_diff(bits(out), bf16.from_f64(prod)) == 0).mean() > 0.95
 
 
-@pytest.mark.parametrize("host_lens", [True, False])
-def test_decode_layer_matches_oracle(gpu, host_lens):
+def test_linear_decode_batch_is_deterministic(gpu):
+    """The K-split partials are summed in a fixed order: repeated calls, with
+    the workspace refilled with garbage in between, give the same bits."""
+    rng = np.random.default_rng(77)
+    rows, n, k = 64, 2048, 8192
+    assert pkv.pkv_linear_workspace_bytes(rows, n, k) > 0
+    assert pkv.pkv_linear_workspace_bytes(65, n, k) == 0 and pkv.pkv_linear_workspace_bytes(64, 2048, 8000) == 0
+    x, w = dev_bf16(W.randn_bf16(rng, (rows, k))), dev_bf16(W.randn_bf16(rng, (n, k), layer.init_scale(k)))
+    ws = torch.empty(pkv.pkv_linear_workspace_bytes(rows, n, k), dtype=torch.uint8, device="cuda")
+    outs = []
+    for fill in (0, 255, 0x7f):
+        ws.fill_(fill)
+        out = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda")
+        pkv.pkv_linear(out, x, w, workspace=ws)
+        outs.append(bits(out))
+    torch.cuda.synchronize()
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+# 4 rows take the decode-batch kernels (q, k, v in one launch, the gated
+# gate/up launch that leaves the gate_up buffer unwritten); 65 rows take
+# rocBLAS and the SiLU kernel
+@pytest.mark.parametrize("host_lens,extra_rows", [(True, 0), (False, 0), (True, 61)])
+def test_decode_layer_matches_oracle(gpu, host_lens, extra_rows):
     rng = np.random.default_rng(5)
     wts = _weights(rng)
     pos = np.array([16, 1, 299, 1000], np.int32)           # new token positions (cached tokens before it)
+    pos = np.concatenate([pos, rng.integers(0, 40, extra_rows).astype(np.int32)])
+    gated = len(pos) <= 64
     B = len(pos)
     nbs = [-(-(int(p) + 1) // 16) for p in pos]
     nb = sum(nbs) + 3
@@ -181,13 +210,22 @@ def test_decode_layer_matches_oracle(gpu, host_lens):
     dr = np.sqrt(np.mean(np.square(b_mid), axis=1, keepdims=True))
     wn = np.abs(f64(wts["mlp_norm"]))
     assert_within(m, ref["m"], wn * (b_mid / r + np.abs(ref["h_mid"]) * dr / r ** 2) * 1.01, "m")
-    g_gpu, u_gpu = gu_[:, :INTER], gu_[:, INTER:]
-    assert_within(gu[:, :INTER], ref["g"], lin_bound(m_, ref["m"], Wf["w_gate_up"][:INTER]), "g")
-    assert_within(gu[:, INTER:], ref["u"], lin_bound(m_, ref["m"], Wf["w_gate_up"][INTER:]), "u")
-    # silu(g) u from the kernel's own g, u: |silu'| <= 1.1, so it moves by at
-    # most 1.1 |dg| |u| + |silu(g)| |du|, plus its rounding
-    dg, du = np.abs(g_gpu - ref["g"]), np.abs(u_gpu - ref["u"])
-    act_bound = 1.1 * dg * np.abs(u_gpu) + np.abs(layer.silu(ref["g"])) * du
+    bg = lin_bound(m_, ref["m"], Wf["w_gate_up"][:INTER])
+    bu = lin_bound(m_, ref["m"], Wf["w_gate_up"][INTER:])
+    if gated:
+        # g and u stay in registers: |g_gpu - g| <= bg plus the two sides'
+        # roundings (1 ulp of the larger), likewise u; |silu'| <= 1.1
+        dg = bg + bf16_ulp(np.abs(ref["g"]) + bg)
+        du = bu + bf16_ulp(np.abs(ref["u"]) + bu)
+        act_bound = 1.1 * dg * (np.abs(ref["u"]) + du) + np.abs(layer.silu(ref["g"])) * du
+    else:
+        g_gpu, u_gpu = gu_[:, :INTER], gu_[:, INTER:]
+        assert_within(gu[:, :INTER], ref["g"], bg, "g")
+        assert_within(gu[:, INTER:], ref["u"], bu, "u")
+        # silu(g) u from the kernel's own g, u: |silu'| <= 1.1, so it moves by
+        # at most 1.1 |dg| |u| + |silu(g)| |du|, plus its rounding
+        dg, du = np.abs(g_gpu - ref["g"]), np.abs(u_gpu - ref["u"])
+        act_bound = 1.1 * dg * np.abs(u_gpu) + np.abs(layer.silu(ref["g"])) * du
     assert_within(act, ref["act"], act_bound, "act")
     assert_within(bits(hd), ref["h"], b_mid + lin_bound(act_, ref["act"], Wf["w_down"]), "h")
     eh = np.abs(f64(bits(hd)) - ref["h"])
