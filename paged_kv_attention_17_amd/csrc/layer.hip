@@ -127,11 +127,13 @@ rocblas_handle blas_handle() {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kDbWaves = 4;     // waves per workgroup, each a quarter of the workgroup's K range
+constexpr int kDbWaves = 4;     // waves per workgroup, each 16 of its 64 features
 constexpr int kDbN = 64;        // output features per workgroup (four MFMA row blocks)
 constexpr int kDbRows = 64;     // decode rows (four MFMA column blocks)
 constexpr int kDbStage = 32;    // K per MFMA step
-constexpr int kDbTilesPerWave = 16 / kDbWaves;
+constexpr int kDbSteps = 4;     // MFMA steps per X slice
+constexpr int kDbSlice = kDbStage * kDbSteps;   // K per X slice in LDS
+constexpr int kXsRow = kDbSlice + 8;            // LDS row pitch (elements): 16 B of padding spreads the rows over the banks
 constexpr int kMaxSeg = 3;
 
 // One product of a launch: C[rows][n] (+)= X[rows][k] W[n][k]^T.  Several
@@ -153,19 +155,23 @@ struct DecodeGemmArgs {
   int inter;          // gated mode: W = [gate; up] of 2 inter rows, C = silu(gate) * up [rows][inter]
 };
 
-// Decode-batch projection, one workgroup per (64 features, K range).  Each
-// of its four waves multiplies a quarter of the range into all 4 x 4 tiles
-// of C^T[64 n][64 b] with v_mfma_f32_16x16x32_bf16 (A = 16 rows of W, B = 16
-// rows of X, 8 k per lane from group lane / 16, 16-byte loads; a lane keeps
-// C^T rows 4 (lane / 16) .. + 3 of column lane % 16 of each tile), so each
-// weight byte is read once and each X byte once per 64 features.  The
-// waves' tiles are summed through LDS in two halves (32 KB), wave w
-// finishing column block w % 4, row blocks w / 4 + (waves / 4) q.  One K
-// range: the sums (plus C when accumulating) are rounded to bf16 into C;
-// several: they go as float32 to the product's partials for
-// decode_reduce_kernel.  Gated mode (kGlu): tile t takes gate rows
-// 32 t .. + 31 (row blocks 0, 1) and the matching up rows (row blocks 2, 3),
-// and writes silu(bf16(gate)) * bf16(up) for features 32 t .. + 31.
+// Decode-batch projection, one workgroup per (64 features, K range), each
+// of its four waves one block of 16 features over the whole range: C^T[16
+// n][64 b] as four 16 x 16 tiles of v_mfma_f32_16x16x32_bf16 (A = the
+// wave's 16 W rows, B = 16 rows of X; 8 k per lane from group lane / 16,
+// 16-byte loads; a lane keeps C^T rows 4 (lane / 16) .. + 3 of column
+// lane % 16 of each tile).  Each wave streams its 16 rows along K, so the
+// workgroup's loads in flight stay within a few DRAM pages per row (a wave
+// per K slice over all 64 rows instead keeps every page of the matrix open
+// at once and streams at half the rate).  X goes through LDS in slices of
+// 128 k (64 rows x 256 B, double-buffered, one barrier per slice), loaded
+// once per workgroup; W and X of the next slice are loaded while the
+// current one is multiplied.  One K range: the sums (plus C when
+// accumulating) are rounded to bf16 into C; several: they go as float32 to
+// the product's partials for decode_reduce_kernel.  Gated mode (kGlu): tile
+// t takes gate rows 32 t .. + 31 (waves 0, 1) and the matching up rows
+// (waves 2, 3), which hand their sums over through LDS; the gate waves
+// write silu(bf16(gate)) * bf16(up) for features 32 t .. + 31.
 template <bool kGlu>
 __global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGemmArgs args) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -178,109 +184,101 @@ __global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGem
   const int n0 = (t - args.seg[si].tile_begin) * kDbN;
   const int k = args.k, rows = args.rows;
   const int split = blockIdx.y;
-  const int kq = args.kchunk / kDbWaves;          // a multiple of kDbStage (checked on the host)
-  const int kbeg = split * args.kchunk + wv * kq;
+  const int nit = args.kchunk / kDbSlice;         // whole slices (checked on the host)
+  const int kbeg = split * args.kchunk;
   const int r16 = lane & 15;
   const int kg = 8 * (lane >> 4);
-  const uint16_t* wrow[4];
-  const uint16_t* xrow[4];
-  bool xok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int wr = kGlu ? (i < 2 ? 0 : args.inter) + 32 * t + 16 * (i & 1) + r16 : n0 + 16 * i + r16;
-    wrow[i] = w + (int64_t)wr * k + kbeg + kg;
-    const int b = 16 * i + r16;
-    xok[i] = b < rows;
-    xrow[i] = args.x + (int64_t)(xok[i] ? b : 0) * k + kbeg + kg;
-  }
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int kk = 0; kk < kq; kk += kDbStage) {
-    uint4 a[4], bx[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = *reinterpret_cast<const uint4*>(wrow[i] + kk);
-      bx[i] = *reinterpret_cast<const uint4*>(xrow[i] + kk);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)   // rows past the batch read row 0 and are zeroed, dword by dword
-      bx[j] = make_uint4(xok[j] ? bx[j].x : 0u, xok[j] ? bx[j].y : 0u, xok[j] ? bx[j].z : 0u,
-                         xok[j] ? bx[j].w : 0u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
-                                                            __builtin_bit_cast(bf16x8, bx[j]), acc[i][j], 0, 0, 0);
-  }
+  const int wr = kGlu ? (wv < 2 ? 0 : args.inter) + 32 * t + 16 * (wv & 1) + r16 : n0 + 16 * wv + r16;
+  const uint16_t* wrow = w + (int64_t)wr * k + kbeg + kg;
+  // X slice loads: thread i brings row i / 4's quarter i % 4 of the slice
+  // (rows past the batch read row 0 and store zeros)
+  constexpr int kXq = kDbSlice / 4 / 8;           // 16-byte loads per thread and slice
+  const int xr = threadIdx.x >> 2, xq = threadIdx.x & 3;
+  const bool xok = xr < rows;
+  const uint16_t* xsrc = args.x + (int64_t)(xok ? xr : 0) * k + kbeg + (kDbSlice / 4) * xq;
+  __shared__ uint16_t xs[2][kDbRows * kXsRow];
+  uint16_t* xdst = &xs[0][xr * kXsRow + (kDbSlice / 4) * xq];
 
-  // the second half of the waves hands its tiles to the first half, which
-  // adds them and publishes the result; every wave then sums its share of
-  // the tiles over the published copies
-  __shared__ f32x4 red[kDbWaves / 2][16][kWave];
-  if (wv >= kDbWaves / 2) {
+  f32x4 acc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // slices it + 1 and it + 2 are in flight while slice it is multiplied:
+  // three register sets for W and X, used in turn (the loop is unrolled by
+  // three so every set is named statically); loads past the last slice
+  // load the last one again (in bounds, its lines in L2)
+  auto load = [&](int it, uint4 (&wd)[kDbSteps], uint4 (&xd)[kXq]) {
+    const int off = (it < nit ? it : nit - 1) * kDbSlice;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) red[wv - kDbWaves / 2][4 * i + j][lane] = acc[i][j];
+    for (int u = 0; u < kDbSteps; ++u) wd[u] = *reinterpret_cast<const uint4*>(wrow + off + kDbStage * u);
+#pragma unroll
+    for (int q = 0; q < kXq; ++q) xd[q] = *reinterpret_cast<const uint4*>(xsrc + off + 8 * q);
+  };
+  auto slice = [&](int it, uint4 (&wu)[kDbSteps], uint4 (&xu)[kXq], uint4 (&wl)[kDbSteps], uint4 (&xl)[kXq]) {
+    const int buf = it & 1;
+    uint4* xd = reinterpret_cast<uint4*>(xdst + buf * kDbRows * kXsRow);
+#pragma unroll
+    for (int q = 0; q < kXq; ++q) xd[q] = xok ? xu[q] : make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    load(it + 2, wl, xl);
+    const uint16_t* xb = &xs[buf][r16 * kXsRow + kg];
+#pragma unroll
+    for (int u = 0; u < kDbSteps; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 bv = *reinterpret_cast<const uint4*>(xb + 16 * j * kXsRow + kDbStage * u);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wu[u]),
+                                                         __builtin_bit_cast(bf16x8, bv), acc[j], 0, 0, 0);
+      }
+  };
+  uint4 w0[kDbSteps], w1[kDbSteps], w2[kDbSteps], x0[kXq], x1[kXq], x2[kXq];
+  load(0, w0, x0);
+  load(1, w1, x1);
+  for (int it = 0;; it += 3) {
+    slice(it, w0, x0, w2, x2);
+    if (it + 1 >= nit) break;
+    slice(it + 1, w1, x1, w0, x0);
+    if (it + 2 >= nit) break;
+    slice(it + 2, w2, x2, w1, x1);
+    if (it + 3 >= nit) break;
   }
-  __syncthreads();
-  if (wv < kDbWaves / 2) {
+  if (kGlu) {   // up waves (2, 3) hand their tiles to gate waves (0, 1)
+    __shared__ f32x4 up[2][4][kWave];
+    if (wv >= 2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j) up[wv - 2][j][lane] = acc[j];
+    }
+    __syncthreads();
+    if (wv >= 2) return;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] += red[wv][4 * i + j][lane];
-  }
-  __syncthreads();
-  if (wv < kDbWaves / 2) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) red[wv][4 * i + j][lane] = acc[i][j];
-  }
-  __syncthreads();
-  // wave w finishes column block w % 4, row blocks w / 4 + (kDbWaves / 4) q
-  const int j = wv & 3;
-  const int b = 16 * j + r16;
-  f32x4 sum[kDbTilesPerWave];
-#pragma unroll
-  for (int q = 0; q < kDbTilesPerWave; ++q) {
-    const int tile = 4 * ((wv >> 2) + (kDbWaves / 4) * q) + j;
-    sum[q] = red[0][tile][lane];
-#pragma unroll
-    for (int u = 1; u < kDbWaves / 2; ++u) sum[q] += red[u][tile][lane];
-  }
-  if (b >= rows) return;
-  if (kGlu) {   // gate tiles are the first half of the wave's row blocks (0, 1), up tiles the second (2, 3)
-#pragma unroll
-    for (int q = 0; q < kDbTilesPerWave / 2; ++q) {
+    for (int j = 0; j < 4; ++j) {
+      const int b = 16 * j + r16;
+      if (b >= rows) continue;
+      const f32x4 u4 = up[wv][j][lane];
       uint32_t o[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         float r[2];
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const float g = bf16_lo(pack_bf16x2(sum[q][2 * e + f], 0.f));
-          const float u = bf16_lo(pack_bf16x2(sum[q + kDbTilesPerWave / 2][2 * e + f], 0.f));
+          const float g = bf16_lo(pack_bf16x2(acc[j][2 * e + f], 0.f));
+          const float u = bf16_lo(pack_bf16x2(u4[2 * e + f], 0.f));
           r[f] = g / (1.0f + expf(-g)) * u;
         }
         o[e] = pack_bf16x2(r[0], r[1]);
       }
-      const int f0 = 32 * t + 16 * ((wv >> 2) + (kDbWaves / 4) * q) + 4 * (lane >> 4);
+      const int f0 = 32 * t + 16 * wv + 4 * (lane >> 4);
       *reinterpret_cast<uint2*>(args.seg[0].c + (int64_t)b * args.inter + f0) = make_uint2(o[0], o[1]);
     }
     return;
   }
+  const int nn = n0 + 16 * wv + 4 * (lane >> 4);    // C^T rows nn .. nn + 3 of column b
 #pragma unroll
-  for (int q = 0; q < kDbTilesPerWave; ++q) {
-    const int nn = n0 + 16 * ((wv >> 2) + (kDbWaves / 4) * q) + 4 * (lane >> 4);   // C^T rows nn .. nn + 3 of column b
+  for (int j = 0; j < 4; ++j) {
+    const int b = 16 * j + r16;
+    if (b >= rows) continue;
     if (gridDim.y == 1) {
       uint16_t* crow = args.seg[si].c + (int64_t)b * n + nn;
-      float v[4] = {sum[q][0], sum[q][1], sum[q][2], sum[q][3]};
+      float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
       if (args.accumulate) {
         const uint2 old = *reinterpret_cast<const uint2*>(crow);
         v[0] += bf16_lo(old.x);
@@ -290,7 +288,7 @@ __global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGem
       }
       *reinterpret_cast<uint2*>(crow) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     } else {
-      *reinterpret_cast<f32x4*>(args.seg[si].part + ((int64_t)split * rows + b) * n + nn) = sum[q];
+      *reinterpret_cast<f32x4*>(args.seg[si].part + ((int64_t)split * rows + b) * n + nn) = acc[j];
     }
   }
 }
@@ -400,13 +398,15 @@ __global__ __launch_bounds__(kNormThreads) void reduce_residual_norm_kernel(uint
   }
 }
 
-// K splits for a decode-batch launch of `tiles` 64-feature tiles: the fewest
-// that give >= 256 workgroups (the chip's CUs), each wave keeping whole
-// stages; 0 if the shape does not fit the kernel.
+// K splits for a decode-batch launch of `tiles` 64-feature tiles: the most
+// (a power of two) that keep the workgroups within one round of the chip's
+// 256 CUs, each keeping whole X slices; 0 if the shape does not fit the
+// kernel.  (A second, partial round of workgroups costs more than the
+// parallelism it adds: 48 tiles x 8 splits ran 30% slower than x 4.)
 int decode_gemm_splits(int rows, int tiles, int k) {
-  if (rows <= 0 || rows > kDbRows || tiles <= 0 || k % (kDbStage * kDbWaves)) return 0;
+  if (rows <= 0 || rows > kDbRows || tiles <= 0 || k % kDbSlice) return 0;
   int s = 1;
-  while (tiles * s < 256 && k % (kDbStage * kDbWaves * s * 2) == 0) s *= 2;
+  while (tiles * s * 2 <= 256 && k % (kDbSlice * s * 2) == 0) s *= 2;
   return s;
 }
 
@@ -476,7 +476,7 @@ int decode_gemm(int nseg, uint16_t* const* c, const uint16_t* const* w, const in
 // PKV_ERR_INVALID_ARG (nothing launched) when the shape does not fit.
 int decode_gemm_glu(uint16_t* act, const uint16_t* x, const uint16_t* w, int rows, int inter, int k,
                     hipStream_t stream) {
-  if (rows <= 0 || rows > kDbRows || inter <= 0 || inter % 32 || k % (kDbStage * kDbWaves)) return PKV_ERR_INVALID_ARG;
+  if (rows <= 0 || rows > kDbRows || inter <= 0 || inter % 32 || k % kDbSlice) return PKV_ERR_INVALID_ARG;
   DecodeGemmArgs a{};
   a.seg[0] = GemmSeg{w, act, nullptr, 2 * inter, 0, inter / 32};
   a.x = x;

@@ -88,12 +88,14 @@ def test_silu_mul_within_one_ulp(gpu):
     assert d.max() <= 1 and (d == 0).mean() > 0.95
 
 
-# the projections of a decode batch (K split over 1 to 16 workgroups), a
-# wider batch and ragged shapes (both on rocBLAS), and a split shape handed a
-# null workspace (rocBLAS too)
+# the projections of a decode batch (K split over 1 to 16 workgroups, ragged
+# rows, one to three 128-wide X slices per workgroup), a wider batch and
+# K % 128 != 0 (both on rocBLAS), and a split shape handed a null workspace
+# (rocBLAS too)
 @pytest.mark.parametrize("rows,n,k,ws", [(64, 3072, 2048, None), (1, 512, 2048, None), (13, 2048, 8192, None),
                                          (64, 16384, 2048, None), (64, 2048, 2048, None), (64, 2048, 8192, None),
-                                         (37, 192, 384, None), (100, 512, 2048, None), (8, 64, 96, None),
+                                         (37, 192, 384, None), (100, 512, 2048, None), (8, 64, 104, None),
+                                         (5, 64, 128, None), (8, 64, 96, None),
                                          (64, 2048, 8192, False)])
 def test_linear_within_one_ulp(gpu, rows, n, k, ws):
     rng = np.random.default_rng(rows + n + k)
@@ -119,7 +121,7 @@ def test_linear_decode_batch_is_deterministic(gpu):
     rng = np.random.default_rng(77)
     rows, n, k = 64, 2048, 8192
     assert pkv.pkv_linear_workspace_bytes(rows, n, k) > 0
-    assert pkv.pkv_linear_workspace_bytes(65, n, k) == 0 and pkv.pkv_linear_workspace_bytes(64, 2048, 8000) == 0
+    assert pkv.pkv_linear_workspace_bytes(65, n, k) == 0 and pkv.pkv_linear_workspace_bytes(64, 2048, 8008) == 0
     x, w = dev_bf16(W.randn_bf16(rng, (rows, k))), dev_bf16(W.randn_bf16(rng, (n, k), layer.init_scale(k)))
     ws = torch.empty(pkv.pkv_linear_workspace_bytes(rows, n, k), dtype=torch.uint8, device="cuda")
     outs = []
