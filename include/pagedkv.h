@@ -551,7 +551,8 @@ typedef struct {
  * gate_up | act, each [batch][width] (widths hidden, n_q*64, n_kv*64, n_kv*64,
  * n_q*64, hidden, 2*intermediate, intermediate), in that order, then room for
  * the projections' float32 partials (the largest pkv_linear_workspace_bytes
- * of the six); 0 for invalid sizes. */
+ * over the layer's launches, Q/K/V together as one product of width
+ * (n_q + 2 n_kv) * 64); 0 for invalid sizes. */
 size_t pkv_decode_layer_scratch_elems(int batch, int hidden, int intermediate, int n_q_heads, int n_kv_heads);
 
 /* One layer's decode step for `batch` rows, in place on the residual stream
@@ -562,8 +563,12 @@ size_t pkv_decode_layer_scratch_elems(int batch, int hidden, int intermediate, i
  *   h += o Wo^T;  m = rmsnorm(h, mlp_norm);  gate_up = m Wgu^T;
  *   act = silu(gate) * up;  h += act Wd^T.
  * scratch: caller-owned device bf16, >= pkv_decode_layer_scratch_elems(...)
- * elements, any contents (the intermediates are left there).  All launches
- * go to `stream`. */
+ * elements, any contents (the intermediates are left there, except gate_up
+ * when the gated decode-batch launch computes act directly: batch <= 64,
+ * intermediate % 32 == 0, hidden % 128 == 0).  Decode batches run Q, K and
+ * V as one launch and fold the output projection's partials, the residual
+ * add and the MLP's RMSNorm into one kernel; results are deterministic.
+ * All launches go to `stream`. */
 int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* weights, int hidden, int intermediate,
                      pkv_bf16* scratch, size_t scratch_elems, pkv_bf16* k_pool, pkv_bf16* v_pool,
                      int num_blocks, const int32_t* block_table, int64_t bt_row_stride, int num_slots,

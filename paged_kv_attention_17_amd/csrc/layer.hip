@@ -431,12 +431,12 @@ int decode_gemm(int nseg, uint16_t* const* c, const uint16_t* const* w, const in
   if (nseg < 1 || nseg > kMaxSeg) return PKV_ERR_INVALID_ARG;
   int tiles = 0, ntot = 0;
   for (int i = 0; i < nseg; ++i) {
-    if (n[i] <= 0 || n[i] % kDbN) return PKV_ERR_INVALID_ARG;
+    if (n[i] <= 0 || n[i] % kDbN || n[i] > (1 << 24)) return PKV_ERR_INVALID_ARG;
     tiles += n[i] / kDbN;
     ntot += n[i];
   }
   const int splits = decode_gemm_splits(rows, tiles, k);
-  if (splits == 0) return PKV_ERR_INVALID_ARG;
+  if (splits == 0 || (int64_t)rows * ntot / 8 > 0x7fffff00) return PKV_ERR_INVALID_ARG;
   if (splits > 1 && (!part || part_bytes < (size_t)splits * rows * ntot * sizeof(float))) return PKV_ERR_INVALID_ARG;
   if (splits_out) *splits_out = splits;
   DecodeGemmArgs a{};
