@@ -134,10 +134,11 @@ def test_linear_decode_batch_is_deterministic(gpu):
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-# 4 rows take the decode-batch kernels (q, k, v in one launch, the gated
-# gate/up launch that leaves the gate_up buffer unwritten); 65 rows take
-# rocBLAS and the SiLU kernel
-@pytest.mark.parametrize("host_lens,extra_rows", [(True, 0), (False, 0), (True, 61)])
+# 4 and 64 rows (the most the decode-batch kernels take: every MFMA column
+# block full) take the decode-batch kernels (q, k, v in one launch, the
+# gated gate/up launch that leaves the gate_up buffer unwritten); 65 rows
+# take rocBLAS and the SiLU kernel
+@pytest.mark.parametrize("host_lens,extra_rows", [(True, 0), (False, 0), (False, 60), (True, 61)])
 def test_decode_layer_matches_oracle(gpu, host_lens, extra_rows):
     rng = np.random.default_rng(5)
     wts = _weights(rng)
