@@ -165,7 +165,7 @@ struct DecodeGemmArgs {
 // per K slice over all 64 rows instead keeps every page of the matrix open
 // at once and streams at half the rate).  X goes through LDS in slices of
 // 128 k (64 rows x 256 B, double-buffered, one barrier per slice), loaded
-// once per workgroup; W and X of the next slice are loaded while the
+// once per workgroup; W and X of the next two slices are in flight while the
 // current one is multiplied.  One K range: the sums (plus C when
 // accumulating) are rounded to bf16 into C; several: they go as float32 to
 // the product's partials for decode_reduce_kernel.  Gated mode (kGlu): tile
