@@ -490,12 +490,13 @@ def serving_leg(torch, np, pkv, W, n_req: int = 128, n_slots: int = 64, budget: 
 
 
 def decode_layer_leg(torch, np, pkv, eng, ctx_now, stream, iters: int = 5):
-    """Whole Llama-3.2-1B decode layers (pkv_decode_layer: RMSNorm, the
-    decode-batch projections, the fused paged attention, the gated MLP) for the B=64 rows
-    of the main workload, 16 layers, synthetic bf16 weights ~ N(0, 1/fan_in)
-    on the device (121 MB per layer).  Each layer's attention re-writes the
-    last token in place, like the attention timing.  HIP events around each
-    16-layer pass."""
+    """Whole Llama-3.2-1B decode layers (pkv_decode_layers: RMSNorm, the
+    decode-batch projections, the fused paged attention, the gated MLP; all
+    16 layers in one call) for the B=64 rows of the main workload, synthetic
+    bf16 weights ~ N(0, 1/fan_in) on the device (121 MB per layer).  Each
+    layer's attention re-writes the last token in place, like the attention
+    timing.  HIP events around each 16-layer pass; the same pass as one
+    pkv_decode_layer call per layer is timed too."""
     HID, INTER, NQ, NKV = 2048, 8192, 32, 8
     L = eng.n_layers
     B = len(ctx_now)
@@ -516,28 +517,38 @@ def decode_layer_leg(torch, np, pkv, eng, ctx_now, stream, iters: int = 5):
     scratch = torch.empty(pkv.pkv_decode_layer_scratch_elems(B, HID, INTER, NQ, NKV), dtype=torch.bfloat16,
                           device="cuda")
 
-    def one_pass():
+    def per_layer_calls():
         for layer in range(L):
             pkv.pkv_decode_layer(h, weights[layer], scratch, eng.k_pool, eng.v_pool, eng.bt_dev[:, layer, :], None,
                                  eng.ctx_dev, eng.max_context_len, eng.cos_sin, eng.scale, eng.workspace,
                                  row_lens_host=ctx_now, stream=stream)
 
-    one_pass()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(iters):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        one_pass()
-        e1.record(stream)
+    def one_call():
+        pkv.pkv_decode_layers(h, weights, scratch, eng.k_pool, eng.v_pool, eng.bt_dev, None, eng.ctx_dev,
+                              eng.max_context_len, eng.cos_sin, eng.scale, eng.workspace, row_lens_host=ctx_now,
+                              stream=stream)
+
+    def timed(fn):
+        fn()
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / 1e3)
-    t = float(np.median(times))
+        times = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 1e3)
+        return float(np.median(times))
+
+    t_calls = timed(per_layer_calls)
+    t = timed(one_call)
     del weights
     torch.cuda.empty_cache()
     return {"workload": f"Llama-3.2-1B decode step, B={B}, {L} layers, hidden 2048, intermediate 8192, synthetic "
                         "bf16 weights, the main workload's paged cache (ctx U[512,4096])",
             "ms_per_step": round(t * 1e3, 4), "us_per_layer": round(t / L * 1e6, 2),
+            "ms_per_step_layer_calls": round(t_calls * 1e3, 4),
             "tokens_per_s": round(B / t, 1), "weight_bytes_per_layer": wbytes,
             "kv_bytes_per_layer": int(ctx_now.sum()) * KV_BYTES_PER_TOKEN}
 

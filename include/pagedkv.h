@@ -567,7 +567,8 @@ size_t pkv_decode_layer_scratch_elems(int batch, int hidden, int intermediate, i
  * when the gated decode-batch launch computes act directly: batch <= 64,
  * intermediate % 32 == 0, hidden % 128 == 0).  Decode batches run Q, K and
  * V as one launch and fold the output projection's partials, the residual
- * add and the MLP's RMSNorm into one kernel; results are deterministic.
+ * add and the MLP's RMSNorm into one kernel; the projections are
+ * deterministic (K-split partials summed in a fixed order).
  * All launches go to `stream`. */
 int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* weights, int hidden, int intermediate,
                      pkv_bf16* scratch, size_t scratch_elems, pkv_bf16* k_pool, pkv_bf16* v_pool,
@@ -576,6 +577,27 @@ int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* weights, int hidden, 
                      const int32_t* row_lens_host, int batch, int max_context_len, int n_q_heads,
                      int n_kv_heads, const float* cos_sin, int max_pos, float scale, float eps,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* n_layers decode layers in one call, in place on h [batch][hidden]: layer l
+ * uses layers[l] and the block table block_table + l * bt_layer_stride (the
+ * layer views of a [slots][layers][max_blocks] table: bt_row_stride =
+ * layers * max_blocks, bt_layer_stride = max_blocks); every other argument
+ * as pkv_decode_layer, shared by the layers (one pool, one scratch, one
+ * workspace).  It runs the kernels and roundings of calling
+ * pkv_decode_layer for l = 0 .. n_layers - 1, except that between layers
+ * the down projection's K-split partials, the residual add and the next
+ * layer's attention RMSNorm are one kernel (bit-identical to the separate
+ * ones).  (In either form the streaming attention's float32 summation order
+ * depends on which of a KV head's two waves claims which block, so rows of
+ * more than one block may differ in the last bits from call to call.)
+ * Arguments of every layer are checked before anything is launched. */
+int pkv_decode_layers(pkv_bf16* h, const pkv_layer_weights* layers, int n_layers, int hidden, int intermediate,
+                      pkv_bf16* scratch, size_t scratch_elems, pkv_bf16* k_pool, pkv_bf16* v_pool,
+                      int num_blocks, const int32_t* block_table, int64_t bt_row_stride, int64_t bt_layer_stride,
+                      int num_slots, int max_blocks_per_seq, const int32_t* slot_ids, const int32_t* context_lens,
+                      const int32_t* row_lens_host, int batch, int max_context_len, int n_q_heads,
+                      int n_kv_heads, const float* cos_sin, int max_pos, float scale, float eps,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -16,5 +16,5 @@ from ._abi import (  # noqa: F401
     pkv_decode_workspace_bytes, pkv_decode_partition_size, pkv_paged_attn_decode, pkv_paged_attn_prefill,
     pkv_decode_step, pkv_decode_workspace_init, pkv_paged_decode_fused, decode_workspace, Scheduler,
     pkv_rmsnorm, pkv_silu_mul, pkv_linear, pkv_linear_workspace_bytes, pkv_decode_layer,
-    pkv_decode_layer_scratch_elems,
+    pkv_decode_layer_scratch_elems, pkv_decode_layers,
 )

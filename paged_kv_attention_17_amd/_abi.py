@@ -76,6 +76,8 @@ SIGNATURES = {
     "pkv_decode_layer_scratch_elems": (_sz, [_i, _i, _i, _i, _i]),
     "pkv_decode_layer": (_i, [_p, _p, _i, _i, _p, _sz, _p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _i, _i, _i, _p,
                               _i, _f, _f, _p, _sz, _p]),
+    "pkv_decode_layers": (_i, [_p, _p, _i, _i, _i, _p, _sz, _p, _p, _i, _p, _i64, _i64, _i, _i, _p, _p, _p, _i, _i, _i,
+                               _i, _p, _i, _f, _f, _p, _sz, _p]),
     "pkv_sched_run": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _p, _i, _f, _p, _sz, _p]),
 }
 
@@ -787,6 +789,57 @@ class LayerWeights(C.Structure):
 
 def pkv_decode_layer_scratch_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads):
     return load().pkv_decode_layer_scratch_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads)
+
+
+def _layer_weights(weights, hidden, n_q_heads, lw=None):
+    """Fill a LayerWeights from a dict of device bf16 tensors; returns it
+    with the intermediate width."""
+    bt16 = _bf16_types()
+    lw = LayerWeights() if lw is None else lw
+    inter = weights["w_down"].shape[1]
+    for name in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate_up", "w_down"):
+        _contig(weights[name], name)
+        setattr(lw, name, _dev_ptr(weights[name], name, bt16))
+    if weights["wq"].shape != (n_q_heads * 64, hidden) or weights["w_gate_up"].shape != (2 * inter, hidden):
+        raise ValueError("weight shapes do not match hidden / heads / intermediate")
+    return lw, inter
+
+
+def pkv_decode_layers(h, layers, scratch, k_pool, v_pool, block_table, slot_ids, context_lens, max_context_len,
+                      cos_sin, scale, workspace, row_lens_host=None, eps=1e-5, n_q_heads=32, stream=None):
+    """len(layers) decode layers in one call, in place on h [B, hidden]
+    (pkv_decode_layers).  layers: list of weight dicts as for
+    pkv_decode_layer; block_table: int32 [slots, >= len(layers), max_blocks]
+    with unit inner stride (layer l uses block_table[:, l, :])."""
+    import torch
+    bt16 = _bf16_types()
+    for t, n in ((h, "h"), (scratch, "scratch"), (k_pool, "k_pool"), (v_pool, "v_pool"), (cos_sin, "cos_sin"),
+                 (workspace, "workspace")):
+        _contig(t, n)
+    B, hidden = h.shape
+    L = len(layers)
+    if block_table.dtype != torch.int32 or block_table.dim() != 3 or block_table.stride(2) != 1:
+        raise ValueError("block_table must be an int32 [slots, layers, max_blocks] tensor with unit inner stride")
+    if block_table.shape[1] < L:
+        raise ValueError("block_table has fewer layers than weights")
+    arr = (LayerWeights * max(L, 1))()
+    inter = None
+    for l, wd in enumerate(layers):
+        _, il = _layer_weights(wd, hidden, n_q_heads, arr[l])
+        if inter is not None and il != inter:
+            raise ValueError("layers disagree on the intermediate width")
+        inter = il
+    if inter is None:
+        return
+    rl, rl_ptr = _row_lens(row_lens_host, B)
+    _check("pkv_decode_layers", load().pkv_decode_layers(
+        _dev_ptr(h, "h", bt16), arr, L, hidden, inter, _dev_ptr(scratch, "scratch", bt16), scratch.numel(),
+        _dev_ptr(k_pool, "k_pool", bt16), _dev_ptr(v_pool, "v_pool", bt16), k_pool.shape[0],
+        _dev_ptr(block_table, "block_table"), block_table.stride(0), block_table.stride(1), block_table.shape[0],
+        block_table.shape[2], _dev_ptr(slot_ids, "slot_ids", (torch.int32,)),
+        _dev_ptr(context_lens, "context_lens", (torch.int32,)), rl_ptr, B, int(max_context_len), n_q_heads,
+        k_pool.shape[2], _dev_ptr(cos_sin, "cos_sin", (torch.float32,)), cos_sin.shape[0], float(scale), float(eps),
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def pkv_decode_layer(h, weights, scratch, k_pool, v_pool, block_table, slot_ids, context_lens, max_context_len,

@@ -600,22 +600,21 @@ extern "C" size_t pkv_decode_layer_scratch_elems(int batch, int hidden, int inte
          layer_partial_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads);
 }
 
-extern "C" int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int intermediate,
-                                pkv_bf16* scratch, size_t scratch_elems, pkv_bf16* k_pool, pkv_bf16* v_pool,
-                                int num_blocks, const int32_t* block_table, int64_t bt_row_stride, int num_slots,
-                                int max_blocks_per_seq, const int32_t* slot_ids, const int32_t* context_lens,
-                                const int32_t* row_lens_host, int batch, int max_context_len, int n_q_heads,
-                                int n_kv_heads, const float* cos_sin, int max_pos, float scale, float eps,
-                                void* workspace, size_t workspace_bytes, void* stream) {
-  if (batch < 0 || hidden <= 0 || intermediate <= 0 || n_q_heads <= 0 || n_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
-  if (batch == 0) return PKV_OK;
-  if (!h || !w || !scratch || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->mlp_norm ||
-      !w->w_gate_up || !w->w_down)
-    return PKV_ERR_NULL;
-  if (hidden % 8 || intermediate % 8) return PKV_ERR_INVALID_ARG;
-  if (scratch_elems < pkv_decode_layer_scratch_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads))
-    return PKV_ERR_CAPACITY;
-  if (!aligned16(h) || !aligned16(scratch)) return PKV_ERR_MISALIGNED;
+namespace {
+
+// One layer; `a_ready`: the scratch's a already holds rmsnorm(h, attn_norm)
+// (left there by the previous layer).  With `next_norm` the layer ends by
+// leaving a = rmsnorm(h, next_norm) for the next layer: where the down
+// projection's K is split, its partials, the residual add and that norm are
+// one kernel (as the output projection's are with the MLP's norm).  Argument
+// checks are the callers'.
+int decode_layer_impl(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int intermediate, pkv_bf16* scratch,
+                      pkv_bf16* k_pool, pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
+                      int64_t bt_row_stride, int num_slots, int max_blocks_per_seq, const int32_t* slot_ids,
+                      const int32_t* context_lens, const int32_t* row_lens_host, int batch, int max_context_len,
+                      int n_q_heads, int n_kv_heads, const float* cos_sin, int max_pos, float scale, float eps,
+                      void* workspace, size_t workspace_bytes, void* stream, bool a_ready,
+                      const pkv_bf16* next_norm) {
   const int qd = n_q_heads * kHeadDim, kvd = n_kv_heads * kHeadDim;
   pkv_bf16* a = scratch;
   pkv_bf16* q = a + (size_t)batch * hidden;
@@ -629,7 +628,7 @@ extern "C" int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* w, int hid
   const size_t part_bytes = 2 * layer_partial_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   int rc;
-  if ((rc = pkv_rmsnorm(a, h, w->attn_norm, batch, hidden, eps, stream)) != PKV_OK) return rc;
+  if (!a_ready && (rc = pkv_rmsnorm(a, h, w->attn_norm, batch, hidden, eps, stream)) != PKV_OK) return rc;
   // q, k and v in one launch where the decode-batch kernel takes the shape
   {
     uint16_t* cs[3] = {q, k, v};
@@ -648,22 +647,21 @@ extern "C" int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* w, int hid
                                    n_q_heads, n_kv_heads, kHeadDim, cos_sin, max_pos, scale, 0, workspace,
                                    workspace_bytes, stream)) != PKV_OK)
     return rc;
-  // h += o Wo^T; with K split, the partials' sum, the residual add and the
-  // MLP's RMSNorm are one kernel
-  {
+  // h += x W^T, then (norm_w given) y = rmsnorm(h, norm_w): with K split, the
+  // partials' sum, the residual add and the norm are one kernel
+  auto residual = [&](const uint16_t* x, const uint16_t* wt, int kdim, const pkv_bf16* norm_w, pkv_bf16* y) {
     uint16_t* cs[1] = {h};
-    const uint16_t* ws[1] = {w->wo};
+    const uint16_t* ws[1] = {wt};
     const int ns[1] = {hidden};
     int splits = 0;
-    rc = decode_gemm(1, cs, ws, ns, o, batch, qd, true, part, part_bytes, st, false, &splits);
-    if (rc == PKV_OK && splits > 1) {
-      rc = reduce_residual_norm(h, m, static_cast<const float*>(part), w->mlp_norm, batch, hidden, splits, eps, st);
-    } else {
-      if (rc == PKV_ERR_INVALID_ARG) rc = pkv_linear(h, o, w->wo, batch, hidden, qd, 1, part, part_bytes, stream);
-      if (rc == PKV_OK) rc = pkv_rmsnorm(m, h, w->mlp_norm, batch, hidden, eps, stream);
-    }
-    if (rc != PKV_OK) return rc;
-  }
+    int r = decode_gemm(1, cs, ws, ns, x, batch, kdim, true, part, part_bytes, st, norm_w == nullptr, &splits);
+    if (r == PKV_OK && splits > 1 && norm_w)
+      return reduce_residual_norm(h, y, static_cast<const float*>(part), norm_w, batch, hidden, splits, eps, st);
+    if (r == PKV_ERR_INVALID_ARG) r = pkv_linear(h, x, wt, batch, hidden, kdim, 1, part, part_bytes, stream);
+    if (r == PKV_OK && norm_w) r = pkv_rmsnorm(y, h, norm_w, batch, hidden, eps, stream);
+    return r;
+  };
+  if ((rc = residual(o, w->wo, qd, w->mlp_norm, m)) != PKV_OK) return rc;
   // act = silu(m Wg^T) * (m Wu^T): one gated launch where it fits, else the
   // product into gate_up and the SiLU kernel
   rc = decode_gemm_glu(act, m, w->w_gate_up, batch, intermediate, hidden, st);
@@ -673,5 +671,65 @@ extern "C" int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* w, int hid
     rc = pkv_silu_mul(act, gu, batch, intermediate, stream);
   }
   if (rc != PKV_OK) return rc;
-  return pkv_linear(h, act, w->w_down, batch, hidden, intermediate, 1, part, part_bytes, stream);
+  return residual(act, w->w_down, intermediate, next_norm, a);
+}
+
+int check_layer_args(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int intermediate, pkv_bf16* scratch,
+                     size_t scratch_elems, int batch, int n_q_heads, int n_kv_heads) {
+  if (hidden <= 0 || intermediate <= 0 || n_q_heads <= 0 || n_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
+  if (!h || !w || !scratch || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->mlp_norm ||
+      !w->w_gate_up || !w->w_down)
+    return PKV_ERR_NULL;
+  if (hidden % 8 || intermediate % 8) return PKV_ERR_INVALID_ARG;
+  if (scratch_elems < pkv_decode_layer_scratch_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads))
+    return PKV_ERR_CAPACITY;
+  if (!aligned16(h) || !aligned16(scratch)) return PKV_ERR_MISALIGNED;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int intermediate,
+                                pkv_bf16* scratch, size_t scratch_elems, pkv_bf16* k_pool, pkv_bf16* v_pool,
+                                int num_blocks, const int32_t* block_table, int64_t bt_row_stride, int num_slots,
+                                int max_blocks_per_seq, const int32_t* slot_ids, const int32_t* context_lens,
+                                const int32_t* row_lens_host, int batch, int max_context_len, int n_q_heads,
+                                int n_kv_heads, const float* cos_sin, int max_pos, float scale, float eps,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0) return PKV_ERR_INVALID_ARG;
+  if (batch == 0) return hidden > 0 && intermediate > 0 && n_q_heads > 0 && n_kv_heads > 0 ? PKV_OK
+                                                                                          : PKV_ERR_INVALID_ARG;
+  int rc = check_layer_args(h, w, hidden, intermediate, scratch, scratch_elems, batch, n_q_heads, n_kv_heads);
+  if (rc != PKV_OK) return rc;
+  return decode_layer_impl(h, w, hidden, intermediate, scratch, k_pool, v_pool, num_blocks, block_table,
+                           bt_row_stride, num_slots, max_blocks_per_seq, slot_ids, context_lens, row_lens_host, batch,
+                           max_context_len, n_q_heads, n_kv_heads, cos_sin, max_pos, scale, eps, workspace,
+                           workspace_bytes, stream, false, nullptr);
+}
+
+extern "C" int pkv_decode_layers(pkv_bf16* h, const pkv_layer_weights* layers, int n_layers, int hidden,
+                                 int intermediate, pkv_bf16* scratch, size_t scratch_elems, pkv_bf16* k_pool,
+                                 pkv_bf16* v_pool, int num_blocks, const int32_t* block_table, int64_t bt_row_stride,
+                                 int64_t bt_layer_stride, int num_slots, int max_blocks_per_seq,
+                                 const int32_t* slot_ids, const int32_t* context_lens, const int32_t* row_lens_host,
+                                 int batch, int max_context_len, int n_q_heads, int n_kv_heads, const float* cos_sin,
+                                 int max_pos, float scale, float eps, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (n_layers < 0 || batch < 0 || bt_layer_stride < 0) return PKV_ERR_INVALID_ARG;
+  if (n_layers == 0 || batch == 0) return PKV_OK;
+  if (!layers || !block_table) return PKV_ERR_NULL;
+  for (int l = 0; l < n_layers; ++l) {
+    const int rc = check_layer_args(h, &layers[l], hidden, intermediate, scratch, scratch_elems, batch, n_q_heads,
+                                    n_kv_heads);
+    if (rc != PKV_OK) return rc;
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    const int rc = decode_layer_impl(h, &layers[l], hidden, intermediate, scratch, k_pool, v_pool, num_blocks,
+                                     block_table + bt_layer_stride * l, bt_row_stride, num_slots, max_blocks_per_seq,
+                                     slot_ids, context_lens, row_lens_host, batch, max_context_len, n_q_heads,
+                                     n_kv_heads, cos_sin, max_pos, scale, eps, workspace, workspace_bytes, stream,
+                                     l > 0, l + 1 < n_layers ? layers[l + 1].attn_norm : nullptr);
+    if (rc != PKV_OK) return rc;
+  }
+  return PKV_OK;
 }
