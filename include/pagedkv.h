@@ -275,7 +275,11 @@ int pkv_decode_partition_size(int batch, int n_kv_heads, int max_context_len);
  * (context_lens[slot_ids[b]]), batch <= 256.  When given, only the partitions
  * that exist are launched, longest first; the kernels still take their lengths
  * from context_lens, and the two must agree (otherwise the result is
- * unspecified).  NULL launches the max_context_len grid.
+ * unspecified).  NULL launches the max_context_len grid.  With host lengths
+ * the streaming kernel, when it serves the call, hands a row's blocks to a
+ * KV head's two waves as they ask for them, so a row of several blocks is
+ * summed in a timing-dependent float32 order (its output may differ in the
+ * last bits from call to call); without them the order is fixed.
  * partition_size: 0 = automatic, else a positive multiple of 16.
  * workspace: at least pkv_decode_workspace_bytes(...) bytes of device memory,
  * 16-byte aligned, any contents (every value read is written first in the same
