@@ -116,6 +116,52 @@ def test_other_entry_points_argument_errors(lib):
     assert lib.pkv_block_table_patch(FAKE, 10, offs.ctypes.data, offs.ctypes.data, 0, None) == E.PKV_OK
 
 
+
+def test_layer_sizes_and_argument_errors(lib):
+    E = _abi
+    # K-split partials: splits x rows x features x 4 bytes, the most splits
+    # (a power of two) that keep the workgroups within 256 and K in whole
+    # 128-wide slices; nothing for shapes the decode-batch kernel does not take
+    assert pkv.pkv_linear_workspace_bytes(64, 2048, 8192) == 8 * 64 * 2048 * 4
+    assert pkv.pkv_linear_workspace_bytes(64, 3072, 2048) == 4 * 64 * 3072 * 4
+    assert pkv.pkv_linear_workspace_bytes(1, 512, 2048) == 16 * 1 * 512 * 4
+    assert pkv.pkv_linear_workspace_bytes(64, 16384, 2048) == 0       # 256 tiles: no split
+    assert pkv.pkv_linear_workspace_bytes(65, 2048, 8192) == 0        # rows past the kernel's 64
+    assert pkv.pkv_linear_workspace_bytes(64, 2048, 8008) == 0        # K % 128
+    assert pkv.pkv_linear_workspace_bytes(64, 100, 2048) == 0         # features % 64
+    # layer scratch: the eight activations, then the largest partials (the
+    # 2048-wide products at 8 splits, 4 MiB = 2 Mi bf16 elements)
+    acts = 64 * (2048 * 2 + 2048 * 2 + 512 * 2 + 8192 * 3)
+    assert pkv.pkv_decode_layer_scratch_elems(64, 2048, 8192, 32, 8) == acts + 4 * 64 * 2048 * 8 // 2
+    assert pkv.pkv_decode_layer_scratch_elems(0, 2048, 8192, 32, 8) == 0
+    # pkv_linear: checks before any launch
+    assert lib.pkv_linear(FAKE, FAKE, FAKE, -1, 64, 128, 0, None, 0, None) == E.PKV_ERR_INVALID_ARG
+    assert lib.pkv_linear(FAKE, FAKE, FAKE, 0, 64, 128, 0, None, 0, None) == E.PKV_OK
+    assert lib.pkv_linear(None, FAKE, FAKE, 4, 64, 128, 0, None, 0, None) == E.PKV_ERR_NULL
+    assert lib.pkv_linear(FAKE, FAKE + 8, FAKE, 4, 64, 128, 0, None, 0, None) == E.PKV_ERR_MISALIGNED
+    assert lib.pkv_linear(FAKE, FAKE, FAKE, 4, 64, 128, 0, FAKE + 4, 64, None) == E.PKV_ERR_MISALIGNED
+    # the layer calls: a null weight, a short scratch, the multi-layer call's own arguments
+    lw = _abi.LayerWeights(*([FAKE] * 8))
+    lw_null = _abi.LayerWeights(*([FAKE] * 7 + [None]))
+    need = pkv.pkv_decode_layer_scratch_elems(4, 2048, 8192, 32, 8)
+
+    def layer(w, scratch_elems):
+        return lib.pkv_decode_layer(FAKE, C.byref(w), 2048, 8192, FAKE, scratch_elems, FAKE, FAKE, 8, FAKE, 4, 4, 2,
+                                    None, FAKE, None, 4, 17, 32, 8, FAKE, 100, 0.125, 1e-5, FAKE, 1 << 20, None)
+    assert layer(lw_null, need) == E.PKV_ERR_NULL
+    assert layer(lw, need - 1) == E.PKV_ERR_CAPACITY
+
+    def layers(arr, n, scratch_elems=need, bt=FAKE):
+        return lib.pkv_decode_layers(FAKE, arr, n, 2048, 8192, FAKE, scratch_elems, FAKE, FAKE, 8, bt, 8, 4, 4, 2,
+                                     None, FAKE, None, 4, 17, 32, 8, FAKE, 100, 0.125, 1e-5, FAKE, 1 << 20, None)
+    two = (_abi.LayerWeights * 2)(lw, lw_null)
+    assert layers(two, -1) == E.PKV_ERR_INVALID_ARG
+    assert layers(two, 0) == E.PKV_OK
+    assert layers(None, 2) == E.PKV_ERR_NULL
+    assert layers(two, 2, bt=None) == E.PKV_ERR_NULL
+    assert layers(two, 2) == E.PKV_ERR_NULL                   # the second layer's null weight, found before any launch
+    assert layers((_abi.LayerWeights * 1)(lw), 1, scratch_elems=need - 1) == E.PKV_ERR_CAPACITY
+
 # ------------------------------------------------------- block allocation --
 
 def test_blocks_assign_walk_is_valid_every_step(lib):
