@@ -151,7 +151,7 @@ struct GemmSeg {
 struct DecodeGemmArgs {
   GemmSeg seg[kMaxSeg];
   const uint16_t* x;
-  int nseg, rows, k, kchunk, accumulate;
+  int nseg, rows, k, kchunk, splits, accumulate;
   int inter;          // gated mode: W = [gate; up] of 2 inter rows, C = silu(gate) * up [rows][inter]
 };
 
@@ -176,14 +176,17 @@ template <bool kGlu>
 __global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGemmArgs args) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int t = blockIdx.x;
+  // workgroup id = tile x splits + split: ids go to the 8 XCDs in turn, so
+  // with 8 splits each XCD (its own L2) takes one K range and fetches only
+  // that eighth of X; numbered tile-first, every XCD would fetch all of X
+  const int t = blockIdx.x / args.splits;
+  const int split = blockIdx.x % args.splits;
   int si = 0;
   while (si + 1 < args.nseg && t >= args.seg[si].tile_end) ++si;
   const uint16_t* __restrict__ w = args.seg[si].w;
   const int n = args.seg[si].n;
   const int n0 = (t - args.seg[si].tile_begin) * kDbN;
   const int k = args.k, rows = args.rows;
-  const int split = blockIdx.y;
   const int nit = args.kchunk / kDbSlice;         // whole slices (checked on the host)
   const int kbeg = split * args.kchunk;
   const int r16 = lane & 15;
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGem
   for (int j = 0; j < 4; ++j) {
     const int b = 16 * j + r16;
     if (b >= rows) continue;
-    if (gridDim.y == 1) {
+    if (args.splits == 1) {
       uint16_t* crow = args.seg[si].c + (int64_t)b * n + nn;
       float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
       if (args.accumulate) {
@@ -457,9 +460,10 @@ int decode_gemm(int nseg, uint16_t* const* c, const uint16_t* const* w, const in
   a.rows = rows;
   a.k = k;
   a.kchunk = k / splits;
+  a.splits = splits;
   a.accumulate = accumulate ? 1 : 0;
   void* args[] = {&a};
-  int rc = launch_status(hipLaunchKernel((const void*)decode_gemm_kernel<false>, dim3(tiles, splits),
+  int rc = launch_status(hipLaunchKernel((const void*)decode_gemm_kernel<false>, dim3(tiles * splits),
                                          dim3(kDbWaves * kWave), args, 0, stream));
   if (rc != PKV_OK || splits == 1 || !reduce) return rc;
   ra.nseg = nseg;
@@ -484,6 +488,7 @@ int decode_gemm_glu(uint16_t* act, const uint16_t* x, const uint16_t* w, int row
   a.rows = rows;
   a.k = k;
   a.kchunk = k;
+  a.splits = 1;
   a.inter = inter;
   void* args[] = {&a};
   return launch_status(hipLaunchKernel((const void*)decode_gemm_kernel<true>, dim3(inter / 32, 1),
