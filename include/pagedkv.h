@@ -275,11 +275,10 @@ int pkv_decode_partition_size(int batch, int n_kv_heads, int max_context_len);
  * (context_lens[slot_ids[b]]), batch <= 256.  When given, only the partitions
  * that exist are launched, longest first; the kernels still take their lengths
  * from context_lens, and the two must agree (otherwise the result is
- * unspecified).  NULL launches the max_context_len grid.  With host lengths
- * the streaming kernel, when it serves the call, hands a row's blocks to a
- * KV head's two waves as they ask for them, so a row of several blocks is
- * summed in a timing-dependent float32 order (its output may differ in the
- * last bits from call to call); without them the order is fixed.
+ * unspecified).  NULL launches the max_context_len grid.  Either way a row's
+ * float32 sums are taken in an order fixed by the row lengths (and the
+ * partition size): the same inputs give the same bits from call to call and
+ * under any placement of the row's blocks in the pool.
  * partition_size: 0 = automatic, else a positive multiple of 16.
  * workspace: at least pkv_decode_workspace_bytes(...) bytes of device memory,
  * 16-byte aligned, any contents (every value read is written first in the same
@@ -522,21 +521,20 @@ int pkv_rmsnorm(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weight, int ro
  * intermediate % 8 == 0. */
 int pkv_silu_mul(pkv_bf16* act, const pkv_bf16* gate_up, int rows, int intermediate, void* stream);
 
-/* Bytes of float32 partials pkv_linear needs for this shape (0: none).
- * Nonzero only for decode-batch shapes (rows <= 64, out_features % 64 == 0,
- * in_features % 128 == 0) where K is split across workgroups. */
+/* Bytes of float32 partials pkv_linear needs for this shape (0: none):
+ * nonzero where the product's K is split across workgroups (few output
+ * tiles for the chip's 256 CUs). */
 size_t pkv_linear_workspace_bytes(int rows, int out_features, int in_features);
 
 /* out[rows][out_features] = x[rows][in_features] weight^T (+ out when
- * accumulate != 0), float32 sums, one rounding per output.  Decode-batch
- * shapes (see pkv_linear_workspace_bytes) run on the library's MFMA kernel,
- * deterministic (partials summed in a fixed order); when that shape needs
- * partials and `workspace` (caller-owned device memory, 16-byte aligned,
+ * accumulate != 0), float32 sums, one rounding per output, on the library's
+ * MFMA projection kernel (one workgroup per 64 features and 64-row block,
+ * deterministic: K-split partials summed in a fixed order).  When the shape
+ * splits K and `workspace` (caller-owned device memory, 16-byte aligned,
  * contents ignored and overwritten) is null or smaller than
- * pkv_linear_workspace_bytes(...), and for every other shape, the product
- * is a rocBLAS bf16 GEMM (one rocBLAS handle per device, kept for the
- * process; concurrent calls on one device from several host threads must be
- * serialised by the caller).  out must not overlap x or weight. */
+ * pkv_linear_workspace_bytes(...), the product runs as one K range.
+ * out_features and in_features must be multiples of 8
+ * (PKV_ERR_UNSUPPORTED otherwise).  out must not overlap x or weight. */
 int pkv_linear(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weight, int rows, int out_features,
                int in_features, int accumulate, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -568,11 +566,12 @@ size_t pkv_decode_layer_scratch_elems(int batch, int hidden, int intermediate, i
  *   act = silu(gate) * up;  h += act Wd^T.
  * scratch: caller-owned device bf16, >= pkv_decode_layer_scratch_elems(...)
  * elements, any contents (the intermediates are left there, except gate_up
- * when the gated decode-batch launch computes act directly: batch <= 64,
- * intermediate % 32 == 0, hidden % 128 == 0).  Decode batches run Q, K and
- * V as one launch and fold the output projection's partials, the residual
- * add and the MLP's RMSNorm into one kernel; the projections are
- * deterministic (K-split partials summed in a fixed order).
+ * when the gated launch computes act directly: intermediate % 32 == 0).
+ * Q, K and V run as one launch, and the output projection's K-split
+ * partials, the residual add and the MLP's RMSNorm are one kernel; the
+ * projections are deterministic (partials summed in a fixed order).
+ * hidden and intermediate must be multiples of 8.  Every argument, the
+ * attention call's included, is checked before anything is launched.
  * All launches go to `stream`. */
 int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* weights, int hidden, int intermediate,
                      pkv_bf16* scratch, size_t scratch_elems, pkv_bf16* k_pool, pkv_bf16* v_pool,
@@ -591,10 +590,7 @@ int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* weights, int hidden, 
  * pkv_decode_layer for l = 0 .. n_layers - 1, except that between layers
  * the down projection's K-split partials, the residual add and the next
  * layer's attention RMSNorm are one kernel (bit-identical to the separate
- * ones).  (In either form the streaming attention's float32 summation order
- * depends on which of a KV head's two waves claims which block, so rows of
- * more than one block may differ in the last bits from call to call.)
- * Arguments of every layer are checked before anything is launched. */
+ * ones).  Arguments of every layer are checked before anything is launched. */
 int pkv_decode_layers(pkv_bf16* h, const pkv_layer_weights* layers, int n_layers, int hidden, int intermediate,
                       pkv_bf16* scratch, size_t scratch_elems, pkv_bf16* k_pool, pkv_bf16* v_pool,
                       int num_blocks, const int32_t* block_table, int64_t bt_row_stride, int64_t bt_layer_stride,

@@ -66,20 +66,6 @@ def decode(q_bits, k_pool, v_pool, bt, slot_ids, context_lens, scale):
     return out
 
 
-def decode_rows(q_bits, k_pool, v_pool, bt, slot_ids, context_lens, scale, rows):
-    """``decode`` for a subset of batch rows only (for sampled checks at
-    full size).  Returns {row: [n_q][d] float64}."""
-    q = bf16.to_f64(q_bits)
-    res = {}
-    for b in rows:
-        s = int(slot_ids[b])
-        n = int(context_lens[s])
-        K = bf16.to_f64(paging.gather(k_pool, bt[s], n))
-        V = bf16.to_f64(paging.gather(v_pool, bt[s], n))
-        res[b] = _attend(q[b], K, V, scale)
-    return res
-
-
 def prefill(q_bits, cu_q_lens, q_start, slot_ids, k_pool, v_pool, bt, scale):
     """Causal attention for query tokens packed along dimension 0.
 

@@ -759,8 +759,8 @@ def pkv_linear(out, x, weight, accumulate=False, workspace=None, stream=None):
     """out = x weight^T (+ out when accumulate); x [rows, in], weight [out, in].
     workspace: device tensor of at least pkv_linear_workspace_bytes(...) bytes
     for the K-split partials, allocated here when None and the shape needs
-    it; False hands the library a null workspace (such shapes then run on
-    rocBLAS)."""
+    it; False hands the library a null workspace (the product then runs as
+    one K range)."""
     import torch
     for t, n in ((out, "out"), (x, "x"), (weight, "weight")):
         _contig(t, n)

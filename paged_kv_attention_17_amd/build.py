@@ -2,9 +2,10 @@
 
     python -m paged_kv_attention_17_amd.build        (or __graft_entry__.build())
 
-Every .hip file under csrc/ is compiled for gfx950 only; host_blocks.cpp is
-plain C++ (no device code).  Objects go to <repo>/_build/, the shared library
-to the package directory, where the Python binding looks for it.
+Every .hip file under csrc/ is compiled for gfx950 only; the .cpp files are
+plain C++ (no device code).  The library links nothing beyond the HIP
+runtime.  Objects go to <repo>/_build/, the shared library to the package
+directory, where the Python binding looks for it.
 """
 from __future__ import annotations
 
@@ -68,8 +69,7 @@ def build(verbose: bool = False) -> str:
                 print(r.stdout, r.stderr, file=sys.stderr)
     objs = [j[-1] for j in jobs]
     tmp = LIB + ".tmp"
-    # rocBLAS serves the layer's plain projections (pkv_linear)
-    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-lrocblas", "-o", tmp])
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

@@ -39,7 +39,7 @@
 // attention from registers, and the workgroup of the last partition writes the
 // rotated key and the value into their pool row at the end of the kernel.
 #include "attn_block.h"
-#include "decode_stream.h"
+#include "decode_api.h"
 
 #include <algorithm>
 
@@ -448,42 +448,13 @@ static void build_plan(DecodeArgs& a, const int32_t* row_lens_host, int batch) {
   a.n_items = a.full_items + batch;
 }
 
-static int decode_launch(bool fused, DecodeArgs& a, float scale, int batch, int max_context_len,
-                         int partition_size, const int32_t* row_lens_host, void* workspace,
-                         size_t workspace_bytes, hipStream_t st) {
-  if (row_lens_host) {
-    StreamCall sc{};
-    sc.out = a.out;
-    sc.q = a.q;
-    sc.k_new = a.k_new;
-    sc.v_new = a.v_new;
-    sc.k_pool = a.k_pool;
-    sc.v_pool = a.v_pool;
-    sc.num_blocks = a.num_blocks;
-    sc.block_table = a.bt;
-    sc.bt_row_stride = a.bt_stride;
-    sc.num_slots = a.num_slots;
-    sc.max_blocks = a.max_blocks;
-    sc.slot_ids = a.slot_ids;
-    sc.row_lens_host = row_lens_host;
-    sc.batch = batch;
-    sc.n_q = a.n_q;
-    sc.n_kv = a.n_kv;
-    sc.cos_sin = reinterpret_cast<const float*>(a.rope);
-    sc.max_pos = a.max_pos;
-    sc.scale = scale;
-    sc.workspace = workspace;
-    sc.workspace_bytes = workspace_bytes;
-    sc.stream = st;
-    const int rc = stream_decode(fused, sc);
-    if (rc != -1) return rc;
-  }
+// The per-partition kernels (and their merge) for a checked call.
+static int partition_launch(bool fused, DecodeArgs& a, int batch, int max_context_len, int partition_size,
+                            const int32_t* row_lens_host, void* workspace, hipStream_t st) {
   a.ps = partition_size > 0 ? partition_size : auto_partition(batch, a.n_kv, max_context_len);
   const int64_t P = decode_parts(max_context_len, a.ps);
-  if (P > 65535) return PKV_ERR_INVALID_ARG;
   a.P = (int)P;
   const WsLayout L = ws_layout(batch, a.n_q, a.n_kv, P);
-  if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return PKV_ERR_CAPACITY;
   char* ws = static_cast<char*>(workspace);
   a.ws_o = L.total ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_ml = L.total ? reinterpret_cast<float*>(ws + L.o_bytes) : nullptr;
@@ -493,7 +464,6 @@ static int decode_launch(bool fused, DecodeArgs& a, float scale, int batch, int 
   if (row_lens_host && batch <= kMaxPlanSeqs && a.max_blocks <= 0xffff) build_plan(a, row_lens_host, batch);
   const int64_t items = a.plan_seqs > 0 ? (int64_t)a.n_items : (int64_t)batch * a.P;
   const int64_t grid = (items + 7) / 8 * 8 * a.n_kv;
-  if (grid > 0x7fffffff) return PKV_ERR_INVALID_ARG;
   const void* fn = fused ? pick_kernel<true>(G) : pick_kernel<false>(G);
   void* args[] = {&a};
   const int rc = launch_status(hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kWaves * kWave), args, 0, st));
@@ -526,7 +496,7 @@ extern "C" size_t pkv_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_
     return 0;
   const int ps = partition_size > 0 ? partition_size : auto_partition(batch, n_kv_heads, max_context_len);
   return std::max(ws_layout(batch, n_q_heads, n_kv_heads, decode_parts(max_context_len, ps)).total,
-                  stream_workspace_bytes(n_q_heads, n_kv_heads));
+                  2 * stream_records_bytes(n_q_heads));
 }
 
 extern "C" int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -565,27 +535,111 @@ static int decode_common_checks(const pkv_bf16* out, const pkv_bf16* q, const pk
   return PKV_OK;
 }
 
-static DecodeArgs base_args(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_pool, const pkv_bf16* v_pool,
-                            int num_blocks, const int32_t* block_table, int64_t bt_row_stride, int num_slots,
-                            int max_blocks_per_seq, const int32_t* slot_ids, const int32_t* context_lens,
-                            int n_q_heads, int n_kv_heads, float scale) {
+static DecodeArgs base_args(const DecodeCall& c) {
   DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_pool = const_cast<uint16_t*>(k_pool);
-  a.v_pool = const_cast<uint16_t*>(v_pool);
-  a.bt = block_table;
-  a.slot_ids = slot_ids;
-  a.ctx_lens = context_lens;
-  a.bt_stride = bt_row_stride;
-  a.num_blocks = num_blocks;
-  a.num_slots = num_slots;
-  a.max_blocks = max_blocks_per_seq;
-  a.n_q = n_q_heads;
-  a.n_kv = n_kv_heads;
-  a.scale_log2e = scale * kLog2e;
+  a.out = c.out;
+  a.q = c.q;
+  a.k_new = c.k_new;
+  a.v_new = c.v_new;
+  a.k_pool = c.k_pool;
+  a.v_pool = c.v_pool;
+  a.bt = c.block_table;
+  a.slot_ids = c.slot_ids;
+  a.ctx_lens = c.context_lens;
+  a.rope = reinterpret_cast<const float2*>(c.cos_sin);
+  a.max_pos = c.max_pos;
+  a.bt_stride = c.bt_row_stride;
+  a.num_blocks = c.num_blocks;
+  a.num_slots = c.num_slots;
+  a.max_blocks = c.max_blocks_per_seq;
+  a.n_q = c.n_q_heads;
+  a.n_kv = c.n_kv_heads;
+  a.scale_log2e = c.scale * kLog2e;
   return a;
 }
+
+namespace pkv {
+
+int decode_prepare(const DecodeCall& c, DecodeLaunch* L) {
+  L->c = c;
+  L->path = 0;
+  int rc = decode_common_checks(c.out, c.q, c.k_pool, c.v_pool, c.num_blocks, c.block_table, c.bt_row_stride,
+                                c.num_slots, c.max_blocks_per_seq, c.slot_ids, c.context_lens, c.batch,
+                                c.max_context_len, c.n_q_heads, c.n_kv_heads, c.head_dim, c.scale,
+                                c.partition_size, c.workspace);
+  if (rc < 0) return c.out_prev ? PKV_ERR_INVALID_ARG : PKV_OK;   // empty batch: nothing to do
+  if (rc != PKV_OK) return rc;
+  if (c.fused) {
+    if (c.max_pos < 1) return PKV_ERR_INVALID_ARG;
+    if (!c.k_new || !c.v_new || !c.cos_sin) return PKV_ERR_NULL;
+    if (!aligned16(c.k_new) || !aligned16(c.v_new) || !aligned16(c.cos_sin)) return PKV_ERR_MISALIGNED;
+  }
+  if (c.records_half < 0 || c.records_half > 1) return PKV_ERR_INVALID_ARG;
+  // the streaming kernel: host row lengths and room for its records
+  const size_t R = stream_records_bytes(c.n_q_heads);
+  const size_t need = (size_t)(c.records_half + 1) * R;
+  if (c.row_lens_host && c.workspace && c.workspace_bytes >= need && (!c.out_prev || c.workspace_bytes >= 2 * R)) {
+    char* ws = static_cast<char*>(c.workspace);
+    StreamCall sc{};
+    sc.out = c.out;
+    sc.q = c.q;
+    sc.k_new = c.k_new;
+    sc.v_new = c.v_new;
+    sc.k_pool = c.k_pool;
+    sc.v_pool = c.v_pool;
+    sc.num_blocks = c.num_blocks;
+    sc.block_table = c.block_table;
+    sc.bt_row_stride = c.bt_row_stride;
+    sc.num_slots = c.num_slots;
+    sc.max_blocks = c.max_blocks_per_seq;
+    sc.slot_ids = c.slot_ids;
+    sc.slot_ids_host = c.slot_ids_host;
+    sc.row_lens_host = c.row_lens_host;
+    sc.batch = c.batch;
+    sc.n_q = c.n_q_heads;
+    sc.n_kv = c.n_kv_heads;
+    sc.cos_sin = c.cos_sin;
+    sc.max_pos = c.max_pos;
+    sc.scale = c.scale;
+    sc.records = reinterpret_cast<float*>(ws + c.records_half * R);
+    sc.records_bytes = R;
+    sc.out_prev = c.out_prev;
+    sc.records_prev = c.out_prev ? reinterpret_cast<const float*>(ws + (1 - c.records_half) * R) : nullptr;
+    if (stream_prepare(c.fused, sc, &L->s) == PKV_OK) {
+      L->path = 1;
+      return PKV_OK;
+    }
+  }
+  if (c.out_prev) return PKV_ERR_INVALID_ARG;   // chaining exists on the streaming path only
+  // the per-partition kernels
+  const int ps = c.partition_size > 0 ? c.partition_size : auto_partition(c.batch, c.n_kv_heads, c.max_context_len);
+  const int64_t P = decode_parts(c.max_context_len, ps);
+  if (P > 65535) return PKV_ERR_INVALID_ARG;
+  const WsLayout W = ws_layout(c.batch, c.n_q_heads, c.n_kv_heads, P);
+  if (W.total > 0 && (!c.workspace || c.workspace_bytes < W.total)) return PKV_ERR_CAPACITY;
+  const int64_t items = (int64_t)c.batch * P;   // the host schedule launches at most this many
+  if ((items + 7) / 8 * 8 * c.n_kv_heads > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  L->path = 2;
+  return PKV_OK;
+}
+
+bool decode_chainable(const DecodeLaunch& L) {
+  return L.path == 1 && L.c.workspace_bytes >= 2 * stream_records_bytes(L.c.n_q_heads);
+}
+
+int decode_enqueue(const DecodeLaunch& L, hipStream_t st, bool merge) {
+  if (L.path == 0) return PKV_OK;
+  if (L.path == 1) return stream_enqueue(L.s, st, merge);
+  DecodeArgs a = base_args(L.c);
+  return partition_launch(L.c.fused, a, L.c.batch, L.c.max_context_len, L.c.partition_size, L.c.row_lens_host,
+                          L.c.workspace, st);
+}
+
+int decode_finish(const DecodeLaunch& L, hipStream_t st) {
+  return L.path == 1 ? stream_merge_enqueue(L.s, st) : PKV_OK;
+}
+
+}  // namespace pkv
 
 extern "C" int pkv_paged_attn_decode(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_pool,
                                      const pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
@@ -594,14 +648,33 @@ extern "C" int pkv_paged_attn_decode(pkv_bf16* out, const pkv_bf16* q, const pkv
                                      const int32_t* row_lens_host, int batch, int max_context_len, int n_q_heads,
                                      int n_kv_heads, int head_dim, float scale, int partition_size,
                                      void* workspace, size_t workspace_bytes, void* stream) {
-  const int rc = decode_common_checks(out, q, k_pool, v_pool, num_blocks, block_table, bt_row_stride, num_slots,
-                                      max_blocks_per_seq, slot_ids, context_lens, batch, max_context_len,
-                                      n_q_heads, n_kv_heads, head_dim, scale, partition_size, workspace);
-  if (rc != PKV_OK) return rc < 0 ? PKV_OK : rc;
-  DecodeArgs a = base_args(out, q, k_pool, v_pool, num_blocks, block_table, bt_row_stride, num_slots,
-                           max_blocks_per_seq, slot_ids, context_lens, n_q_heads, n_kv_heads, scale);
-  return decode_launch(false, a, scale, batch, max_context_len, partition_size, row_lens_host, workspace,
-                       workspace_bytes, (hipStream_t)stream);
+  DecodeCall c{};
+  c.fused = false;
+  c.out = out;
+  c.q = q;
+  c.k_pool = const_cast<pkv_bf16*>(k_pool);
+  c.v_pool = const_cast<pkv_bf16*>(v_pool);
+  c.num_blocks = num_blocks;
+  c.block_table = block_table;
+  c.bt_row_stride = bt_row_stride;
+  c.num_slots = num_slots;
+  c.max_blocks_per_seq = max_blocks_per_seq;
+  c.slot_ids = slot_ids;
+  c.context_lens = context_lens;
+  c.row_lens_host = row_lens_host;
+  c.batch = batch;
+  c.max_context_len = max_context_len;
+  c.n_q_heads = n_q_heads;
+  c.n_kv_heads = n_kv_heads;
+  c.head_dim = head_dim;
+  c.scale = scale;
+  c.partition_size = partition_size;
+  c.workspace = workspace;
+  c.workspace_bytes = workspace_bytes;
+  DecodeLaunch L;
+  const int rc = decode_prepare(c, &L);
+  if (rc != PKV_OK) return rc;
+  return decode_enqueue(L, (hipStream_t)stream);
 }
 
 extern "C" int pkv_paged_decode_fused(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_new,
@@ -612,19 +685,35 @@ extern "C" int pkv_paged_decode_fused(pkv_bf16* out, const pkv_bf16* q, const pk
                                       int n_kv_heads, int head_dim,
                                       const float* cos_sin, int max_pos, float scale, int partition_size,
                                       void* workspace, size_t workspace_bytes, void* stream) {
-  const int rc = decode_common_checks(out, q, k_pool, v_pool, num_blocks, block_table, bt_row_stride, num_slots,
-                                      max_blocks_per_seq, slot_ids, context_lens, batch, max_context_len,
-                                      n_q_heads, n_kv_heads, head_dim, scale, partition_size, workspace);
-  if (rc != PKV_OK) return rc < 0 ? PKV_OK : rc;
-  if (max_pos < 1) return PKV_ERR_INVALID_ARG;
-  if (!k_new || !v_new || !cos_sin) return PKV_ERR_NULL;
-  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(cos_sin)) return PKV_ERR_MISALIGNED;
-  DecodeArgs a = base_args(out, q, k_pool, v_pool, num_blocks, block_table, bt_row_stride, num_slots,
-                           max_blocks_per_seq, slot_ids, context_lens, n_q_heads, n_kv_heads, scale);
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.rope = reinterpret_cast<const float2*>(cos_sin);
-  a.max_pos = max_pos;
-  return decode_launch(true, a, scale, batch, max_context_len, partition_size, row_lens_host, workspace,
-                       workspace_bytes, (hipStream_t)stream);
+  DecodeCall c{};
+  c.fused = true;
+  c.out = out;
+  c.q = q;
+  c.k_new = k_new;
+  c.v_new = v_new;
+  c.k_pool = k_pool;
+  c.v_pool = v_pool;
+  c.num_blocks = num_blocks;
+  c.block_table = block_table;
+  c.bt_row_stride = bt_row_stride;
+  c.num_slots = num_slots;
+  c.max_blocks_per_seq = max_blocks_per_seq;
+  c.slot_ids = slot_ids;
+  c.context_lens = context_lens;
+  c.row_lens_host = row_lens_host;
+  c.batch = batch;
+  c.max_context_len = max_context_len;
+  c.n_q_heads = n_q_heads;
+  c.n_kv_heads = n_kv_heads;
+  c.head_dim = head_dim;
+  c.cos_sin = cos_sin;
+  c.max_pos = max_pos;
+  c.scale = scale;
+  c.partition_size = partition_size;
+  c.workspace = workspace;
+  c.workspace_bytes = workspace_bytes;
+  DecodeLaunch L;
+  const int rc = decode_prepare(c, &L);
+  if (rc != PKV_OK) return rc;
+  return decode_enqueue(L, (hipStream_t)stream);
 }

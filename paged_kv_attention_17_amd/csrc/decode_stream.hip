@@ -14,24 +14,33 @@
 // on one CU progress at very different speeds, and the last ones run alone.
 // Here the batch's blocks are laid end to end (row by row, the block stream)
 // and cut into equal shares, one per CU; every block is read whole (all KV
-// heads, 16 KB of K and V each), so a CU streams contiguous 1 KB token rows.
+// heads, 16 KB of K and V each) in whole 128-byte lines.
 //
 // Work inside a workgroup.  16 waves = n_kv heads x (16 / n_kv) lanes of
 // blocks: wave w serves KV head w % n_kv and takes every (16 / n_kv)-th block
-// of the share, with two blocks in flight.  The block's arithmetic runs on the
-// matrix cores: scores S^T = K . Q^T (two 16x16x32 products, K straight from
-// its loads, the G query heads as columns), then O^T += V^T . P^T (four
-// 16x16x16 products, V transposed through a per-wave LDS tile), so the vector
-// ALU is left with the masks, the exponentials and the rare rescale.  The rows
-// the share touches (at most kMaxRows) have their
-// queries staged in LDS, rotated when fused.  When a wave's next block belongs
-// to another row it folds its state for the finished row (DPP and lane
-// shuffles over the 8 row groups) into that row's LDS slot, without waiting
-// for the other waves.  After the last block one barrier, then the waves of
-// each KV head are merged per row: a row that lies inside the share is
-// finished in place, a row cut by the share's ends leaves (max, sum,
-// unnormalised output) in one of the share's two workspace records, and a
-// small kernel merges those records.
+// of the share, starting at block w / n_kv, with two blocks in flight.  The
+// assignment is fixed, so a row's float32 sums are taken in an order that
+// depends only on the row lengths (never on timing or on where the blocks sit
+// in the pool): the same inputs give the same bits, under any placement of the
+// blocks.  Each wave's first two blocks are looked up and requested before the
+// share's table slice and queries are staged in LDS, so the first K/V bytes
+// are on their way while the staging waits.
+//
+// A block's arithmetic runs on the matrix cores: scores S^T = K . Q^T (two
+// 16x16x32 products, the G query heads as columns), then O^T += V^T . P^T
+// (four 16x16x16 products, V transposed through a per-wave LDS tile), so the
+// vector ALU is left with the masks, the exponentials and the rare rescale.
+// K is loaded in whole lines (each load brings 8 token rows x 128 bytes) and
+// put into the product's operand layout with one DPP row rotation.  When a
+// wave's next block belongs to another row it folds its state for the finished
+// row into that row's LDS slot, without waiting for the other waves.  After
+// the last block one barrier, then the waves of each KV head are merged per
+// row: a row that lies inside the share is finished in place, a row cut by the
+// share's ends leaves (max, sum, unnormalised output) in one of the share's two
+// records.  Those records are merged either by a small kernel after the launch
+// or, when launches are chained over the layers of one step (same rows, same
+// lengths), in the prologue of the next launch, where their loads overlap that
+// launch's own start-up.
 //
 // Fused variant.  The workgroup holding a row's last block rotates the row's
 // new key and keeps key and value in LDS.  Pool reads of that block stop
@@ -51,50 +60,30 @@ namespace pkv {
 namespace {
 
 constexpr int kWaves = 16;
+constexpr int kDepth = 2;             // blocks in flight per wave
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxRows = 4;           // rows one share may touch
-constexpr int kMaxSeqs = 256;         // batch rows described in the arguments
 constexpr int kMaxQ = 32;             // query heads staged per row
-constexpr int kMaxGrid = 512;         // workgroups (one per CU)
-constexpr int kRec = kHeadDim + 2;    // partial record per query head: o[64], max, sum
+constexpr int kMaxKv = 16;            // KV heads
+constexpr int kRec = kStreamRec;
 constexpr int kWin = kThreads;        // blocks whose table entries are staged in LDS at a time
-
-struct StreamArgs {
-  uint16_t* out;
-  const uint16_t* q;
-  const uint16_t* k_new;
-  const uint16_t* v_new;
-  uint16_t* k_pool;
-  uint16_t* v_pool;
-  const int32_t* bt;
-  const int32_t* slot_ids;
-  const float2* rope;
-  float* ws;                   // records [2 * grid][n_q][kRec]
-  int64_t bt_stride;
-  int num_blocks;
-  int num_slots;
-  int max_blocks;
-  int n_q;
-  int n_kv;
-  int max_pos;
-  int batch;
-  float scale_log2e;
-  int share;                   // blocks per workgroup
-  int total;                   // blocks in the stream
-  int32_t row_start[kMaxSeqs + 1];   // first stream block of each row
-  int32_t row_n[kMaxSeqs];           // tokens of each row
-  uint16_t wg_rows[kMaxGrid];        // per workgroup: first row << 3 | rows touched
-};
-static_assert(sizeof(StreamArgs) <= 4096, "kernel argument block");
+constexpr int kPrevSpan = 8;          // shares a row may span for the prologue merge of chained launches
+static_assert(kRec == kHeadDim + 2, "record layout");
+static_assert(kMaxRows * kMaxQ * 8 <= kThreads, "one query chunk per thread");
 
 __device__ __forceinline__ int row_slot(const StreamArgs& a, int b) {
+  if (a.slots_in_args) {
+    const int s = a.row_slot[b];
+    return s == 0xffff ? -1 : s;
+  }
   const int s = a.slot_ids ? a.slot_ids[b] : b;
   return (s >= 0 && s < a.num_slots) ? s : -1;
 }
 
 // Rotate chunk `own` (8 dims starting at 8 * ch) against its pair partner
-// chunk (ch ^ 4) with the position's cos/sin row.
-__device__ __forceinline__ uint4 rope_own_chunk(uint4 own, uint4 oth, const float2* trow, int ch) {
+// chunk (ch ^ 4); t: the (cos, sin) of the chunk's 8 pairs, two per float4
+// (pairs 8 (ch % 4) .. + 7 of the position's table row).
+__device__ __forceinline__ uint4 rope_own_chunk(uint4 own, uint4 oth, const float4 (&t)[4], int ch) {
   const uint32_t o[4] = {own.x, own.y, own.z, own.w};
   const uint32_t p[4] = {oth.x, oth.y, oth.z, oth.w};
   uint32_t res[4];
@@ -106,8 +95,9 @@ __device__ __forceinline__ uint4 rope_own_chunk(uint4 own, uint4 oth, const floa
     for (int e = 0; e < 2; ++e) {
       const float mine = e ? bf16_hi(o[j]) : bf16_lo(o[j]);
       const float other = e ? bf16_hi(p[j]) : bf16_lo(p[j]);
-      const float2 t = trow[(ch & 3) * 8 + 2 * j + e];
-      r[e] = first_half ? rope_first(mine, other, t.x, t.y) : rope_second(other, mine, t.x, t.y);
+      const float c = e ? t[j].z : t[j].x;
+      const float sn = e ? t[j].w : t[j].y;
+      r[e] = first_half ? rope_first(mine, other, c, sn) : rope_second(other, mine, c, sn);
     }
     res[j] = pack_bf16x2(r[0], r[1]);
   }
@@ -132,6 +122,14 @@ __device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
   const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(const_cast<uint16_t*>(p)));
   return __builtin_bit_cast(uint2, r);
+}
+
+// Lane i of each row of 16 lanes takes the value of lane (i + 8) mod 16.
+__device__ __forceinline__ uint4 row_rotate8(uint4 x) {
+  auto r = [](uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor8, 0xF, 0xF, false);
+  };
+  return make_uint4(r(x.x), r(x.y), r(x.z), r(x.w));
 }
 
 // Scores S^T[token][col] += K[token][k] . Q^T[k][col] over 32 dims: lane l
@@ -167,16 +165,16 @@ struct MfmaAcc {
     for (int t = 0; t < 4; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One 16-token block: V rows go through the wave's LDS tile (rows past the
+  // One 16-token block.  k0 / k1: the K operands for dims 0..31 and 32..63
+  // (token lane % 16).  V rows go through the wave's LDS tile (rows past the
   // context, or of a block whose id is out of range, are zeroed there so NaN
   // in unused pool slots cannot reach the output); scores of such tokens are
   // replaced by -inf (a select, never a product).  `extra` is a token slot
   // that takes part whatever the block (the fused step's new token), or -1.
-  __device__ __forceinline__ void block(uint4 qb0, uint4 qb1, const KVRegs& R, uint16_t* vtile, int wr0, int wr1,
-                                        const int (&rd)[4], int r, int q4, bool blk_ok, int valid, int extra,
-                                        float C, float invC) {
+  __device__ __forceinline__ void block(uint4 qb0, uint4 qb1, uint4 k0, uint4 k1, uint4 v0, uint4 v1,
+                                        uint16_t* vtile, int wr0, int wr1, const int (&rd)[4], int r, int q4,
+                                        bool blk_ok, int valid, int extra, float C, float invC) {
     const bool full = blk_ok && valid == kBlock;
-    uint4 v0 = R.v0, v1 = R.v1;
     if (!full) {
       const uint4 z = make_uint4(0, 0, 0, 0);
       v0 = sel4((blk_ok && r < valid) || r == extra, v0, z);
@@ -186,8 +184,8 @@ struct MfmaAcc {
     *reinterpret_cast<uint4*>(vtile + wr1) = v1;
 
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-    sc = mfma_qk(R.k0, qb0, sc);
-    sc = mfma_qk(R.k1, qb1, sc);
+    sc = mfma_qk(k0, qb0, sc);
+    sc = mfma_qk(k1, qb1, sc);
     float sv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -218,12 +216,112 @@ struct MfmaAcc {
   }
 };
 
-template <int G, bool FUSED>
+// Output element (row b, query head qh, dim d) of a row cut by share ends:
+// the records of every share the row spans, combined in share order.  Share
+// w holds the row in record 2w when the row contains the share's first block,
+// else in record 2w + 1.  Empty rows get zeros; rows inside one share were
+// finished by their workgroup and are left alone.
+__device__ __forceinline__ void merge_element(const StreamArgs& a, uint16_t* out, const float* ws, int b, int qh,
+                                              int d) {
+  const int64_t o = ((int64_t)b * a.n_q + qh) * kHeadDim + d;
+  if (a.row_n[b] <= 0) {
+    out[o] = 0;
+    return;
+  }
+  const int start = a.row_start[b];
+  const int w0 = start / a.share;
+  const int w1 = (a.row_start[b + 1] - 1) / a.share;
+  if (w0 == w1) return;
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int w = w0; w <= w1; w += 8) {
+    float mv[8], lv[8], ov[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ww = w + j <= w1 ? w + j : w1;
+      const int rec = 2 * ww + ((ww > w0 || start == w0 * a.share) ? 0 : 1);
+      const float* src = ws + ((int64_t)rec * a.n_q + qh) * kRec;
+      mv[j] = w + j <= w1 ? src[kHeadDim] : -INFINITY;
+      lv[j] = src[kHeadDim + 1];
+      ov[j] = src[d];
+    }
+    float mm = M;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mm = fmaxf(mm, mv[j]);
+    const float f0 = M == -INFINITY ? 0.f : fast_exp2(M - mm);
+    L *= f0;
+    O *= f0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = mv[j] == -INFINITY ? 0.f : fast_exp2(mv[j] - mm);
+      L += f * lv[j];
+      O += f * ov[j];
+    }
+    M = mm;
+  }
+  out[o] = to_bf16(L > 0.f ? O / L : 0.f);
+}
+
+// The prologue merge of a chained launch, split so that its loads go out with
+// the launch's other staging loads: (row b, query head qh, dim d) of the
+// previous launch, whose rows span at most kPrevSpan shares.
+struct PrevMerge {
+  float m[kPrevSpan], l[kPrevSpan], o[kPrevSpan];
+  int64_t at;                  // output element, or -1: nothing to do
+  bool empty;                  // the row is empty: write zero
+};
+
+__device__ __forceinline__ void prev_load(const StreamArgs& a, int b, int qh, int d, PrevMerge& P) {
+  P.at = -1;
+  P.empty = false;
+  if (b >= a.batch) return;
+  const int64_t o = ((int64_t)b * a.n_q + qh) * kHeadDim + d;
+  if (a.row_n[b] <= 0) {
+    P.at = o;
+    P.empty = true;
+    return;
+  }
+  const int start = a.row_start[b];
+  const int w0 = start / a.share;
+  const int w1 = (a.row_start[b + 1] - 1) / a.share;
+  if (w0 == w1) return;
+  P.at = o;
+#pragma unroll
+  for (int j = 0; j < kPrevSpan; ++j) {
+    const int ww = w0 + j <= w1 ? w0 + j : w1;
+    const int rec = 2 * ww + ((ww > w0 || start == w0 * a.share) ? 0 : 1);
+    const float* src = a.ws_prev + ((int64_t)rec * a.n_q + qh) * kRec;
+    P.m[j] = w0 + j <= w1 ? src[kHeadDim] : -INFINITY;
+    P.l[j] = src[kHeadDim + 1];
+    P.o[j] = src[d];
+  }
+}
+
+__device__ __forceinline__ void prev_finish(const StreamArgs& a, const PrevMerge& P) {
+  if (P.at < 0) return;
+  if (P.empty) {
+    a.out_prev[P.at] = 0;
+    return;
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kPrevSpan; ++j) M = fmaxf(M, P.m[j]);
+  float L = 0.f, O = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPrevSpan; ++j) {
+    const float f = P.m[j] == -INFINITY ? 0.f : fast_exp2(P.m[j] - M);
+    L += f * P.l[j];
+    O += f * P.o[j];
+  }
+  a.out_prev[P.at] = to_bf16(L > 0.f ? O / L : 0.f);
+}
+
+template <int G, bool FUSED, bool PREV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void stream_kernel(StreamArgs a) {
   const int B0 = blockIdx.x * a.share;
   const int B1 = min(B0 + a.share, a.total);
-  if (B0 >= B1) return;
+  const int len = B1 - B0;
+  if (len <= 0) return;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = wave_uniform(tid >> 6);
@@ -241,34 +339,33 @@ void stream_kernel(StreamArgs a) {
   const float invC = 1.0f / C;
 
   __shared__ uint4 sq[kMaxRows][kMaxQ * 8];                 // queries: [row][head][chunk]
-  __shared__ uint4 snew[kMaxRows][2][kWaves * 8];           // fused: new key / value [row][k|v][head][chunk]
+  __shared__ uint4 snew[kMaxRows][2][kMaxKv * 8];           // fused: new key / value [row][k|v][head][chunk]
   __shared__ float sp[kMaxRows][kWaves][G][kRec];           // per-wave partials of each row
   __shared__ int srow_ok[kMaxRows];                         // the row's table slot is valid
+  __shared__ int s_app[kMaxRows];                           // fused: pool block of the row's new token, or -1
   __shared__ uint16_t svt[kWaves][kBlock * kHeadDim];       // per-wave V tile (transposed reads)
   __shared__ int s_tab[kWin];                               // window's blocks: pool block id or -1
   __shared__ int s_meta[kWin];                              // and row << 8 | tokens read from the pool
-  __shared__ int s_next[kWaves];                            // per KV head: next unclaimed block of the window
 
-  // ---- the share's blocks -------------------------------------------------
-  // The share is walked in windows of kWin blocks.  Each window's table slice
-  // is computed into LDS (thread t: block t of the window); then the waves of
-  // each KV head claim the window's blocks one at a time from the head's LDS
-  // counter, so a wave that runs ahead takes more blocks and the waves of the
-  // workgroup finish together (with a fixed split the youngest waves of a CU
-  // ended long after the oldest).  A wave's claims increase, so it still
-  // meets the share's rows in order.
-  const int len = B1 - B0;
   const uint32_t block_bytes = (uint32_t)(kBlock * row_elems * 2);
-  const uint32_t lane_off = (uint32_t)(((int64_t)r * row_elems + h * kHeadDim + c * 8) * 2);
-  const uint32_t lane_off8 = lane_off + (uint32_t)(8 * row_elems * 2);
-  // K in the MFMA operand layout: token lane % 16, dims 8 (lane / 16) .. + 7
-  // (and the same 32 dims further on for the second operand)
-  const uint32_t k_off = (uint32_t)(((int64_t)(lane & 15) * row_elems + h * kHeadDim + 8 * (lane >> 4)) * 2);
+  const uint32_t head_off = (uint32_t)(h * kHeadDim * 2);
+  // V: lane = 8 r + c reads dims 8c .. 8c + 7 of token rows r and r + 8
+  const uint32_t v_off0 = (uint32_t)(r * row_elems * 2) + head_off + 16u * c;
+  const uint32_t v_off1 = v_off0 + (uint32_t)(8 * row_elems * 2);
+  // K in whole lines: load A covers token rows 0..7, load B rows 8..15, all 8
+  // chunks of each.  Lane l takes chunk l / 16 of row l % 16 when that row is
+  // the load's, else chunk 4 + l / 16 of row l % 8 (A) or 8 + l % 8 (B), the
+  // piece that lane l ^ 8 needs for the second operand (see fix_k).
+  const uint32_t k_offA = (uint32_t)((lane & 7) * row_elems * 2) + head_off +
+                          16u * (uint32_t)((lane >> 4) | ((lane & 8) >> 1));
+  const uint32_t k_offB = (uint32_t)((8 + (lane & 7)) * row_elems * 2) + head_off +
+                          16u * (uint32_t)((lane >> 4) | ((~lane & 8) >> 1));
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
 
-  // stream block p -> pool block id and (row << 8 | tokens to read from the
-  // pool; the fused step's new token is not among them)
+  // stream block p -> pool block id (-1 for none or out of range) and
+  // (row << 8 | tokens to read from the pool; the fused step's new token is
+  // not among them)
   auto block_info = [&](int p, int& tab, int& meta) {
     int ri = 0;
     for (int i = 1; i < nrows; ++i) ri = p >= a.row_start[bf + i] ? i : ri;
@@ -288,65 +385,90 @@ void stream_kernel(StreamArgs a) {
     }
     meta = (ri << 8) | valid;
   };
+  // Loads of one block for this wave's KV head.  blk < 0 reads nothing (a
+  // zero-size buffer returns zeros without a memory access).
   auto issue = [&](KVRegs& R, int blk) {
-    blk = blk < 0 ? 0 : blk;
-    const auto rk = buf_rsrc(kbase + (size_t)blk * block_bytes, block_bytes);
-    const auto rv = buf_rsrc(vbase + (size_t)blk * block_bytes, block_bytes);
-    R.k0 = buf_load16(rk, k_off);
-    R.k1 = buf_load16(rk, k_off + 64);
-    R.v0 = buf_load16(rv, lane_off);
-    R.v1 = buf_load16(rv, lane_off8);
+    const bool ok = blk >= 0;
+    const size_t base = ok ? (size_t)blk * block_bytes : 0;
+    const auto rk = buf_rsrc(kbase + base, ok ? block_bytes : 0u);
+    const auto rv = buf_rsrc(vbase + base, ok ? block_bytes : 0u);
+    R.k0 = buf_load16(rk, k_offA);
+    R.k1 = buf_load16(rk, k_offB);
+    R.v0 = buf_load16(rv, v_off0);
+    R.v1 = buf_load16(rv, v_off1);
   };
-  // the first window's table slice is requested before the staging below
-  // waits (and written to LDS after it)
+
+  // ---- this wave's first blocks, requested before anything is staged ----
+  KVRegs R[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    int tb = -1, mt = 0;
+    if (s + d * S < len) block_info(B0 + s + d * S, tb, mt);
+    issue(R[d], wave_uniform(tb));
+  }
+  // the first window's table slice is requested next (written to LDS after
+  // the staging below): thread t, block t
   int tab = -1, meta = 0;
   if (tid < min(kWin, len)) block_info(B0 + tid, tab, meta);
 
-  // ---- queries of the share's rows (rotated by position n - 1 when fused) ----
-  for (int e = tid; e < nrows * a.n_q * 8; e += kThreads) {
-    const int i = e / (a.n_q * 8);
-    const int rem = e - i * a.n_q * 8;
-    const int ch = rem & 7;
-    const int b = bf + i;
-    const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (rem >> 3)) * kHeadDim;
-    uint4 v = *reinterpret_cast<const uint4*>(qrow + ch * 8);
+  // ---- chained launches: the previous launch's rows cut by share ends, one
+  // (row, query head) pair per 64 threads ---------------------------------------
+  if constexpr (PREV) {
+    PrevMerge pm;
+    const int pp = blockIdx.x + a.grid * (tid >> 6);
+    prev_load(a, pp / a.n_q, pp % a.n_q, lane, pm);
+    prev_finish(a, pm);
+  }
+
+  // ---- queries of the share's rows (rotated by position n - 1 when fused),
+  // one 8-dim chunk per thread ---------------------------------------------------
+  if (tid < nrows * a.n_q * 8) {
+    const int qi = tid / (a.n_q * 8);
+    const int qrem = tid - qi * a.n_q * 8;
+    const int qch = qrem & 7;
+    const uint16_t* qrow = a.q + ((int64_t)(bf + qi) * a.n_q + (qrem >> 3)) * kHeadDim;
+    uint4 qv = *reinterpret_cast<const uint4*>(qrow + qch * 8);
     if constexpr (FUSED) {
-      const int pos = a.row_n[b] - 1;
+      const int pos = a.row_n[bf + qi] - 1;
       if (pos >= 0 && pos < a.max_pos) {
-        const uint4 p = *reinterpret_cast<const uint4*>(qrow + (ch ^ 4) * 8);
-        v = rope_own_chunk(v, p, a.rope + (int64_t)pos * (kHeadDim / 2), ch);
+        const uint4 qp = *reinterpret_cast<const uint4*>(qrow + (qch ^ 4) * 8);
+        const float4* tr = reinterpret_cast<const float4*>(a.rope + ((int64_t)pos * (kHeadDim / 2) + (qch & 3) * 8) * 2);
+        const float4 qt[4] = {tr[0], tr[1], tr[2], tr[3]};
+        qv = rope_own_chunk(qv, qp, qt, qch & 4);
       }
     }
-    sq[i][rem] = v;
+    sq[qi][qrem] = qv;
   }
   // ---- fused: the new token of every row whose last block is here: rotated
   // key and value into LDS (it joins the attention from there).  Its pool
   // write waits for the end of the workgroup's stream (no workgroup reads that
-  // pool row in this launch), which keeps the table lookup it needs off the
-  // start-up path.  nrows * n_kv * 8 <= kMaxRows * kWaves * 8 <= kThreads: one
-  // 8-dim chunk per thread.
-  int app_blk = -1;                      // pool block of this thread's new-token chunk
+  // pool row in this launch), which keeps the table lookup for it off the
+  // start-up path.  nrows * n_kv * 8 <= kThreads: one 8-dim chunk per thread.
+  const int ni = tid / (n_kv * 8);
+  const int nrem = tid - ni * n_kv * 8;
   if constexpr (FUSED) {
     if (tid < nrows) srow_ok[tid] = row_slot(a, bf + tid) >= 0;
     if (tid < nrows * n_kv * 8) {
-      const int i = tid / (n_kv * 8);
-      const int rem = tid - i * n_kv * 8;
-      const int ch = rem & 7;
-      const int kvh = rem >> 3;
-      const int b = bf + i;
+      const int ch = nrem & 7;
+      const int b = bf + ni;
       const int n = a.row_n[b];
       const int last = a.row_start[b + 1] - 1;
       if (n > 0 && last >= B0 && last < B1) {
         const int pos = n - 1;
-        const uint16_t* krow = a.k_new + ((int64_t)b * n_kv + kvh) * kHeadDim;
-        uint4 k = *reinterpret_cast<const uint4*>(krow + ch * 8);
-        const uint4 p = *reinterpret_cast<const uint4*>(krow + (ch ^ 4) * 8);
-        const uint4 v = *reinterpret_cast<const uint4*>(a.v_new + ((int64_t)b * n_kv + kvh) * kHeadDim + ch * 8);
+        const uint16_t* krow = a.k_new + ((int64_t)b * n_kv + (nrem >> 3)) * kHeadDim;
+        uint4 nk = *reinterpret_cast<const uint4*>(krow + ch * 8);
+        const uint4 nv = *reinterpret_cast<const uint4*>(a.v_new + ((int64_t)b * n_kv + (nrem >> 3)) * kHeadDim + ch * 8);
         const int slot = row_slot(a, b);
-        if (slot >= 0) app_blk = a.bt[(int64_t)slot * a.bt_stride + pos / kBlock];
-        if (pos < a.max_pos) k = rope_own_chunk(k, p, a.rope + (int64_t)pos * (kHeadDim / 2), ch);
-        snew[i][0][rem] = k;
-        snew[i][1][rem] = v;
+        if (nrem == 0)
+          s_app[ni] = slot >= 0 && pos / kBlock < a.max_blocks ? a.bt[(int64_t)slot * a.bt_stride + pos / kBlock] : -1;
+        if (pos < a.max_pos) {
+          const uint4 np = *reinterpret_cast<const uint4*>(krow + (ch ^ 4) * 8);
+          const float4* tr = reinterpret_cast<const float4*>(a.rope + ((int64_t)pos * (kHeadDim / 2) + (ch & 3) * 8) * 2);
+          const float4 nt[4] = {tr[0], tr[1], tr[2], tr[3]};
+          nk = rope_own_chunk(nk, np, nt, ch & 4);
+        }
+        snew[ni][0][nrem] = nk;
+        snew[ni][1][nrem] = nv;
       }
     }
   }
@@ -354,13 +476,13 @@ void stream_kernel(StreamArgs a) {
     s_tab[tid] = tab;
     s_meta[tid] = meta;
   }
-  if (tid < kWaves) s_next[tid] = 0;
   __syncthreads();
 
   MfmaAcc acc;
   acc.reset();
   const int col = lane & 15;             // MFMA column: query head of the KV head's group
   const int q4 = lane >> 4;              // MFMA lane group
+  const bool lo8 = (lane & 8) == 0;
   uint4 qb0, qb1;                        // Q^T operands: dims 8 q4 .. and 32 + 8 q4 ..
   int cur = 0;                           // row of the share being accumulated
   int row_last = -1;                     // fused: stream block holding the row's new token, or -1
@@ -404,12 +526,6 @@ void stream_kernel(StreamArgs a) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) v_rd[t] = vt_index(lane >> 2, 16 * t + 4 * (lane & 3));
 
-  // the next block of this wave's KV head in the current window (wave-uniform)
-  auto claim = [&]() {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&s_next[h], 1);
-    return wave_uniform(v);
-  };
   for (int w0 = 0; w0 < len; w0 += kWin) {
     const int wl = min(kWin, len - w0);
     if (w0 > 0) {
@@ -419,57 +535,63 @@ void stream_kernel(StreamArgs a) {
         s_tab[tid] = tab;
         s_meta[tid] = meta;
       }
-      if (tid < kWaves) s_next[tid] = 0;
       __syncthreads();
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) issue(R[d], s + d * S < wl ? wave_uniform(s_tab[s + d * S]) : -1);
     }
-    auto step = [&](KVRegs R, int i) {
+    auto step = [&](const KVRegs& R, int i) {
       const int mt = wave_uniform(s_meta[i]);
       while (cur < (mt >> 8)) flush();
       const bool blk_ok = wave_uniform(s_tab[i]) >= 0;
       const int valid = mt & 0xff;       // tokens read from the pool
+      // K operands: lanes whose row is in load A take it from there, the
+      // others from load B; the second operand comes from lane l ^ 8
+      uint4 k0 = sel4(lo8, R.k0, R.k1);
+      uint4 k1 = row_rotate8(sel4(lo8, R.k1, R.k0));
+      uint4 v0 = R.v0, v1 = R.v1;
       int extra = -1;                    // fused: slot of the new token in this block
       if constexpr (FUSED) {
         // the row's last block: the new token (rotated key, value) from LDS
         if (B0 + w0 + i == row_last) {
           extra = valid;
           if (col == extra) {
-            R.k0 = snew[cur][0][h * 8 + q4];
-            R.k1 = snew[cur][0][h * 8 + q4 + 4];
+            k0 = snew[cur][0][h * 8 + q4];
+            k1 = snew[cur][0][h * 8 + q4 + 4];
           }
-          if (r == extra) R.v0 = snew[cur][1][h * 8 + c];
-          if (r + 8 == extra) R.v1 = snew[cur][1][h * 8 + c];
+          if (r == extra) v0 = snew[cur][1][h * 8 + c];
+          if (r + 8 == extra) v1 = snew[cur][1][h * 8 + c];
         }
       }
-      acc.block(qb0, qb1, R, vtile, v_wr0, v_wr1, v_rd, r, q4, blk_ok, valid, extra, C, invC);
+      acc.block(qb0, qb1, k0, k1, v0, v1, vtile, v_wr0, v_wr1, v_rd, r, q4, blk_ok, valid, extra, C, invC);
     };
-    // two blocks in flight in two register sets; loads are issued for every
-    // claim (a claim past the window reloads the window's last block and is
-    // not used), so each step waits for exactly the older set
-    KVRegs X, Y;
-    int ia = claim();
-    issue(X, s_tab[min(ia, wl - 1)]);
-    int ib = claim();
-    issue(Y, s_tab[min(ib, wl - 1)]);
-    while (ia < wl) {
-      step(X, ia);
-      ia = claim();
-      issue(X, s_tab[min(ia, wl - 1)]);
-      if (ib >= wl) break;
-      step(Y, ib);
-      ib = claim();
-      issue(Y, s_tab[min(ib, wl - 1)]);
+    // fixed sequence s, s + S, s + 2S, ... with kDepth blocks in flight in
+    // as many register sets; a load past the window reads nothing.  Every set
+    // is reissued on every path through the loop body, so the compiler's wait
+    // before each block covers exactly the oldest set.
+    for (int i = s; i < wl; i += kDepth * S) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int idx = i + d * S;
+        if (idx < wl) step(R[d], idx);
+        issue(R[d], idx + kDepth * S < wl ? wave_uniform(s_tab[idx + kDepth * S]) : -1);
+      }
     }
   }
   while (cur < nrows) flush();
   if constexpr (FUSED) {
     // the new token into the pool (position context_len - 1 of its row)
-    if (app_blk >= 0 && app_blk < a.num_blocks) {
-      const int i = tid / (n_kv * 8);
-      const int rem = tid - i * n_kv * 8;
-      const int pos = a.row_n[bf + i] - 1;
-      const int64_t off = ((int64_t)app_blk * kBlock + pos % kBlock) * row_elems + (rem >> 3) * kHeadDim + (rem & 7) * 8;
-      *reinterpret_cast<uint4*>(a.k_pool + off) = snew[i][0][rem];
-      *reinterpret_cast<uint4*>(a.v_pool + off) = snew[i][1][rem];
+    if (tid < nrows * n_kv * 8) {
+      const int b = bf + ni;
+      const int n = a.row_n[b];
+      const int last = a.row_start[b + 1] - 1;
+      const int blk = n > 0 && last >= B0 && last < B1 ? s_app[ni] : -1;
+      if (blk >= 0 && blk < a.num_blocks) {
+        const int pos = n - 1;
+        const int64_t off =
+            ((int64_t)blk * kBlock + pos % kBlock) * row_elems + (nrem >> 3) * kHeadDim + (nrem & 7) * 8;
+        *reinterpret_cast<uint4*>(a.k_pool + off) = snew[ni][0][nrem];
+        *reinterpret_cast<uint4*>(a.v_pool + off) = snew[ni][1][nrem];
+      }
     }
   }
   __syncthreads();
@@ -509,63 +631,22 @@ void stream_kernel(StreamArgs a) {
 }
 
 // Merge of the records of rows cut by share ends: one workgroup per (row, KV
-// head), thread = (query head, dim).  Share w holds the row in record 2w when
-// the row contains the share's first block, else in record 2w + 1.  Empty
-// rows get zeros; rows inside one share were finished there.
+// head), thread = (query head of the group, dim).
 template <int G>
 __global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs a) {
   const int kvh = blockIdx.x;
   const int b = blockIdx.y;
-  const int n = a.row_n[b];
-  const int64_t obase = ((int64_t)b * a.n_q + kvh * G) * kHeadDim;
-  if (n <= 0) {
-    for (int e = threadIdx.x; e < G * kHeadDim; e += blockDim.x) a.out[obase + e] = 0;
-    return;
-  }
-  const int start = a.row_start[b];
-  const int w0 = start / a.share;
-  const int w1 = (a.row_start[b + 1] - 1) / a.share;
-  if (w0 == w1) return;
-  for (int e = threadIdx.x; e < G * kHeadDim; e += blockDim.x) {
-    const int qh = kvh * G + e / kHeadDim;
-    const int d = e % kHeadDim;
-    float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int w = w0; w <= w1; w += 8) {
-      float mv[8], lv[8], ov[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ww = w + j <= w1 ? w + j : w1;
-        const int rec = 2 * ww + ((ww > w0 || start == w0 * a.share) ? 0 : 1);
-        const float* src = a.ws + ((int64_t)rec * a.n_q + qh) * kRec;
-        mv[j] = w + j <= w1 ? src[kHeadDim] : -INFINITY;
-        lv[j] = src[kHeadDim + 1];
-        ov[j] = src[d];
-      }
-      float mm = M;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mm = fmaxf(mm, mv[j]);
-      const float f0 = M == -INFINITY ? 0.f : fast_exp2(M - mm);
-      L *= f0;
-      O *= f0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float f = mv[j] == -INFINITY ? 0.f : fast_exp2(mv[j] - mm);
-        L += f * lv[j];
-        O += f * ov[j];
-      }
-      M = mm;
-    }
-    a.out[obase + e] = to_bf16(L > 0.f ? O / L : 0.f);
-  }
+  for (int e = threadIdx.x; e < G * kHeadDim; e += blockDim.x)
+    merge_element(a, a.out, a.ws, b, kvh * G + e / kHeadDim, e % kHeadDim);
 }
 
 // The same merge for batches whose rows span many shares (few rows, long
 // contexts): one workgroup per (row, query head), 16 groups of 64 threads
 // (thread = dim); group j takes records j, j + 16, ..., eight of them with
 // their loads in flight at once, and the groups' partial (max, sum, output)
-// are combined through LDS.  More workgroups and shorter chains of dependent
-// loads per thread than the kernel above, which leaves a batch of one row
-// on n_kv workgroups walking hundreds of records each.
+// are combined through LDS in group order.  More workgroups and shorter chains
+// of dependent loads per thread than the kernel above, which leaves a batch of
+// one row on n_kv workgroups walking hundreds of records each.
 __global__ __launch_bounds__(1024) void stream_merge_wide_kernel(StreamArgs a) {
   constexpr int kGroups = 16;
   __shared__ float part[kGroups][kHeadDim][3];
@@ -641,26 +722,26 @@ int device_cus() {
   return n;
 }
 
-template <bool FUSED>
+template <bool FUSED, bool PREV>
 const void* pick_stream(int G) {
-  return G == 1 ? (const void*)stream_kernel<1, FUSED>
-       : G == 2 ? (const void*)stream_kernel<2, FUSED>
-                : (const void*)stream_kernel<4, FUSED>;
+  return G == 1 ? (const void*)stream_kernel<1, FUSED, PREV>
+       : G == 2 ? (const void*)stream_kernel<2, FUSED, PREV>
+                : (const void*)stream_kernel<4, FUSED, PREV>;
 }
 
 }  // namespace
 
-size_t stream_workspace_bytes(int n_q, int n_kv) {
-  (void)n_kv;
-  return (size_t)2 * kMaxGrid * n_q * kRec * sizeof(float);
+size_t stream_records_bytes(int n_q) {
+  return n_q > 0 ? (size_t)2 * kStreamMaxGrid * n_q * kRec * sizeof(float) : 0;
 }
 
-int stream_decode(bool fused, const StreamCall& c) {
+int stream_prepare(bool fused, const StreamCall& c, StreamLaunch* L) {
   const int G = c.n_kv > 0 ? c.n_q / c.n_kv : 0;
-  if (!c.row_lens_host || c.batch <= 0 || c.batch > kMaxSeqs || G > 4 || c.n_q > kMaxQ ||
-      c.n_kv > kWaves || kWaves % c.n_kv || !c.workspace)
+  if (!c.row_lens_host || c.batch <= 0 || c.batch > kStreamMaxSeqs || G > 4 || c.n_q > kMaxQ ||
+      c.n_kv > kWaves || kWaves % c.n_kv || !c.records)
     return -1;
-  StreamArgs a{};
+  StreamArgs& a = L->a;
+  a = StreamArgs{};
   a.out = c.out;
   a.q = c.q;
   a.k_new = c.k_new;
@@ -669,7 +750,7 @@ int stream_decode(bool fused, const StreamCall& c) {
   a.v_pool = c.v_pool;
   a.bt = c.block_table;
   a.slot_ids = c.slot_ids;
-  a.rope = reinterpret_cast<const float2*>(c.cos_sin);
+  a.rope = c.cos_sin;
   a.bt_stride = c.bt_row_stride;
   a.num_blocks = c.num_blocks;
   a.num_slots = c.num_slots;
@@ -679,6 +760,18 @@ int stream_decode(bool fused, const StreamCall& c) {
   a.max_pos = c.max_pos;
   a.batch = c.batch;
   a.scale_log2e = c.scale * kLog2e;
+  // each row's slot in the arguments when the host knows it (one dependent
+  // memory read less before the first K/V load)
+  if (c.slot_ids_host && c.num_slots <= 0xffff) {
+    a.slots_in_args = 1;
+    for (int b = 0; b < c.batch; ++b) {
+      const int s = c.slot_ids_host[b];
+      a.row_slot[b] = (uint16_t)((s >= 0 && s < c.num_slots) ? s : 0xffff);
+    }
+  } else if (!c.slot_ids && c.batch <= c.num_slots && c.num_slots <= 0xffff) {
+    a.slots_in_args = 1;
+    for (int b = 0; b < c.batch; ++b) a.row_slot[b] = (uint16_t)b;
+  }
   // the block stream: rows end to end, each ceil(n / 16) blocks
   int64_t total = 0;
   a.row_start[0] = 0;
@@ -693,12 +786,13 @@ int stream_decode(bool fused, const StreamCall& c) {
   if (total == 0) return -1;
   const int cus = device_cus();
   if (cus <= 0) return -1;
-  int grid = std::min(cus, kMaxGrid);
+  int grid = std::min(cus, kStreamMaxGrid);
   a.share = (int)((total + grid - 1) / grid);
   grid = (int)((total + a.share - 1) / a.share);
   a.total = (int)total;
-  if (c.workspace_bytes < (size_t)2 * grid * c.n_q * kRec * sizeof(float)) return -1;
-  a.ws = static_cast<float*>(c.workspace);
+  a.grid = grid;
+  if (c.records_bytes < (size_t)2 * grid * c.n_q * kRec * sizeof(float)) return -1;
+  a.ws = c.records;
   // rows of each share (the row of a block is the last row whose start is at
   // or before it: empty rows share their start with the next row and are
   // passed over); every share must touch at most kMaxRows rows, empty rows in
@@ -712,23 +806,52 @@ int stream_decode(bool fused, const StreamCall& c) {
     if (e - b + 1 > kMaxRows) return -1;
     a.wg_rows[g] = (uint16_t)(b << 3 | (e - b + 1));
   }
-  void* args[] = {&a};
-  hipStream_t st = static_cast<hipStream_t>(c.stream);
-  const void* fn = fused ? pick_stream<true>(G) : pick_stream<false>(G);
-  int rc = launch_status(hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st));
-  if (rc != PKV_OK) return rc;
-  // rows that span many shares (few rows) are merged per query head by 16
-  // groups of threads
+  L->prev = c.out_prev != nullptr;
+  if (L->prev) {
+    if (!c.records_prev) return -1;
+    a.out_prev = c.out_prev;
+    a.ws_prev = c.records_prev;
+  }
+  L->fused = fused;
+  L->G = G;
+  // a merge launch is needed for empty rows and rows cut by share ends; rows
+  // that span many shares (few rows) are merged per query head
   int most = 1;
-  for (int b = 0; b < c.batch; ++b)
-    if (a.row_n[b] > 0) most = std::max(most, (a.row_start[b + 1] - 1) / a.share - a.row_start[b] / a.share + 1);
-  if (most > 32)
-    return launch_status(hipLaunchKernel((const void*)stream_merge_wide_kernel, dim3(c.n_q, c.batch), dim3(1024),
+  bool need = false;
+  for (int b = 0; b < c.batch; ++b) {
+    if (a.row_n[b] <= 0) {
+      need = true;
+      continue;
+    }
+    const int span = (a.row_start[b + 1] - 1) / a.share - a.row_start[b] / a.share + 1;
+    need |= span > 1;
+    most = std::max(most, span);
+  }
+  L->merge = !need ? 0 : (most > 32 ? 2 : 1);
+  return PKV_OK;
+}
+
+int stream_enqueue(const StreamLaunch& L, hipStream_t st, bool merge) {
+  StreamArgs a = L.a;
+  void* args[] = {&a};
+  const void* fn = L.fused ? (L.prev ? pick_stream<true, true>(L.G) : pick_stream<true, false>(L.G))
+                           : (L.prev ? pick_stream<false, true>(L.G) : pick_stream<false, false>(L.G));
+  const int rc = launch_status(hipLaunchKernel(fn, dim3(a.grid), dim3(kThreads), args, 0, st));
+  if (rc != PKV_OK || !merge) return rc;
+  return stream_merge_enqueue(L, st);
+}
+
+int stream_merge_enqueue(const StreamLaunch& L, hipStream_t st) {
+  if (L.merge == 0) return PKV_OK;
+  StreamArgs a = L.a;
+  void* args[] = {&a};
+  if (L.merge == 2)
+    return launch_status(hipLaunchKernel((const void*)stream_merge_wide_kernel, dim3(a.n_q, a.batch), dim3(1024),
                                          args, 0, st));
-  const void* mg = G == 1 ? (const void*)stream_merge_kernel<1>
-                 : G == 2 ? (const void*)stream_merge_kernel<2>
-                          : (const void*)stream_merge_kernel<4>;
-  return launch_status(hipLaunchKernel(mg, dim3(c.n_kv, c.batch), dim3(256), args, 0, st));
+  const void* mg = L.G == 1 ? (const void*)stream_merge_kernel<1>
+                 : L.G == 2 ? (const void*)stream_merge_kernel<2>
+                            : (const void*)stream_merge_kernel<4>;
+  return launch_status(hipLaunchKernel(mg, dim3(a.n_kv, a.batch), dim3(256), args, 0, st));
 }
 
 }  // namespace pkv

@@ -1,16 +1,16 @@
 // The rest of a Llama decode layer around the paged attention, for gfx950:
 // RMSNorm and the gated-SiLU product as HIP kernels, the projections as bf16
-// products with float32 sums (an MFMA kernel for decode batches, rocBLAS for
-// other shapes), and pkv_decode_layer, which runs one layer's decode step.
+// products with float32 sums on the library's own MFMA kernel, and
+// pkv_decode_layer, which runs one layer's decode step.
 //
 // Source: "An Inference Engine in 1,500 Lines of CUDA: The Map" -- the engine
 // runs Llama 3.2 1B (opening paragraph), has its own RMSNorm kernel (Korean
 // page, "What is in the box": rmsNormKernel), keeps a 2048-wide hidden state
 // (the buf_2048_* buffers of "A function with 51 parameters") and leaves the
-// projections to the vendor GEMM (chapter-4 title).  The formulas are the
-// public Llama ones: rmsnorm(x) = x / sqrt(mean(x^2) + eps) * w, the gated
-// MLP (silu(x W_gate^T) * (x W_up^T)) W_down^T, residual adds after the
-// attention and the MLP.
+// projections to the vendor GEMM (chapter-4 title); here they are this
+// library's own kernel.  The formulas are the public Llama ones: rmsnorm(x) =
+// x / sqrt(mean(x^2) + eps) * w, the gated MLP (silu(x W_gate^T) *
+// (x W_up^T)) W_down^T, residual adds after the attention and the MLP.
 //
 // Design.  At decode batch sizes (up to 64 rows) the projections are
 // matrix x skinny-matrix products bound by reading the weights once: one
@@ -19,20 +19,19 @@
 // 64 features; K is split over the workgroup's four waves and, where 64-wide
 // feature tiles alone would leave the chip's 256 CUs idle, over workgroups
 // too, whose float32 partials a second kernel sums in a fixed order (no
-// atomics: the result does not depend on scheduling).  Other shapes go to
-// rocBLAS: the row-major product C[B][N] = X[B][K] W[N][K]^T is handed to the
-// column-major library as C^T = W X^T (op(W) = transpose).  Either way the
-// residual adds are folded in (beta = 1), so h is read, summed in float32
-// and rounded once.  RMSNorm
-// is one workgroup per row: 16-byte loads, a float32 sum of squares reduced
-// across the workgroup, one rounding per output.
+// atomics: the result does not depend on scheduling).  Larger batches run
+// the same kernel once per 64-row block (a second grid dimension; the weights
+// are then read once per row block), and a K or feature count that is not a
+// multiple of the tiles is masked, so every shape with K and the feature
+// count multiples of 8 runs here.  The residual adds are folded in, so h is
+// read, summed in float32 and rounded once.  RMSNorm is one workgroup per
+// row: 16-byte loads, a float32 sum of squares reduced across the workgroup,
+// one rounding per output.
 #include "common.h"
-
-#include <rocblas/rocblas.h>
+#include "decode_api.h"
 
 #include <algorithm>
-#include <atomic>
-#include <mutex>
+#include <vector>
 
 namespace pkv {
 
@@ -103,27 +102,6 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(uint16_t* __restrict__ ac
   reinterpret_cast<uint4*>(act + (int64_t)r * inter)[c] = make_uint4(res[0], res[1], res[2], res[3]);
 }
 
-// One rocBLAS handle per device, created on first use and kept for the
-// process (a handle holds the library's per-device state); calls set the
-// stream each time.  Calls on one device from several host threads at once
-// must be serialised by the caller (the handle is shared).
-rocblas_handle blas_handle() {
-  constexpr int kMaxDev = 64;
-  static std::atomic<rocblas_handle> handles[kMaxDev];
-  static std::mutex mu;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
-  rocblas_handle h = handles[dev].load(std::memory_order_acquire);
-  if (h) return h;
-  std::lock_guard<std::mutex> lock(mu);
-  h = handles[dev].load(std::memory_order_relaxed);
-  if (!h) {
-    if (rocblas_create_handle(&h) != rocblas_status_success) return nullptr;
-    handles[dev].store(h, std::memory_order_release);
-  }
-  return h;
-}
-
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -143,7 +121,7 @@ struct GemmSeg {
   const uint16_t* w;
   uint16_t* c;
   float* part;        // [splits][rows][n] float32 partials when K is split
-  int n;              // output features, a multiple of 64
+  int n;              // output features, a multiple of 8
   int tile_begin;     // first tile of this product
   int tile_end;       // one past its last tile
 };
@@ -155,23 +133,25 @@ struct DecodeGemmArgs {
   int inter;          // gated mode: W = [gate; up] of 2 inter rows, C = silu(gate) * up [rows][inter]
 };
 
-// Decode-batch projection, one workgroup per (64 features, K range), each
-// of its four waves one block of 16 features over the whole range: C^T[16
-// n][64 b] as four 16 x 16 tiles of v_mfma_f32_16x16x32_bf16 (A = the
-// wave's 16 W rows, B = 16 rows of X; 8 k per lane from group lane / 16,
-// 16-byte loads; a lane keeps C^T rows 4 (lane / 16) .. + 3 of column
-// lane % 16 of each tile).  Each wave streams its 16 rows along K, so the
-// workgroup's loads in flight stay within a few DRAM pages per row (a wave
-// per K slice over all 64 rows instead keeps every page of the matrix open
-// at once and streams at half the rate).  X goes through LDS in slices of
-// 128 k (64 rows x 256 B, double-buffered, one barrier per slice), loaded
+// Decode-batch projection, one workgroup per (64 features, K range, 64-row
+// block), each of its four waves one block of 16 features over the whole
+// range: C^T[16 n][64 b] as four 16 x 16 tiles of v_mfma_f32_16x16x32_bf16
+// (A = the wave's 16 W rows, B = 16 rows of X; 8 k per lane from group
+// lane / 16, 16-byte loads; a lane keeps C^T rows 4 (lane / 16) .. + 3 of
+// column lane % 16 of each tile).  Each wave streams its 16 rows along K, so
+// the workgroup's loads in flight stay within a few DRAM pages per row (a
+// wave per K slice over all 64 rows instead keeps every page of the matrix
+// open at once and streams at half the rate).  X goes through LDS in slices
+// of 128 k (64 rows x 256 B, double-buffered, one barrier per slice), loaded
 // once per workgroup; W and X of the next two slices are in flight while the
-// current one is multiplied.  One K range: the sums (plus C when
-// accumulating) are rounded to bf16 into C; several: they go as float32 to
-// the product's partials for decode_reduce_kernel.  Gated mode (kGlu): tile
-// t takes gate rows 32 t .. + 31 (waves 0, 1) and the matching up rows
-// (waves 2, 3), which hand their sums over through LDS; the gate waves
-// write silu(bf16(gate)) * bf16(up) for features 32 t .. + 31.
+// current one is multiplied.  Elements past the K range (a K that is not a
+// multiple of 128) load as zeros; features past n load the last feature row
+// and are not stored.  One K range: the sums (plus C when accumulating) are
+// rounded to bf16 into C; several: they go as float32 to the product's
+// partials for decode_reduce_kernel.  Gated mode (kGlu): tile t takes gate
+// rows 32 t .. + 31 (waves 0, 1) and the matching up rows (waves 2, 3), which
+// hand their sums over through LDS; the gate waves write
+// silu(bf16(gate)) * bf16(up) for features 32 t .. + 31.
 template <bool kGlu>
 __global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGemmArgs args) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -181,48 +161,35 @@ __global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGem
   // that eighth of X; numbered tile-first, every XCD would fetch all of X
   const int t = blockIdx.x / args.splits;
   const int split = blockIdx.x % args.splits;
+  const int row0 = blockIdx.y * kDbRows;
   int si = 0;
   while (si + 1 < args.nseg && t >= args.seg[si].tile_end) ++si;
   const uint16_t* __restrict__ w = args.seg[si].w;
   const int n = args.seg[si].n;
   const int n0 = (t - args.seg[si].tile_begin) * kDbN;
-  const int k = args.k, rows = args.rows;
-  const int nit = args.kchunk / kDbSlice;         // whole slices (checked on the host)
+  const int k = args.k;
+  const int rows = min(kDbRows, args.rows - row0);  // rows of this block
   const int kbeg = split * args.kchunk;
+  const int kc = min(args.kchunk, k - kbeg);        // K range of this workgroup (a multiple of 8)
+  const int nfull = kc / kDbSlice;                  // whole 128-wide slices
   const int r16 = lane & 15;
   const int kg = 8 * (lane >> 4);
-  const int wr = kGlu ? (wv < 2 ? 0 : args.inter) + 32 * t + 16 * (wv & 1) + r16 : n0 + 16 * wv + r16;
+  int wr = kGlu ? (wv < 2 ? 0 : args.inter) + 32 * t + 16 * (wv & 1) + r16 : n0 + 16 * wv + r16;
+  if (!kGlu) wr = min(wr, n - 1);
   const uint16_t* wrow = w + (int64_t)wr * k + kbeg + kg;
   // X slice loads: thread i brings row i / 4's quarter i % 4 of the slice
-  // (rows past the batch read row 0 and store zeros)
+  // (rows past the block read its first row and store zeros)
   constexpr int kXq = kDbSlice / 4 / 8;           // 16-byte loads per thread and slice
   const int xr = threadIdx.x >> 2, xq = threadIdx.x & 3;
   const bool xok = xr < rows;
-  const uint16_t* xsrc = args.x + (int64_t)(xok ? xr : 0) * k + kbeg + (kDbSlice / 4) * xq;
+  const uint16_t* xsrc = args.x + (int64_t)(row0 + (xok ? xr : 0)) * k + kbeg + (kDbSlice / 4) * xq;
   __shared__ uint16_t xs[2][kDbRows * kXsRow];
   uint16_t* xdst = &xs[0][xr * kXsRow + (kDbSlice / 4) * xq];
 
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // slices it + 1 and it + 2 are in flight while slice it is multiplied:
-  // three register sets for W and X, used in turn (the loop is unrolled by
-  // three so every set is named statically); loads past the last slice
-  // load the last one again (in bounds, its lines in L2)
-  auto load = [&](int it, uint4 (&wd)[kDbSteps], uint4 (&xd)[kXq]) {
-    const int off = (it < nit ? it : nit - 1) * kDbSlice;
-#pragma unroll
-    for (int u = 0; u < kDbSteps; ++u) wd[u] = *reinterpret_cast<const uint4*>(wrow + off + kDbStage * u);
-#pragma unroll
-    for (int q = 0; q < kXq; ++q) xd[q] = *reinterpret_cast<const uint4*>(xsrc + off + 8 * q);
-  };
-  auto slice = [&](int it, uint4 (&wu)[kDbSteps], uint4 (&xu)[kXq], uint4 (&wl)[kDbSteps], uint4 (&xl)[kXq]) {
-    const int buf = it & 1;
-    uint4* xd = reinterpret_cast<uint4*>(xdst + buf * kDbRows * kXsRow);
-#pragma unroll
-    for (int q = 0; q < kXq; ++q) xd[q] = xok ? xu[q] : make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
-    load(it + 2, wl, xl);
+  auto mul = [&](int buf, const uint4 (&wu)[kDbSteps]) {
     const uint16_t* xb = &xs[buf][r16 * kXsRow + kg];
 #pragma unroll
     for (int u = 0; u < kDbSteps; ++u)
@@ -233,16 +200,64 @@ __global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGem
                                                          __builtin_bit_cast(bf16x8, bv), acc[j], 0, 0, 0);
       }
   };
-  uint4 w0[kDbSteps], w1[kDbSteps], w2[kDbSteps], x0[kXq], x1[kXq], x2[kXq];
-  load(0, w0, x0);
-  load(1, w1, x1);
-  for (int it = 0;; it += 3) {
-    slice(it, w0, x0, w2, x2);
-    if (it + 1 >= nit) break;
-    slice(it + 1, w1, x1, w0, x0);
-    if (it + 2 >= nit) break;
-    slice(it + 2, w2, x2, w1, x1);
-    if (it + 3 >= nit) break;
+  if (nfull > 0) {
+    // slices it + 1 and it + 2 are in flight while slice it is multiplied:
+    // three register sets for W and X, used in turn (the loop is unrolled by
+    // three so every set is named statically); loads past the last whole
+    // slice load that one again (in bounds, its lines in L2)
+    auto load = [&](int it, uint4 (&wd)[kDbSteps], uint4 (&xd)[kXq]) {
+      const int off = (it < nfull ? it : nfull - 1) * kDbSlice;
+#pragma unroll
+      for (int u = 0; u < kDbSteps; ++u) wd[u] = *reinterpret_cast<const uint4*>(wrow + off + kDbStage * u);
+#pragma unroll
+      for (int q = 0; q < kXq; ++q) xd[q] = *reinterpret_cast<const uint4*>(xsrc + off + 8 * q);
+    };
+    auto slice = [&](int it, uint4 (&wu)[kDbSteps], uint4 (&xu)[kXq], uint4 (&wl)[kDbSteps], uint4 (&xl)[kXq]) {
+      const int buf = it & 1;
+      uint4* xd = reinterpret_cast<uint4*>(xdst + buf * kDbRows * kXsRow);
+#pragma unroll
+      for (int q = 0; q < kXq; ++q) xd[q] = xok ? xu[q] : make_uint4(0u, 0u, 0u, 0u);
+      __syncthreads();
+      load(it + 2, wl, xl);
+      mul(buf, wu);
+    };
+    uint4 w0[kDbSteps], w1[kDbSteps], w2[kDbSteps], x0[kXq], x1[kXq], x2[kXq];
+    load(0, w0, x0);
+    load(1, w1, x1);
+    for (int it = 0;; it += 3) {
+      slice(it, w0, x0, w2, x2);
+      if (it + 1 >= nfull) break;
+      slice(it + 1, w1, x1, w0, x0);
+      if (it + 2 >= nfull) break;
+      slice(it + 2, w2, x2, w1, x1);
+      if (it + 3 >= nfull) break;
+    }
+  }
+  if (kc > nfull * kDbSlice) {
+    // a short last slice (K not a multiple of 128): elements past the K range
+    // read as zeros through buffer descriptors over the whole matrices
+    // (under 2^31 bytes, checked on the host): an offset past the
+    // descriptor's range reads zeros without touching memory
+    constexpr uint32_t kOut = 0x80000000u;
+    const int off = nfull * kDbSlice;
+    const int w_rows = kGlu ? 2 * args.inter : n;
+    const auto wres = buf_rsrc(w, (uint32_t)((int64_t)w_rows * k * 2));
+    const auto xres = buf_rsrc(args.x, (uint32_t)((int64_t)args.rows * k * 2));
+    const uint32_t woff = (uint32_t)(((int64_t)wr * k + kbeg + off + kg) * 2);
+    const uint32_t xoff = (uint32_t)(((int64_t)(row0 + (xok ? xr : 0)) * k + kbeg + off + (kDbSlice / 4) * xq) * 2);
+    uint4 wt[kDbSteps], xt[kXq];
+#pragma unroll
+    for (int u = 0; u < kDbSteps; ++u)
+      wt[u] = buf_load16(wres, off + kDbStage * u + kg < kc ? woff + 2u * (kDbStage * u) : kOut);
+#pragma unroll
+    for (int q = 0; q < kXq; ++q)
+      xt[q] = buf_load16(xres, xok && off + (kDbSlice / 4) * xq + 8 * q < kc ? xoff + 16u * q : kOut);
+    const int buf = nfull & 1;
+    uint4* xd = reinterpret_cast<uint4*>(xdst + buf * kDbRows * kXsRow);
+#pragma unroll
+    for (int q = 0; q < kXq; ++q) xd[q] = xt[q];
+    __syncthreads();
+    mul(buf, wt);
   }
   if (kGlu) {   // up waves (2, 3) hand their tiles to gate waves (0, 1)
     __shared__ f32x4 up[2][4][kWave];
@@ -270,17 +285,19 @@ __global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGem
         o[e] = pack_bf16x2(r[0], r[1]);
       }
       const int f0 = 32 * t + 16 * wv + 4 * (lane >> 4);
-      *reinterpret_cast<uint2*>(args.seg[0].c + (int64_t)b * args.inter + f0) = make_uint2(o[0], o[1]);
+      *reinterpret_cast<uint2*>(args.seg[0].c + (int64_t)(row0 + b) * args.inter + f0) = make_uint2(o[0], o[1]);
     }
     return;
   }
   const int nn = n0 + 16 * wv + 4 * (lane >> 4);    // C^T rows nn .. nn + 3 of column b
+  if (nn >= n) return;                              // n % 8 == 0: the four columns are in or out together
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int b = 16 * j + r16;
     if (b >= rows) continue;
+    const int64_t gb = row0 + b;
     if (args.splits == 1) {
-      uint16_t* crow = args.seg[si].c + (int64_t)b * n + nn;
+      uint16_t* crow = args.seg[si].c + gb * n + nn;
       float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
       if (args.accumulate) {
         const uint2 old = *reinterpret_cast<const uint2*>(crow);
@@ -291,7 +308,7 @@ __global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGem
       }
       *reinterpret_cast<uint2*>(crow) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     } else {
-      *reinterpret_cast<f32x4*>(args.seg[si].part + ((int64_t)split * rows + b) * n + nn) = acc[j];
+      *reinterpret_cast<f32x4*>(args.seg[si].part + ((int64_t)split * args.rows + gb) * n + nn) = acc[j];
     }
   }
 }
@@ -401,86 +418,113 @@ __global__ __launch_bounds__(kNormThreads) void reduce_residual_norm_kernel(uint
   }
 }
 
-// K splits for a decode-batch launch of `tiles` 64-feature tiles: the most
-// (a power of two) that keep the workgroups within one round of the chip's
-// 256 CUs, each keeping whole X slices; 0 if the shape does not fit the
-// kernel.  (A second, partial round of workgroups costs more than the
-// parallelism it adds: 48 tiles x 8 splits ran 30% slower than x 4.)
+// K splits for a launch of `tiles` 64-feature tiles over `rows` rows: the
+// most (a power of two) that keep the workgroups within one round of the
+// chip's 256 CUs, each taking whole 128-wide X slices (only the last K range
+// may be shorter); 0 if the shape does not fit the kernel (K or rows not
+// positive, K not a multiple of 8).  (A second, partial round of workgroups
+// costs more than the parallelism it adds: 48 tiles x 8 splits ran 30%
+// slower than x 4.)
 int decode_gemm_splits(int rows, int tiles, int k) {
-  if (rows <= 0 || rows > kDbRows || tiles <= 0 || k % kDbSlice) return 0;
+  if (rows <= 0 || tiles <= 0 || k <= 0 || k % 8) return 0;
+  const int64_t blocks = (int64_t)tiles * ((rows + kDbRows - 1) / kDbRows);
   int s = 1;
-  while (tiles * s * 2 <= 256 && k % (kDbSlice * s * 2) == 0) s *= 2;
+  while (blocks * s * 2 <= 256 && k >= kDbSlice * s * 2) s *= 2;
   return s;
+}
+
+// K per split for `splits` splits: whole slices, the last range shorter.
+int decode_gemm_kchunk(int k, int splits) {
+  const int per = (k + splits - 1) / splits;
+  return (per + kDbSlice - 1) / kDbSlice * kDbSlice;
 }
 
 }  // namespace
 
 size_t decode_gemm_workspace_bytes(int rows, int n, int k) {
-  if (n % kDbN) return 0;
-  const int s = decode_gemm_splits(rows, n / kDbN, k);
+  if (n <= 0 || n % 8) return 0;
+  int s = decode_gemm_splits(rows, (n + kDbN - 1) / kDbN, k);
+  if (s > 1) s = (k + decode_gemm_kchunk(k, s) - 1) / decode_gemm_kchunk(k, s);
   return s > 1 ? (size_t)s * rows * n * sizeof(float) : 0;
 }
 
 // Products sharing X [rows][k] (1 to kMaxSeg of them: w[i] [n[i]][k] into
-// c[i] [rows][n[i]]) on the decode-batch kernel, K-split partials in
-// `part` (part_bytes) when needed.  Returns PKV_ERR_INVALID_ARG (nothing
-// launched) when the shape does not fit the kernel or the partials do not
-// fit `part`; the caller then takes another route.
-// With reduce == false and K split the partials are left for the caller
-// (the number of splits goes to *splits_out when not null).
+// c[i] [rows][n[i]]) on the projection kernel, K-split partials in `part`
+// (part_bytes) when the split pays and they fit (else one K range).
+// PKV_ERR_UNSUPPORTED (nothing launched) when the shape does not fit the
+// kernel (a feature count or K that is not a multiple of 8).  With reduce ==
+// false and K split the partials are left for the caller (the number of
+// splits goes to *splits_out when not null).
 int decode_gemm(int nseg, uint16_t* const* c, const uint16_t* const* w, const int* n, const uint16_t* x, int rows,
                 int k, bool accumulate, void* part, size_t part_bytes, hipStream_t stream, bool reduce = true,
                 int* splits_out = nullptr) {
   if (nseg < 1 || nseg > kMaxSeg) return PKV_ERR_INVALID_ARG;
-  int tiles = 0, ntot = 0;
+  int tiles = 0;
+  int64_t ntot = 0;
   for (int i = 0; i < nseg; ++i) {
-    if (n[i] <= 0 || n[i] % kDbN || n[i] > (1 << 24)) return PKV_ERR_INVALID_ARG;
-    tiles += n[i] / kDbN;
+    if (n[i] <= 0 || n[i] % 8 || n[i] > (1 << 24)) return PKV_ERR_UNSUPPORTED;
+    tiles += (n[i] + kDbN - 1) / kDbN;
     ntot += n[i];
   }
-  const int splits = decode_gemm_splits(rows, tiles, k);
-  if (splits == 0 || (int64_t)rows * ntot / 8 > 0x7fffff00) return PKV_ERR_INVALID_ARG;
-  if (splits > 1 && (!part || part_bytes < (size_t)splits * rows * ntot * sizeof(float))) return PKV_ERR_INVALID_ARG;
+  int splits = decode_gemm_splits(rows, tiles, k);
+  if (splits == 0) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)rows * k * 2 > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;     // 31-bit buffer offsets
+  for (int i = 0; i < nseg; ++i)
+    if ((int64_t)n[i] * k * 2 > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+  const int64_t row_blocks = (rows + kDbRows - 1) / kDbRows;
+  if (row_blocks > 65535 || (int64_t)rows * ntot / 8 > 0x7fffff00) return PKV_ERR_INVALID_ARG;
+  int kchunk = decode_gemm_kchunk(k, splits);
+  splits = (k + kchunk - 1) / kchunk;
+  if (splits > 1 && (!part || part_bytes < (size_t)splits * rows * ntot * sizeof(float))) {
+    splits = 1;                         // no room for partials: one K range
+    kchunk = k;
+  }
   if (splits_out) *splits_out = splits;
   DecodeGemmArgs a{};
   ReduceArgs ra{};
   int t0 = 0;
   size_t poff = 0;
-  int gend = 0;
+  int64_t gend = 0;
   for (int i = 0; i < nseg; ++i) {
     float* pp = splits > 1 ? static_cast<float*>(part) + poff : nullptr;
-    a.seg[i] = GemmSeg{w[i], c[i], pp, n[i], t0, t0 + n[i] / kDbN};
-    t0 += n[i] / kDbN;
+    const int nt = (n[i] + kDbN - 1) / kDbN;
+    a.seg[i] = GemmSeg{w[i], c[i], pp, n[i], t0, t0 + nt};
+    t0 += nt;
     poff += (size_t)splits * rows * n[i];
-    gend += rows * (n[i] / 8);
-    ra.seg[i] = ReduceSeg{c[i], pp, n[i], gend};
+    gend += (int64_t)rows * (n[i] / 8);
+    ra.seg[i] = ReduceSeg{c[i], pp, n[i], (int)gend};
   }
   a.x = x;
   a.nseg = nseg;
   a.rows = rows;
   a.k = k;
-  a.kchunk = k / splits;
+  a.kchunk = kchunk;
   a.splits = splits;
   a.accumulate = accumulate ? 1 : 0;
   void* args[] = {&a};
-  int rc = launch_status(hipLaunchKernel((const void*)decode_gemm_kernel<false>, dim3(tiles * splits),
-                                         dim3(kDbWaves * kWave), args, 0, stream));
+  int rc = launch_status(hipLaunchKernel((const void*)decode_gemm_kernel<false>,
+                                         dim3(tiles * splits, (unsigned)row_blocks), dim3(kDbWaves * kWave), args, 0,
+                                         stream));
   if (rc != PKV_OK || splits == 1 || !reduce) return rc;
   ra.nseg = nseg;
   ra.rows = rows;
   ra.splits = splits;
   ra.accumulate = a.accumulate;
   void* rargs[] = {&ra};
-  return launch_status(hipLaunchKernel((const void*)decode_reduce_kernel, dim3((gend + 255) / 256), dim3(256), rargs,
-                                       0, stream));
+  return launch_status(hipLaunchKernel((const void*)decode_reduce_kernel, dim3((unsigned)((gend + 255) / 256)),
+                                       dim3(256), rargs, 0, stream));
 }
 
 // act[rows][inter] = silu(bf16(X Wg^T)) * bf16(X Wu^T) for W = [Wg; Wu]
-// [2 inter][k], on the decode-batch kernel in gated mode (K never split).
-// PKV_ERR_INVALID_ARG (nothing launched) when the shape does not fit.
+// [2 inter][k], on the projection kernel in gated mode (K never split).
+// PKV_ERR_UNSUPPORTED (nothing launched) when the shape does not fit
+// (inter % 32, K % 8); the caller then runs the product and the SiLU kernel.
 int decode_gemm_glu(uint16_t* act, const uint16_t* x, const uint16_t* w, int rows, int inter, int k,
                     hipStream_t stream) {
-  if (rows <= 0 || rows > kDbRows || inter <= 0 || inter % 32 || k % kDbSlice) return PKV_ERR_INVALID_ARG;
+  if (rows <= 0 || inter <= 0 || inter % 32 || k <= 0 || k % 8) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)rows * k * 2 > 0x7fffffffLL || (int64_t)2 * inter * k * 2 > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+  const int64_t row_blocks = (rows + kDbRows - 1) / kDbRows;
+  if (row_blocks > 65535) return PKV_ERR_INVALID_ARG;
   DecodeGemmArgs a{};
   a.seg[0] = GemmSeg{w, act, nullptr, 2 * inter, 0, inter / 32};
   a.x = x;
@@ -491,7 +535,7 @@ int decode_gemm_glu(uint16_t* act, const uint16_t* x, const uint16_t* w, int row
   a.splits = 1;
   a.inter = inter;
   void* args[] = {&a};
-  return launch_status(hipLaunchKernel((const void*)decode_gemm_kernel<true>, dim3(inter / 32, 1),
+  return launch_status(hipLaunchKernel((const void*)decode_gemm_kernel<true>, dim3(inter / 32, (unsigned)row_blocks),
                                        dim3(kDbWaves * kWave), args, 0, stream));
 }
 
@@ -501,30 +545,6 @@ int reduce_residual_norm(uint16_t* h, uint16_t* m, const float* part, const uint
   void* args[] = {&h, &m, &part, &w, &rows, &dim, &splits, &eps};
   return launch_status(hipLaunchKernel((const void*)reduce_residual_norm_kernel, dim3(rows), dim3(kNormThreads),
                                        args, 0, stream));
-}
-
-// C[rows][n] = beta * C + X[rows][k] W[n][k]^T, bf16 in and out, float32 sums:
-// the decode-batch kernel where the shape fits it, else rocBLAS.
-int gemm_xwt(uint16_t* c, const uint16_t* x, const uint16_t* w, int rows, int n, int k, float beta, void* stream,
-             void* workspace, size_t workspace_bytes) {
-  if (beta == 0.0f || beta == 1.0f) {
-    uint16_t* cc[1] = {c};
-    const uint16_t* ww[1] = {w};
-    const int nn[1] = {n};
-    const int rc = decode_gemm(1, cc, ww, nn, x, rows, k, beta == 1.0f, workspace, workspace_bytes,
-                               static_cast<hipStream_t>(stream));
-    if (rc != PKV_ERR_INVALID_ARG) return rc;
-  }
-  rocblas_handle h = blas_handle();
-  if (!h) return PKV_ERR_HIP;
-  if (rocblas_set_stream(h, static_cast<hipStream_t>(stream)) != rocblas_status_success) return PKV_ERR_HIP;
-  const float alpha = 1.0f;
-  // column-major view: C^T [n][rows] = op(W^T [k][n]) X^T [k][rows], op = transpose
-  const rocblas_status st = rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, n, rows, k,
-                                            &alpha, w, rocblas_datatype_bf16_r, k, x, rocblas_datatype_bf16_r, k,
-                                            &beta, c, rocblas_datatype_bf16_r, n, c, rocblas_datatype_bf16_r, n,
-                                            rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  return st == rocblas_status_success ? PKV_OK : PKV_ERR_HIP;
 }
 
 }  // namespace pkv
@@ -569,23 +589,25 @@ extern "C" size_t pkv_linear_workspace_bytes(int rows, int out_features, int in_
 extern "C" int pkv_linear(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weight, int rows, int out_features,
                           int in_features, int accumulate, void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 0 || out_features <= 0 || in_features <= 0) return PKV_ERR_INVALID_ARG;
+  if (out_features % 8 || in_features % 8) return PKV_ERR_UNSUPPORTED;
   if (rows == 0) return PKV_OK;
   if (!out || !x || !weight) return PKV_ERR_NULL;
   if (!aligned16(out) || !aligned16(x) || !aligned16(weight) || (workspace && !aligned16(workspace)))
     return PKV_ERR_MISALIGNED;
-  return gemm_xwt(out, x, weight, rows, out_features, in_features, accumulate ? 1.0f : 0.0f, stream, workspace,
-                  workspace_bytes);
+  uint16_t* cc[1] = {out};
+  const uint16_t* ww[1] = {weight};
+  const int nn[1] = {out_features};
+  return decode_gemm(1, cc, ww, nn, x, rows, in_features, accumulate != 0, workspace, workspace_bytes,
+                     static_cast<hipStream_t>(stream));
 }
 
 namespace {
 
 // bf16 elements of the float32 K-split partials the layer's projections need
-// (the largest over its launches, fallbacks included), placed after the
-// activations.
+// (the largest over its launches), placed after the activations.
 size_t layer_partial_elems(int batch, int hidden, int intermediate, int n_q_heads, int n_kv_heads) {
   const int qd = n_q_heads * kHeadDim, kvd = n_kv_heads * kHeadDim;
   const size_t sizes[] = {decode_gemm_workspace_bytes(batch, qd + 2 * kvd, hidden),
-                          decode_gemm_workspace_bytes(batch, qd, hidden), decode_gemm_workspace_bytes(batch, kvd, hidden),
                           decode_gemm_workspace_bytes(batch, hidden, qd),
                           decode_gemm_workspace_bytes(batch, 2 * intermediate, hidden),
                           decode_gemm_workspace_bytes(batch, hidden, intermediate)};
@@ -607,51 +629,53 @@ extern "C" size_t pkv_decode_layer_scratch_elems(int batch, int hidden, int inte
 
 namespace {
 
-// One layer; `a_ready`: the scratch's a already holds rmsnorm(h, attn_norm)
-// (left there by the previous layer).  With `next_norm` the layer ends by
-// leaving a = rmsnorm(h, next_norm) for the next layer: where the down
-// projection's K is split, its partials, the residual add and that norm are
-// one kernel (as the output projection's are with the MLP's norm).  Argument
-// checks are the callers'.
+// The scratch regions of one layer (see pkv_decode_layer_scratch_elems).
+struct LayerScratch {
+  pkv_bf16 *a, *q, *k, *v, *o, *m, *gu, *act;
+  void* part;
+  size_t part_bytes;
+};
+
+LayerScratch layer_scratch(pkv_bf16* scratch, int batch, int hidden, int intermediate, int n_q_heads,
+                           int n_kv_heads) {
+  const size_t qd = (size_t)n_q_heads * kHeadDim, kvd = (size_t)n_kv_heads * kHeadDim;
+  LayerScratch s;
+  s.a = scratch;
+  s.q = s.a + (size_t)batch * hidden;
+  s.k = s.q + (size_t)batch * qd;
+  s.v = s.k + (size_t)batch * kvd;
+  s.o = s.v + (size_t)batch * kvd;
+  s.m = s.o + (size_t)batch * qd;
+  s.gu = s.m + (size_t)batch * hidden;
+  s.act = s.gu + (size_t)batch * 2 * intermediate;
+  s.part = s.act + (size_t)batch * intermediate;   // 16-byte aligned: every region is a multiple of 8 elements
+  s.part_bytes = 2 * layer_partial_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads);
+  return s;
+}
+
+// One layer; `att`: its attention call, checked and planned.  `a_ready`: the
+// scratch's a already holds rmsnorm(h, attn_norm) (left there by the previous
+// layer).  With `next_norm` the layer ends by leaving a = rmsnorm(h,
+// next_norm) for the next layer: where the down projection's K is split, its
+// partials, the residual add and that norm are one kernel (as the output
+// projection's are with the MLP's norm).  Argument checks are the callers'
+// (check_layer_args), so every launch here takes a shape its kernel runs.
 int decode_layer_impl(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int intermediate, pkv_bf16* scratch,
-                      pkv_bf16* k_pool, pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
-                      int64_t bt_row_stride, int num_slots, int max_blocks_per_seq, const int32_t* slot_ids,
-                      const int32_t* context_lens, const int32_t* row_lens_host, int batch, int max_context_len,
-                      int n_q_heads, int n_kv_heads, const float* cos_sin, int max_pos, float scale, float eps,
-                      void* workspace, size_t workspace_bytes, void* stream, bool a_ready,
-                      const pkv_bf16* next_norm) {
+                      const DecodeLaunch& att, int batch, int n_q_heads, int n_kv_heads, float eps, void* stream,
+                      bool a_ready, const pkv_bf16* next_norm) {
   const int qd = n_q_heads * kHeadDim, kvd = n_kv_heads * kHeadDim;
-  pkv_bf16* a = scratch;
-  pkv_bf16* q = a + (size_t)batch * hidden;
-  pkv_bf16* k = q + (size_t)batch * qd;
-  pkv_bf16* v = k + (size_t)batch * kvd;
-  pkv_bf16* o = v + (size_t)batch * kvd;
-  pkv_bf16* m = o + (size_t)batch * qd;
-  pkv_bf16* gu = m + (size_t)batch * hidden;
-  pkv_bf16* act = gu + (size_t)batch * 2 * intermediate;
-  void* part = act + (size_t)batch * intermediate;   // 16-byte aligned: every region is a multiple of 8 elements
-  const size_t part_bytes = 2 * layer_partial_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads);
+  const LayerScratch S = layer_scratch(scratch, batch, hidden, intermediate, n_q_heads, n_kv_heads);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   int rc;
-  if (!a_ready && (rc = pkv_rmsnorm(a, h, w->attn_norm, batch, hidden, eps, stream)) != PKV_OK) return rc;
-  // q, k and v in one launch where the decode-batch kernel takes the shape
+  if (!a_ready && (rc = pkv_rmsnorm(S.a, h, w->attn_norm, batch, hidden, eps, stream)) != PKV_OK) return rc;
+  // q, k and v in one launch
   {
-    uint16_t* cs[3] = {q, k, v};
+    uint16_t* cs[3] = {S.q, S.k, S.v};
     const uint16_t* ws[3] = {w->wq, w->wk, w->wv};
     const int ns[3] = {qd, kvd, kvd};
-    rc = decode_gemm(3, cs, ws, ns, a, batch, hidden, false, part, part_bytes, st);
+    if ((rc = decode_gemm(3, cs, ws, ns, S.a, batch, hidden, false, S.part, S.part_bytes, st)) != PKV_OK) return rc;
   }
-  if (rc == PKV_ERR_INVALID_ARG) {
-    if ((rc = pkv_linear(q, a, w->wq, batch, qd, hidden, 0, part, part_bytes, stream)) != PKV_OK) return rc;
-    if ((rc = pkv_linear(k, a, w->wk, batch, kvd, hidden, 0, part, part_bytes, stream)) != PKV_OK) return rc;
-    rc = pkv_linear(v, a, w->wv, batch, kvd, hidden, 0, part, part_bytes, stream);
-  }
-  if (rc != PKV_OK) return rc;
-  if ((rc = pkv_paged_decode_fused(o, q, k, v, k_pool, v_pool, num_blocks, block_table, bt_row_stride, num_slots,
-                                   max_blocks_per_seq, slot_ids, context_lens, row_lens_host, batch, max_context_len,
-                                   n_q_heads, n_kv_heads, kHeadDim, cos_sin, max_pos, scale, 0, workspace,
-                                   workspace_bytes, stream)) != PKV_OK)
-    return rc;
+  if ((rc = decode_enqueue(att, st)) != PKV_OK) return rc;
   // h += x W^T, then (norm_w given) y = rmsnorm(h, norm_w): with K split, the
   // partials' sum, the residual add and the norm are one kernel
   auto residual = [&](const uint16_t* x, const uint16_t* wt, int kdim, const pkv_bf16* norm_w, pkv_bf16* y) {
@@ -659,37 +683,78 @@ int decode_layer_impl(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int i
     const uint16_t* ws[1] = {wt};
     const int ns[1] = {hidden};
     int splits = 0;
-    int r = decode_gemm(1, cs, ws, ns, x, batch, kdim, true, part, part_bytes, st, norm_w == nullptr, &splits);
+    int r = decode_gemm(1, cs, ws, ns, x, batch, kdim, true, S.part, S.part_bytes, st, norm_w == nullptr, &splits);
     if (r == PKV_OK && splits > 1 && norm_w)
-      return reduce_residual_norm(h, y, static_cast<const float*>(part), norm_w, batch, hidden, splits, eps, st);
-    if (r == PKV_ERR_INVALID_ARG) r = pkv_linear(h, x, wt, batch, hidden, kdim, 1, part, part_bytes, stream);
+      return reduce_residual_norm(h, y, static_cast<const float*>(S.part), norm_w, batch, hidden, splits, eps, st);
     if (r == PKV_OK && norm_w) r = pkv_rmsnorm(y, h, norm_w, batch, hidden, eps, stream);
     return r;
   };
-  if ((rc = residual(o, w->wo, qd, w->mlp_norm, m)) != PKV_OK) return rc;
+  if ((rc = residual(S.o, w->wo, qd, w->mlp_norm, S.m)) != PKV_OK) return rc;
   // act = silu(m Wg^T) * (m Wu^T): one gated launch where it fits, else the
   // product into gate_up and the SiLU kernel
-  rc = decode_gemm_glu(act, m, w->w_gate_up, batch, intermediate, hidden, st);
-  if (rc == PKV_ERR_INVALID_ARG) {
-    if ((rc = pkv_linear(gu, m, w->w_gate_up, batch, 2 * intermediate, hidden, 0, part, part_bytes, stream)) != PKV_OK)
-      return rc;
-    rc = pkv_silu_mul(act, gu, batch, intermediate, stream);
+  if (intermediate % 32 == 0) {
+    rc = decode_gemm_glu(S.act, S.m, w->w_gate_up, batch, intermediate, hidden, st);
+  } else {
+    uint16_t* cs[1] = {S.gu};
+    const uint16_t* ws[1] = {w->w_gate_up};
+    const int ns[1] = {2 * intermediate};
+    rc = decode_gemm(1, cs, ws, ns, S.m, batch, hidden, false, S.part, S.part_bytes, st);
+    if (rc == PKV_OK) rc = pkv_silu_mul(S.act, S.gu, batch, intermediate, stream);
   }
   if (rc != PKV_OK) return rc;
-  return residual(act, w->w_down, intermediate, next_norm, a);
+  return residual(S.act, w->w_down, intermediate, next_norm, S.a);
 }
 
+// Everything a layer's launches need, checked before any of them: sizes,
+// weights, scratch, and the attention call (planned into `att`, with the
+// layer's q, k, v and o in the scratch).
 int check_layer_args(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int intermediate, pkv_bf16* scratch,
-                     size_t scratch_elems, int batch, int n_q_heads, int n_kv_heads) {
-  if (hidden <= 0 || intermediate <= 0 || n_q_heads <= 0 || n_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
+                     size_t scratch_elems, pkv_bf16* k_pool, pkv_bf16* v_pool, int num_blocks,
+                     const int32_t* block_table, int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,
+                     const int32_t* slot_ids, const int32_t* context_lens, const int32_t* row_lens_host, int batch,
+                     int max_context_len, int n_q_heads, int n_kv_heads, const float* cos_sin, int max_pos,
+                     float scale, float eps, void* workspace, size_t workspace_bytes, DecodeLaunch* att) {
+  if (hidden <= 0 || intermediate <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || !(eps >= 0.f))
+    return PKV_ERR_INVALID_ARG;
   if (!h || !w || !scratch || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->mlp_norm ||
       !w->w_gate_up || !w->w_down)
     return PKV_ERR_NULL;
   if (hidden % 8 || intermediate % 8) return PKV_ERR_INVALID_ARG;
+  if ((int64_t)batch > (int64_t)65535 * 64) return PKV_ERR_INVALID_ARG;
   if (scratch_elems < pkv_decode_layer_scratch_elems(batch, hidden, intermediate, n_q_heads, n_kv_heads))
     return PKV_ERR_CAPACITY;
   if (!aligned16(h) || !aligned16(scratch)) return PKV_ERR_MISALIGNED;
-  return PKV_OK;
+  const pkv_bf16* ws[] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w_gate_up, w->w_down};
+  for (const pkv_bf16* p : ws)
+    if (!aligned16(p)) return PKV_ERR_MISALIGNED;
+  const LayerScratch S = layer_scratch(scratch, batch, hidden, intermediate, n_q_heads, n_kv_heads);
+  DecodeCall c{};
+  c.fused = true;
+  c.out = S.o;
+  c.q = S.q;
+  c.k_new = S.k;
+  c.v_new = S.v;
+  c.k_pool = k_pool;
+  c.v_pool = v_pool;
+  c.num_blocks = num_blocks;
+  c.block_table = block_table;
+  c.bt_row_stride = bt_row_stride;
+  c.num_slots = num_slots;
+  c.max_blocks_per_seq = max_blocks_per_seq;
+  c.slot_ids = slot_ids;
+  c.context_lens = context_lens;
+  c.row_lens_host = row_lens_host;
+  c.batch = batch;
+  c.max_context_len = max_context_len;
+  c.n_q_heads = n_q_heads;
+  c.n_kv_heads = n_kv_heads;
+  c.head_dim = kHeadDim;
+  c.cos_sin = cos_sin;
+  c.max_pos = max_pos;
+  c.scale = scale;
+  c.workspace = workspace;
+  c.workspace_bytes = workspace_bytes;
+  return decode_prepare(c, att);
 }
 
 }  // namespace
@@ -704,12 +769,14 @@ extern "C" int pkv_decode_layer(pkv_bf16* h, const pkv_layer_weights* w, int hid
   if (batch < 0) return PKV_ERR_INVALID_ARG;
   if (batch == 0) return hidden > 0 && intermediate > 0 && n_q_heads > 0 && n_kv_heads > 0 ? PKV_OK
                                                                                           : PKV_ERR_INVALID_ARG;
-  int rc = check_layer_args(h, w, hidden, intermediate, scratch, scratch_elems, batch, n_q_heads, n_kv_heads);
+  thread_local DecodeLaunch att;
+  const int rc = check_layer_args(h, w, hidden, intermediate, scratch, scratch_elems, k_pool, v_pool, num_blocks,
+                                  block_table, bt_row_stride, num_slots, max_blocks_per_seq, slot_ids, context_lens,
+                                  row_lens_host, batch, max_context_len, n_q_heads, n_kv_heads, cos_sin, max_pos, scale,
+                                  eps, workspace, workspace_bytes, &att);
   if (rc != PKV_OK) return rc;
-  return decode_layer_impl(h, w, hidden, intermediate, scratch, k_pool, v_pool, num_blocks, block_table,
-                           bt_row_stride, num_slots, max_blocks_per_seq, slot_ids, context_lens, row_lens_host, batch,
-                           max_context_len, n_q_heads, n_kv_heads, cos_sin, max_pos, scale, eps, workspace,
-                           workspace_bytes, stream, false, nullptr);
+  return decode_layer_impl(h, w, hidden, intermediate, scratch, att, batch, n_q_heads, n_kv_heads, eps, stream, false,
+                           nullptr);
 }
 
 extern "C" int pkv_decode_layers(pkv_bf16* h, const pkv_layer_weights* layers, int n_layers, int hidden,
@@ -723,17 +790,19 @@ extern "C" int pkv_decode_layers(pkv_bf16* h, const pkv_layer_weights* layers, i
   if (n_layers < 0 || batch < 0 || bt_layer_stride < 0) return PKV_ERR_INVALID_ARG;
   if (n_layers == 0 || batch == 0) return PKV_OK;
   if (!layers || !block_table) return PKV_ERR_NULL;
+  thread_local std::vector<DecodeLaunch> att;
+  att.resize(n_layers);
   for (int l = 0; l < n_layers; ++l) {
-    const int rc = check_layer_args(h, &layers[l], hidden, intermediate, scratch, scratch_elems, batch, n_q_heads,
-                                    n_kv_heads);
+    const int rc = check_layer_args(h, &layers[l], hidden, intermediate, scratch, scratch_elems, k_pool, v_pool,
+                                    num_blocks, block_table + bt_layer_stride * l, bt_row_stride, num_slots,
+                                    max_blocks_per_seq, slot_ids, context_lens, row_lens_host, batch, max_context_len,
+                                    n_q_heads, n_kv_heads, cos_sin, max_pos, scale, eps, workspace, workspace_bytes,
+                                    &att[l]);
     if (rc != PKV_OK) return rc;
   }
   for (int l = 0; l < n_layers; ++l) {
-    const int rc = decode_layer_impl(h, &layers[l], hidden, intermediate, scratch, k_pool, v_pool, num_blocks,
-                                     block_table + bt_layer_stride * l, bt_row_stride, num_slots, max_blocks_per_seq,
-                                     slot_ids, context_lens, row_lens_host, batch, max_context_len, n_q_heads,
-                                     n_kv_heads, cos_sin, max_pos, scale, eps, workspace, workspace_bytes, stream,
-                                     l > 0, l + 1 < n_layers ? layers[l + 1].attn_norm : nullptr);
+    const int rc = decode_layer_impl(h, &layers[l], hidden, intermediate, scratch, att[l], batch, n_q_heads,
+                                     n_kv_heads, eps, stream, l > 0, l + 1 < n_layers ? layers[l + 1].attn_norm : nullptr);
     if (rc != PKV_OK) return rc;
   }
   return PKV_OK;

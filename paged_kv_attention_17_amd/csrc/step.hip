@@ -11,7 +11,10 @@
 #include <cstdint>
 #include <vector>
 
-#include "../../include/pagedkv.h"
+#include "common.h"
+#include "decode_api.h"
+
+using namespace pkv;
 
 extern "C" int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const* k, const pkv_bf16* const* v,
                                pkv_bf16* const* out, pkv_bf16* k_pool, pkv_bf16* v_pool, int num_blocks,
@@ -30,6 +33,7 @@ extern "C" int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const
   const int64_t row_stride = (int64_t)n_layers * max_blocks_per_seq;
   const int64_t bt_elems = (int64_t)num_slots * row_stride;
   if (bt_elems > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
 
   // 1. Host allocation, checked for capacity before anything changes.
   int64_t need = 0;
@@ -46,6 +50,61 @@ extern "C" int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const
   }
   if (need > *n_free) return PKV_ERR_CAPACITY;
 
+  // 2. Every layer's attention launch, planned and checked before anything
+  // changes or is enqueued.  The layers share the rows and their lengths, so
+  // their streaming launches chain: each merges the previous layer's rows cut
+  // by share ends in its prologue, and one merge launch follows the last.  An
+  // identity batch (row b = slot b) passes no device slot ids.
+  bool identity = batch <= num_slots;
+  for (int b = 0; b < batch && identity; ++b) identity = slot_ids_host[b] == b;
+  thread_local std::vector<int32_t> row_lens;
+  row_lens.resize(batch);
+  for (int b = 0; b < batch; ++b) row_lens[b] = cached_lens_host[slot_ids_host[b]] + 1;
+  const int32_t* ctx_dev = meta_dev;
+  const int32_t* sid_dev = identity ? nullptr : meta_dev + num_slots + batch;
+  thread_local std::vector<DecodeLaunch> launches;
+  launches.resize(n_layers);
+  bool chain = false;
+  for (int l = 0; l < n_layers; ++l) {
+    DecodeCall c{};
+    c.fused = true;
+    c.out = out[l];
+    c.q = q[l];
+    c.k_new = k[l];
+    c.v_new = v[l];
+    c.k_pool = k_pool;
+    c.v_pool = v_pool;
+    c.num_blocks = num_blocks;
+    c.block_table = bt_dev + l * layer_stride;
+    c.bt_row_stride = row_stride;
+    c.num_slots = num_slots;
+    c.max_blocks_per_seq = max_blocks_per_seq;
+    c.slot_ids = sid_dev;
+    c.slot_ids_host = slot_ids_host;
+    c.context_lens = ctx_dev;
+    c.row_lens_host = row_lens.data();
+    c.batch = batch;
+    c.max_context_len = max_context_len;
+    c.n_q_heads = n_q_heads;
+    c.n_kv_heads = n_kv_heads;
+    c.head_dim = head_dim;
+    c.cos_sin = cos_sin;
+    c.max_pos = max_pos;
+    c.scale = scale;
+    c.partition_size = partition_size;
+    c.workspace = workspace;
+    c.workspace_bytes = workspace_bytes;
+    if (chain) {
+      c.records_half = l & 1;
+      c.out_prev = out[l - 1];
+    }
+    const int rc = decode_prepare(c, &launches[l]);
+    if (rc != PKV_OK) return rc;
+    if (l == 0) chain = n_layers > 1 && decode_chainable(launches[0]);
+  }
+
+  // 3. Allocation and the step's metadata (context lengths, positions, slot
+  // ids), carried to the device in kernel arguments.
   thread_local std::vector<int32_t> t_off, t_val, m_off, m_val;
   t_off.clear();
   t_val.clear();
@@ -63,7 +122,6 @@ extern "C" int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const
       t_val.push_back(blk);
     }
   }
-  // 2. Context lengths, positions and slot ids for the kernels.
   for (int b = 0; b < batch; ++b) {
     const int s = slot_ids_host[b];
     const int p = cached_lens_host[s];
@@ -81,23 +139,8 @@ extern "C" int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const
   rc = pkv_block_table_patch(meta_dev, meta_elems, m_off.data(), m_val.data(), (int)m_off.size(), stream);
   if (rc != PKV_OK) return rc;
 
-  // 3. Per layer: RoPE, append and attention in one launch.  An identity
-  // batch (row b = slot b) passes no slot ids, which saves the kernels one
-  // dependent memory read before their first K/V load.
-  bool identity = batch <= num_slots;
-  for (int b = 0; b < batch && identity; ++b) identity = slot_ids_host[b] == b;
-  thread_local std::vector<int32_t> row_lens;
-  row_lens.resize(batch);
-  for (int b = 0; b < batch; ++b) row_lens[b] = cached_lens_host[slot_ids_host[b]];
-  const int32_t* ctx_dev = meta_dev;
-  const int32_t* sid_dev = identity ? nullptr : meta_dev + num_slots + batch;
-  for (int l = 0; l < n_layers; ++l) {
-    const int32_t* bt_l = bt_dev + l * layer_stride;
-    rc = pkv_paged_decode_fused(out[l], q[l], k[l], v[l], k_pool, v_pool, num_blocks, bt_l, row_stride, num_slots,
-                                max_blocks_per_seq, sid_dev, ctx_dev, row_lens.data(), batch, max_context_len, n_q_heads,
-                                n_kv_heads, head_dim, cos_sin, max_pos, scale, partition_size, workspace,
-                                workspace_bytes, stream);
-    if (rc != PKV_OK) return rc;
-  }
-  return PKV_OK;
+  // 4. Per layer: RoPE, append and attention in one launch.
+  for (int l = 0; l < n_layers; ++l)
+    if ((rc = decode_enqueue(launches[l], st, !chain)) != PKV_OK) return rc;
+  return chain ? decode_finish(launches[n_layers - 1], st) : PKV_OK;
 }

@@ -36,7 +36,9 @@ def test_status_strings(lib):
 
 
 def test_workspace_and_partition_sizes(lib):
-    stream = 2 * 512 * 32 * 66 * 4      # streaming kernel: two records per CU (at most 512 CUs)
+    # streaming kernel: two regions (launches chained over a step's layers
+    # alternate) of two records per CU (at most 512 CUs)
+    stream = 2 * 2 * 512 * 32 * 66 * 4
     assert pkv.pkv_decode_workspace_bytes(1, 32, 8, 64, 17, 0) == stream
     ps = pkv.pkv_decode_partition_size(64, 8, 4096)
     assert ps % 16 == 0 and ps >= 64
@@ -45,7 +47,7 @@ def test_workspace_and_partition_sizes(lib):
 
     def expect(B, nq, nkv, P):
         # the larger of: per-partition outputs + (max, sum), and the streaming records
-        return max(up(B * nq * P * 64 * 4) + up(B * nq * P * 2 * 4), 2 * 512 * nq * 66 * 4)
+        return max(up(B * nq * P * 64 * 4) + up(B * nq * P * 2 * 4), 2 * 2 * 512 * nq * 66 * 4)
     assert pkv.pkv_decode_workspace_bytes(64, 32, 8, 64, 4096, 0) == expect(64, 32, 8, P)
     assert pkv.pkv_decode_workspace_bytes(2, 32, 8, 64, 100, 16) == expect(2, 32, 8, 7)
     assert pkv.pkv_decode_workspace_bytes(2, 32, 8, 32, 100, 16) == 0       # unsupported head_dim
@@ -120,15 +122,16 @@ def test_other_entry_points_argument_errors(lib):
 def test_layer_sizes_and_argument_errors(lib):
     E = _abi
     # K-split partials: splits x rows x features x 4 bytes, the most splits
-    # (a power of two) that keep the workgroups within 256 and K in whole
-    # 128-wide slices; nothing for shapes the decode-batch kernel does not take
+    # (a power of two) that keep the workgroups (tiles x 64-row blocks x
+    # splits) within 256, each split whole 128-wide slices but the last
     assert pkv.pkv_linear_workspace_bytes(64, 2048, 8192) == 8 * 64 * 2048 * 4
     assert pkv.pkv_linear_workspace_bytes(64, 3072, 2048) == 4 * 64 * 3072 * 4
     assert pkv.pkv_linear_workspace_bytes(1, 512, 2048) == 16 * 1 * 512 * 4
     assert pkv.pkv_linear_workspace_bytes(64, 16384, 2048) == 0       # 256 tiles: no split
-    assert pkv.pkv_linear_workspace_bytes(65, 2048, 8192) == 0        # rows past the kernel's 64
-    assert pkv.pkv_linear_workspace_bytes(64, 2048, 8008) == 0        # K % 128
-    assert pkv.pkv_linear_workspace_bytes(64, 100, 2048) == 0         # features % 64
+    assert pkv.pkv_linear_workspace_bytes(65, 2048, 8192) == 4 * 65 * 2048 * 4   # two row blocks
+    assert pkv.pkv_linear_workspace_bytes(64, 2048, 8008) == 8 * 64 * 2048 * 4   # last K range shorter
+    assert pkv.pkv_linear_workspace_bytes(64, 100, 2048) == 0         # features % 8: not taken
+    assert pkv.pkv_linear_workspace_bytes(64, 2048, 2044) == 0        # K % 8: not taken
     # layer scratch: the eight activations, then the largest partials (the
     # 2048-wide products at 8 splits, 4 MiB = 2 Mi bf16 elements)
     acts = 64 * (2048 * 2 + 2048 * 2 + 512 * 2 + 8192 * 3)
@@ -140,16 +143,28 @@ def test_layer_sizes_and_argument_errors(lib):
     assert lib.pkv_linear(None, FAKE, FAKE, 4, 64, 128, 0, None, 0, None) == E.PKV_ERR_NULL
     assert lib.pkv_linear(FAKE, FAKE + 8, FAKE, 4, 64, 128, 0, None, 0, None) == E.PKV_ERR_MISALIGNED
     assert lib.pkv_linear(FAKE, FAKE, FAKE, 4, 64, 128, 0, FAKE + 4, 64, None) == E.PKV_ERR_MISALIGNED
+    assert lib.pkv_linear(FAKE, FAKE, FAKE, 4, 60, 128, 0, None, 0, None) == E.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_linear(FAKE, FAKE, FAKE, 4, 64, 100, 0, None, 0, None) == E.PKV_ERR_UNSUPPORTED
     # the layer calls: a null weight, a short scratch, the multi-layer call's own arguments
     lw = _abi.LayerWeights(*([FAKE] * 8))
     lw_null = _abi.LayerWeights(*([FAKE] * 7 + [None]))
     need = pkv.pkv_decode_layer_scratch_elems(4, 2048, 8192, 32, 8)
 
-    def layer(w, scratch_elems):
-        return lib.pkv_decode_layer(FAKE, C.byref(w), 2048, 8192, FAKE, scratch_elems, FAKE, FAKE, 8, FAKE, 4, 4, 2,
-                                    None, FAKE, None, 4, 17, 32, 8, FAKE, 100, 0.125, 1e-5, FAKE, 1 << 20, None)
+    def layer(w, scratch_elems, kp=FAKE, ctx=FAKE, cos=FAKE, max_pos=100, max_ctx=17, ws=FAKE, wsb=1 << 20,
+              nq=32, nkv=8):
+        return lib.pkv_decode_layer(FAKE, C.byref(w), 2048, 8192, FAKE, scratch_elems, kp, FAKE, 8, FAKE, 4, 4, 2,
+                                    None, ctx, None, 4, max_ctx, nq, nkv, cos, max_pos, 0.125, 1e-5, ws, wsb, None)
     assert layer(lw_null, need) == E.PKV_ERR_NULL
     assert layer(lw, need - 1) == E.PKV_ERR_CAPACITY
+    # the attention's own arguments, found before the layer's first launch
+    assert layer(lw, need, kp=None) == E.PKV_ERR_NULL
+    assert layer(lw, need, ctx=None) == E.PKV_ERR_NULL
+    assert layer(lw, need, cos=None) == E.PKV_ERR_NULL
+    assert layer(lw, need, max_pos=0) == E.PKV_ERR_INVALID_ARG
+    assert layer(lw, need, nq=24, nkv=8) == E.PKV_ERR_UNSUPPORTED
+    # contexts of up to 5,000 tokens split into partitions need partials
+    assert layer(lw, need, max_ctx=5000, ws=None, wsb=0) == E.PKV_ERR_CAPACITY
+    assert layer(lw, need, max_ctx=5000, wsb=1024) == E.PKV_ERR_CAPACITY
 
     def layers(arr, n, scratch_elems=need, bt=FAKE):
         return lib.pkv_decode_layers(FAKE, arr, n, 2048, 8192, FAKE, scratch_elems, FAKE, FAKE, 8, bt, 8, 4, 4, 2,

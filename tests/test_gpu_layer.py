@@ -1,6 +1,6 @@
 """GPU parity for the rest of the Llama decode layer: RMSNorm, the gated
-SiLU product, the projections (decode-batch MFMA kernel, rocBLAS for other
-shapes) and pkv_decode_layer (Llama-3.2-1B
+SiLU product, the projections (the library's MFMA kernel for every
+shape) and pkv_decode_layer (Llama-3.2-1B
 shapes: hidden 2048, 32 / 8 heads of 64, intermediate 8192, synthetic bf16
 weights ~ N(0, 1/fan_in)) against the float64 oracle with bf16 rounding where
 the engine keeps a buffer.
@@ -89,13 +89,15 @@ def test_silu_mul_within_one_ulp(gpu):
 
 
 # the projections of a decode batch (K split over 1 to 16 workgroups, ragged
-# rows, one to three 128-wide X slices per workgroup), a wider batch and
-# K % 128 != 0 (both on rocBLAS), and a split shape handed a null workspace
-# (rocBLAS too)
+# rows, one to three 128-wide X slices per workgroup), wider batches (two and
+# three 64-row blocks), K that is not a multiple of 128 (a short last slice,
+# a short last K range), feature counts that are not a multiple of 64, and a
+# split shape handed a null workspace (one K range)
 @pytest.mark.parametrize("rows,n,k,ws", [(64, 3072, 2048, None), (1, 512, 2048, None), (13, 2048, 8192, None),
                                          (64, 16384, 2048, None), (64, 2048, 2048, None), (64, 2048, 8192, None),
                                          (37, 192, 384, None), (100, 512, 2048, None), (8, 64, 104, None),
-                                         (5, 64, 128, None), (8, 64, 96, None),
+                                         (5, 64, 128, None), (8, 64, 96, None), (150, 200, 520, None),
+                                         (65, 2048, 2056, None), (3, 24, 8, None),
                                          (64, 2048, 8192, False)])
 def test_linear_within_one_ulp(gpu, rows, n, k, ws):
     rng = np.random.default_rng(rows + n + k)
@@ -121,7 +123,8 @@ def test_linear_decode_batch_is_deterministic(gpu):
     rng = np.random.default_rng(77)
     rows, n, k = 64, 2048, 8192
     assert pkv.pkv_linear_workspace_bytes(rows, n, k) > 0
-    assert pkv.pkv_linear_workspace_bytes(65, n, k) == 0 and pkv.pkv_linear_workspace_bytes(64, 2048, 8008) == 0
+    assert pkv.pkv_linear_workspace_bytes(64, 2048, 8012) == 0          # K % 8: not a shape the kernel takes
+    assert pkv.pkv_linear_workspace_bytes(65, n, k) > 0
     x, w = dev_bf16(W.randn_bf16(rng, (rows, k))), dev_bf16(W.randn_bf16(rng, (n, k), layer.init_scale(k)))
     ws = torch.empty(pkv.pkv_linear_workspace_bytes(rows, n, k), dtype=torch.uint8, device="cuda")
     outs = []
@@ -134,17 +137,18 @@ def test_linear_decode_batch_is_deterministic(gpu):
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-# 4 and 64 rows (the most the decode-batch kernels take: every MFMA column
-# block full) take the decode-batch kernels (q, k, v in one launch, the
-# gated gate/up launch that leaves the gate_up buffer unwritten); 65 rows
-# take rocBLAS and the SiLU kernel
-@pytest.mark.parametrize("host_lens,extra_rows", [(True, 0), (False, 0), (False, 60), (True, 61)])
+# 4 rows, 64 rows (one full 64-row block; with host lengths this is the
+# bench's combination: streaming attention and the decode-batch projections)
+# and 65 rows (two row blocks, one holding a single row), all with q, k, v in
+# one launch and the gated gate/up launch that leaves the gate_up buffer
+# unwritten
+@pytest.mark.parametrize("host_lens,extra_rows", [(True, 0), (False, 0), (False, 60), (True, 60), (True, 61)])
 def test_decode_layer_matches_oracle(gpu, host_lens, extra_rows):
     rng = np.random.default_rng(5)
     wts = _weights(rng)
     pos = np.array([16, 1, 299, 1000], np.int32)           # new token positions (cached tokens before it)
     pos = np.concatenate([pos, rng.integers(0, 40, extra_rows).astype(np.int32)])
-    gated = len(pos) <= 64
+    gated = True                                            # intermediate % 32 == 0
     B = len(pos)
     nbs = [-(-(int(p) + 1) // 16) for p in pos]
     nb = sum(nbs) + 3
@@ -257,15 +261,13 @@ def _device_layer_weights(gen, inter=INTER):
 # the multi-layer call against one call per layer, bit for bit: h after the
 # last layer and every cache row.  Both run the same kernels except the
 # fused down-partials / residual / next-norm kernel between layers, which
-# is what this checks.  The attention must be reproducible for that: with
-# host row lengths the streaming kernel's two waves per KV head claim blocks
-# dynamically, so its float32 summation order varies once a row spans
-# several blocks; rows of one block (contexts <= 16 tokens) fix it.  Longer
-# contexts run without host lengths, on the per-partition kernel, whose
-# order is fixed.  4 and 64 rows run the decode-batch kernels, 65 rows
-# rocBLAS.
-@pytest.mark.parametrize("B,short", [(4, True), (64, True), (65, True), (64, False)])
-def test_decode_layers_match_per_layer_calls(gpu, B, short):
+# is what this checks (every kernel's summation order is fixed, so the two
+# forms must agree exactly).  Rows of up to 16 tokens or up to 300, with
+# host lengths (streaming attention) or without (per-partition attention);
+# 4 and 64 rows are one row block of the projections, 65 rows two.
+@pytest.mark.parametrize("B,short,host", [(4, True, True), (64, True, True), (65, True, True), (64, False, True),
+                                          (64, False, False)])
+def test_decode_layers_match_per_layer_calls(gpu, B, short, host):
     L = 3
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234 + B)
@@ -293,7 +295,7 @@ def test_decode_layers_match_per_layer_calls(gpu, B, short):
     ws = pkv.decode_workspace(B, NQ, NKV, int(ctx.max()))
     n_scr = pkv.pkv_decode_layer_scratch_elems(B, HID, INTER, NQ, NKV)
 
-    lens = ctx if short else None
+    lens = ctx if host else None
     h1, kp1, vp1 = h0.clone(), kp.clone(), vp.clone()
     scr1 = torch.empty(n_scr, dtype=torch.bfloat16, device="cuda")
     for l in range(L):
