@@ -314,6 +314,28 @@ int pkv_paged_decode_fused(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_n
                            int max_pos, float scale, int partition_size, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* pkv_paged_decode_fused without a workspace argument, for callers that
+ * cannot allocate device memory (code under graph capture, serving loops or
+ * harnesses that forbid allocation).  The partial records go to a device
+ * array of PKV_NOALLOC_SCRATCH_BYTES inside the library (one per GPU it runs
+ * on, held until the process ends; its address is looked up once per device
+ * on the first call there).  Arguments and results as pkv_paged_decode_fused;
+ * a call whose partials would not fit (pkv_decode_workspace_bytes of its
+ * sizes, for the path it takes) returns PKV_ERR_CAPACITY before anything is
+ * enqueued.  The call allocates nothing.  Every call on one GPU shares the
+ * array: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller.  Nothing in the array needs to
+ * start at zero: every value read is written first in the same call. */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int pkv_paged_decode_fused_noalloc(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_new,
+                                   const pkv_bf16* v_new, pkv_bf16* k_pool, pkv_bf16* v_pool,
+                                   int num_blocks, const int32_t* block_table, int64_t bt_row_stride,
+                                   int num_slots, int max_blocks_per_seq, const int32_t* slot_ids,
+                                   const int32_t* context_lens, const int32_t* row_lens_host, int batch,
+                                   int max_context_len, int n_q_heads, int n_kv_heads, int head_dim,
+                                   const float* cos_sin, int max_pos, float scale, int partition_size,
+                                   void* stream);
+
 /* ------------------------------------------------------------------------ *
  * Chunked causal prefill.  Source: "The path of one inference", closing
  * paragraph (prefill pushes the whole prompt through at once, matrix x

@@ -35,6 +35,8 @@ _d = C.c_double
 _sz = C.c_size_t
 _ip = C.POINTER(C.c_int)
 
+NOALLOC_SCRATCH_BYTES = 16 << 20     # PKV_NOALLOC_SCRATCH_BYTES (include/pagedkv.h)
+
 SIGNATURES = {
     "pkv_status_str": (C.c_char_p, [_i]),
     "pkv_abi_version": (_i, []),
@@ -60,6 +62,8 @@ SIGNATURES = {
     "pkv_decode_workspace_init": (_i, [_p, _sz, _p]),
     "pkv_paged_decode_fused": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _p,
                                     _i, _f, _i, _p, _sz, _p]),
+    "pkv_paged_decode_fused_noalloc": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _i, _i,
+                                            _i, _i, _p, _i, _f, _i, _p]),
     "pkv_decode_step": (_i, [_i, _p, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _p, _ip, _p, _p, _p, _i, _i, _i, _i,
                              _p, _i, _f, _i, _i, _p, _sz, _p]),
     "pkv_sched_create": (_i, [C.POINTER(_p), _i, _i, _i, _i, _i]),
@@ -493,6 +497,39 @@ def pkv_paged_decode_fused(out, q, k_new, v_new, k_pool, v_pool, block_table, sl
         _dev_ptr(context_lens, "context_lens", (torch.int32,)), rl, B, max_context_len, n_q, k_pool.shape[2], d,
         _dev_ptr(cos_sin, "cos_sin", (torch.float32,)), cos_sin.shape[0], float(scale), partition_size, ws_ptr,
         ws_bytes, _stream(stream)))
+
+
+def pkv_paged_decode_fused_noalloc(out, q, k_new, v_new, k_pool, v_pool, block_table, slot_ids, context_lens,
+                                   max_context_len, cos_sin, scale, partition_size=0, stream=None,
+                                   row_lens_host=None):
+    """pkv_paged_decode_fused with the library's own device scratch array in
+    place of a workspace (the call allocates nothing; calls overlapping on one
+    GPU must be serialised by the caller)."""
+    import torch
+    for t, n in ((out, "out"), (q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool"),
+                 (slot_ids, "slot_ids"), (context_lens, "context_lens"), (cos_sin, "cos_sin")):
+        _contig(t, n)
+    B, n_q, d = q.shape
+    if out.shape != q.shape or k_pool.shape != v_pool.shape or k_new.shape != v_new.shape:
+        raise ValueError("shape mismatch")
+    if k_new.shape[0] != B or k_new.shape[1] != k_pool.shape[2]:
+        raise ValueError("k_new must be [batch, n_kv, 64]")
+    bt, stride, rows, mb = _table(block_table)
+    if context_lens.shape[0] < rows:
+        raise ValueError("context_lens must have an entry per table row")
+    if slot_ids is not None and slot_ids.shape[0] != B:
+        raise ValueError("slot_ids must have one entry per batch row")
+    if slot_ids is None and B > rows:
+        raise ValueError("batch larger than the table without slot_ids")
+    keep, rl = _row_lens(row_lens_host, B)
+    _check("pkv_paged_decode_fused_noalloc", load().pkv_paged_decode_fused_noalloc(
+        _dev_ptr(out, "out", _bf16_types()), _dev_ptr(q, "q", _bf16_types()),
+        _dev_ptr(k_new, "k_new", _bf16_types()), _dev_ptr(v_new, "v_new", _bf16_types()),
+        _dev_ptr(k_pool, "k_pool", _bf16_types()), _dev_ptr(v_pool, "v_pool", _bf16_types()), k_pool.shape[0],
+        bt, stride, rows, mb, _dev_ptr(slot_ids, "slot_ids", (torch.int32,)),
+        _dev_ptr(context_lens, "context_lens", (torch.int32,)), rl, B, max_context_len, n_q, k_pool.shape[2], d,
+        _dev_ptr(cos_sin, "cos_sin", (torch.float32,)), cos_sin.shape[0], float(scale), partition_size,
+        _stream(stream)))
 
 
 def pkv_paged_attn_decode(out, q, k_pool, v_pool, block_table, slot_ids, context_lens, max_context_len,

@@ -42,6 +42,8 @@
 #include "decode_api.h"
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 namespace pkv {
 
@@ -715,5 +717,86 @@ extern "C" int pkv_paged_decode_fused(pkv_bf16* out, const pkv_bf16* q, const pk
   DecodeLaunch L;
   const int rc = decode_prepare(c, &L);
   if (rc != PKV_OK) return rc;
+  return decode_enqueue(L, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------------
+// The decode step of one layer without a caller workspace, for callers that
+// cannot allocate (code under graph capture, serving loops that forbid
+// allocation): the partial records live in this file's device array.  Its
+// host-side name is only a stand-in for the symbol; the device address is
+// looked up once per device (with that device current) and kept.
+// ------------------------------------------------------------------------
+
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device, or null.
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" int pkv_paged_decode_fused_noalloc(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_new,
+                                              const pkv_bf16* v_new, pkv_bf16* k_pool, pkv_bf16* v_pool,
+                                              int num_blocks, const int32_t* block_table, int64_t bt_row_stride,
+                                              int num_slots, int max_blocks_per_seq, const int32_t* slot_ids,
+                                              const int32_t* context_lens, const int32_t* row_lens_host, int batch,
+                                              int max_context_len, int n_q_heads, int n_kv_heads, int head_dim,
+                                              const float* cos_sin, int max_pos, float scale, int partition_size,
+                                              void* stream) {
+  DecodeCall c{};
+  c.fused = true;
+  c.out = out;
+  c.q = q;
+  c.k_new = k_new;
+  c.v_new = v_new;
+  c.k_pool = k_pool;
+  c.v_pool = v_pool;
+  c.num_blocks = num_blocks;
+  c.block_table = block_table;
+  c.bt_row_stride = bt_row_stride;
+  c.num_slots = num_slots;
+  c.max_blocks_per_seq = max_blocks_per_seq;
+  c.slot_ids = slot_ids;
+  c.context_lens = context_lens;
+  c.row_lens_host = row_lens_host;
+  c.batch = batch;
+  c.max_context_len = max_context_len;
+  c.n_q_heads = n_q_heads;
+  c.n_kv_heads = n_kv_heads;
+  c.head_dim = head_dim;
+  c.cos_sin = cos_sin;
+  c.max_pos = max_pos;
+  c.scale = scale;
+  c.partition_size = partition_size;
+  c.workspace_bytes = PKV_NOALLOC_SCRATCH_BYTES;
+  // Plan with a stand-in address first (nothing is dereferenced on the host),
+  // so that argument errors and a workspace need beyond the array's size are
+  // reported before the device is touched.
+  c.workspace = reinterpret_cast<void*>((uintptr_t)256);
+  DecodeLaunch L;
+  int rc = decode_prepare(c, &L);
+  if (rc != PKV_OK || L.path == 0) return rc;
+  void* p = scratch_ptr();
+  if (!p) return PKV_ERR_HIP;
+  c.workspace = p;
+  if ((rc = decode_prepare(c, &L)) != PKV_OK) return rc;
   return decode_enqueue(L, (hipStream_t)stream);
 }

@@ -177,6 +177,26 @@ def test_layer_sizes_and_argument_errors(lib):
     assert layers(two, 2) == E.PKV_ERR_NULL                   # the second layer's null weight, found before any launch
     assert layers((_abi.LayerWeights * 1)(lw), 1, scratch_elems=need - 1) == E.PKV_ERR_CAPACITY
 
+def test_noalloc_decode_argument_errors_before_launch(lib):
+    """The allocation-free decode call reports argument errors, and partials
+    beyond its device array, before it touches a device (fake pointers)."""
+    E = _abi
+
+    def call(batch=4, maxctx=17, nq=32, nkv=8, d=64, out=FAKE, cos=FAKE, max_pos=100):
+        return lib.pkv_paged_decode_fused_noalloc(out, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 4, 4, 2, None, FAKE,
+                                                  None, batch, maxctx, nq, nkv, d, cos, max_pos, 0.125, 0, None)
+    assert call(batch=0) == E.PKV_OK
+    assert call(d=128) == E.PKV_ERR_UNSUPPORTED
+    assert call(out=None) == E.PKV_ERR_NULL
+    assert call(cos=None) == E.PKV_ERR_NULL
+    assert call(max_pos=0) == E.PKV_ERR_INVALID_ARG
+    # 64 rows of up to a million tokens on the per-partition kernels: the
+    # partials (about 528 MB) exceed the array
+    need = pkv.pkv_decode_workspace_bytes(64, 32, 8, 64, 1_000_000, 0)
+    assert need > _abi.NOALLOC_SCRATCH_BYTES
+    assert call(batch=64, maxctx=1_000_000) == E.PKV_ERR_CAPACITY
+
+
 # ------------------------------------------------------- block allocation --
 
 def test_blocks_assign_walk_is_valid_every_step(lib):
