@@ -394,6 +394,59 @@ int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const* k, const 
                     int partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * The same decode step in two halves, for a device half captured once as a
+ * HIP graph and replayed every step.  Source: the category page's mini-sglang
+ * chapter-7 title (the step's ledger becomes kernel arguments; the launches are
+ * captured as a graph) and "The path of one inference" (the step itself).
+ * The device half's launch shapes depend only on (n_layers, batch, heads,
+ * num_slots), never on the lengths: everything that changes from step to step
+ * travels through a staging area that the caller copies to the device inside
+ * the captured sequence.
+ *
+ * pkv_decode_step_staging_bytes: size of the staging area (host and device
+ * copies alike) for n_layers, batch and num_slots; 0 for invalid sizes or
+ * batch > 256.
+ *
+ * pkv_decode_step_host: step 1 and 2 of pkv_decode_step on the host (same
+ * allocation rule, same all-or-nothing checks, same PKV_ERR_CAPACITY), written
+ * into staging_host (any host memory; pinned when it is copied by a captured
+ * copy): the table changes, the new metadata (context lengths per slot |
+ * positions | slot ids) and the streaming kernel's plan.  Nothing is enqueued.
+ * PKV_ERR_UNSUPPORTED, with no change at all, when the rows do not suit the
+ * replayed launches (a workgroup share would touch more than 4 rows, or a row
+ * spans more than 8 shares: a few long rows); the caller then takes
+ * pkv_decode_step for this step.
+ *
+ * pkv_decode_step_device: enqueues, in a fixed sequence, one small kernel that
+ * applies staging_dev (table changes into bt_dev, metadata into meta_dev),
+ * then one fused streaming launch per layer (RoPE, append, attention; each
+ * merges the previous layer's rows cut by workgroup shares) reading the plan
+ * from staging_dev at every launch, then one merge launch.  staging_dev must
+ * hold a copy of staging_host (made by the caller on `stream` before this
+ * call's launches, e.g. an async copy captured in the same graph); the host
+ * copy is read only to check the launches when this call is made (capture
+ * time).  Replays of a capture serve any later step whose host half used the
+ * same n_layers, batch and num_slots.  The caller must not rewrite
+ * staging_host while a replay's copy of it may still be pending.  The other
+ * arguments are pkv_decode_step's; the workspace must hold two record regions
+ * (pkv_decode_workspace_bytes for the batch).  Errors: PKV_ERR_UNSUPPORTED
+ * when the staged rows or the shapes do not suit the streaming kernel,
+ * PKV_ERR_CAPACITY when the workspace is too small, else as pkv_decode_step.
+ * ------------------------------------------------------------------------ */
+size_t pkv_decode_step_staging_bytes(int n_layers, int batch, int num_slots);
+
+int pkv_decode_step_host(int n_layers, int32_t* bt_host, int num_slots, int max_blocks_per_seq,
+                         int32_t* free_list_host, int* n_free, int32_t* cached_lens_host,
+                         const int32_t* slot_ids_host, int batch, void* staging_host);
+
+int pkv_decode_step_device(int n_layers, pkv_bf16* const* q, pkv_bf16* const* k, const pkv_bf16* const* v,
+                           pkv_bf16* const* out, pkv_bf16* k_pool, pkv_bf16* v_pool, int num_blocks,
+                           int32_t* bt_dev, int num_slots, int max_blocks_per_seq, int32_t* meta_dev,
+                           int batch, int n_q_heads, int n_kv_heads, int head_dim, const float* cos_sin,
+                           int max_pos, float scale, const void* staging_host, const void* staging_dev,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Continuous batching (host scheduler + device iteration).  Source: "The path
  * of one inference" (a fixed set of sequence slots; prompts wait in a queue;
  * a free slot takes the next prompt, which is prefilled; a decode step gives

@@ -66,6 +66,10 @@ SIGNATURES = {
                                             _i, _i, _p, _i, _f, _i, _p]),
     "pkv_decode_step": (_i, [_i, _p, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _p, _ip, _p, _p, _p, _i, _i, _i, _i,
                              _p, _i, _f, _i, _i, _p, _sz, _p]),
+    "pkv_decode_step_staging_bytes": (_sz, [_i, _i, _i]),
+    "pkv_decode_step_host": (_i, [_i, _p, _i, _i, _p, _ip, _p, _p, _i, _p]),
+    "pkv_decode_step_device": (_i, [_i, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _p, _i, _i, _i, _i, _p, _i, _f, _p,
+                                    _p, _p, _sz, _p]),
     "pkv_sched_create": (_i, [C.POINTER(_p), _i, _i, _i, _i, _i]),
     "pkv_sched_destroy": (_i, [_p]),
     "pkv_sched_submit": (_i, [_p, _i64, _i, _i]),
@@ -645,6 +649,99 @@ def pkv_decode_step(q, k, v, out, k_pool, v_pool, bt_host, bt_dev, free_list, n_
         q[0].shape[2], _dev_ptr(cos_sin, "cos_sin", (torch.float32,)), cos_sin.shape[0], float(scale),
         max_context_len, partition_size, ws_ptr, ws_bytes, _stream(stream)))
     return nf.value
+
+
+def pkv_decode_step_staging_bytes(n_layers, batch, num_slots):
+    """Bytes of the two-half step's staging area (0: sizes not served)."""
+    return load().pkv_decode_step_staging_bytes(n_layers, batch, num_slots)
+
+
+def _host_buffer(buf, name, nbytes):
+    """Address of a host buffer: a CPU torch tensor (pinned or not) or a
+    writable numpy array, contiguous, at least nbytes long."""
+    import torch
+    if isinstance(buf, torch.Tensor):
+        if buf.is_cuda or not buf.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous host tensor")
+        have, ptr = buf.numel() * buf.element_size(), buf.data_ptr()
+    elif isinstance(buf, np.ndarray):
+        if not buf.flags.c_contiguous or not buf.flags.writeable:
+            raise ValueError(f"{name} must be a contiguous writable array")
+        have, ptr = buf.nbytes, buf.ctypes.data
+    else:
+        raise TypeError(f"{name} must be a host tensor or numpy array")
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, needs {nbytes}")
+    return ptr
+
+
+def pkv_decode_step_host(bt_host, free_list, n_free, cached_lens, slot_ids, staging_host):
+    """Host half of the two-half decode step (see pkv_decode_step_host in
+    pagedkv.h): allocation and the step's staging area.  bt_host [slots, L,
+    max_blocks], free_list and cached_lens are numpy int32 updated in place;
+    staging_host a host buffer of pkv_decode_step_staging_bytes.  Returns
+    n_free; raises PagedKVError (status PKV_ERR_UNSUPPORTED: rows the replayed
+    launches do not serve, nothing changed)."""
+    _np_i32(bt_host, "bt_host", writable=True)
+    _np_i32(free_list, "free_list", writable=True)
+    _np_i32(cached_lens, "cached_lens", writable=True)
+    if bt_host.ndim != 3 or not bt_host.flags.c_contiguous:
+        raise ValueError("bt_host must be a contiguous [slots, layers, max_blocks] array")
+    slots, L, mb = bt_host.shape
+    sid = np.ascontiguousarray(slot_ids, dtype=np.int32)
+    if len(cached_lens) != slots or not 0 <= n_free <= len(free_list):
+        raise ValueError("cached_lens / n_free inconsistent")
+    need = pkv_decode_step_staging_bytes(L, len(sid), slots)
+    if need == 0:
+        raise ValueError("layers, batch or slots outside what the two-half step serves")
+    ptr = _host_buffer(staging_host, "staging_host", need)
+    nf = C.c_int(n_free)
+    _check("pkv_decode_step_host", load().pkv_decode_step_host(
+        L, bt_host.ctypes.data, slots, mb, free_list.ctypes.data, C.byref(nf), cached_lens.ctypes.data,
+        sid.ctypes.data, len(sid), ptr))
+    return nf.value
+
+
+def pkv_decode_step_device(q, k, v, out, k_pool, v_pool, bt_dev, meta_dev, cos_sin, scale, staging_host,
+                           staging_dev, workspace, stream=None):
+    """Device half of the two-half decode step (see pkv_decode_step_device in
+    pagedkv.h); enqueues only, so it may be captured in a graph.  q/out
+    [L, B, n_q, 64], k/v [L, B, n_kv, 64] device bf16 (or lists of L tensors);
+    bt_dev device int32 [slots, L, max_blocks]; meta_dev device int32
+    [slots + 2B]; staging_host the host staging area the host half wrote and
+    staging_dev its device copy (the caller copies it on the same stream
+    first); workspace with two record regions."""
+    import torch
+    L = len(q)
+    B = q[0].shape[0]
+    if bt_dev.ndim != 3 or not bt_dev.is_contiguous() or bt_dev.dtype != torch.int32 or bt_dev.shape[1] != L:
+        raise ValueError("bt_dev must be a contiguous int32 [slots, layers, max_blocks] device tensor")
+    slots, _, mb = bt_dev.shape
+    if meta_dev.numel() != slots + 2 * B or not meta_dev.is_contiguous():
+        raise ValueError("meta_dev must be int32 [slots + 2 * batch]")
+    need = pkv_decode_step_staging_bytes(L, B, slots)
+    if need == 0:
+        raise ValueError("layers, batch or slots outside what the two-half step serves")
+    sh = _host_buffer(staging_host, "staging_host", need)
+    _contig(staging_dev, "staging_dev")
+    if staging_dev.numel() * staging_dev.element_size() < need:
+        raise ValueError(f"staging_dev needs {need} bytes")
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool"), (workspace, "workspace")):
+        _contig(t, n)
+    ptrs = []
+    for arr, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if len(arr) != L:
+            raise ValueError(f"{name} needs one tensor per layer")
+        for t in arr:
+            _contig(t, name)
+        ptrs.append((C.c_void_p * L)(*[_dev_ptr(t, name, _bf16_types()) for t in arr]))
+    _check("pkv_decode_step_device", load().pkv_decode_step_device(
+        L, ptrs[0], ptrs[1], ptrs[2], ptrs[3], _dev_ptr(k_pool, "k_pool", _bf16_types()),
+        _dev_ptr(v_pool, "v_pool", _bf16_types()), k_pool.shape[0], _dev_ptr(bt_dev, "bt_dev", (torch.int32,)),
+        slots, mb, _dev_ptr(meta_dev, "meta_dev", (torch.int32,)), B, q[0].shape[1], k_pool.shape[2],
+        q[0].shape[2], _dev_ptr(cos_sin, "cos_sin", (torch.float32,)), cos_sin.shape[0], float(scale), sh,
+        _dev_ptr(staging_dev, "staging_dev"), _dev_ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 # ------------------------------------------------------ continuous batching --

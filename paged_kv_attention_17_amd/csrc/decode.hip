@@ -607,12 +607,15 @@ int decode_prepare(const DecodeCall& c, DecodeLaunch* L) {
     sc.records_bytes = R;
     sc.out_prev = c.out_prev;
     sc.records_prev = c.out_prev ? reinterpret_cast<const float*>(ws + (1 - c.records_half) * R) : nullptr;
+    sc.plan_dev = c.plan_dev;
+    sc.chain_plan = c.chain_plan;
     if (stream_prepare(c.fused, sc, &L->s) == PKV_OK) {
       L->path = 1;
       return PKV_OK;
     }
   }
-  if (c.out_prev) return PKV_ERR_INVALID_ARG;   // chaining exists on the streaming path only
+  // chaining and device plans exist on the streaming path only
+  if (c.out_prev || c.plan_dev) return c.plan_dev ? PKV_ERR_UNSUPPORTED : PKV_ERR_INVALID_ARG;
   // the per-partition kernels
   const int ps = c.partition_size > 0 ? c.partition_size : auto_partition(c.batch, c.n_kv_heads, c.max_context_len);
   const int64_t P = decode_parts(c.max_context_len, ps);
@@ -626,7 +629,7 @@ int decode_prepare(const DecodeCall& c, DecodeLaunch* L) {
 }
 
 bool decode_chainable(const DecodeLaunch& L) {
-  return L.path == 1 && L.c.workspace_bytes >= 2 * stream_records_bytes(L.c.n_q_heads);
+  return L.path == 1 && !L.s.long_rows && L.c.workspace_bytes >= 2 * stream_records_bytes(L.c.n_q_heads);
 }
 
 int decode_enqueue(const DecodeLaunch& L, hipStream_t st, bool merge) {

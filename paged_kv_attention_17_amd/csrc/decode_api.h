@@ -45,6 +45,11 @@ struct DecodeCall {
   // out_prev in its prologue.
   int records_half;
   uint16_t* out_prev;
+  bool chain_plan;             // plan the shares for chaining (every launch of a chain sets it)
+  // Non-null: the streaming kernel reads its plan from this device copy at
+  // every launch (launch shapes fixed; the call fails rather than take the
+  // per-partition kernels).  The plan built from row_lens_host checks the call.
+  const StreamPlan* plan_dev;
 };
 
 struct DecodeLaunch {

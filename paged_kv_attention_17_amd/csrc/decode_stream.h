@@ -12,6 +12,21 @@ constexpr int kStreamMaxSeqs = 256;   // batch rows one launch describes
 constexpr int kStreamMaxGrid = 512;   // workgroups (one per CU)
 constexpr int kStreamRec = 66;        // record per query head: 64 unnormalised outputs, max, sum
 
+// How the batch's blocks are cut into workgroup shares: rows laid end to end
+// (the block stream), each workgroup an equal, contiguous share.  Built on the
+// host; travels in the kernel arguments, or (launches captured once and
+// replayed as the lengths change) in device memory.
+struct StreamPlan {
+  int32_t share;               // blocks per workgroup
+  int32_t total;               // blocks in the stream
+  int32_t grid;                // workgroups with blocks
+  int32_t slots_in_args;       // row_slot holds each row's slot (0xffff = none)
+  int32_t row_start[kStreamMaxSeqs + 1];   // first stream block of each row
+  int32_t row_n[kStreamMaxSeqs];           // tokens of each row
+  uint16_t row_slot[kStreamMaxSeqs];
+  uint16_t wg_rows[kStreamMaxGrid];        // per workgroup: first row << 3 | rows touched
+};
+
 // Kernel arguments (one block of at most 4 KB, passed by value).
 struct StreamArgs {
   uint16_t* out;
@@ -35,14 +50,8 @@ struct StreamArgs {
   int max_pos;
   int batch;
   float scale_log2e;
-  int share;                   // blocks per workgroup
-  int total;                   // blocks in the stream
-  int grid;
-  int slots_in_args;           // row_slot holds each row's slot (0xffff = none)
-  int32_t row_start[kStreamMaxSeqs + 1];   // first stream block of each row
-  int32_t row_n[kStreamMaxSeqs];           // tokens of each row
-  uint16_t row_slot[kStreamMaxSeqs];
-  uint16_t wg_rows[kStreamMaxGrid];        // per workgroup: first row << 3 | rows touched
+  const struct StreamPlan* plan_dev;   // device-plan launches: the plan in device memory
+  StreamPlan plan;                     // argument-plan launches: the plan itself
 };
 static_assert(sizeof(StreamArgs) <= 4096, "kernel argument block");
 
@@ -70,15 +79,37 @@ struct StreamCall {
   size_t records_bytes;
   uint16_t* out_prev;          // non-null: this launch also merges the previous launch's
   const float* records_prev;   //   rows (same rows and lengths), written to out_prev
+  const StreamPlan* plan_dev;  // non-null: the kernels read their plan here at every launch
+                               //   (launch shapes fixed; for launches captured once and replayed)
+  bool chain_plan;             // shares sized for chained launches (see stream_plan_build)
 };
 
 struct StreamLaunch {
   StreamArgs a;
   bool fused;
   bool prev;
+  bool devplan;
+  bool long_rows;              // a row spans more shares than a chained prologue merges
   int G;
+  int grid;                    // workgroups launched
   int merge;                   // merge launch needed: 0 none, 1 per (row, KV head), 2 per (row, query head)
 };
+
+// Workgroups of a device-plan launch (one per CU, at most kStreamMaxGrid).
+int stream_launch_grid();
+
+// The plan for `batch` rows of host-known lengths (row_lens_host), with the
+// rows' slots from slot_ids_host when given (else identity when there are no
+// device slot ids).  Shares are equal, ceil(blocks / workgroups); with
+// `chain` they are raised, where the rows allow it, until no row spans more
+// shares than a chained launch's prologue merges (a few long rows then run on
+// fewer workgroups, but every layer's merge rides on the next launch).
+// Returns -1 when the streaming kernel cannot serve these rows (a share would
+// touch more rows than it stages), 1 when some row spans more shares than a
+// chained launch's prologue merges, 0 otherwise; *merge_kind as
+// StreamLaunch::merge.
+int stream_plan_build(int batch, const int32_t* row_lens_host, int max_blocks, const int32_t* slot_ids_host,
+                      bool slot_ids_dev, int num_slots, bool chain, StreamPlan* P, int* merge_kind);
 
 // Bytes of records one streaming launch may write for n_q query heads.
 size_t stream_records_bytes(int n_q);

@@ -71,9 +71,9 @@ constexpr int kPrevSpan = 8;          // shares a row may span for the prologue 
 static_assert(kRec == kHeadDim + 2, "record layout");
 static_assert(kMaxRows * kMaxQ * 8 <= kThreads, "one query chunk per thread");
 
-__device__ __forceinline__ int row_slot(const StreamArgs& a, int b) {
-  if (a.slots_in_args) {
-    const int s = a.row_slot[b];
+__device__ __forceinline__ int row_slot(const StreamArgs& a, const StreamPlan& P, int b) {
+  if (P.slots_in_args) {
+    const int s = P.row_slot[b];
     return s == 0xffff ? -1 : s;
   }
   const int s = a.slot_ids ? a.slot_ids[b] : b;
@@ -221,16 +221,17 @@ struct MfmaAcc {
 // w holds the row in record 2w when the row contains the share's first block,
 // else in record 2w + 1.  Empty rows get zeros; rows inside one share were
 // finished by their workgroup and are left alone.
-__device__ __forceinline__ void merge_element(const StreamArgs& a, uint16_t* out, const float* ws, int b, int qh,
+__device__ __forceinline__ void merge_element(const StreamArgs& a, const StreamPlan& P, uint16_t* out, const float* ws,
+                                              int b, int qh,
                                               int d) {
   const int64_t o = ((int64_t)b * a.n_q + qh) * kHeadDim + d;
-  if (a.row_n[b] <= 0) {
+  if (P.row_n[b] <= 0) {
     out[o] = 0;
     return;
   }
-  const int start = a.row_start[b];
-  const int w0 = start / a.share;
-  const int w1 = (a.row_start[b + 1] - 1) / a.share;
+  const int start = P.row_start[b];
+  const int w0 = start / P.share;
+  const int w1 = (P.row_start[b + 1] - 1) / P.share;
   if (w0 == w1) return;
   float M = -INFINITY, L = 0.f, O = 0.f;
   for (int w = w0; w <= w1; w += 8) {
@@ -238,7 +239,7 @@ __device__ __forceinline__ void merge_element(const StreamArgs& a, uint16_t* out
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int ww = w + j <= w1 ? w + j : w1;
-      const int rec = 2 * ww + ((ww > w0 || start == w0 * a.share) ? 0 : 1);
+      const int rec = 2 * ww + ((ww > w0 || start == w0 * P.share) ? 0 : 1);
       const float* src = ws + ((int64_t)rec * a.n_q + qh) * kRec;
       mv[j] = w + j <= w1 ? src[kHeadDim] : -INFINITY;
       lv[j] = src[kHeadDim + 1];
@@ -270,56 +271,57 @@ struct PrevMerge {
   bool empty;                  // the row is empty: write zero
 };
 
-__device__ __forceinline__ void prev_load(const StreamArgs& a, int b, int qh, int d, PrevMerge& P) {
-  P.at = -1;
-  P.empty = false;
+__device__ __forceinline__ void prev_load(const StreamArgs& a, const StreamPlan& P, int b, int qh, int d, PrevMerge& M) {
+  M.at = -1;
+  M.empty = false;
   if (b >= a.batch) return;
   const int64_t o = ((int64_t)b * a.n_q + qh) * kHeadDim + d;
-  if (a.row_n[b] <= 0) {
-    P.at = o;
-    P.empty = true;
+  if (P.row_n[b] <= 0) {
+    M.at = o;
+    M.empty = true;
     return;
   }
-  const int start = a.row_start[b];
-  const int w0 = start / a.share;
-  const int w1 = (a.row_start[b + 1] - 1) / a.share;
+  const int start = P.row_start[b];
+  const int w0 = start / P.share;
+  const int w1 = (P.row_start[b + 1] - 1) / P.share;
   if (w0 == w1) return;
-  P.at = o;
+  M.at = o;
 #pragma unroll
   for (int j = 0; j < kPrevSpan; ++j) {
     const int ww = w0 + j <= w1 ? w0 + j : w1;
-    const int rec = 2 * ww + ((ww > w0 || start == w0 * a.share) ? 0 : 1);
+    const int rec = 2 * ww + ((ww > w0 || start == w0 * P.share) ? 0 : 1);
     const float* src = a.ws_prev + ((int64_t)rec * a.n_q + qh) * kRec;
-    P.m[j] = w0 + j <= w1 ? src[kHeadDim] : -INFINITY;
-    P.l[j] = src[kHeadDim + 1];
-    P.o[j] = src[d];
+    M.m[j] = w0 + j <= w1 ? src[kHeadDim] : -INFINITY;
+    M.l[j] = src[kHeadDim + 1];
+    M.o[j] = src[d];
   }
 }
 
-__device__ __forceinline__ void prev_finish(const StreamArgs& a, const PrevMerge& P) {
-  if (P.at < 0) return;
-  if (P.empty) {
-    a.out_prev[P.at] = 0;
+__device__ __forceinline__ void prev_finish(const StreamArgs& a, const PrevMerge& pm) {
+  if (pm.at < 0) return;
+  if (pm.empty) {
+    a.out_prev[pm.at] = 0;
     return;
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kPrevSpan; ++j) M = fmaxf(M, P.m[j]);
+  for (int j = 0; j < kPrevSpan; ++j) M = fmaxf(M, pm.m[j]);
   float L = 0.f, O = 0.f;
 #pragma unroll
   for (int j = 0; j < kPrevSpan; ++j) {
-    const float f = P.m[j] == -INFINITY ? 0.f : fast_exp2(P.m[j] - M);
-    L += f * P.l[j];
-    O += f * P.o[j];
+    const float f = pm.m[j] == -INFINITY ? 0.f : fast_exp2(pm.m[j] - M);
+    L += f * pm.l[j];
+    O += f * pm.o[j];
   }
-  a.out_prev[P.at] = to_bf16(L > 0.f ? O / L : 0.f);
+  a.out_prev[pm.at] = to_bf16(L > 0.f ? O / L : 0.f);
 }
 
-template <int G, bool FUSED, bool PREV>
+template <int G, bool FUSED, bool PREV, bool DEVPLAN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void stream_kernel(StreamArgs a) {
-  const int B0 = blockIdx.x * a.share;
-  const int B1 = min(B0 + a.share, a.total);
+  const StreamPlan& P = DEVPLAN ? *a.plan_dev : a.plan;
+  const int B0 = blockIdx.x * P.share;
+  const int B1 = min(B0 + P.share, P.total);
   const int len = B1 - B0;
   if (len <= 0) return;
   const int tid = threadIdx.x;
@@ -331,7 +333,7 @@ void stream_kernel(StreamArgs a) {
   const int S = kWaves / n_kv;           // waves per KV head
   const int h = w % n_kv;                // this wave's KV head
   const int s = w / n_kv;                // and its lane of blocks
-  const int wr = a.wg_rows[blockIdx.x];
+  const int wr = P.wg_rows[blockIdx.x];
   const int bf = wr >> 3;                // first row of the share
   const int nrows = wr & 7;              // rows it touches
   const int64_t row_elems = (int64_t)n_kv * kHeadDim;
@@ -368,14 +370,14 @@ void stream_kernel(StreamArgs a) {
   // not among them)
   auto block_info = [&](int p, int& tab, int& meta) {
     int ri = 0;
-    for (int i = 1; i < nrows; ++i) ri = p >= a.row_start[bf + i] ? i : ri;
-    int start = a.row_start[bf], n = a.row_n[bf];
+    for (int i = 1; i < nrows; ++i) ri = p >= P.row_start[bf + i] ? i : ri;
+    int start = P.row_start[bf], n = P.row_n[bf];
     for (int i = 1; i < nrows; ++i) {
-      start = i == ri ? a.row_start[bf + i] : start;
-      n = i == ri ? a.row_n[bf + i] : n;
+      start = i == ri ? P.row_start[bf + i] : start;
+      n = i == ri ? P.row_n[bf + i] : n;
     }
     const int j = p - start;
-    const int slot = row_slot(a, bf + ri);
+    const int slot = row_slot(a, P, bf + ri);
     int valid = (FUSED ? n - 1 : n) - j * kBlock;
     valid = valid > kBlock ? kBlock : (valid < 0 ? 0 : valid);
     tab = -1;
@@ -412,12 +414,15 @@ void stream_kernel(StreamArgs a) {
   if (tid < min(kWin, len)) block_info(B0 + tid, tab, meta);
 
   // ---- chained launches: the previous launch's rows cut by share ends, one
-  // (row, query head) pair per 64 threads ---------------------------------------
+  // (row, query head) pair per 64 threads (pairs grid x 16 apart: a small grid
+  // takes several) -----------------------------------------------------------------
   if constexpr (PREV) {
-    PrevMerge pm;
-    const int pp = blockIdx.x + a.grid * (tid >> 6);
-    prev_load(a, pp / a.n_q, pp % a.n_q, lane, pm);
-    prev_finish(a, pm);
+    const int pairs = a.batch * a.n_q;
+    for (int pp = blockIdx.x + P.grid * w; pp < pairs; pp += P.grid * kWaves) {
+      PrevMerge pm;
+      prev_load(a, P, pp / a.n_q, pp % a.n_q, lane, pm);
+      prev_finish(a, pm);
+    }
   }
 
   // ---- queries of the share's rows (rotated by position n - 1 when fused),
@@ -429,7 +434,7 @@ void stream_kernel(StreamArgs a) {
     const uint16_t* qrow = a.q + ((int64_t)(bf + qi) * a.n_q + (qrem >> 3)) * kHeadDim;
     uint4 qv = *reinterpret_cast<const uint4*>(qrow + qch * 8);
     if constexpr (FUSED) {
-      const int pos = a.row_n[bf + qi] - 1;
+      const int pos = P.row_n[bf + qi] - 1;
       if (pos >= 0 && pos < a.max_pos) {
         const uint4 qp = *reinterpret_cast<const uint4*>(qrow + (qch ^ 4) * 8);
         const float4* tr = reinterpret_cast<const float4*>(a.rope + ((int64_t)pos * (kHeadDim / 2) + (qch & 3) * 8) * 2);
@@ -447,18 +452,18 @@ void stream_kernel(StreamArgs a) {
   const int ni = tid / (n_kv * 8);
   const int nrem = tid - ni * n_kv * 8;
   if constexpr (FUSED) {
-    if (tid < nrows) srow_ok[tid] = row_slot(a, bf + tid) >= 0;
+    if (tid < nrows) srow_ok[tid] = row_slot(a, P, bf + tid) >= 0;
     if (tid < nrows * n_kv * 8) {
       const int ch = nrem & 7;
       const int b = bf + ni;
-      const int n = a.row_n[b];
-      const int last = a.row_start[b + 1] - 1;
+      const int n = P.row_n[b];
+      const int last = P.row_start[b + 1] - 1;
       if (n > 0 && last >= B0 && last < B1) {
         const int pos = n - 1;
         const uint16_t* krow = a.k_new + ((int64_t)b * n_kv + (nrem >> 3)) * kHeadDim;
         uint4 nk = *reinterpret_cast<const uint4*>(krow + ch * 8);
         const uint4 nv = *reinterpret_cast<const uint4*>(a.v_new + ((int64_t)b * n_kv + (nrem >> 3)) * kHeadDim + ch * 8);
-        const int slot = row_slot(a, b);
+        const int slot = row_slot(a, P, b);
         if (nrem == 0)
           s_app[ni] = slot >= 0 && pos / kBlock < a.max_blocks ? a.bt[(int64_t)slot * a.bt_stride + pos / kBlock] : -1;
         if (pos < a.max_pos) {
@@ -492,7 +497,7 @@ void stream_kernel(StreamArgs a) {
     qb1 = col < G ? sq[cur][(h * G + col) * 8 + q4 + 4] : z;
     if constexpr (FUSED) {
       const int b = bf + cur;
-      row_last = wave_uniform(a.row_n[b] > 0 && srow_ok[cur] ? a.row_start[b + 1] - 1 : -1);
+      row_last = wave_uniform(P.row_n[b] > 0 && srow_ok[cur] ? P.row_start[b + 1] - 1 : -1);
     }
   };
   load_q();
@@ -582,8 +587,8 @@ void stream_kernel(StreamArgs a) {
     // the new token into the pool (position context_len - 1 of its row)
     if (tid < nrows * n_kv * 8) {
       const int b = bf + ni;
-      const int n = a.row_n[b];
-      const int last = a.row_start[b + 1] - 1;
+      const int n = P.row_n[b];
+      const int last = P.row_start[b + 1] - 1;
       const int blk = n > 0 && last >= B0 && last < B1 ? s_app[ni] : -1;
       if (blk >= 0 && blk < a.num_blocks) {
         const int pos = n - 1;
@@ -602,7 +607,7 @@ void stream_kernel(StreamArgs a) {
     const int i = e / (a.n_q * kHeadDim);
     const int rem = e - i * a.n_q * kHeadDim;
     const int b = bf + i;
-    if (a.row_n[b] <= 0) continue;
+    if (P.row_n[b] <= 0) continue;
     const int qh = rem / kHeadDim;
     const int d = rem % kHeadDim;
     const int hh = qh / G;
@@ -616,7 +621,7 @@ void stream_kernel(StreamArgs a) {
       L += f * src[kHeadDim + 1];
       O += f * src[d];
     }
-    if (a.row_start[b] >= B0 && a.row_start[b + 1] <= B1) {
+    if (P.row_start[b] >= B0 && P.row_start[b + 1] <= B1) {
       a.out[((int64_t)b * a.n_q + qh) * kHeadDim + d] = to_bf16(L > 0.f ? O / L : 0.f);
     } else {
       const int rec = 2 * (int)blockIdx.x + (i == 0 ? 0 : 1);
@@ -632,12 +637,13 @@ void stream_kernel(StreamArgs a) {
 
 // Merge of the records of rows cut by share ends: one workgroup per (row, KV
 // head), thread = (query head of the group, dim).
-template <int G>
+template <int G, bool DEVPLAN>
 __global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs a) {
+  const StreamPlan& P = DEVPLAN ? *a.plan_dev : a.plan;
   const int kvh = blockIdx.x;
   const int b = blockIdx.y;
   for (int e = threadIdx.x; e < G * kHeadDim; e += blockDim.x)
-    merge_element(a, a.out, a.ws, b, kvh * G + e / kHeadDim, e % kHeadDim);
+    merge_element(a, P, a.out, a.ws, b, kvh * G + e / kHeadDim, e % kHeadDim);
 }
 
 // The same merge for batches whose rows span many shares (few rows, long
@@ -647,12 +653,14 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs a) {
 // are combined through LDS in group order.  More workgroups and shorter chains
 // of dependent loads per thread than the kernel above, which leaves a batch of
 // one row on n_kv workgroups walking hundreds of records each.
+template <bool DEVPLAN>
 __global__ __launch_bounds__(1024) void stream_merge_wide_kernel(StreamArgs a) {
+  const StreamPlan& P = DEVPLAN ? *a.plan_dev : a.plan;
   constexpr int kGroups = 16;
   __shared__ float part[kGroups][kHeadDim][3];
   const int qh = blockIdx.x;
   const int b = blockIdx.y;
-  const int n = a.row_n[b];
+  const int n = P.row_n[b];
   const int d = threadIdx.x % kHeadDim;
   const int grp = threadIdx.x / kHeadDim;
   const int64_t obase = ((int64_t)b * a.n_q + qh) * kHeadDim;
@@ -660,9 +668,9 @@ __global__ __launch_bounds__(1024) void stream_merge_wide_kernel(StreamArgs a) {
     if (grp == 0) a.out[obase + d] = 0;
     return;
   }
-  const int start = a.row_start[b];
-  const int w0 = start / a.share;
-  const int w1 = (a.row_start[b + 1] - 1) / a.share;
+  const int start = P.row_start[b];
+  const int w0 = start / P.share;
+  const int w1 = (P.row_start[b + 1] - 1) / P.share;
   if (w0 == w1) return;
   float M = -INFINITY, L = 0.f, O = 0.f;
   for (int w = w0 + grp; w <= w1; w += 8 * kGroups) {
@@ -671,7 +679,7 @@ __global__ __launch_bounds__(1024) void stream_merge_wide_kernel(StreamArgs a) {
     for (int j = 0; j < 8; ++j) {
       const int wj = w + j * kGroups;
       const int ww = wj <= w1 ? wj : w1;
-      const int rec = 2 * ww + ((ww > w0 || start == w0 * a.share) ? 0 : 1);
+      const int rec = 2 * ww + ((ww > w0 || start == w0 * P.share) ? 0 : 1);
       const float* src = a.ws + ((int64_t)rec * a.n_q + qh) * kRec;
       mv[j] = wj <= w1 ? src[kHeadDim] : -INFINITY;
       lv[j] = src[kHeadDim + 1];
@@ -722,17 +730,110 @@ int device_cus() {
   return n;
 }
 
-template <bool FUSED, bool PREV>
+template <bool FUSED, bool PREV, bool DEVPLAN>
 const void* pick_stream(int G) {
-  return G == 1 ? (const void*)stream_kernel<1, FUSED, PREV>
-       : G == 2 ? (const void*)stream_kernel<2, FUSED, PREV>
-                : (const void*)stream_kernel<4, FUSED, PREV>;
+  return G == 1 ? (const void*)stream_kernel<1, FUSED, PREV, DEVPLAN>
+       : G == 2 ? (const void*)stream_kernel<2, FUSED, PREV, DEVPLAN>
+                : (const void*)stream_kernel<4, FUSED, PREV, DEVPLAN>;
+}
+
+template <bool DEVPLAN>
+const void* pick_merge(int G) {
+  return G == 1 ? (const void*)stream_merge_kernel<1, DEVPLAN>
+       : G == 2 ? (const void*)stream_merge_kernel<2, DEVPLAN>
+                : (const void*)stream_merge_kernel<4, DEVPLAN>;
 }
 
 }  // namespace
 
 size_t stream_records_bytes(int n_q) {
   return n_q > 0 ? (size_t)2 * kStreamMaxGrid * n_q * kRec * sizeof(float) : 0;
+}
+
+int stream_launch_grid() {
+  const int cus = device_cus();
+  return cus <= 0 ? 0 : std::min(cus, kStreamMaxGrid);
+}
+
+namespace {
+
+// Rows touched by each share of `share` blocks, into P->wg_rows (the row of a
+// block is the last row whose start is at or before it: empty rows share
+// their start with the next row and are passed over).  False when a share
+// would touch more than kMaxRows rows, empty rows in between included.
+bool plan_shares(StreamPlan* P, int batch, int share, int grid_max) {
+  const int grid = (int)((P->total + (int64_t)share - 1) / share);
+  if (grid > grid_max) return false;
+  P->share = share;
+  P->grid = grid;
+  for (int g = 0, b = 0; g < grid; ++g) {
+    const int p0 = g * share;
+    const int p1 = std::min(p0 + share, P->total) - 1;
+    while (b + 1 < batch && P->row_start[b + 1] <= p0) ++b;
+    int e = b;
+    while (e + 1 < batch && P->row_start[e + 1] <= p1) ++e;
+    if (e - b + 1 > kMaxRows) return false;
+    P->wg_rows[g] = (uint16_t)(b << 3 | (e - b + 1));
+  }
+  return true;
+}
+
+}  // namespace
+
+int stream_plan_build(int batch, const int32_t* row_lens_host, int max_blocks, const int32_t* slot_ids_host,
+                      bool slot_ids_dev, int num_slots, bool chain, StreamPlan* P, int* merge_kind) {
+  if (!row_lens_host || batch <= 0 || batch > kStreamMaxSeqs) return -1;
+  *P = StreamPlan{};
+  // each row's slot in the plan when the host knows it (one dependent memory
+  // read less before the first K/V load)
+  if (slot_ids_host && num_slots <= 0xffff) {
+    P->slots_in_args = 1;
+    for (int b = 0; b < batch; ++b) {
+      const int s = slot_ids_host[b];
+      P->row_slot[b] = (uint16_t)((s >= 0 && s < num_slots) ? s : 0xffff);
+    }
+  } else if (!slot_ids_dev && batch <= num_slots && num_slots <= 0xffff) {
+    P->slots_in_args = 1;
+    for (int b = 0; b < batch; ++b) P->row_slot[b] = (uint16_t)b;
+  }
+  // the block stream: rows end to end, each ceil(n / 16) blocks
+  int64_t total = 0;
+  int longest = 0;
+  P->row_start[0] = 0;
+  for (int b = 0; b < batch; ++b) {
+    int n = row_lens_host[b];
+    n = n < 0 ? 0 : (n > max_blocks * kBlock ? max_blocks * kBlock : n);
+    P->row_n[b] = n;
+    const int nb = (n + kBlock - 1) / kBlock;
+    longest = std::max(longest, nb);
+    total += nb;
+    if (total > 0x3fffffff) return -1;
+    P->row_start[b + 1] = (int32_t)total;
+  }
+  if (total == 0) return -1;
+  const int grid_max = stream_launch_grid();
+  if (grid_max <= 0) return -1;
+  P->total = (int)total;
+  const int even = (int)((total + grid_max - 1) / grid_max);
+  // a row of n blocks spans at most ceil((n - 1) / share) + 1 shares
+  const int chained = std::max(even, (longest - 1 + kPrevSpan - 2) / (kPrevSpan - 1));
+  if (!(chain && chained > even && plan_shares(P, batch, chained, grid_max)) && !plan_shares(P, batch, even, grid_max))
+    return -1;
+  // a merge launch is needed for empty rows and rows cut by share ends; rows
+  // that span many shares (few rows) are merged per query head
+  int most = 1;
+  bool need = false;
+  for (int b = 0; b < batch; ++b) {
+    if (P->row_n[b] <= 0) {
+      need = true;
+      continue;
+    }
+    const int span = (P->row_start[b + 1] - 1) / P->share - P->row_start[b] / P->share + 1;
+    need |= span > 1;
+    most = std::max(most, span);
+  }
+  *merge_kind = !need ? 0 : (most > 32 ? 2 : 1);
+  return most > kPrevSpan ? 1 : 0;
 }
 
 int stream_prepare(bool fused, const StreamCall& c, StreamLaunch* L) {
@@ -760,83 +861,46 @@ int stream_prepare(bool fused, const StreamCall& c, StreamLaunch* L) {
   a.max_pos = c.max_pos;
   a.batch = c.batch;
   a.scale_log2e = c.scale * kLog2e;
-  // each row's slot in the arguments when the host knows it (one dependent
-  // memory read less before the first K/V load)
-  if (c.slot_ids_host && c.num_slots <= 0xffff) {
-    a.slots_in_args = 1;
-    for (int b = 0; b < c.batch; ++b) {
-      const int s = c.slot_ids_host[b];
-      a.row_slot[b] = (uint16_t)((s >= 0 && s < c.num_slots) ? s : 0xffff);
-    }
-  } else if (!c.slot_ids && c.batch <= c.num_slots && c.num_slots <= 0xffff) {
-    a.slots_in_args = 1;
-    for (int b = 0; b < c.batch; ++b) a.row_slot[b] = (uint16_t)b;
-  }
-  // the block stream: rows end to end, each ceil(n / 16) blocks
-  int64_t total = 0;
-  a.row_start[0] = 0;
-  for (int b = 0; b < c.batch; ++b) {
-    int n = c.row_lens_host[b];
-    n = n < 0 ? 0 : (n > c.max_blocks * kBlock ? c.max_blocks * kBlock : n);
-    a.row_n[b] = n;
-    total += (n + kBlock - 1) / kBlock;
-    if (total > 0x3fffffff) return -1;
-    a.row_start[b + 1] = (int32_t)total;
-  }
-  if (total == 0) return -1;
-  const int cus = device_cus();
-  if (cus <= 0) return -1;
-  int grid = std::min(cus, kStreamMaxGrid);
-  a.share = (int)((total + grid - 1) / grid);
-  grid = (int)((total + a.share - 1) / a.share);
-  a.total = (int)total;
-  a.grid = grid;
-  if (c.records_bytes < (size_t)2 * grid * c.n_q * kRec * sizeof(float)) return -1;
+  int merge = 0;
+  const int pr = stream_plan_build(c.batch, c.row_lens_host, c.max_blocks, c.slot_ids_host, c.slot_ids != nullptr,
+                                   c.num_slots, c.chain_plan, &a.plan, &merge);
+  if (pr < 0) return -1;
+  L->long_rows = pr > 0;                // a row spans more shares than a chained prologue merges
+  const int launched = c.plan_dev ? stream_launch_grid() : a.plan.grid;
+  if (c.records_bytes < (size_t)2 * launched * c.n_q * kRec * sizeof(float)) return -1;
   a.ws = c.records;
-  // rows of each share (the row of a block is the last row whose start is at
-  // or before it: empty rows share their start with the next row and are
-  // passed over); every share must touch at most kMaxRows rows, empty rows in
-  // between included
-  for (int g = 0, b = 0; g < grid; ++g) {
-    const int p0 = g * a.share;
-    const int p1 = std::min(p0 + a.share, a.total) - 1;
-    while (b + 1 < c.batch && a.row_start[b + 1] <= p0) ++b;
-    int e = b;
-    while (e + 1 < c.batch && a.row_start[e + 1] <= p1) ++e;
-    if (e - b + 1 > kMaxRows) return -1;
-    a.wg_rows[g] = (uint16_t)(b << 3 | (e - b + 1));
-  }
   L->prev = c.out_prev != nullptr;
   if (L->prev) {
-    if (!c.records_prev) return -1;
+    if (!c.records_prev || L->long_rows) return -1;
     a.out_prev = c.out_prev;
     a.ws_prev = c.records_prev;
   }
+  L->devplan = c.plan_dev != nullptr;
+  if (L->devplan) {
+    // the plan comes from device memory at every launch: the launch shapes
+    // may not depend on it (one workgroup per CU, workgroups past the plan's
+    // shares exit; the per-KV-head merge always runs)
+    if (L->long_rows) return -1;
+    a.plan_dev = c.plan_dev;
+    merge = 1;
+  }
+  L->grid = launched;
   L->fused = fused;
   L->G = G;
-  // a merge launch is needed for empty rows and rows cut by share ends; rows
-  // that span many shares (few rows) are merged per query head
-  int most = 1;
-  bool need = false;
-  for (int b = 0; b < c.batch; ++b) {
-    if (a.row_n[b] <= 0) {
-      need = true;
-      continue;
-    }
-    const int span = (a.row_start[b + 1] - 1) / a.share - a.row_start[b] / a.share + 1;
-    need |= span > 1;
-    most = std::max(most, span);
-  }
-  L->merge = !need ? 0 : (most > 32 ? 2 : 1);
+  L->merge = merge;
   return PKV_OK;
 }
 
 int stream_enqueue(const StreamLaunch& L, hipStream_t st, bool merge) {
   StreamArgs a = L.a;
   void* args[] = {&a};
-  const void* fn = L.fused ? (L.prev ? pick_stream<true, true>(L.G) : pick_stream<true, false>(L.G))
-                           : (L.prev ? pick_stream<false, true>(L.G) : pick_stream<false, false>(L.G));
-  const int rc = launch_status(hipLaunchKernel(fn, dim3(a.grid), dim3(kThreads), args, 0, st));
+  const void* fn;
+  if (L.devplan)
+    fn = L.prev ? pick_stream<true, true, true>(L.G) : pick_stream<true, false, true>(L.G);
+  else
+    fn = L.fused ? (L.prev ? pick_stream<true, true, false>(L.G) : pick_stream<true, false, false>(L.G))
+                 : (L.prev ? pick_stream<false, true, false>(L.G) : pick_stream<false, false, false>(L.G));
+  const int rc = launch_status(hipLaunchKernel(fn, dim3(L.grid), dim3(kThreads), args, 0, st));
   if (rc != PKV_OK || !merge) return rc;
   return stream_merge_enqueue(L, st);
 }
@@ -846,11 +910,9 @@ int stream_merge_enqueue(const StreamLaunch& L, hipStream_t st) {
   StreamArgs a = L.a;
   void* args[] = {&a};
   if (L.merge == 2)
-    return launch_status(hipLaunchKernel((const void*)stream_merge_wide_kernel, dim3(a.n_q, a.batch), dim3(1024),
-                                         args, 0, st));
-  const void* mg = L.G == 1 ? (const void*)stream_merge_kernel<1>
-                 : L.G == 2 ? (const void*)stream_merge_kernel<2>
-                            : (const void*)stream_merge_kernel<4>;
+    return launch_status(hipLaunchKernel((const void*)stream_merge_wide_kernel<false>, dim3(a.n_q, a.batch),
+                                         dim3(1024), args, 0, st));
+  const void* mg = L.devplan ? pick_merge<true>(L.G) : pick_merge<false>(L.G);
   return launch_status(hipLaunchKernel(mg, dim3(a.n_kv, a.batch), dim3(256), args, 0, st));
 }
 

@@ -20,6 +20,16 @@ one call of the native ``pkv_decode_step``:
   unrotated values)
 
 The engine owns no arithmetic and allocates every buffer once, here.
+
+``GraphStep`` runs the same step as a HIP graph captured once and replayed
+(the category page's mini-sglang chapter 7: the step's ledger becomes kernel
+arguments, and the launches are captured): the native host half
+(``pkv_decode_step_host``) allocates blocks and writes the table changes, the
+metadata and the streaming kernel's plan into a pinned staging area; the graph
+copies it to the device and runs ``pkv_decode_step_device`` (apply, one fused
+launch per layer, one merge), whose launch shapes never depend on the lengths.
+A step whose rows the replayed launches do not serve (a few very long rows)
+runs eagerly through ``pkv_decode_step`` instead.
 """
 from __future__ import annotations
 
@@ -80,3 +90,77 @@ class DecodeEngine:
             q, k, v, out, self.k_pool, self.v_pool, self.bt_host, self.bt_dev, self.free, self.n_free,
             self.cached, self.meta_view(len(slot_ids)), slot_ids, self.cos_sin, self.scale,
             self.max_context_len, self.partition_size, self.workspace, stream=self.stream)
+
+
+class GraphStep:
+    """Decode steps of a fixed batch size over one DecodeEngine, replayed from
+    captured HIP graphs.  The caller writes each step's q, k, v into
+    ``self.q``/``self.k``/``self.v`` ([L, B, n_q|n_kv, 64] bf16) and reads
+    ``self.out`` after ``step``; the rows' slots may change from step to step.
+
+    ``depth`` staging areas (each with its own captured graph, whose copy
+    reads it) let the host half of the next step run while the previous
+    replays execute; a staging area is rewritten only after the replay that
+    read it has finished."""
+
+    def __init__(self, engine: DecodeEngine, batch: int, depth: int = 2):
+        e = engine
+        self.eng, self.batch = e, batch
+        L, dev = e.n_layers, e.dev
+        n = abi.pkv_decode_step_staging_bytes(L, batch, e.n_slots)
+        if n == 0:
+            raise ValueError("batch or slots outside what the replayed step serves")
+        self.stage_host = [torch.empty(n, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
+        self.stage_dev = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.q = torch.zeros((L, batch, e.n_q, e.d), dtype=torch.bfloat16, device=dev)
+        self.k = torch.zeros((L, batch, e.n_kv, e.d), dtype=torch.bfloat16, device=dev)
+        self.v = torch.zeros_like(self.k)
+        self.out = torch.zeros_like(self.q)
+        self.graphs = [None] * depth
+        self.done = [torch.cuda.Event() for _ in range(depth)]
+        self.pending = [False] * depth
+        self.next = 0
+        self.replays = self.eager_steps = 0
+
+    def capture(self, i: int):
+        """Capture the device half reading staging area i, which must hold a
+        step that the host half accepted (its rows check the launches); the
+        graph runs nothing until replayed."""
+        e = self.eng
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.stage_dev.copy_(self.stage_host[i], non_blocking=True)
+            abi.pkv_decode_step_device(self.q, self.k, self.v, self.out, e.k_pool, e.v_pool, e.bt_dev,
+                                       e.meta_view(self.batch), e.cos_sin, e.scale, self.stage_host[i],
+                                       self.stage_dev, e.workspace)
+        self.graphs[i] = g
+
+    def step(self, slot_ids):
+        """One decode step for batch row b = slot slot_ids[b], enqueued on the
+        current stream; returns True when it ran as a replay, False when it
+        ran eagerly."""
+        e = self.eng
+        slot_ids = np.asarray(slot_ids, dtype=np.int32)
+        if len(slot_ids) != self.batch:
+            raise ValueError("the replayed step serves a fixed batch size")
+        i = self.next
+        if self.pending[i]:
+            self.done[i].synchronize()        # the replay that read staging area i has finished
+            self.pending[i] = False
+        try:
+            e.n_free = abi.pkv_decode_step_host(e.bt_host, e.free, e.n_free, e.cached, slot_ids,
+                                                self.stage_host[i])
+        except abi.PagedKVError as err:
+            if err.status != abi.PKV_ERR_UNSUPPORTED:
+                raise
+            e.step(slot_ids, self.q, self.k, self.v, self.out)
+            self.eager_steps += 1
+            return False
+        if self.graphs[i] is None:
+            self.capture(i)
+        self.graphs[i].replay()
+        self.done[i].record()
+        self.pending[i] = True
+        self.next = (i + 1) % len(self.graphs)
+        self.replays += 1
+        return True

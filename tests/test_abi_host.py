@@ -197,6 +197,58 @@ def test_noalloc_decode_argument_errors_before_launch(lib):
     assert call(batch=64, maxctx=1_000_000) == E.PKV_ERR_CAPACITY
 
 
+def test_two_half_step_host_errors_change_nothing(lib):
+    """The host half of the replayed step checks everything before it
+    changes anything (same rules as pkv_decode_step), and the device half
+    rejects a staging area written for other sizes before any launch."""
+    E = _abi
+    L, slots, mb = 2, 3, 4
+    assert lib.pkv_decode_step_staging_bytes(L, 0, slots) == 0
+    assert lib.pkv_decode_step_staging_bytes(L, 257, 300) == 0
+    nbytes = lib.pkv_decode_step_staging_bytes(L, 2, slots)
+    assert nbytes % 4 == 0 and nbytes > 4 * (4 + slots + 4 + 2 * 2 * L)
+    bt = np.full((slots, L, mb), -1, np.int32)
+    bt[:, :, 0] = np.arange(slots * L, dtype=np.int32).reshape(slots, L)
+    free = np.arange(10, 14, dtype=np.int32)
+    cached = np.array([16, 5, 16], np.int32)        # slots 0 and 2 open a block per layer
+    stage = np.zeros(nbytes // 4, np.int32)
+
+    def host(sids, n_free):
+        nf = C.c_int(n_free)
+        sids = np.asarray(sids, np.int32)
+        rc = lib.pkv_decode_step_host(L, bt.ctypes.data, slots, mb, free.ctypes.data, C.byref(nf),
+                                      cached.ctypes.data, sids.ctypes.data, len(sids), stage.ctypes.data)
+        return rc, nf.value
+
+    before = (bt.copy(), cached.copy(), free.copy(), stage.copy())
+    assert host([0, 0], 4) == (E.PKV_ERR_INVALID_ARG, 4)        # a slot twice
+    assert host([0, 3], 4) == (E.PKV_ERR_INVALID_ARG, 4)        # no such slot
+    assert host([0, 2], 3) == (E.PKV_ERR_CAPACITY, 3)           # four blocks needed, three free
+    cached[1] = mb * 16
+    assert host([1, 0], 4) == (E.PKV_ERR_CAPACITY, 4)           # the table row is full
+    cached[1] = 5
+    for a, b in zip((bt, cached, free, stage), before):
+        np.testing.assert_array_equal(a, b)
+    rc, nf = host([2, 0], 4)
+    if rc == E.PKV_OK:                                          # a device to plan for
+        assert nf == 0 and list(cached) == [17, 5, 17]
+        assert stage[0] == 4 and list(stage[1:4]) == [2, L, slots]
+    else:                                                       # no device: nothing changed
+        assert rc == E.PKV_ERR_UNSUPPORTED and nf == 4
+        for a, b in zip((bt, cached, free, stage), before):
+            np.testing.assert_array_equal(a, b)
+    # device half: staging written for another batch size, null and misaligned staging
+    stage[1:4] = [3, L, slots]
+    ptrs = (C.c_void_p * L)(FAKE, FAKE)
+
+    def device(stage_host, stage_dev):
+        return lib.pkv_decode_step_device(L, ptrs, ptrs, ptrs, ptrs, FAKE, FAKE, 64, FAKE, slots, mb, FAKE, 2, 32,
+                                          8, 64, FAKE, 100, 0.125, stage_host, stage_dev, FAKE, 1 << 20, None)
+    assert device(stage.ctypes.data, FAKE) == E.PKV_ERR_INVALID_ARG
+    assert device(None, FAKE) == E.PKV_ERR_NULL
+    assert device(stage.ctypes.data, FAKE + 4) == E.PKV_ERR_MISALIGNED
+
+
 # ------------------------------------------------------- block allocation --
 
 def test_blocks_assign_walk_is_valid_every_step(lib):
