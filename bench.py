@@ -502,7 +502,9 @@ def graph_leg(torch, np, W, eng3, q3, k3, v3, stream, steps_small: int = 200, st
     layer, one merge), us/step from HIP events around the steps and host wall
     time.  Configs 1 and 2 (one layer) run on two engines from the same
     start; config 3 runs eager then replayed steps on the main engine (the
-    contexts differ by the eager steps' tokens)."""
+    contexts differ by the eager steps' tokens).  The GPU side alone: a few
+    eager steps, and replays of the last staged step, queued behind a spin
+    kernel (None when the host could not enqueue them before it ended)."""
     from paged_kv_attention_17_amd.engine import DecodeEngine, GraphStep
 
     def timed(fn, n):
@@ -518,8 +520,39 @@ def graph_leg(torch, np, W, eng3, q3, k3, v3, stream, steps_small: int = 200, st
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / n, (time.perf_counter() - w0) * 1e6 / n
 
+    # GPU-side time per step: n steps queued behind a spin kernel, so that the
+    # host has enqueued them all before the GPU starts on them (checked: the
+    # enqueue must end before the spin does)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    torch.cuda._sleep(10_000_000)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    spin_ms_per_cycle = e0.elapsed_time(e1) / 1e7
+
+    def gpu_only(fn, n, spin_ms):
+        fn()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(spin_ms / spin_ms_per_cycle))
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        enq_ms = (time.perf_counter() - w0) * 1e3
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n, enq_ms < 0.8 * spin_ms
+
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    def gpu_fields(eager_step, gs, n, spin_ms):
+        ge, ok_e = gpu_only(eager_step, n, spin_ms)
+        g = gs.graphs[(gs.next - 1) % len(gs.graphs)]       # replays of the last staged step (same tokens again)
+        gg, ok_g = gpu_only(lambda: g.replay(), n, spin_ms)
+        return {"eager_gpu_us_per_step": round(ge, 2) if ok_e else None,
+                "graph_gpu_us_per_step": round(gg, 2) if ok_g else None}
 
     res = {}
     small = (("config1", lambda n: W.make_decode(1701, [17], n_layers=1, num_blocks=64, extra_steps=n),
@@ -542,6 +575,7 @@ def graph_leg(torch, np, W, eng3, q3, k3, v3, stream, steps_small: int = 200, st
         res[name] = {"workload": desc, "eager_us_per_step": round(eager[0], 2), "graph_us_per_step": round(graph[0], 2),
                      "eager_host_us_per_step": round(eager[1], 2), "graph_host_us_per_step": round(graph[1], 2),
                      "replayed_steps": gs.replays, "eager_fallback_steps": gs.eager_steps}
+        res[name].update(gpu_fields(lambda: engs[0].step(sids, q, k, v, out), gs, 8, 20.0))
         del engs, gs
     sids = np.arange(q3.shape[1], dtype=np.int32)
     out3 = torch.empty_like(q3)
@@ -555,6 +589,7 @@ def graph_leg(torch, np, W, eng3, q3, k3, v3, stream, steps_small: int = 200, st
                       "eager_us_per_step": round(eager[0], 2), "graph_us_per_step": round(graph[0], 2),
                       "eager_host_us_per_step": round(eager[1], 2), "graph_host_us_per_step": round(graph[1], 2),
                       "replayed_steps": gs.replays, "eager_fallback_steps": gs.eager_steps}
+    res["config3"].update(gpu_fields(lambda: eng3.step(sids, q3, k3, v3, out3), gs, 4, 40.0))
     del gs
     torch.cuda.synchronize()
     return res
@@ -735,7 +770,8 @@ def main():
     for name, r in gl.items():
         log(f"{name} eager vs graph: {r['eager_us_per_step']:.1f} vs {r['graph_us_per_step']:.1f} us/step "
             f"(host {r['eager_host_us_per_step']:.1f} vs {r['graph_host_us_per_step']:.1f} us/step; "
-            f"{r['replayed_steps']} replays, {r['eager_fallback_steps']} eager fallbacks)")
+            f"{r['replayed_steps']} replays, {r['eager_fallback_steps']} eager fallbacks); GPU side alone "
+            f"{r['eager_gpu_us_per_step']} vs {r['graph_gpu_us_per_step']} us/step")
 
     pre = prefill_leg(torch, np, pkv, W)
     log(f"prefill: {pre['us_per_pass']:.1f} us per pass over {pre['calls']} chunk calls, "

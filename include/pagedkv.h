@@ -252,11 +252,14 @@ int pkv_check_block_table(const int32_t* bt_host, int64_t bt_row_stride, int num
 
 /* Bytes of workspace the decode calls need for these sizes: the larger of
  * the per-partition kernels' partials (batch x n_q_heads x partitions records)
- * and the streaming kernel's records (two per workgroup, at most 512
- * workgroups), each record 66 floats per query head (output, max, sum).
- * Returns 0 for invalid arguments.  partition_size 0 = the automatic choice,
- * which depends only on the arguments given here.  A call given less than the
- * streaming kernel's share of this size uses the per-partition kernels. */
+ * and the streaming kernel's share: two record regions (two records per
+ * workgroup, at most 512 workgroups; a decode step's chained launches
+ * alternate between them), each record 66 floats per query head (output, max,
+ * sum), then 3,840 bytes for the row plan a step's first launch stores for the
+ * others.  Returns 0 for invalid arguments.  partition_size 0 = the automatic
+ * choice, which depends only on the arguments given here.  A call given less
+ * than one record region uses the per-partition kernels; a decode step given
+ * less than the whole share runs its layers unchained. */
 size_t pkv_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
                                   int max_context_len, int partition_size);
 
@@ -413,23 +416,24 @@ int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const* k, const 
  * copy): the table changes, the new metadata (context lengths per slot |
  * positions | slot ids) and the streaming kernel's plan.  Nothing is enqueued.
  * PKV_ERR_UNSUPPORTED, with no change at all, when the rows do not suit the
- * replayed launches (a workgroup share would touch more than 4 rows, or a row
- * spans more than 8 shares: a few long rows); the caller then takes
- * pkv_decode_step for this step.
+ * replayed launches (a workgroup share would touch more than 4 rows, or, over
+ * several layers, a row spans more than 8 shares: a few long rows beside many
+ * short ones); the caller then takes pkv_decode_step for this step.
  *
  * pkv_decode_step_device: enqueues, in a fixed sequence, one small kernel that
  * applies staging_dev (table changes into bt_dev, metadata into meta_dev),
  * then one fused streaming launch per layer (RoPE, append, attention; each
  * merges the previous layer's rows cut by workgroup shares) reading the plan
- * from staging_dev at every launch, then one merge launch.  staging_dev must
+ * from staging_dev at every launch, then one merge launch (per KV head over
+ * several layers, per query head for one layer).  staging_dev must
  * hold a copy of staging_host (made by the caller on `stream` before this
  * call's launches, e.g. an async copy captured in the same graph); the host
  * copy is read only to check the launches when this call is made (capture
  * time).  Replays of a capture serve any later step whose host half used the
  * same n_layers, batch and num_slots.  The caller must not rewrite
  * staging_host while a replay's copy of it may still be pending.  The other
- * arguments are pkv_decode_step's; the workspace must hold two record regions
- * (pkv_decode_workspace_bytes for the batch).  Errors: PKV_ERR_UNSUPPORTED
+ * arguments are pkv_decode_step's; the workspace must hold the streaming
+ * kernel's share (pkv_decode_workspace_bytes for the batch).  Errors: PKV_ERR_UNSUPPORTED
  * when the staged rows or the shapes do not suit the streaming kernel,
  * PKV_ERR_CAPACITY when the workspace is too small, else as pkv_decode_step.
  * ------------------------------------------------------------------------ */

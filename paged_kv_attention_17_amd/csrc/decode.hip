@@ -498,7 +498,7 @@ extern "C" size_t pkv_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_
     return 0;
   const int ps = partition_size > 0 ? partition_size : auto_partition(batch, n_kv_heads, max_context_len);
   return std::max(ws_layout(batch, n_q_heads, n_kv_heads, decode_parts(max_context_len, ps)).total,
-                  2 * stream_records_bytes(n_q_heads));
+                  decode_plan_offset(n_q_heads) + kStreamPlanBytes);
 }
 
 extern "C" int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -608,6 +608,8 @@ int decode_prepare(const DecodeCall& c, DecodeLaunch* L) {
     sc.out_prev = c.out_prev;
     sc.records_prev = c.out_prev ? reinterpret_cast<const float*>(ws + (1 - c.records_half) * R) : nullptr;
     sc.plan_dev = c.plan_dev;
+    sc.fixed_shape = c.fixed_shape;
+    sc.plan_out = c.plan_out;
     sc.chain_plan = c.chain_plan;
     if (stream_prepare(c.fused, sc, &L->s) == PKV_OK) {
       L->path = 1;
@@ -628,8 +630,10 @@ int decode_prepare(const DecodeCall& c, DecodeLaunch* L) {
   return PKV_OK;
 }
 
+size_t decode_plan_offset(int n_q_heads) { return 2 * stream_records_bytes(n_q_heads); }
+
 bool decode_chainable(const DecodeLaunch& L) {
-  return L.path == 1 && !L.s.long_rows && L.c.workspace_bytes >= 2 * stream_records_bytes(L.c.n_q_heads);
+  return L.path == 1 && !L.s.long_rows && L.c.workspace_bytes >= decode_plan_offset(L.c.n_q_heads) + kStreamPlanBytes;
 }
 
 int decode_enqueue(const DecodeLaunch& L, hipStream_t st, bool merge) {

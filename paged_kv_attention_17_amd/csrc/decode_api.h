@@ -46,10 +46,15 @@ struct DecodeCall {
   int records_half;
   uint16_t* out_prev;
   bool chain_plan;             // plan the shares for chaining (every launch of a chain sets it)
-  // Non-null: the streaming kernel reads its plan from this device copy at
-  // every launch (launch shapes fixed; the call fails rather than take the
-  // per-partition kernels).  The plan built from row_lens_host checks the call.
+  // Non-null: the streaming kernel reads its plan from this device copy (the
+  // call fails rather than take the per-partition kernels).  The plan built
+  // from row_lens_host checks the call.  With fixed_shape the launch shapes
+  // do not depend on the plan (launches captured once and replayed).
   const StreamPlan* plan_dev;
+  bool fixed_shape;
+  // Non-null: the streaming launch also stores its plan here (device memory)
+  // for later launches with plan_dev.
+  StreamPlan* plan_out;
 };
 
 struct DecodeLaunch {
@@ -60,7 +65,10 @@ struct DecodeLaunch {
 
 // Check the call and plan its launches; nothing is enqueued.  PKV_OK or a
 // status.  A call that can run chained (streaming path, workspace with two
-// record regions) reports it through decode_chainable.
+// record regions and a plan) reports it through decode_chainable.
+
+// The workspace's plan area (after the two record regions) for n_q query heads.
+size_t decode_plan_offset(int n_q_heads);
 int decode_prepare(const DecodeCall& c, DecodeLaunch* L);
 bool decode_chainable(const DecodeLaunch& L);
 

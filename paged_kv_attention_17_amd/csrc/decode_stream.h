@@ -27,8 +27,11 @@ struct StreamPlan {
   uint16_t wg_rows[kStreamMaxGrid];        // per workgroup: first row << 3 | rows touched
 };
 
-// Kernel arguments (one block of at most 4 KB, passed by value).
-struct StreamArgs {
+// Kernel arguments: the pointers and sizes (StreamCore, what a launch that
+// reads its plan from device memory takes), plus the plan itself for
+// launches that carry it (StreamArgs, one block of at most 4 KB, passed by
+// value).
+struct StreamCore {
   uint16_t* out;
   const uint16_t* q;
   const uint16_t* k_new;       // fused only
@@ -50,8 +53,11 @@ struct StreamArgs {
   int max_pos;
   int batch;
   float scale_log2e;
-  const struct StreamPlan* plan_dev;   // device-plan launches: the plan in device memory
-  StreamPlan plan;                     // argument-plan launches: the plan itself
+  const StreamPlan* plan_dev;  // device-plan launches: the plan in device memory
+  StreamPlan* plan_out;        // argument-plan launches: workgroup 0 also stores the plan here
+};
+struct StreamArgs : StreamCore {
+  StreamPlan plan;             // argument-plan launches: the plan itself
 };
 static_assert(sizeof(StreamArgs) <= 4096, "kernel argument block");
 
@@ -79,8 +85,10 @@ struct StreamCall {
   size_t records_bytes;
   uint16_t* out_prev;          // non-null: this launch also merges the previous launch's
   const float* records_prev;   //   rows (same rows and lengths), written to out_prev
-  const StreamPlan* plan_dev;  // non-null: the kernels read their plan here at every launch
-                               //   (launch shapes fixed; for launches captured once and replayed)
+  const StreamPlan* plan_dev;  // non-null: the kernels read their plan here (small kernel arguments)
+  bool fixed_shape;            // with plan_dev: launch shapes independent of the plan (launches
+                               //   captured once and replayed; the plan may change between replays)
+  StreamPlan* plan_out;        // non-null: the launch also stores its plan here, in device memory
   bool chain_plan;             // shares sized for chained launches (see stream_plan_build)
 };
 
@@ -113,6 +121,9 @@ int stream_plan_build(int batch, const int32_t* row_lens_host, int max_blocks, c
 
 // Bytes of records one streaming launch may write for n_q query heads.
 size_t stream_records_bytes(int n_q);
+
+// Bytes a plan takes in device memory (a multiple of 256).
+constexpr size_t kStreamPlanBytes = (sizeof(StreamPlan) + 255) / 256 * 256;
 
 // Build the launch for `c`.  Returns -1 (nothing prepared) when the shapes
 // are outside what the kernel supports, PKV_OK otherwise.

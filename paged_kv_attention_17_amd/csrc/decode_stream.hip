@@ -54,6 +54,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 namespace pkv {
 
@@ -71,7 +72,7 @@ constexpr int kPrevSpan = 8;          // shares a row may span for the prologue 
 static_assert(kRec == kHeadDim + 2, "record layout");
 static_assert(kMaxRows * kMaxQ * 8 <= kThreads, "one query chunk per thread");
 
-__device__ __forceinline__ int row_slot(const StreamArgs& a, const StreamPlan& P, int b) {
+__device__ __forceinline__ int row_slot(const StreamCore& a, const StreamPlan& P, int b) {
   if (P.slots_in_args) {
     const int s = P.row_slot[b];
     return s == 0xffff ? -1 : s;
@@ -221,7 +222,7 @@ struct MfmaAcc {
 // w holds the row in record 2w when the row contains the share's first block,
 // else in record 2w + 1.  Empty rows get zeros; rows inside one share were
 // finished by their workgroup and are left alone.
-__device__ __forceinline__ void merge_element(const StreamArgs& a, const StreamPlan& P, uint16_t* out, const float* ws,
+__device__ __forceinline__ void merge_element(const StreamCore& a, const StreamPlan& P, uint16_t* out, const float* ws,
                                               int b, int qh,
                                               int d) {
   const int64_t o = ((int64_t)b * a.n_q + qh) * kHeadDim + d;
@@ -271,7 +272,7 @@ struct PrevMerge {
   bool empty;                  // the row is empty: write zero
 };
 
-__device__ __forceinline__ void prev_load(const StreamArgs& a, const StreamPlan& P, int b, int qh, int d, PrevMerge& M) {
+__device__ __forceinline__ void prev_load(const StreamCore& a, const StreamPlan& P, int b, int qh, int d, PrevMerge& M) {
   M.at = -1;
   M.empty = false;
   if (b >= a.batch) return;
@@ -297,7 +298,7 @@ __device__ __forceinline__ void prev_load(const StreamArgs& a, const StreamPlan&
   }
 }
 
-__device__ __forceinline__ void prev_finish(const StreamArgs& a, const PrevMerge& pm) {
+__device__ __forceinline__ void prev_finish(const StreamCore& a, const PrevMerge& pm) {
   if (pm.at < 0) return;
   if (pm.empty) {
     a.out_prev[pm.at] = 0;
@@ -316,15 +317,36 @@ __device__ __forceinline__ void prev_finish(const StreamArgs& a, const PrevMerge
   a.out_prev[pm.at] = to_bf16(L > 0.f ? O / L : 0.f);
 }
 
+// The kernels' argument block: the core alone when the plan is in device memory.
+template <bool DEVPLAN>
+using ArgsOf = std::conditional_t<DEVPLAN, StreamCore, StreamArgs>;
+
+template <bool DEVPLAN>
+__device__ __forceinline__ const StreamPlan& plan_of(const ArgsOf<DEVPLAN>& a) {
+  if constexpr (DEVPLAN)
+    return *a.plan_dev;
+  else
+    return a.plan;
+}
+
 template <int G, bool FUSED, bool PREV, bool DEVPLAN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void stream_kernel(StreamArgs a) {
-  const StreamPlan& P = DEVPLAN ? *a.plan_dev : a.plan;
+void stream_kernel(ArgsOf<DEVPLAN> a) {
+  const StreamPlan& P = plan_of<DEVPLAN>(a);
   const int B0 = blockIdx.x * P.share;
   const int B1 = min(B0 + P.share, P.total);
   const int len = B1 - B0;
   if (len <= 0) return;
   const int tid = threadIdx.x;
+  if constexpr (!DEVPLAN) {
+    // the plan for later launches that read it from device memory
+    if (a.plan_out != nullptr && blockIdx.x == 0) {
+      constexpr int kWords = (int)(sizeof(StreamPlan) / 4);
+      static_assert(kWords <= kThreads, "one word per thread");
+      if (tid < kWords)
+        reinterpret_cast<uint32_t*>(a.plan_out)[tid] = reinterpret_cast<const uint32_t*>(&a.plan)[tid];
+    }
+  }
   const int lane = tid & (kWave - 1);
   const int w = wave_uniform(tid >> 6);
   const int c = lane & 7;
@@ -638,8 +660,8 @@ void stream_kernel(StreamArgs a) {
 // Merge of the records of rows cut by share ends: one workgroup per (row, KV
 // head), thread = (query head of the group, dim).
 template <int G, bool DEVPLAN>
-__global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs a) {
-  const StreamPlan& P = DEVPLAN ? *a.plan_dev : a.plan;
+__global__ __launch_bounds__(256) void stream_merge_kernel(ArgsOf<DEVPLAN> a) {
+  const StreamPlan& P = plan_of<DEVPLAN>(a);
   const int kvh = blockIdx.x;
   const int b = blockIdx.y;
   for (int e = threadIdx.x; e < G * kHeadDim; e += blockDim.x)
@@ -654,8 +676,8 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs a) {
 // of dependent loads per thread than the kernel above, which leaves a batch of
 // one row on n_kv workgroups walking hundreds of records each.
 template <bool DEVPLAN>
-__global__ __launch_bounds__(1024) void stream_merge_wide_kernel(StreamArgs a) {
-  const StreamPlan& P = DEVPLAN ? *a.plan_dev : a.plan;
+__global__ __launch_bounds__(1024) void stream_merge_wide_kernel(ArgsOf<DEVPLAN> a) {
+  const StreamPlan& P = plan_of<DEVPLAN>(a);
   constexpr int kGroups = 16;
   __shared__ float part[kGroups][kHeadDim][3];
   const int qh = blockIdx.x;
@@ -866,7 +888,7 @@ int stream_prepare(bool fused, const StreamCall& c, StreamLaunch* L) {
                                    c.num_slots, c.chain_plan, &a.plan, &merge);
   if (pr < 0) return -1;
   L->long_rows = pr > 0;                // a row spans more shares than a chained prologue merges
-  const int launched = c.plan_dev ? stream_launch_grid() : a.plan.grid;
+  const int launched = c.fixed_shape ? stream_launch_grid() : a.plan.grid;
   if (c.records_bytes < (size_t)2 * launched * c.n_q * kRec * sizeof(float)) return -1;
   a.ws = c.records;
   L->prev = c.out_prev != nullptr;
@@ -877,13 +899,19 @@ int stream_prepare(bool fused, const StreamCall& c, StreamLaunch* L) {
   }
   L->devplan = c.plan_dev != nullptr;
   if (L->devplan) {
-    // the plan comes from device memory at every launch: the launch shapes
-    // may not depend on it (one workgroup per CU, workgroups past the plan's
-    // shares exit; the per-KV-head merge always runs)
-    if (L->long_rows) return -1;
     a.plan_dev = c.plan_dev;
-    merge = 1;
+    if (c.fixed_shape) {
+      // the plan may change between replays: the launch shapes may not depend
+      // on it (one workgroup per CU, workgroups past the plan's shares exit;
+      // a merge launch always follows: per KV head for chained launches,
+      // whose rows span at most kPrevSpan shares, else per query head)
+      if (c.chain_plan && L->long_rows) return -1;
+      merge = c.chain_plan ? 1 : 2;
+    }
+  } else if (c.fixed_shape) {
+    return -1;
   }
+  a.plan_out = c.plan_out;
   L->grid = launched;
   L->fused = fused;
   L->G = G;
@@ -893,7 +921,8 @@ int stream_prepare(bool fused, const StreamCall& c, StreamLaunch* L) {
 
 int stream_enqueue(const StreamLaunch& L, hipStream_t st, bool merge) {
   StreamArgs a = L.a;
-  void* args[] = {&a};
+  StreamCore core = L.a;               // device-plan launches pass the core alone
+  void* args[] = {L.devplan ? static_cast<void*>(&core) : static_cast<void*>(&a)};
   const void* fn;
   if (L.devplan)
     fn = L.prev ? pick_stream<true, true, true>(L.G) : pick_stream<true, false, true>(L.G);
@@ -908,10 +937,12 @@ int stream_enqueue(const StreamLaunch& L, hipStream_t st, bool merge) {
 int stream_merge_enqueue(const StreamLaunch& L, hipStream_t st) {
   if (L.merge == 0) return PKV_OK;
   StreamArgs a = L.a;
-  void* args[] = {&a};
+  StreamCore core = L.a;
+  void* args[] = {L.devplan ? static_cast<void*>(&core) : static_cast<void*>(&a)};
   if (L.merge == 2)
-    return launch_status(hipLaunchKernel((const void*)stream_merge_wide_kernel<false>, dim3(a.n_q, a.batch),
-                                         dim3(1024), args, 0, st));
+    return launch_status(hipLaunchKernel(L.devplan ? (const void*)stream_merge_wide_kernel<true>
+                                                   : (const void*)stream_merge_wide_kernel<false>,
+                                         dim3(a.n_q, a.batch), dim3(1024), args, 0, st));
   const void* mg = L.devplan ? pick_merge<true>(L.G) : pick_merge<false>(L.G);
   return launch_status(hipLaunchKernel(mg, dim3(a.n_kv, a.batch), dim3(256), args, 0, st));
 }

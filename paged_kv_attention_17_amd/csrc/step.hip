@@ -75,6 +75,10 @@ extern "C" int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const
   thread_local std::vector<DecodeLaunch> launches;
   launches.resize(n_layers);
   bool chain = false;
+  const size_t plan_off = decode_plan_offset(n_q_heads);
+  StreamPlan* plan_ws = n_layers > 1 && workspace && n_q_heads > 0 && workspace_bytes >= plan_off + kStreamPlanBytes
+                            ? reinterpret_cast<StreamPlan*>(static_cast<char*>(workspace) + plan_off)
+                            : nullptr;
   for (int l = 0; l < n_layers; ++l) {
     DecodeCall c{};
     c.fused = true;
@@ -105,9 +109,13 @@ extern "C" int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const
     c.workspace = workspace;
     c.workspace_bytes = workspace_bytes;
     c.chain_plan = n_layers > 1;
+    // chained launches: the first stores its plan in the workspace, the others
+    // read it from there (small kernel arguments)
+    if (l == 0 && plan_ws) c.plan_out = plan_ws;
     if (chain) {
       c.records_half = l & 1;
       c.out_prev = out[l - 1];
+      c.plan_dev = plan_ws;
     }
     const int rc = decode_prepare(c, &launches[l]);
     if (rc != PKV_OK) return rc;
@@ -225,12 +233,14 @@ extern "C" int pkv_decode_step_host(int n_layers, int32_t* bt_host, int num_slot
     row_lens[b] = p + 1;
   }
   if (need > *n_free) return PKV_ERR_CAPACITY;
-  // the rows must suit the streaming kernel and the chained prologue merge
+  // the rows must suit the streaming kernel and, over several layers, the
+  // chained prologue merge
   thread_local StreamPlan plan;
   int merge = 0;
-  if (stream_plan_build(batch, row_lens.data(), max_blocks_per_seq, slot_ids_host, true, num_slots, true, &plan,
-                        &merge) != 0)
-    return PKV_ERR_UNSUPPORTED;
+  const bool chain = n_layers > 1;
+  const int pr = stream_plan_build(batch, row_lens.data(), max_blocks_per_seq, slot_ids_host, true, num_slots, chain,
+                                   &plan, &merge);
+  if (pr < 0 || (chain && pr != 0)) return PKV_ERR_UNSUPPORTED;
   const StagingLayout SL = staging_layout(n_layers, batch, num_slots);
   int32_t* st = static_cast<int32_t*>(staging_host);
   std::memcpy(st + SL.plan, &plan, sizeof(StreamPlan));
@@ -322,7 +332,8 @@ extern "C" int pkv_decode_step_device(int n_layers, pkv_bf16* const* q, pkv_bf16
     c.workspace = workspace;
     c.workspace_bytes = workspace_bytes;
     c.plan_dev = plan_d;
-    c.chain_plan = true;
+    c.fixed_shape = true;
+    c.chain_plan = n_layers > 1;
     if (n_layers > 1) {
       c.records_half = l & 1;
       c.out_prev = l > 0 ? out[l - 1] : nullptr;
