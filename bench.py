@@ -749,6 +749,23 @@ def main():
     torch.cuda.synchronize()
     durs = np.array([a.elapsed_time(b) / 1e3 / L for a, b in passes])
     t_call = float(durs.mean())
+    # the same launches' K/V reads alone (the library's diagnostic read probe:
+    # same plan, shares, wave split and loads, no arithmetic), 16 per pass
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    probe = []
+    for it in range(args.attn_iters + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for layer in range(L):
+            pkv.pkv_paged_read_probe(kp, vp, eng.bt_dev[:, layer, :], None, ctx_now, sink, stream=stream)
+        e1.record(stream)
+        if it > 0:
+            probe.append((e0, e1))
+    torch.cuda.synchronize()
+    t_probe = float(np.mean([a.elapsed_time(b) / 1e3 / L for a, b in probe]))
+    probe_bytes = int(ctx_now.sum()) * KV_BYTES_PER_TOKEN
+    log(f"paged read probe (the launch's K/V reads alone): {t_probe * 1e6:.2f} us per launch, "
+        f"{probe_bytes / t_probe / 1e9:.0f} GB/s")
     log(f"streaming launch in the step: <= {t_attn * 1e6:.2f} us (step / {L}), {achieved:.0f} GB/s = "
         f"{achieved / HBM_PEAK_GBS:.1%} of peak; standalone fused call {t_call * 1e6:.2f} us "
         f"(16 back to back, p10 {np.percentile(durs, 10) * 1e6:.2f}, p90 {np.percentile(durs, 90) * 1e6:.2f})")
@@ -849,6 +866,10 @@ def main():
                      "standalone_call_us_p10": round(float(np.percentile(durs, 10)) * 1e6, 3),
                      "standalone_call_us_p90": round(float(np.percentile(durs, 90)) * 1e6, 3),
                      "source_hash": src_hash},
+        "paged_read_probe": {"us_per_launch": round(t_probe * 1e6, 3),
+                             "GBps": round(probe_bytes / t_probe / 1e9, 1),
+                             "what": "pkv_paged_read_probe over each layer's table view, 16 back to back per pass: "
+                                     "the streaming launch's K/V reads alone"},
         "copy_kernel_GBps": round(copy_gbs, 1),
         "read_kernel_GBps": round(read_gbs, 1),
         "unfused_layer_us": unf,

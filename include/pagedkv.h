@@ -133,6 +133,19 @@ int pkv_paged_gather(pkv_bf16* k_dense, pkv_bf16* v_dense, const pkv_bf16* k_poo
  * XOR to a fixed pattern, so the reads cannot be optimised away. */
 int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* Diagnostic, off the attention path: the K/V reads of pkv_paged_attn_decode's
+ * streaming kernel alone, for the same arguments (pools, table view, slots,
+ * host row lengths): the same plan, per-CU shares, wave split and loads, no
+ * arithmetic and no output.  `sink` as pkv_hbm_read_probe.  It measures what
+ * reading a batch's blocks in this pattern costs on its own, the floor the
+ * decode kernel is compared with.  PKV_ERR_UNSUPPORTED when the streaming
+ * kernel cannot serve the arguments or a workgroup's share exceeds 1,024
+ * blocks. */
+int pkv_paged_read_probe(const pkv_bf16* k_pool, const pkv_bf16* v_pool, int num_blocks,
+                         const int32_t* block_table, int64_t bt_row_stride, int num_slots,
+                         int max_blocks_per_seq, const int32_t* slot_ids, const int32_t* row_lens_host,
+                         int batch, int n_kv_heads, int head_dim, uint32_t* sink, void* stream);
+
 /* Host-side block allocation for one step ("The path of one inference",
  * step (4): blocks come off a free list; -1 marks an unassigned entry).
  * For every token t whose table entry bt_host[slot_ids_host[t]][positions_host[t] / 16]

@@ -45,6 +45,7 @@ SIGNATURES = {
     "pkv_paged_kv_append": (_i, [_p, _p, _i, _p, _p, _p, _i64, _i, _i, _p, _p, _i, _i, _i, _p]),
     "pkv_paged_gather": (_i, [_p, _p, _p, _p, _i, _p, _i64, _i, _i, _i, _i, _i, _p]),
     "pkv_hbm_read_probe": (_i, [_p, _sz, _p, _p]),
+    "pkv_paged_read_probe": (_i, [_p, _p, _i, _p, _i64, _i, _i, _p, _p, _i, _i, _i, _p, _p]),
     "pkv_blocks_assign": (_i, [_p, _i64, _i, _i, _p, _ip, _p, _p, _i, _p, _p, _ip]),
     "pkv_blocks_release": (_i, [_p, _i64, _i, _i, _i, _p, _ip, _i, _p, _p, _ip]),
     "pkv_block_table_patch": (_i, [_p, _i64, _p, _p, _i, _p]),
@@ -290,6 +291,26 @@ def pkv_hbm_read_probe(buf, sink, stream=None):
     _contig(buf, "buf")
     _check("pkv_hbm_read_probe", load().pkv_hbm_read_probe(
         _dev_ptr(buf, "buf"), buf.numel() * buf.element_size(), _dev_ptr(sink, "sink"), _stream(stream)))
+
+
+def pkv_paged_read_probe(k_pool, v_pool, block_table, slot_ids, row_lens_host, sink, stream=None):
+    """The streaming decode kernel's K/V reads alone (diagnostic): pools
+    [NB, 16, n_kv, 64]; block_table [rows, max_blocks] (row-strided view ok);
+    slot_ids [B] int32 or None; row_lens_host numpy lengths per batch row;
+    sink a device int32/uint32 tensor of at least one element."""
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool"), (slot_ids, "slot_ids"), (sink, "sink")):
+        _contig(t, n)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("shape mismatch")
+    bt, stride, rows, mb = _table(block_table)
+    rl = np.ascontiguousarray(row_lens_host, dtype=np.int32)
+    B = len(rl)
+    if slot_ids is not None and slot_ids.shape[0] != B:
+        raise ValueError("slot_ids must have one entry per batch row")
+    _check("pkv_paged_read_probe", load().pkv_paged_read_probe(
+        _dev_ptr(k_pool, "k_pool", _bf16_types()), _dev_ptr(v_pool, "v_pool", _bf16_types()), k_pool.shape[0], bt,
+        stride, rows, mb, None if slot_ids is None else _dev_ptr(slot_ids, "slot_ids"), rl.ctypes.data, B,
+        k_pool.shape[2], k_pool.shape[3], _dev_ptr(sink, "sink"), _stream(stream)))
 
 
 def pkv_blocks_assign(bt_host, free_list, n_free, slot_ids, positions):

@@ -650,6 +650,34 @@ int decode_finish(const DecodeLaunch& L, hipStream_t st) {
 
 }  // namespace pkv
 
+extern "C" int pkv_paged_read_probe(const pkv_bf16* k_pool, const pkv_bf16* v_pool, int num_blocks,
+                                    const int32_t* block_table, int64_t bt_row_stride, int num_slots,
+                                    int max_blocks_per_seq, const int32_t* slot_ids, const int32_t* row_lens_host,
+                                    int batch, int n_kv_heads, int head_dim, uint32_t* sink, void* stream) {
+  if (batch < 0 || num_blocks < 0 || num_slots < 0 || max_blocks_per_seq < 0 || bt_row_stride < max_blocks_per_seq)
+    return PKV_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return PKV_ERR_UNSUPPORTED;
+  if (batch == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !block_table || !row_lens_host || !sink) return PKV_ERR_NULL;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned4(block_table) || !aligned4(sink) ||
+      (slot_ids && !aligned4(slot_ids)))
+    return PKV_ERR_MISALIGNED;
+  if (!slot_ids && batch > num_slots) return PKV_ERR_INVALID_ARG;
+  StreamCall c{};
+  c.k_pool = const_cast<uint16_t*>(k_pool);
+  c.v_pool = const_cast<uint16_t*>(v_pool);
+  c.num_blocks = num_blocks;
+  c.block_table = block_table;
+  c.bt_row_stride = bt_row_stride;
+  c.num_slots = num_slots;
+  c.max_blocks = max_blocks_per_seq;
+  c.slot_ids = slot_ids;
+  c.row_lens_host = row_lens_host;
+  c.batch = batch;
+  c.n_kv = n_kv_heads;
+  return stream_read_probe(c, sink, static_cast<hipStream_t>(stream));
+}
+
 extern "C" int pkv_paged_attn_decode(pkv_bf16* out, const pkv_bf16* q, const pkv_bf16* k_pool,
                                      const pkv_bf16* v_pool, int num_blocks, const int32_t* block_table,
                                      int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,

@@ -135,4 +135,9 @@ int stream_enqueue(const StreamLaunch& L, hipStream_t st, bool merge);
 // The merge kernel alone (for the last launch of a chain).
 int stream_merge_enqueue(const StreamLaunch& L, hipStream_t st);
 
+// Diagnostic: the streaming kernel's K/V reads alone for the call `c`
+// (records are not written).  PKV_ERR_UNSUPPORTED when the kernel cannot
+// serve the call or a share exceeds one table window.
+int stream_read_probe(const StreamCall& c, uint32_t* sink, hipStream_t st);
+
 }  // namespace pkv

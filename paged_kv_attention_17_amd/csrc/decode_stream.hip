@@ -739,6 +739,82 @@ __global__ __launch_bounds__(1024) void stream_merge_wide_kernel(ArgsOf<DEVPLAN>
   a.out[obase + d] = to_bf16(L > 0.f ? O / L : 0.f);
 }
 
+// Diagnostic, off the attention path: the streaming kernel's K/V reads with
+// nothing else (same plan, same table window in LDS, same wave split, the
+// same four 16-byte loads per lane and block, kDepth blocks in flight per
+// wave); the data are XOR-ed into `sink` under a condition they never meet.
+// It gives the time that reading a batch's blocks in this pattern takes on
+// its own.
+__global__ __launch_bounds__(kThreads) void stream_read_probe_kernel(StreamArgs a, uint32_t* sink) {
+  const StreamPlan& P = a.plan;
+  const int B0 = blockIdx.x * P.share;
+  const int B1 = min(B0 + P.share, P.total);
+  const int len = B1 - B0;
+  if (len <= 0) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = wave_uniform(tid >> 6);
+  const int c = lane & 7;
+  const int r = lane >> 3;
+  const int n_kv = a.n_kv;
+  const int S = kWaves / n_kv;
+  const int h = w % n_kv;
+  const int s = w / n_kv;
+  const int wr = P.wg_rows[blockIdx.x];
+  const int bf = wr >> 3;
+  const int nrows = wr & 7;
+  const int64_t row_elems = (int64_t)n_kv * kHeadDim;
+  __shared__ int s_tab[kWin];
+  const uint32_t block_bytes = (uint32_t)(kBlock * row_elems * 2);
+  const uint32_t head_off = (uint32_t)(h * kHeadDim * 2);
+  const uint32_t v_off0 = (uint32_t)(r * row_elems * 2) + head_off + 16u * c;
+  const uint32_t v_off1 = v_off0 + (uint32_t)(8 * row_elems * 2);
+  const uint32_t k_offA = (uint32_t)((lane & 7) * row_elems * 2) + head_off +
+                          16u * (uint32_t)((lane >> 4) | ((lane & 8) >> 1));
+  const uint32_t k_offB = (uint32_t)((8 + (lane & 7)) * row_elems * 2) + head_off +
+                          16u * (uint32_t)((lane >> 4) | ((~lane & 8) >> 1));
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+  // block t of the share (t = thread): its pool block id, or -1
+  if (tid < len) {
+    const int p = B0 + tid;
+    int ri = 0;
+    for (int i = 1; i < nrows; ++i) ri = p >= P.row_start[bf + i] ? i : ri;
+    const int j = p - P.row_start[bf + ri];
+    const int slot = row_slot(a, P, bf + ri);
+    int blk = -1;
+    if (slot >= 0 && j < a.max_blocks && j * kBlock < P.row_n[bf + ri]) {
+      const int b = a.bt[(int64_t)slot * a.bt_stride + j];
+      blk = (b >= 0 && b < a.num_blocks) ? b : -1;
+    }
+    s_tab[tid] = blk;
+  }
+  __syncthreads();
+  auto issue = [&](KVRegs& R, int blk) {
+    const bool ok = blk >= 0;
+    const size_t base = ok ? (size_t)blk * block_bytes : 0;
+    const auto rk = buf_rsrc(kbase + base, ok ? block_bytes : 0u);
+    const auto rv = buf_rsrc(vbase + base, ok ? block_bytes : 0u);
+    R.k0 = buf_load16(rk, k_offA);
+    R.k1 = buf_load16(rk, k_offB);
+    R.v0 = buf_load16(rv, v_off0);
+    R.v1 = buf_load16(rv, v_off1);
+  };
+  KVRegs R[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) issue(R[d], s + d * S < len ? wave_uniform(s_tab[s + d * S]) : -1);
+  uint32_t x = 0;
+  for (int i = s; i < len; i += kDepth * S) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int idx = i + d * S;
+      x ^= R[d].k0.x ^ R[d].k0.w ^ R[d].k1.y ^ R[d].k1.z ^ R[d].v0.x ^ R[d].v0.w ^ R[d].v1.y ^ R[d].v1.z;
+      issue(R[d], idx + kDepth * S < len ? wave_uniform(s_tab[idx + kDepth * S]) : -1);
+    }
+  }
+  if (x == 0x9e3779b9u) *sink = x;
+}
+
 int device_cus() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cus[kMaxDev];
@@ -932,6 +1008,31 @@ int stream_enqueue(const StreamLaunch& L, hipStream_t st, bool merge) {
   const int rc = launch_status(hipLaunchKernel(fn, dim3(L.grid), dim3(kThreads), args, 0, st));
   if (rc != PKV_OK || !merge) return rc;
   return stream_merge_enqueue(L, st);
+}
+
+int stream_read_probe(const StreamCall& c, uint32_t* sink, hipStream_t st) {
+  if (!c.row_lens_host || c.batch <= 0 || c.batch > kStreamMaxSeqs || c.n_kv <= 0 || c.n_kv > kWaves ||
+      kWaves % c.n_kv)
+    return PKV_ERR_UNSUPPORTED;
+  StreamArgs a{};
+  a.k_pool = c.k_pool;
+  a.v_pool = c.v_pool;
+  a.bt = c.block_table;
+  a.slot_ids = c.slot_ids;
+  a.bt_stride = c.bt_row_stride;
+  a.num_blocks = c.num_blocks;
+  a.num_slots = c.num_slots;
+  a.max_blocks = c.max_blocks;
+  a.n_kv = c.n_kv;
+  a.batch = c.batch;
+  int merge = 0;
+  if (stream_plan_build(c.batch, c.row_lens_host, c.max_blocks, c.slot_ids_host, c.slot_ids != nullptr, c.num_slots,
+                        false, &a.plan, &merge) < 0)
+    return PKV_ERR_UNSUPPORTED;
+  if (a.plan.share > kWin) return PKV_ERR_UNSUPPORTED;     // one table window per share
+  void* args[] = {&a, &sink};
+  return launch_status(hipLaunchKernel((const void*)stream_read_probe_kernel, dim3(a.plan.grid), dim3(kThreads),
+                                       args, 0, st));
 }
 
 int stream_merge_enqueue(const StreamLaunch& L, hipStream_t st) {

@@ -335,6 +335,21 @@ def test_check_block_table_reports_first_problem(lib):
     assert pkv.pkv_check_block_table(bt3[:, 1, :], None, ctx, 8)[0] == 0
 
 
+def test_paged_read_probe_argument_errors(lib):
+    E = _abi
+    lens = np.array([17, 40], np.int32)
+
+    def call(k=FAKE, sink=FAKE, d=64, batch=2, rl=lens.ctypes.data, stride=4, sid=None):
+        return lib.pkv_paged_read_probe(k, FAKE, 64, FAKE, stride, 2, 4, sid, rl, batch, 8, d, sink, None)
+    assert call(batch=0) == E.PKV_OK
+    assert call(d=128) == E.PKV_ERR_UNSUPPORTED
+    assert call(k=None) == E.PKV_ERR_NULL
+    assert call(rl=None) == E.PKV_ERR_NULL
+    assert call(sink=FAKE + 2) == E.PKV_ERR_MISALIGNED
+    assert call(stride=3) == E.PKV_ERR_INVALID_ARG
+    assert call(batch=3) == E.PKV_ERR_INVALID_ARG      # more rows than the table without slot ids
+
+
 def test_read_probe_argument_errors(lib):
     E = _abi
     assert lib.pkv_hbm_read_probe(None, 0, None, None) == E.PKV_OK

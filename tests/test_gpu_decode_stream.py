@@ -345,3 +345,20 @@ def test_stream_few_rows_over_every_share(gpu, lens):
     check_attention(got, ref, f"few rows {lens.tolist()}")
     bound = cross_bound(ref, attention.decode(q, kp, abs_pool(vp), bt, np.arange(len(lens)), lens, 0.125))
     check_close_evaluations(_decode(q, kp, vp, bt, None, lens, None), got, "few rows vs per-partition", bound)
+
+
+def test_paged_read_probe_reads_without_writing(gpu):
+    """The diagnostic read probe runs over the streaming kernel's plan
+    (several rows per share, rows over several shares) and writes nothing:
+    the pools are unchanged and the sink keeps its value."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 700, size=40).astype(np.int32)
+    kp, vp, bt = _batch(rng, lens, 8, poison=False)
+    kpd, vpd = dev_bf16(kp), dev_bf16(vp)
+    sink = torch.full((1,), 5, dtype=torch.int32, device="cuda")
+    pkv.pkv_paged_read_probe(kpd, vpd, dev_i32(bt), None, lens, sink)
+    pkv.pkv_paged_read_probe(kpd, vpd, dev_i32(bt), dev_i32(np.arange(40)[::-1].copy()), lens[::-1].copy(), sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 5
+    np.testing.assert_array_equal(bits(kpd), kp)
+    np.testing.assert_array_equal(bits(vpd), vp)
