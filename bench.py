@@ -668,6 +668,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--leg", choices=["prefill"], default=None,
+                    help="run one leg alone and print its JSON (for profiling it)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -685,6 +687,9 @@ def main():
         build.build()
     pkv.load()
     torch.cuda.set_device(0)
+    if args.leg == "prefill":
+        print(json.dumps(prefill_leg(torch, np, pkv, W, iters=args.steps)), flush=True)
+        return
     steps_total = args.warmup + args.steps
     log(f"building workload (B=64, 16 layers, ctx U[512,4096]) ...")
     w = W.config3(fill_pool=False, extra_steps=steps_total + 64)     # room for the graph leg's steps

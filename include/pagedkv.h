@@ -267,8 +267,8 @@ int pkv_check_block_table(const int32_t* bt_host, int64_t bt_row_stride, int num
  * the per-partition kernels' partials (batch x n_q_heads x partitions records)
  * and the streaming kernel's share: two record regions (two records per
  * workgroup, at most 512 workgroups; a decode step's chained launches
- * alternate between them), each record 66 floats per query head (output, max,
- * sum), then 3,840 bytes for the row plan a step's first launch stores for the
+ * alternate between them), each record 68 floats per query head (output, max,
+ * sum, two of padding), then 3,840 bytes for the row plan a step's first launch stores for the
  * others.  Returns 0 for invalid arguments.  partition_size 0 = the automatic
  * choice, which depends only on the arguments given here.  A call given less
  * than one record region uses the per-partition kernels; a decode step given

@@ -10,7 +10,7 @@ namespace pkv {
 
 constexpr int kStreamMaxSeqs = 256;   // batch rows one launch describes
 constexpr int kStreamMaxGrid = 512;   // workgroups (one per CU)
-constexpr int kStreamRec = 66;        // record per query head: 64 unnormalised outputs, max, sum
+constexpr int kStreamRec = 68;        // record per query head: 64 unnormalised outputs, max, sum, 2 pad (16-byte rows)
 
 // How the batch's blocks are cut into workgroup shares: rows laid end to end
 // (the block stream), each workgroup an equal, contiguous share.  Built on the

@@ -69,7 +69,7 @@ constexpr int kMaxKv = 16;            // KV heads
 constexpr int kRec = kStreamRec;
 constexpr int kWin = kThreads;        // blocks whose table entries are staged in LDS at a time
 constexpr int kPrevSpan = 8;          // shares a row may span for the prologue merge of chained launches
-static_assert(kRec == kHeadDim + 2, "record layout");
+static_assert(kRec == kHeadDim + 4, "record layout: outputs, max, sum, padding to 16 bytes");
 static_assert(kMaxRows * kMaxQ * 8 <= kThreads, "one query chunk per thread");
 
 __device__ __forceinline__ int row_slot(const StreamCore& a, const StreamPlan& P, int b) {
@@ -364,7 +364,8 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
 
   __shared__ uint4 sq[kMaxRows][kMaxQ * 8];                 // queries: [row][head][chunk]
   __shared__ uint4 snew[kMaxRows][2][kMaxKv * 8];           // fused: new key / value [row][k|v][head][chunk]
-  __shared__ float sp[kMaxRows][kWaves][G][kRec];           // per-wave partials of each row
+  __shared__ __attribute__((aligned(16))) float spo[kMaxRows][kWaves][G][kHeadDim];  // per-wave partial outputs of each row
+  __shared__ float2 spm[kMaxRows][kWaves][G];               // and their (max, sum)
   __shared__ int srow_ok[kMaxRows];                         // the row's table slot is valid
   __shared__ int s_app[kMaxRows];                           // fused: pool block of the row's new token, or -1
   __shared__ uint16_t svt[kWaves][kBlock * kHeadDim];       // per-wave V tile (transposed reads)
@@ -531,14 +532,11 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
     if (col < G) {
-      float* dst = sp[cur][w][col];
+      float* dst = spo[cur][w][col];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         *reinterpret_cast<float4*>(dst + 16 * t + 4 * q4) = make_float4(acc.o[t][0], acc.o[t][1], acc.o[t][2], acc.o[t][3]);
-      if (q4 == 0) {
-        dst[kHeadDim] = acc.m;
-        dst[kHeadDim + 1] = l;
-      }
+      if (q4 == 0) spm[cur][w][col] = make_float2(acc.m, l);
     }
     ++cur;
     acc.reset();
@@ -624,35 +622,49 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
   __syncthreads();
 
   // ---- merge the KV heads' waves per row: finish rows inside the share,
-  // leave records for rows cut by its ends ------------------------------------
-  for (int e = tid; e < nrows * a.n_q * kHeadDim; e += kThreads) {
-    const int i = e / (a.n_q * kHeadDim);
-    const int rem = e - i * a.n_q * kHeadDim;
+  // leave records for rows cut by its ends.  One thread per (row, query
+  // head, 8 dims): 16-byte LDS reads, one 16-byte output store ------------------
+  for (int e = tid; e < nrows * a.n_q * 8; e += kThreads) {
+    const int i = e / (a.n_q * 8);
+    const int rem = e - i * a.n_q * 8;
     const int b = bf + i;
     if (P.row_n[b] <= 0) continue;
-    const int qh = rem / kHeadDim;
-    const int d = rem % kHeadDim;
+    const int qh = rem >> 3;
+    const int c8 = rem & 7;
     const int hh = qh / G;
     const int g = qh % G;
-    float M = sp[i][hh][g][kHeadDim];
-    for (int t = 1; t < S; ++t) M = fmaxf(M, sp[i][hh + t * n_kv][g][kHeadDim]);
-    float L = 0.f, O = 0.f;
+    float M = spm[i][hh][g].x;
+    for (int t = 1; t < S; ++t) M = fmaxf(M, spm[i][hh + t * n_kv][g].x);
+    float L = 0.f;
+    float O[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int t = 0; t < S; ++t) {
-      const float* src = sp[i][hh + t * n_kv][g];
-      const float f = fast_exp2(src[kHeadDim] - M);
-      L += f * src[kHeadDim + 1];
-      O += f * src[d];
+      const float2 ml = spm[i][hh + t * n_kv][g];
+      const float f = fast_exp2(ml.x - M);
+      L += f * ml.y;
+      const float4* src = reinterpret_cast<const float4*>(&spo[i][hh + t * n_kv][g][8 * c8]);
+      const float4 o0 = src[0], o1 = src[1];
+      O[0] += f * o0.x;
+      O[1] += f * o0.y;
+      O[2] += f * o0.z;
+      O[3] += f * o0.w;
+      O[4] += f * o1.x;
+      O[5] += f * o1.y;
+      O[6] += f * o1.z;
+      O[7] += f * o1.w;
     }
     if (P.row_start[b] >= B0 && P.row_start[b + 1] <= B1) {
-      a.out[((int64_t)b * a.n_q + qh) * kHeadDim + d] = to_bf16(L > 0.f ? O / L : 0.f);
+      uint4 v;
+      v.x = pack_bf16x2(L > 0.f ? O[0] / L : 0.f, L > 0.f ? O[1] / L : 0.f);
+      v.y = pack_bf16x2(L > 0.f ? O[2] / L : 0.f, L > 0.f ? O[3] / L : 0.f);
+      v.z = pack_bf16x2(L > 0.f ? O[4] / L : 0.f, L > 0.f ? O[5] / L : 0.f);
+      v.w = pack_bf16x2(L > 0.f ? O[6] / L : 0.f, L > 0.f ? O[7] / L : 0.f);
+      *reinterpret_cast<uint4*>(a.out + ((int64_t)b * a.n_q + qh) * kHeadDim + 8 * c8) = v;
     } else {
       const int rec = 2 * (int)blockIdx.x + (i == 0 ? 0 : 1);
       float* dst = a.ws + ((int64_t)rec * a.n_q + qh) * kRec;
-      dst[d] = O;
-      if (d == 0) {
-        dst[kHeadDim] = M;
-        dst[kHeadDim + 1] = L;
-      }
+      reinterpret_cast<float4*>(dst + 8 * c8)[0] = make_float4(O[0], O[1], O[2], O[3]);
+      reinterpret_cast<float4*>(dst + 8 * c8)[1] = make_float4(O[4], O[5], O[6], O[7]);
+      if (c8 == 0) *reinterpret_cast<float2*>(dst + kHeadDim) = make_float2(M, L);
     }
   }
 }
@@ -808,7 +820,9 @@ __global__ __launch_bounds__(kThreads) void stream_read_probe_kernel(StreamArgs 
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       const int idx = i + d * S;
-      x ^= R[d].k0.x ^ R[d].k0.w ^ R[d].k1.y ^ R[d].k1.z ^ R[d].v0.x ^ R[d].v0.w ^ R[d].v1.y ^ R[d].v1.z;
+      // every loaded dword takes part, so that no load is narrowed
+      x ^= R[d].k0.x ^ R[d].k0.y ^ R[d].k0.z ^ R[d].k0.w ^ R[d].k1.x ^ R[d].k1.y ^ R[d].k1.z ^ R[d].k1.w;
+      x ^= R[d].v0.x ^ R[d].v0.y ^ R[d].v0.z ^ R[d].v0.w ^ R[d].v1.x ^ R[d].v1.y ^ R[d].v1.z ^ R[d].v1.w;
       issue(R[d], idx + kDepth * S < len ? wave_uniform(s_tab[idx + kDepth * S]) : -1);
     }
   }

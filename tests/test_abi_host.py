@@ -41,7 +41,7 @@ def test_workspace_and_partition_sizes(lib):
     # first chained launch stores for the others (16 + 257 x 4 + 256 x 4 +
     # 256 x 2 + 512 x 2 = 3,604 bytes, rounded up to 256)
     plan = 3840
-    stream = 2 * 2 * 512 * 32 * 66 * 4 + plan
+    stream = 2 * 2 * 512 * 32 * 68 * 4 + plan
     assert pkv.pkv_decode_workspace_bytes(1, 32, 8, 64, 17, 0) == stream
     ps = pkv.pkv_decode_partition_size(64, 8, 4096)
     assert ps % 16 == 0 and ps >= 64
@@ -50,7 +50,7 @@ def test_workspace_and_partition_sizes(lib):
 
     def expect(B, nq, nkv, P):
         # the larger of: per-partition outputs + (max, sum), and the streaming records
-        return max(up(B * nq * P * 64 * 4) + up(B * nq * P * 2 * 4), 2 * 2 * 512 * nq * 66 * 4 + plan)
+        return max(up(B * nq * P * 64 * 4) + up(B * nq * P * 2 * 4), 2 * 2 * 512 * nq * 68 * 4 + plan)
     assert pkv.pkv_decode_workspace_bytes(64, 32, 8, 64, 4096, 0) == expect(64, 32, 8, P)
     assert pkv.pkv_decode_workspace_bytes(2, 32, 8, 64, 100, 16) == expect(2, 32, 8, 7)
     assert pkv.pkv_decode_workspace_bytes(2, 32, 8, 32, 100, 16) == 0       # unsupported head_dim
