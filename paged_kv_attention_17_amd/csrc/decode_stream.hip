@@ -72,6 +72,41 @@ constexpr int kPrevSpan = 8;          // shares a row may span for the prologue 
 static_assert(kRec == kHeadDim + 4, "record layout: outputs, max, sum, padding to 16 bytes");
 static_assert(kMaxRows * kMaxQ * 8 <= kThreads, "one query chunk per thread");
 
+// A 16-bit plan entry at a wave-uniform index, read as its aligned dword (a
+// scalar load; there is no 16-bit scalar load).
+__device__ __forceinline__ int plan_u16(const uint16_t* arr, int idx) {
+  const int i = wave_uniform(idx);
+  const uint32_t wd = reinterpret_cast<const uint32_t*>(arr)[i >> 1];
+  return (int)((i & 1) ? (wd >> 16) : (wd & 0xffffu));
+}
+
+// The rows a share touches (at most kMaxRows = 4), held in registers: their
+// starts in the block stream (and the end of the last), lengths and table
+// rows.  Accessors take a row index that may differ between lanes.
+struct ShareRows {
+  int s0, s1, s2, s3, s4;      // starts of rows 0..3, and the start after row 3
+  int n0, n1, n2, n3;          // tokens
+  int t0, t1, t2, t3;          // table rows (-1: none)
+  __device__ __forceinline__ static int sel(int i, int a0, int a1, int a2, int a3) {
+    return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
+  }
+  __device__ __forceinline__ int start(int i) const { return i == 4 ? s4 : sel(i, s0, s1, s2, s3); }
+  __device__ __forceinline__ int end(int i) const { return start(i + 1); }
+  __device__ __forceinline__ int len(int i) const { return sel(i, n0, n1, n2, n3); }
+  __device__ __forceinline__ int slot(int i) const { return sel(i, t0, t1, t2, t3); }
+};
+static_assert(kMaxRows == 4, "ShareRows holds four rows");
+
+// Table row of batch row b (wave-uniform b), or -1.
+__device__ __forceinline__ int row_slot_u(const StreamCore& a, const StreamPlan& P, int b) {
+  if (P.slots_in_args) {
+    const int s = plan_u16(P.row_slot, b);
+    return s == 0xffff ? -1 : s;
+  }
+  const int s = a.slot_ids ? a.slot_ids[wave_uniform(b)] : b;
+  return (s >= 0 && s < a.num_slots) ? s : -1;
+}
+
 __device__ __forceinline__ int row_slot(const StreamCore& a, const StreamPlan& P, int b) {
   if (P.slots_in_args) {
     const int s = P.row_slot[b];
@@ -287,14 +322,17 @@ __device__ __forceinline__ void prev_load(const StreamCore& a, const StreamPlan&
   const int w1 = (P.row_start[b + 1] - 1) / P.share;
   if (w0 == w1) return;
   M.at = o;
+  // (max, sum) of a record are the same for every lane: read as constant
+  // memory (the previous launch wrote them) they become scalar loads
+  const __attribute__((address_space(4))) float* ws_c = (const __attribute__((address_space(4))) float*)a.ws_prev;
 #pragma unroll
   for (int j = 0; j < kPrevSpan; ++j) {
     const int ww = w0 + j <= w1 ? w0 + j : w1;
     const int rec = 2 * ww + ((ww > w0 || start == w0 * P.share) ? 0 : 1);
-    const float* src = a.ws_prev + ((int64_t)rec * a.n_q + qh) * kRec;
-    M.m[j] = w0 + j <= w1 ? src[kHeadDim] : -INFINITY;
-    M.l[j] = src[kHeadDim + 1];
-    M.o[j] = src[d];
+    const int64_t base = ((int64_t)rec * a.n_q + qh) * kRec;
+    M.m[j] = w0 + j <= w1 ? ws_c[base + kHeadDim] : -INFINITY;
+    M.l[j] = ws_c[base + kHeadDim + 1];
+    M.o[j] = a.ws_prev[base + d];
   }
 }
 
@@ -338,15 +376,6 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
   const int len = B1 - B0;
   if (len <= 0) return;
   const int tid = threadIdx.x;
-  if constexpr (!DEVPLAN) {
-    // the plan for later launches that read it from device memory
-    if (a.plan_out != nullptr && blockIdx.x == 0) {
-      constexpr int kWords = (int)(sizeof(StreamPlan) / 4);
-      static_assert(kWords <= kThreads, "one word per thread");
-      if (tid < kWords)
-        reinterpret_cast<uint32_t*>(a.plan_out)[tid] = reinterpret_cast<const uint32_t*>(&a.plan)[tid];
-    }
-  }
   const int lane = tid & (kWave - 1);
   const int w = wave_uniform(tid >> 6);
   const int c = lane & 7;
@@ -355,12 +384,27 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
   const int S = kWaves / n_kv;           // waves per KV head
   const int h = w % n_kv;                // this wave's KV head
   const int s = w / n_kv;                // and its lane of blocks
-  const int wr = P.wg_rows[blockIdx.x];
+  const int wr = plan_u16(P.wg_rows, blockIdx.x);
   const int bf = wr >> 3;                // first row of the share
   const int nrows = wr & 7;              // rows it touches
   const int64_t row_elems = (int64_t)n_kv * kHeadDim;
   const float C = a.scale_log2e;
   const float invC = 1.0f / C;
+  // the share's rows, read once with scalar loads
+  constexpr int kFar = 0x7fffffff;
+  const ShareRows RW{P.row_start[bf],
+                     nrows >= 1 ? P.row_start[bf + 1] : kFar,
+                     nrows >= 2 ? P.row_start[bf + 2] : kFar,
+                     nrows >= 3 ? P.row_start[bf + 3] : kFar,
+                     nrows >= 4 ? P.row_start[bf + 4] : kFar,
+                     nrows > 0 ? P.row_n[bf] : 0,
+                     nrows > 1 ? P.row_n[bf + 1] : 0,
+                     nrows > 2 ? P.row_n[bf + 2] : 0,
+                     nrows > 3 ? P.row_n[bf + 3] : 0,
+                     nrows > 0 ? row_slot_u(a, P, bf) : -1,
+                     nrows > 1 ? row_slot_u(a, P, bf + 1) : -1,
+                     nrows > 2 ? row_slot_u(a, P, bf + 2) : -1,
+                     nrows > 3 ? row_slot_u(a, P, bf + 3) : -1};
 
   __shared__ uint4 sq[kMaxRows][kMaxQ * 8];                 // queries: [row][head][chunk]
   __shared__ uint4 snew[kMaxRows][2][kMaxKv * 8];           // fused: new key / value [row][k|v][head][chunk]
@@ -387,27 +431,25 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
                           16u * (uint32_t)((lane >> 4) | ((~lane & 8) >> 1));
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+  // the table seen as constant memory: wave-uniform reads become scalar loads
+  const __attribute__((address_space(4))) int32_t* bt_const =
+      (const __attribute__((address_space(4))) int32_t*)a.bt;
 
-  // stream block p -> pool block id (-1 for none or out of range) and
+  // stream block p -> its table entry as read (-1 for none; range-checked by
+  // block_ok where it is used, so that nothing waits for the load here) and
   // (row << 8 | tokens to read from the pool; the fused step's new token is
   // not among them)
+  auto block_ok = [&](int blk) { return (blk >= 0 && blk < a.num_blocks) ? blk : -1; };
   auto block_info = [&](int p, int& tab, int& meta) {
-    int ri = 0;
-    for (int i = 1; i < nrows; ++i) ri = p >= P.row_start[bf + i] ? i : ri;
-    int start = P.row_start[bf], n = P.row_n[bf];
-    for (int i = 1; i < nrows; ++i) {
-      start = i == ri ? P.row_start[bf + i] : start;
-      n = i == ri ? P.row_n[bf + i] : n;
-    }
+    const int ri = (p >= RW.s1) + (p >= RW.s2) + (p >= RW.s3);
+    const int start = RW.start(ri);
+    const int n = RW.len(ri);
     const int j = p - start;
-    const int slot = row_slot(a, P, bf + ri);
+    const int slot = RW.slot(ri);
     int valid = (FUSED ? n - 1 : n) - j * kBlock;
     valid = valid > kBlock ? kBlock : (valid < 0 ? 0 : valid);
     tab = -1;
-    if (slot >= 0 && j < a.max_blocks && valid > 0) {
-      const int blk = a.bt[(int64_t)slot * a.bt_stride + j];
-      tab = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
-    }
+    if (slot >= 0 && j < a.max_blocks && valid > 0) tab = a.bt[(int64_t)slot * a.bt_stride + j];
     meta = (ri << 8) | valid;
   };
   // Loads of one block for this wave's KV head.  blk < 0 reads nothing (a
@@ -423,22 +465,116 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
     R.v1 = buf_load16(rv, v_off1);
   };
 
-  // ---- this wave's first blocks, requested before anything is staged ----
-  KVRegs R[kDepth];
+  // ---- start-up.  A wave's vector loads complete in order, so waiting for
+  // a load issued after the first blocks' K/V loads would also wait for those
+  // bytes: every load the staging needs is issued first and the K/V loads
+  // last.  The first blocks' table entries come through the scalar cache
+  // (wave-uniform addresses; nothing in this launch writes the table), which
+  // the K/V issue waits for on a counter of its own.
+  int tb[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
-    int tb = -1, mt = 0;
-    if (s + d * S < len) block_info(B0 + s + d * S, tb, mt);
-    issue(R[d], wave_uniform(tb));
+    tb[d] = -1;
+    const int p = s + d * S;
+    if (p < len) {
+      const int pb = B0 + p;
+      const int ri = (pb >= RW.s1) + (pb >= RW.s2) + (pb >= RW.s3);
+      const int j = wave_uniform(pb - RW.start(ri));
+      const int slot = wave_uniform(RW.slot(ri));
+      if (slot >= 0 && j < a.max_blocks && j * kBlock < RW.len(ri) - (FUSED ? 1 : 0)) {
+        const int blk = bt_const[(int64_t)slot * a.bt_stride + j];
+        tb[d] = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+      }
+    }
   }
-  // the first window's table slice is requested next (written to LDS after
-  // the staging below): thread t, block t
+  // the first window's table slice: thread t, block t (written to LDS below)
   int tab = -1, meta = 0;
   if (tid < min(kWin, len)) block_info(B0 + tid, tab, meta);
 
+  // queries of the share's rows, one 8-dim chunk per thread (with the chunk
+  // holding their RoPE partners and the position's table row when fused)
+  const bool q_thread = tid < nrows * a.n_q * 8;
+  const int qi = tid / (a.n_q * 8);
+  const int qrem = tid - qi * a.n_q * 8;
+  const int qch = qrem & 7;
+  uint4 qv = make_uint4(0, 0, 0, 0), qp = qv;
+  float4 qt[4];
+  bool q_rot = false;
+  if (q_thread) {
+    const uint16_t* qrow = a.q + ((int64_t)(bf + qi) * a.n_q + (qrem >> 3)) * kHeadDim;
+    qv = *reinterpret_cast<const uint4*>(qrow + qch * 8);
+    if constexpr (FUSED) {
+      const int pos = RW.len(qi) - 1;
+      if (pos >= 0 && pos < a.max_pos) {
+        q_rot = true;
+        qp = *reinterpret_cast<const uint4*>(qrow + (qch ^ 4) * 8);
+        const float4* tr = reinterpret_cast<const float4*>(a.rope + ((int64_t)pos * (kHeadDim / 2) + (qch & 3) * 8) * 2);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) qt[t] = tr[t];
+      }
+    }
+  }
+  // fused: the new token of every row whose last block is here (rotated key
+  // and value go to LDS and join the attention from there; the pool write
+  // waits for the end of the workgroup's stream, no workgroup reads that pool
+  // row in this launch).  nrows * n_kv * 8 <= kThreads: one chunk per thread.
+  const int ni = tid / (n_kv * 8);
+  const int nrem = tid - ni * n_kv * 8;
+  const int nch = nrem & 7;
+  bool n_thread = false, n_rot = false;
+  uint4 nk = make_uint4(0, 0, 0, 0), nv = nk, np = nk;
+  float4 nt[4];
+  int napp = -1;
+  if constexpr (FUSED) {
+    if (tid < nrows * n_kv * 8) {
+      const int b = bf + ni;
+      const int n = RW.len(ni);
+      const int last = RW.end(ni) - 1;
+      if (n > 0 && last >= B0 && last < B1) {
+        n_thread = true;
+        const int pos = n - 1;
+        const uint16_t* krow = a.k_new + ((int64_t)b * n_kv + (nrem >> 3)) * kHeadDim;
+        nk = *reinterpret_cast<const uint4*>(krow + nch * 8);
+        nv = *reinterpret_cast<const uint4*>(a.v_new + ((int64_t)b * n_kv + (nrem >> 3)) * kHeadDim + nch * 8);
+        const int slot = RW.slot(ni);
+        if (nrem == 0 && slot >= 0 && pos / kBlock < a.max_blocks)
+          napp = a.bt[(int64_t)slot * a.bt_stride + pos / kBlock];
+        if (pos < a.max_pos) {
+          n_rot = true;
+          np = *reinterpret_cast<const uint4*>(krow + (nch ^ 4) * 8);
+          const float4* tr = reinterpret_cast<const float4*>(a.rope + ((int64_t)pos * (kHeadDim / 2) + (nch & 3) * 8) * 2);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) nt[t] = tr[t];
+        }
+      }
+    }
+  }
+  // ---- the first blocks' K/V ----------------------------------------------
+  KVRegs R[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) issue(R[d], wave_uniform(tb[d]));
+
+  // ---- staging (its waits cover the loads above, not the K/V loads) ---------
+  if (q_thread) sq[qi][qrem] = q_rot ? rope_own_chunk(qv, qp, qt, qch & 4) : qv;
+  if constexpr (FUSED) {
+    if (tid < nrows) srow_ok[tid] = RW.slot(tid) >= 0;
+    if (n_thread) {
+      if (nrem == 0) s_app[ni] = napp;
+      snew[ni][0][nrem] = n_rot ? rope_own_chunk(nk, np, nt, nch & 4) : nk;
+      snew[ni][1][nrem] = nv;
+    }
+  }
+  if (tid < min(kWin, len)) {
+    s_tab[tid] = block_ok(tab);
+    s_meta[tid] = meta;
+  }
+  __syncthreads();
+
   // ---- chained launches: the previous launch's rows cut by share ends, one
-  // (row, query head) pair per 64 threads (pairs grid x 16 apart: a small grid
-  // takes several) -----------------------------------------------------------------
+  // (row, query head) pair per wave, pairs grid x 16 apart (a small grid
+  // takes several).  After the staging, so that its registers and its wait
+  // (which covers the first K/V loads, issued before it) overlap nothing
+  // that the staging needs.
   if constexpr (PREV) {
     const int pairs = a.batch * a.n_q;
     for (int pp = blockIdx.x + P.grid * w; pp < pairs; pp += P.grid * kWaves) {
@@ -447,64 +583,6 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
       prev_finish(a, pm);
     }
   }
-
-  // ---- queries of the share's rows (rotated by position n - 1 when fused),
-  // one 8-dim chunk per thread ---------------------------------------------------
-  if (tid < nrows * a.n_q * 8) {
-    const int qi = tid / (a.n_q * 8);
-    const int qrem = tid - qi * a.n_q * 8;
-    const int qch = qrem & 7;
-    const uint16_t* qrow = a.q + ((int64_t)(bf + qi) * a.n_q + (qrem >> 3)) * kHeadDim;
-    uint4 qv = *reinterpret_cast<const uint4*>(qrow + qch * 8);
-    if constexpr (FUSED) {
-      const int pos = P.row_n[bf + qi] - 1;
-      if (pos >= 0 && pos < a.max_pos) {
-        const uint4 qp = *reinterpret_cast<const uint4*>(qrow + (qch ^ 4) * 8);
-        const float4* tr = reinterpret_cast<const float4*>(a.rope + ((int64_t)pos * (kHeadDim / 2) + (qch & 3) * 8) * 2);
-        const float4 qt[4] = {tr[0], tr[1], tr[2], tr[3]};
-        qv = rope_own_chunk(qv, qp, qt, qch & 4);
-      }
-    }
-    sq[qi][qrem] = qv;
-  }
-  // ---- fused: the new token of every row whose last block is here: rotated
-  // key and value into LDS (it joins the attention from there).  Its pool
-  // write waits for the end of the workgroup's stream (no workgroup reads that
-  // pool row in this launch), which keeps the table lookup for it off the
-  // start-up path.  nrows * n_kv * 8 <= kThreads: one 8-dim chunk per thread.
-  const int ni = tid / (n_kv * 8);
-  const int nrem = tid - ni * n_kv * 8;
-  if constexpr (FUSED) {
-    if (tid < nrows) srow_ok[tid] = row_slot(a, P, bf + tid) >= 0;
-    if (tid < nrows * n_kv * 8) {
-      const int ch = nrem & 7;
-      const int b = bf + ni;
-      const int n = P.row_n[b];
-      const int last = P.row_start[b + 1] - 1;
-      if (n > 0 && last >= B0 && last < B1) {
-        const int pos = n - 1;
-        const uint16_t* krow = a.k_new + ((int64_t)b * n_kv + (nrem >> 3)) * kHeadDim;
-        uint4 nk = *reinterpret_cast<const uint4*>(krow + ch * 8);
-        const uint4 nv = *reinterpret_cast<const uint4*>(a.v_new + ((int64_t)b * n_kv + (nrem >> 3)) * kHeadDim + ch * 8);
-        const int slot = row_slot(a, P, b);
-        if (nrem == 0)
-          s_app[ni] = slot >= 0 && pos / kBlock < a.max_blocks ? a.bt[(int64_t)slot * a.bt_stride + pos / kBlock] : -1;
-        if (pos < a.max_pos) {
-          const uint4 np = *reinterpret_cast<const uint4*>(krow + (ch ^ 4) * 8);
-          const float4* tr = reinterpret_cast<const float4*>(a.rope + ((int64_t)pos * (kHeadDim / 2) + (ch & 3) * 8) * 2);
-          const float4 nt[4] = {tr[0], tr[1], tr[2], tr[3]};
-          nk = rope_own_chunk(nk, np, nt, ch & 4);
-        }
-        snew[ni][0][nrem] = nk;
-        snew[ni][1][nrem] = nv;
-      }
-    }
-  }
-  if (tid < min(kWin, len)) {
-    s_tab[tid] = tab;
-    s_meta[tid] = meta;
-  }
-  __syncthreads();
 
   MfmaAcc acc;
   acc.reset();
@@ -520,7 +598,7 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
     qb1 = col < G ? sq[cur][(h * G + col) * 8 + q4 + 4] : z;
     if constexpr (FUSED) {
       const int b = bf + cur;
-      row_last = wave_uniform(P.row_n[b] > 0 && srow_ok[cur] ? P.row_start[b + 1] - 1 : -1);
+      row_last = wave_uniform(RW.len(cur) > 0 && srow_ok[cur] ? RW.end(cur) - 1 : -1);
     }
   };
   load_q();
@@ -557,7 +635,7 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
       __syncthreads();                   // every wave is done with the previous window
       if (tid < wl) {
         block_info(B0 + w0 + tid, tab, meta);
-        s_tab[tid] = tab;
+        s_tab[tid] = block_ok(tab);
         s_meta[tid] = meta;
       }
       __syncthreads();
@@ -606,9 +684,8 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
   if constexpr (FUSED) {
     // the new token into the pool (position context_len - 1 of its row)
     if (tid < nrows * n_kv * 8) {
-      const int b = bf + ni;
-      const int n = P.row_n[b];
-      const int last = P.row_start[b + 1] - 1;
+      const int n = RW.len(ni);
+      const int last = RW.end(ni) - 1;
       const int blk = n > 0 && last >= B0 && last < B1 ? s_app[ni] : -1;
       if (blk >= 0 && blk < a.num_blocks) {
         const int pos = n - 1;
@@ -628,7 +705,7 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
     const int i = e / (a.n_q * 8);
     const int rem = e - i * a.n_q * 8;
     const int b = bf + i;
-    if (P.row_n[b] <= 0) continue;
+    if (RW.len(i) <= 0) continue;
     const int qh = rem >> 3;
     const int c8 = rem & 7;
     const int hh = qh / G;
@@ -652,7 +729,7 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
       O[6] += f * o1.z;
       O[7] += f * o1.w;
     }
-    if (P.row_start[b] >= B0 && P.row_start[b + 1] <= B1) {
+    if (RW.start(i) >= B0 && RW.end(i) <= B1) {
       uint4 v;
       v.x = pack_bf16x2(L > 0.f ? O[0] / L : 0.f, L > 0.f ? O[1] / L : 0.f);
       v.y = pack_bf16x2(L > 0.f ? O[2] / L : 0.f, L > 0.f ? O[3] / L : 0.f);
@@ -665,6 +742,16 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
       reinterpret_cast<float4*>(dst + 8 * c8)[0] = make_float4(O[0], O[1], O[2], O[3]);
       reinterpret_cast<float4*>(dst + 8 * c8)[1] = make_float4(O[4], O[5], O[6], O[7]);
       if (c8 == 0) *reinterpret_cast<float2*>(dst + kHeadDim) = make_float2(M, L);
+    }
+  }
+  if constexpr (!DEVPLAN) {
+    // the plan for later launches that read it from device memory (last, so
+    // that no global store precedes the start-up loads)
+    if (a.plan_out != nullptr && blockIdx.x == 0) {
+      constexpr int kWords = (int)(sizeof(StreamPlan) / 4);
+      static_assert(kWords <= kThreads, "one word per thread");
+      if (tid < kWords)
+        reinterpret_cast<uint32_t*>(a.plan_out)[tid] = reinterpret_cast<const uint32_t*>(&a.plan)[tid];
     }
   }
 }
