@@ -570,20 +570,6 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
   }
   __syncthreads();
 
-  // ---- chained launches: the previous launch's rows cut by share ends, one
-  // (row, query head) pair per wave, pairs grid x 16 apart (a small grid
-  // takes several).  After the staging, so that its registers and its wait
-  // (which covers the first K/V loads, issued before it) overlap nothing
-  // that the staging needs.
-  if constexpr (PREV) {
-    const int pairs = a.batch * a.n_q;
-    for (int pp = blockIdx.x + P.grid * w; pp < pairs; pp += P.grid * kWaves) {
-      PrevMerge pm;
-      prev_load(a, P, pp / a.n_q, pp % a.n_q, lane, pm);
-      prev_finish(a, pm);
-    }
-  }
-
   MfmaAcc acc;
   acc.reset();
   const int col = lane & 15;             // MFMA column: query head of the KV head's group
@@ -681,6 +667,18 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
     }
   }
   while (cur < nrows) flush();
+  // ---- chained launches: the previous launch's rows cut by share ends, one
+  // (row, query head) pair per wave, pairs grid x 16 apart (a small grid
+  // takes several).  At the end of the wave's stream: the oldest waves, which
+  // get the pairs and finish first, do it while the others still stream.
+  if constexpr (PREV) {
+    const int pairs = a.batch * a.n_q;
+    for (int pp = blockIdx.x + P.grid * w; pp < pairs; pp += P.grid * kWaves) {
+      PrevMerge pm;
+      prev_load(a, P, pp / a.n_q, pp % a.n_q, lane, pm);
+      prev_finish(a, pm);
+    }
+  }
   if constexpr (FUSED) {
     // the new token into the pool (position context_len - 1 of its row)
     if (tid < nrows * n_kv * 8) {
