@@ -126,6 +126,34 @@ int pkv_paged_gather(pkv_bf16* k_dense, pkv_bf16* v_dense, const pkv_bf16* k_poo
                      int64_t bt_row_stride, int max_blocks_per_seq, int slot, int context_len,
                      int n_kv_heads, int head_dim, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * Device error flags.  Source: "The path of one inference", step (4) (table
+ * entries are -1 until a block is assigned; a context must not reach one).
+ * The kernels never read outside the pool or the table whatever the device
+ * data say: a bad entry is skipped (its tokens count as absent).  They also
+ * set a bit in a flag word the library keeps on each device, so that such
+ * input is reported rather than silently masked:
+ *   PKV_DEVERR_BAD_BLOCK     decode: a table entry inside a context (or the
+ *                            new token's entry in the fused step) is -1 or
+ *                            not below num_blocks
+ *   PKV_DEVERR_BAD_SLOT      decode / prefill: a row's table slot (slot_ids)
+ *                            is outside [0, num_slots)
+ *   PKV_DEVERR_LONG_CONTEXT  decode: a device context length exceeds
+ *                            max_blocks_per_seq x 16 (the rest is not read)
+ *   PKV_DEVERR_PREFILL_BLOCK prefill: a table entry a query's keys need is -1
+ *                            or not below num_blocks
+ * pkv_device_errors copies the current device's word to *flags (host) after
+ * the work enqueued on `stream` so far, optionally clears it (clear != 0),
+ * and waits for the stream.  The word accumulates over calls until cleared;
+ * calls on several streams of one device share it.
+ * ------------------------------------------------------------------------ */
+#define PKV_DEVERR_BAD_BLOCK 1u
+#define PKV_DEVERR_BAD_SLOT 2u
+#define PKV_DEVERR_LONG_CONTEXT 4u
+#define PKV_DEVERR_PREFILL_BLOCK 8u
+
+int pkv_device_errors(uint32_t* flags, int clear, void* stream);
+
 /* Diagnostic, off the attention path: read `bytes` bytes of device memory
  * (16-byte aligned, bytes a multiple of 16) once with wide loads spread over
  * the whole chip, as a reference for the HBM read rate the decode kernels are

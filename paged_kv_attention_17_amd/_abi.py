@@ -46,6 +46,7 @@ SIGNATURES = {
     "pkv_paged_gather": (_i, [_p, _p, _p, _p, _i, _p, _i64, _i, _i, _i, _i, _i, _p]),
     "pkv_hbm_read_probe": (_i, [_p, _sz, _p, _p]),
     "pkv_paged_read_probe": (_i, [_p, _p, _i, _p, _i64, _i, _i, _p, _p, _i, _i, _i, _p, _p]),
+    "pkv_device_errors": (_i, [C.POINTER(C.c_uint32), _i, _p]),
     "pkv_blocks_assign": (_i, [_p, _i64, _i, _i, _p, _ip, _p, _p, _i, _p, _p, _ip]),
     "pkv_blocks_release": (_i, [_p, _i64, _i, _i, _i, _p, _ip, _i, _p, _p, _ip]),
     "pkv_block_table_patch": (_i, [_p, _i64, _p, _p, _i, _p]),
@@ -291,6 +292,17 @@ def pkv_hbm_read_probe(buf, sink, stream=None):
     _contig(buf, "buf")
     _check("pkv_hbm_read_probe", load().pkv_hbm_read_probe(
         _dev_ptr(buf, "buf"), buf.numel() * buf.element_size(), _dev_ptr(sink, "sink"), _stream(stream)))
+
+
+PKV_DEVERR_BAD_BLOCK, PKV_DEVERR_BAD_SLOT, PKV_DEVERR_LONG_CONTEXT, PKV_DEVERR_PREFILL_BLOCK = 1, 2, 4, 8
+
+
+def pkv_device_errors(clear=True, stream=None):
+    """The current device's error flags (PKV_DEVERR_* bits) after the work
+    enqueued on `stream` so far; cleared unless clear=False."""
+    flags = C.c_uint32(0)
+    _check("pkv_device_errors", load().pkv_device_errors(C.byref(flags), 1 if clear else 0, _stream(stream)))
+    return flags.value
 
 
 def pkv_paged_read_probe(k_pool, v_pool, block_table, slot_ids, row_lens_host, sink, stream=None):

@@ -33,6 +33,11 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
   return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
 }
 
+// Set bit `bit` of the device error flags (see errors.hip); f may be null.
+__device__ __forceinline__ void report_error(uint32_t* f, uint32_t bit) {
+  if (f) __hip_atomic_fetch_or(f, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Two-term bf16 dot product accumulated in float32: a.lo*b.lo + a.hi*b.hi + c.
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
@@ -101,6 +106,9 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 inline int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+// The device error flags' address on the current device (errors.hip), or null.
+uint32_t* device_errors_ptr();
 
 inline bool ratio_supported(int n_q, int n_kv) {
   if (n_q <= 0 || n_kv <= 0 || n_q % n_kv) return false;

@@ -63,6 +63,7 @@ struct DecodeArgs {
   const float2* rope;          // fused: cos/sin table [max_pos][32]
   float* ws_o;                 // [B][n_kv][P][G][64] unnormalised partial outputs
   float* ws_ml;                // [B][n_kv][P][G][2]  partial (max, sum)
+  uint32_t* errors;            // device error flags (errors.hip), or null
   int64_t bt_stride;
   int num_blocks;
   int num_slots;
@@ -105,6 +106,7 @@ struct Item {
 // max_context_len implies (items past a sequence's length exit at once); with
 // one, only real partitions are launched, longest first.
 __device__ __forceinline__ int clip_len(const DecodeArgs& a, int n) {
+  if (n > a.max_blocks * kBlock && threadIdx.x == 0) report_error(a.errors, PKV_DEVERR_LONG_CONTEXT);
   return n < 0 ? 0 : (n > a.max_blocks * kBlock ? a.max_blocks * kBlock : n);
 }
 
@@ -113,6 +115,7 @@ __device__ __forceinline__ int clip_len(const DecodeArgs& a, int n) {
 __device__ __forceinline__ void row_extent(const DecodeArgs& a, int b, int& slot, int& n, int& nparts, int& ps) {
   slot = a.slot_ids ? a.slot_ids[b] : b;
   const bool slot_ok = slot >= 0 && slot < a.num_slots && a.num_blocks > 0;
+  if (!(slot >= 0 && slot < a.num_slots) && threadIdx.x == 0) report_error(a.errors, PKV_DEVERR_BAD_SLOT);
   slot = slot_ok ? slot : 0;
   if (a.plan_seqs > 0) {
     n = slot_ok ? a.plan_n[b] : 0;
@@ -221,6 +224,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
   for (int cb = 0; cb < nb; cb += kWave) {
     const int ncb = min(kWave, nb - cb);
     int tab = btrow[jb_begin + cb + min(lane, ncb - 1)];
+    if (lane < ncb && !(tab >= 0 && tab < a.num_blocks)) report_error(a.errors, PKV_DEVERR_BAD_BLOCK);
     tab = (tab >= 0 && tab < a.num_blocks && lane < ncb) ? tab : -1;
     if (w >= ncb) continue;
 
@@ -319,6 +323,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
     // each); no workgroup reads this row during the call.
     if (part == nparts - 1 && n > 0 && tid < 8) {
       const int blk = btrow[pos_new / kBlock];
+      if (!(blk >= 0 && blk < a.num_blocks)) report_error(a.errors, PKV_DEVERR_BAD_BLOCK);
       if (blk >= 0 && blk < a.num_blocks) {
         const int64_t off = ((int64_t)blk * kBlock + pos_new % kBlock) * row_elems + kvh * kHeadDim + tid * 8;
         *reinterpret_cast<uint4*>(a.k_pool + off) = knew;
@@ -557,6 +562,7 @@ static DecodeArgs base_args(const DecodeCall& c) {
   a.n_q = c.n_q_heads;
   a.n_kv = c.n_kv_heads;
   a.scale_log2e = c.scale * kLog2e;
+  a.errors = device_errors_ptr();
   return a;
 }
 

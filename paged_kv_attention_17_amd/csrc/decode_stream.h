@@ -55,6 +55,7 @@ struct StreamCore {
   float scale_log2e;
   const StreamPlan* plan_dev;  // device-plan launches: the plan in device memory
   StreamPlan* plan_out;        // argument-plan launches: workgroup 0 also stores the plan here
+  uint32_t* errors;            // device error flags (errors.hip), or null
 };
 struct StreamArgs : StreamCore {
   StreamPlan plan;             // argument-plan launches: the plan itself

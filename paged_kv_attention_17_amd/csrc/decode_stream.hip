@@ -440,7 +440,7 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
   // (row << 8 | tokens to read from the pool; the fused step's new token is
   // not among them)
   auto block_ok = [&](int blk) { return (blk >= 0 && blk < a.num_blocks) ? blk : -1; };
-  auto block_info = [&](int p, int& tab, int& meta) {
+  auto block_info = [&](int p, int& tab, int& meta, uint32_t& err) {
     const int ri = (p >= RW.s1) + (p >= RW.s2) + (p >= RW.s3);
     const int start = RW.start(ri);
     const int n = RW.len(ri);
@@ -451,6 +451,8 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
     tab = -1;
     if (slot >= 0 && j < a.max_blocks && valid > 0) tab = a.bt[(int64_t)slot * a.bt_stride + j];
     meta = (ri << 8) | valid;
+    // what to report if the block has tokens to read and no valid entry
+    err = slot < 0 ? PKV_DEVERR_BAD_SLOT : (j >= a.max_blocks ? PKV_DEVERR_LONG_CONTEXT : PKV_DEVERR_BAD_BLOCK);
   };
   // Loads of one block for this wave's KV head.  blk < 0 reads nothing (a
   // zero-size buffer returns zeros without a memory access).
@@ -489,7 +491,8 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
   }
   // the first window's table slice: thread t, block t (written to LDS below)
   int tab = -1, meta = 0;
-  if (tid < min(kWin, len)) block_info(B0 + tid, tab, meta);
+  uint32_t tab_err = 0;
+  if (tid < min(kWin, len)) block_info(B0 + tid, tab, meta, tab_err);
 
   // queries of the share's rows, one 8-dim chunk per thread (with the chunk
   // holding their RoPE partners and the position's table row when fused)
@@ -567,6 +570,7 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
   if (tid < min(kWin, len)) {
     s_tab[tid] = block_ok(tab);
     s_meta[tid] = meta;
+    if ((meta & 0xff) && block_ok(tab) < 0) report_error(a.errors, tab_err);
   }
   __syncthreads();
 
@@ -620,9 +624,10 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
     if (w0 > 0) {
       __syncthreads();                   // every wave is done with the previous window
       if (tid < wl) {
-        block_info(B0 + w0 + tid, tab, meta);
+        block_info(B0 + w0 + tid, tab, meta, tab_err);
         s_tab[tid] = block_ok(tab);
         s_meta[tid] = meta;
+        if ((meta & 0xff) && block_ok(tab) < 0) report_error(a.errors, tab_err);
       }
       __syncthreads();
 #pragma unroll
@@ -684,7 +689,9 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
     if (tid < nrows * n_kv * 8) {
       const int n = RW.len(ni);
       const int last = RW.end(ni) - 1;
-      const int blk = n > 0 && last >= B0 && last < B1 ? s_app[ni] : -1;
+      const bool here = n > 0 && last >= B0 && last < B1;
+      const int blk = here ? s_app[ni] : -1;
+      if (here && RW.slot(ni) >= 0 && !(blk >= 0 && blk < a.num_blocks)) report_error(a.errors, PKV_DEVERR_BAD_BLOCK);
       if (blk >= 0 && blk < a.num_blocks) {
         const int pos = n - 1;
         const int64_t off =
@@ -1058,6 +1065,7 @@ int stream_prepare(bool fused, const StreamCall& c, StreamLaunch* L) {
   a.max_pos = c.max_pos;
   a.batch = c.batch;
   a.scale_log2e = c.scale * kLog2e;
+  a.errors = device_errors_ptr();
   int merge = 0;
   const int pr = stream_plan_build(c.batch, c.row_lens_host, c.max_blocks, c.slot_ids_host, c.slot_ids != nullptr,
                                    c.num_slots, c.chain_plan, &a.plan, &merge);

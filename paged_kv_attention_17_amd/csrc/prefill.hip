@@ -82,6 +82,7 @@ struct PrefillArgs {
   int q_tiles;        // query tiles per sequence in the grid (fallback order)
   int total_q;
   float scale_log2e;
+  uint32_t* errors;   // device error flags (errors.hip), or null
   int n_items;        // > 0: the grid is n_items x n_kv workgroups taking items[id / n_kv]
   uint32_t items[kPfMaxItems];   // (sequence << 12 | query tile), most key tiles first
 };
@@ -152,7 +153,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
   const int q_len = a.cu_q[seq + 1] - q0;
   if (q0 < 0 || q_len <= 0 || q0 + q_len > a.total_q || tile * kQTile >= q_len) return;
   const int slot = a.slot_ids ? a.slot_ids[seq] : seq;
-  if (slot < 0 || slot >= a.num_slots) return;
+  if (slot < 0 || slot >= a.num_slots) {
+    if (threadIdx.x == 0) report_error(a.errors, PKV_DEVERR_BAD_SLOT);
+    return;
+  }
   const int start = a.q_start[seq];
   const int tok0 = tile * kQTile;                        // first query token of the tile (chunk-relative)
   const int n_q_tile = min(kQTile, q_len - tok0);
@@ -212,6 +216,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
     if (kt - tb >= kWave) load_table(kt);
     const int blk = __builtin_amdgcn_readlane(tabv, kt - tb);
     const bool ok = blk >= 0 && blk < a.num_blocks;
+    if (!ok && kt * kKTile + 8 * w < n_keys && lane == 0) report_error(a.errors, PKV_DEVERR_PREFILL_BLOCK);
     const int key = kt * kKTile + 8 * w + (lane >> 3);
     const uint32_t past = key < n_keys ? 0u : 0x80000000u;
     const int64_t boff = (int64_t)(ok ? blk : 0) * block_bytes;
@@ -410,6 +415,7 @@ extern "C" int pkv_paged_attn_prefill(pkv_bf16* out, const pkv_bf16* q, const in
   a.q_tiles = (max_q_len + pf_qtile(G) - 1) / pf_qtile(G);
   a.total_q = total_q;
   a.scale_log2e = scale * 1.4426950408889634f;
+  a.errors = device_errors_ptr();
   const void* fn = G == 1 ? (const void*)prefill_kernel<1>
                  : G == 2 ? (const void*)prefill_kernel<2>
                  : G == 4 ? (const void*)prefill_kernel<4>

@@ -350,6 +350,10 @@ def test_paged_read_probe_argument_errors(lib):
     assert call(batch=3) == E.PKV_ERR_INVALID_ARG      # more rows than the table without slot ids
 
 
+def test_device_errors_argument_errors(lib):
+    assert lib.pkv_device_errors(None, 0, None) == _abi.PKV_ERR_NULL
+
+
 def test_read_probe_argument_errors(lib):
     E = _abi
     assert lib.pkv_hbm_read_probe(None, 0, None, None) == E.PKV_OK
