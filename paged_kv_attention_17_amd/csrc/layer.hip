@@ -16,10 +16,11 @@
 // matrix x skinny-matrix products bound by reading the weights once: one
 // workgroup per 64 output features and all 64 rows, so each weight byte is
 // fetched once and the activations (at most 64 x K, resident in L2) once per
-// 64 features; K is split over the workgroup's four waves and, where 64-wide
-// feature tiles alone would leave the chip's 256 CUs idle, over workgroups
-// too, whose float32 partials a second kernel sums in a fixed order (no
-// atomics: the result does not depend on scheduling).  Larger batches run
+// 64 features; each of the workgroup's four waves takes 16 of its features
+// along the workgroup's K range, and where 64-wide feature tiles alone would
+// leave the chip's 256 CUs idle K is split over workgroups, whose float32
+// partials a second kernel sums in a fixed order (no atomics: the result
+// does not depend on scheduling).  Larger batches run
 // the same kernel once per 64-row block (a second grid dimension; the weights
 // are then read once per row block), and a K or feature count that is not a
 // multiple of the tiles is masked, so every shape with K and the feature
