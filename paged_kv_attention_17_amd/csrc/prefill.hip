@@ -56,13 +56,22 @@ constexpr int kKTile = 64;            // keys per step (two 32-key MFMA blocks)
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kVsStride = kHeadDim;       // LDS row (bf16) of a V tile, rotated per key
-constexpr int kPfStages = 3;              // K/V tiles in flight per workgroup (LDS ring)
+#ifndef PKV_PF_STAGES
+#define PKV_PF_STAGES 2
+#endif
+constexpr int kPfStages = PKV_PF_STAGES;  // steps whose K/V tiles are in LDS at once (ring)
+constexpr int kPfDist = kPfStages - 1;    // steps requested ahead of the one computed
 constexpr float kPfTau = 8.0f;            // lazy rescale threshold, log2 units
 constexpr int kPfMaxItems = 768;          // host-ordered work items carried in the kernel arguments
 constexpr uint32_t kOnesBf16 = 0x3F803F80u;  // (1, 1) as a bf16 pair
 
-// Query tokens per workgroup for G query heads per KV head.
-__host__ __device__ constexpr int pf_qtile(int G) { return 32 * (kPfWaves / G); }
+// Key-tile parities: with G <= 4 the workgroup's waves are split in two
+// halves that take the even and the odd key tiles (two tiles per step), and
+// the halves' softmax states are merged at the end; with G = 8 every wave is
+// one query head and there is one parity.
+__host__ __device__ constexpr int pf_parities(int G) { return G <= 4 ? 2 : 1; }
+// Query tokens per workgroup for G query heads per KV head (32 per wave).
+__host__ __device__ constexpr int pf_qtile(int G) { return 32 * (kPfWaves / (G * pf_parities(G))); }
 
 struct PrefillArgs {
   uint16_t* out;
@@ -119,9 +128,16 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
 // Written as assembly so that the compiler neither tracks nor waits for these
 // loads: the kernel waits for them itself (s_waitcnt vmcnt, then a barrier).
 __device__ __forceinline__ void lds_dma16(v4u rsrc, uint32_t voff, uint32_t lds) {
+  // the descriptor and the LDS address are wave-uniform; read them as such so
+  // that they sit in scalar registers whatever the compiler inferred
+  const v4u r = {(unsigned)__builtin_amdgcn_readfirstlane((int)rsrc[0]),
+                 (unsigned)__builtin_amdgcn_readfirstlane((int)rsrc[1]),
+                 (unsigned)__builtin_amdgcn_readfirstlane((int)rsrc[2]),
+                 (unsigned)__builtin_amdgcn_readfirstlane((int)rsrc[3])};
+  const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
   __asm__ volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                    :
-                   : "v"(voff), "s"(rsrc), "s"(lds)
+                   : "v"(voff), "s"(r), "s"(l)
                    : "memory", "m0");
 }
 
@@ -168,16 +184,22 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
   const int32_t* btrow = a.bt + (int64_t)slot * a.bt_stride;
   const int64_t row_elems = (int64_t)a.n_kv * kHeadDim;
 
-  // Three stages of one 64-key K tile and one V tile (8 KB each), filled by
-  // buffer loads that write LDS directly: slot s (16 bytes) of K row `key`
-  // holds dims 8 (s ^ (key & 7)) .. + 7, slot s of V row `key` holds dims
-  // 8 ((s - 2 (key & 3)) & 7) .. + 7 (V element (key, d) sits at
-  // vs_index(key, d)); both keep the MFMA-operand reads conflict-free.
-  __shared__ __attribute__((aligned(16))) uint16_t kvs[kPfStages][2][kKTile * kHeadDim];
+  // kPfStages ring slots, each holding a step's kPar 64-key tiles of K and V
+  // (8 KB each), filled by buffer loads that write LDS directly: slot s (16
+  // bytes) of K row `key` holds dims 8 (s ^ (key & 7)) .. + 7, slot s of V
+  // row `key` holds dims 8 ((s - 2 (key & 3)) & 7) .. + 7 (V element
+  // (key, d) sits at vs_index(key, d)); both keep the MFMA-operand reads
+  // conflict-free.  After the loop the ring holds the odd parity's softmax
+  // states for the merge.
+  constexpr int kPar = pf_parities(G);
+  constexpr int kSub = kPfWaves / (G * kPar);           // query subtiles per workgroup
+  __shared__ __attribute__((aligned(16))) uint16_t kvs[kPfStages][kPar][2][kKTile * kHeadDim];
 
-  // This wave: head hh of the group, query subtile sub; this lane: one query.
+  // This wave: head hh of the group, query subtile sub, key-tile parity par
+  // (tiles kt with kt % kPar == par); this lane: one query.
   const int hh = w % G;
-  const int sub = w / G;
+  const int sub = (w / G) % kSub;
+  const int par = w / (G * kSub);
   const int h = g * G + hh;
   const int sub0 = tok0 + sub * 32;                // first query of the subtile (chunk-relative)
   const int my_q = sub0 + col;
@@ -186,12 +208,13 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
   const int sub_last_pos = start + min(sub0 + 31, tok0 + n_q_tile - 1);   // wave-uniform
   const bool sub_live = sub0 < tok0 + n_q_tile;
   const int sub_key_end = min(sub_last_pos + 1, n_keys);                  // keys this subtile sees
+  const int n_steps = (n_ktiles + kPar - 1) / kPar;
 
-  // Loader role: wave w brings keys 8 w .. 8 w + 7 of every tile (half of one
-  // 16-token block), lane i key 8 w + i / 8 into LDS slot i % 8.  Keys past
-  // the cache, and blocks whose id is out of range, read as zeros (offsets
-  // beyond the buffer's size), so no NaN from an unused pool slot reaches a
-  // product.
+  // Loader role: wave w brings keys 8 w .. 8 w + 7 of each of the step's
+  // tiles (half of one 16-token block), lane i key 8 w + i / 8 into LDS slot
+  // i % 8.  Keys past the cache, and blocks whose id is out of range, read as
+  // zeros (offsets beyond the buffer's size), so no NaN from an unused pool
+  // slot reaches a product.
   const int ld_row = 8 * (w & 1) + (lane >> 3);              // row inside the block
   const int ld_kx = (lane >> 3) & 7;                         // key & 7
   const uint32_t block_bytes = (uint32_t)(kBlock * row_elems * 2);
@@ -211,19 +234,26 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
     // path every tile takes
     __builtin_amdgcn_s_waitcnt(0x0F70);
   };
-  const uint32_t lds_base = lds_addr(&kvs[0][0][8 * w * kHeadDim]);   // this wave's rows, stage 0
-  auto issue = [&](int kt, int stage) {
-    if (kt - tb >= kWave) load_table(kt);
-    const int blk = __builtin_amdgcn_readlane(tabv, kt - tb);
-    const bool ok = blk >= 0 && blk < a.num_blocks;
-    if (!ok && kt * kKTile + 8 * w < n_keys && lane == 0) report_error(a.errors, PKV_DEVERR_PREFILL_BLOCK);
-    const int key = kt * kKTile + 8 * w + (lane >> 3);
-    const uint32_t past = key < n_keys ? 0u : 0x80000000u;
-    const int64_t boff = (int64_t)(ok ? blk : 0) * block_bytes;
-    const uint32_t nrec = ok ? block_bytes : 0u;
-    const uint32_t dst = lds_base + (uint32_t)stage * (2 * kKTile * kHeadDim * 2);
-    lds_dma16(rsrc_words(kpool + boff, nrec), ld_koff | past, dst);
-    lds_dma16(rsrc_words(vpool + boff, nrec), ld_voff | past, dst + kKTile * kHeadDim * 2);
+  const uint32_t lds_base = lds_addr(&kvs[0][0][0][8 * w * kHeadDim]);   // this wave's rows, slot 0
+  constexpr uint32_t kTileBytes = kKTile * kHeadDim * 2;
+  // the step's tiles kt = kPar * step + p (a tile past the last reads zeros)
+  auto issue = [&](int step, int slot_) {
+#pragma unroll
+    for (int p = 0; p < kPar; ++p) {
+      const int kt = kPar * step + p;
+      if (kt - tb >= kWave) load_table(kt);
+      const int blk = __builtin_amdgcn_readlane(tabv, kt - tb);
+      const bool ok = blk >= 0 && blk < a.num_blocks;
+      if (!ok && kt < n_ktiles && kt * kKTile + 8 * w < n_keys && lane == 0)
+        report_error(a.errors, PKV_DEVERR_PREFILL_BLOCK);
+      const int key = kt * kKTile + 8 * w + (lane >> 3);
+      const uint32_t past = key < n_keys ? 0u : 0x80000000u;
+      const int64_t boff = (int64_t)(ok ? blk : 0) * block_bytes;
+      const uint32_t nrec = ok ? block_bytes : 0u;
+      const uint32_t dst = lds_base + (uint32_t)((slot_ * kPar + p) * 2) * kTileBytes;
+      lds_dma16(rsrc_words(kpool + boff, nrec), ld_koff | past, dst);
+      lds_dma16(rsrc_words(vpool + boff, nrec), ld_voff | past, dst + kTileBytes);
+    }
   };
 
   // Q^T operand: 4 k-steps of 8 dims each.
@@ -254,27 +284,28 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
   const int k_base = col * kHeadDim + 8 * (half ^ (col & 1));
   const int kc = (col >> 1) & 3;
 
-  // Pipeline: tile kt + 2 is requested while tile kt is computed.  Each wave
-  // waits for its own loads of tile kt (two per tile, counted in order), then
-  // the barrier makes every wave's part visible and frees the stage that tile
-  // kt + 2 overwrites (its previous tile, kt - 1, is done everywhere).
+  // Pipeline: step s + kPfDist (kPar tiles) is requested while step s is
+  // computed.  Each wave waits for its own loads of step s (2 kPar per step,
+  // counted in order), then the barrier makes every wave's part visible and
+  // frees the slot that step s + kPfDist overwrites (its previous step,
+  // s - 1, is done everywhere).
   load_table(0);
-  issue(0, 0);
-  if (n_ktiles > 1) issue(1, 1);
-  int st = 0;                                      // stage of tile kt
-  for (int kt = 0; kt < n_ktiles; ++kt) {
-    const int kbase = kt * kKTile;
-    if (kt + 1 < n_ktiles)
-      __asm__ volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  for (int q = 0; q < kPfDist && q < n_steps; ++q) issue(q, q);
+  int st = 0;                                      // ring slot of step s
+  for (int step = 0; step < n_steps; ++step) {
+    if (kPfDist == 2 && step + 1 < n_steps)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kPar));   // vmcnt(2 kPar): step s + 1's loads may be in flight
     else
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
     __syncthreads();
-    if (kt + 2 < n_ktiles) issue(kt + 2, st == 0 ? 2 : st - 1);
-    const uint16_t* ks = kvs[st][0];
-    const uint16_t* vs = kvs[st][1];
+    if (step + kPfDist < n_steps) issue(step + kPfDist, (st + kPfDist) % kPfStages);
+    const int kt = kPar * step + par;
+    const uint16_t* ks = kvs[st][par][0];
+    const uint16_t* vs = kvs[st][par][1];
     st = st == kPfStages - 1 ? 0 : st + 1;
+    const int kbase = kt * kKTile;
 
-    if (sub_live && kbase < sub_key_end) {
+    if (kt < n_ktiles && sub_live && kbase < sub_key_end) {
       // S^T = K . Q^T for the tile's two 32-key halves (rows: keys, cols: queries)
       f32x16 s[2] = {};
 #pragma unroll
@@ -356,6 +387,35 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
     }
   }
   l += shfl_xor(l, 32);
+  if constexpr (kPar == 2) {
+    // merge the parities, the even one taking the odd one's state from LDS
+    // (the ring is free once every wave is past the loop): per lane m, l
+    // and the 32 accumulators, in a fixed order
+    __syncthreads();
+    float* xs = reinterpret_cast<float*>(&kvs[0][0][0][0]) + (w % (G * kSub)) * (34 * kWave);
+    if (par == 1) {
+      xs[lane] = m;
+      xs[kWave + lane] = l;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        xs[(2 + i) * kWave + lane] = o0[i];
+        xs[(18 + i) * kWave + lane] = o1[i];
+      }
+    }
+    __syncthreads();
+    if (par == 1) return;
+    const float m1 = xs[lane];
+    const float l1 = xs[kWave + lane];
+    const float mm = fmaxf(m, m1);
+    const float f0 = fast_exp2(m - mm);
+    const float f1 = fast_exp2(m1 - mm);
+    l = l * f0 + l1 * f1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      o0[i] = o0[i] * f0 + xs[(2 + i) * kWave + lane] * f1;
+      o1[i] = o1[i] * f0 + xs[(18 + i) * kWave + lane] * f1;
+    }
+  }
   if (!q_ok) return;
   // O^T accumulator i holds dim 8*(i/4) + 4*half + i%4 (+32 for o1) of this lane's query.
   const float inv = l > 0.f ? 1.f / l : 0.f;
