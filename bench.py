@@ -668,8 +668,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--partition-size", type=int, default=0)
-    ap.add_argument("--leg", choices=["prefill"], default=None,
-                    help="run one leg alone and print its JSON (for profiling it)")
+    ap.add_argument("--leg", choices=["prefill", "decode"], default=None,
+                    help="run one leg alone and print its JSON (for profiling it): prefill, or the "
+                         "decode step with its roofline, read probe and the plain copy used to scale counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -774,6 +775,16 @@ def main():
     log(f"streaming launch in the step: <= {t_attn * 1e6:.2f} us (step / {L}), {achieved:.0f} GB/s = "
         f"{achieved / HBM_PEAK_GBS:.1%} of peak; standalone fused call {t_call * 1e6:.2f} us "
         f"(16 back to back, p10 {np.percentile(durs, 10) * 1e6:.2f}, p90 {np.percentile(durs, 90) * 1e6:.2f})")
+
+    if args.leg == "decode":
+        copy_gbs = stream_copy_gbs(torch)
+        print(json.dumps({"metric": METRIC, "ms_per_step": round(t_step * 1e3, 4),
+                          "us_per_layer": round(t_step * 1e6 / L, 3), "value": round(value, 2), "unit": "GB/s",
+                          "roofline_us_per_launch": round(t_attn * 1e6, 3), "bytes_per_launch": bytes_per_launch,
+                          "standalone_call_us": round(t_call * 1e6, 3), "probe_us": round(t_probe * 1e6, 3),
+                          "copy_kernel_GBps": round(copy_gbs, 1), "source_hash": decode_source_hash()}),
+              flush=True)
+        return
 
     dl = decode_layer_leg(torch, np, pkv, eng, ctx_now, stream)
     bytes_layer = dl["weight_bytes_per_layer"] + dl["kv_bytes_per_layer"]
