@@ -82,6 +82,16 @@ __global__ __launch_bounds__(512) void patch_kernel(int32_t* __restrict__ bt, in
   if (i < n && pa.off[i] >= 0 && pa.off[i] < elems) bt[pa.off[i]] = pa.val[i];
 }
 
+// Two arrays in one launch: pairs [0, n_a) go to a, pairs [n_a, n) to b.
+__global__ __launch_bounds__(512) void patch2_kernel(int32_t* __restrict__ a, int64_t a_elems, int n_a,
+                                                     int32_t* __restrict__ b, int64_t b_elems, PatchArgs pa, int n) {
+  const int i = threadIdx.x;
+  if (i >= n) return;
+  int32_t* t = i < n_a ? a : b;
+  const int64_t el = i < n_a ? a_elems : b_elems;
+  if (pa.off[i] >= 0 && pa.off[i] < el) t[pa.off[i]] = pa.val[i];
+}
+
 // Write n (offset, value) pairs whose offsets are distinct: each launch takes
 // up to kPatchPerLaunch of them in its arguments, one thread per pair.
 int patch_distinct(int32_t* bt_dev, int64_t bt_elems, const int32_t* off, const int32_t* val, int n_patch,
@@ -100,6 +110,26 @@ int patch_distinct(int32_t* bt_dev, int64_t bt_elems, const int32_t* off, const 
     if (st != PKV_OK) return st;
   }
   return PKV_OK;
+}
+
+// Distinct (offset, value) pairs into two arrays: when both lists fit one
+// launch's arguments they go in one launch, else one launch per list.
+int patch_two(int32_t* a, int64_t a_elems, const int32_t* a_off, const int32_t* a_val, int n_a, int32_t* b,
+              int64_t b_elems, const int32_t* b_off, const int32_t* b_val, int n_b, void* stream) {
+  if (n_a == 0) return patch_distinct(b, b_elems, b_off, b_val, n_b, stream);
+  if (n_b == 0 || n_a + n_b > kPatchPerLaunch) {
+    const int rc = patch_distinct(a, a_elems, a_off, a_val, n_a, stream);
+    return rc != PKV_OK ? rc : patch_distinct(b, b_elems, b_off, b_val, n_b, stream);
+  }
+  PatchArgs pa;
+  std::copy(a_off, a_off + n_a, pa.off);
+  std::copy(a_val, a_val + n_a, pa.val);
+  std::copy(b_off, b_off + n_b, pa.off + n_a);
+  std::copy(b_val, b_val + n_b, pa.val + n_a);
+  int n = n_a + n_b;
+  void* args[] = {&a, &a_elems, &n_a, &b, &b_elems, &pa, &n};
+  return launch_status(hipLaunchKernel((const void*)patch2_kernel, dim3(1), dim3(512), args, 0,
+                                       (hipStream_t)stream));
 }
 
 }  // namespace pkv

@@ -24,6 +24,11 @@
 #include "common.h"
 #include "decode_api.h"
 
+namespace pkv {
+int patch_two(int32_t* a, int64_t a_elems, const int32_t* a_off, const int32_t* a_val, int n_a, int32_t* b,
+              int64_t b_elems, const int32_t* b_off, const int32_t* b_val, int n_b, void* stream);
+}
+
 using namespace pkv;
 
 extern "C" int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const* k, const pkv_bf16* const* v,
@@ -153,9 +158,10 @@ extern "C" int pkv_decode_step(int n_layers, pkv_bf16* const* q, pkv_bf16* const
     m_val.push_back(s);
   }
   const int64_t meta_elems = (int64_t)num_slots + 2 * (int64_t)batch;
-  int rc = pkv_block_table_patch(bt_dev, bt_elems, t_off.data(), t_val.data(), (int)t_off.size(), stream);
-  if (rc != PKV_OK) return rc;
-  rc = pkv_block_table_patch(meta_dev, meta_elems, m_off.data(), m_val.data(), (int)m_off.size(), stream);
+  // the table changes name distinct entries (one block per (slot, layer) per
+  // step) and so do the metadata pairs: one launch carries both when they fit
+  int rc = patch_two(bt_dev, bt_elems, t_off.data(), t_val.data(), (int)t_off.size(), meta_dev, meta_elems,
+                     m_off.data(), m_val.data(), (int)m_off.size(), stream);
   if (rc != PKV_OK) return rc;
 
   // 4. Per layer: RoPE, append and attention in one launch.
