@@ -154,6 +154,31 @@ int pkv_paged_gather(pkv_bf16* k_dense, pkv_bf16* v_dense, const pkv_bf16* k_poo
 
 int pkv_device_errors(uint32_t* flags, int clear, void* stream);
 
+/* Cache policy of the decode calls' K/V reads (pkv_paged_attn_decode,
+ * pkv_paged_decode_fused and its no-allocation form, pkv_decode_step and its
+ * two halves, pkv_decode_layer(s), pkv_paged_read_probe).  Source: the
+ * chapter-6 title of the category page (each decode step reads all of a
+ * sequence's cached K/V again) and its mini-sglang chapter on a radix cache
+ * (requests that share a prompt share its cached K/V).
+ *   PKV_KV_READ_STREAM (the default): the K/V loads are marked non-temporal.
+ *     When every block is listed by one row, a call reads each K/V byte once;
+ *     the marking keeps that stream from evicting the small data the calls
+ *     reuse (plans, tables, queries, partial records) from the L2 and
+ *     last-level caches.
+ *   PKV_KV_READ_REUSE: ordinary cached loads, for tables whose rows share
+ *     blocks (prefix sharing), so that a block listed by several rows can be
+ *     served from the caches.  pkv_sched_run uses it by itself for the
+ *     iterations whose decode rows share prefix-cache blocks.
+ * Process-wide (every device and thread); a call takes the policy in force
+ * when it is enqueued, and a captured graph keeps the one it was captured
+ * with.  The policy changes speed only, never results.
+ * pkv_set_kv_read_policy: PKV_OK, or PKV_ERR_INVALID_ARG for any other value
+ * (nothing changes).  pkv_kv_read_policy: the current setting. */
+#define PKV_KV_READ_STREAM 1
+#define PKV_KV_READ_REUSE 2
+int pkv_set_kv_read_policy(int policy);
+int pkv_kv_read_policy(void);
+
 /* Diagnostic, off the attention path: read `bytes` bytes of device memory
  * (16-byte aligned, bytes a multiple of 16) once with wide loads spread over
  * the whole chip, as a reference for the HBM read rate the decode kernels are

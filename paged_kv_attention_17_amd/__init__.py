@@ -18,6 +18,7 @@ from ._abi import (  # noqa: F401
     pkv_decode_step, pkv_decode_workspace_init, pkv_paged_decode_fused, pkv_paged_decode_fused_noalloc,
     pkv_decode_step_staging_bytes, pkv_decode_step_host, pkv_decode_step_device,
     pkv_device_errors, PKV_DEVERR_BAD_BLOCK, PKV_DEVERR_BAD_SLOT, PKV_DEVERR_LONG_CONTEXT, PKV_DEVERR_PREFILL_BLOCK,
+    pkv_set_kv_read_policy, pkv_kv_read_policy, PKV_KV_READ_STREAM, PKV_KV_READ_REUSE,
     decode_workspace, Scheduler,
     pkv_rmsnorm, pkv_silu_mul, pkv_linear, pkv_linear_workspace_bytes, pkv_decode_layer,
     pkv_decode_layer_scratch_elems, pkv_decode_layers,

@@ -47,6 +47,8 @@ SIGNATURES = {
     "pkv_hbm_read_probe": (_i, [_p, _sz, _p, _p]),
     "pkv_paged_read_probe": (_i, [_p, _p, _i, _p, _i64, _i, _i, _p, _p, _i, _i, _i, _p, _p]),
     "pkv_device_errors": (_i, [C.POINTER(C.c_uint32), _i, _p]),
+    "pkv_set_kv_read_policy": (_i, [_i]),
+    "pkv_kv_read_policy": (_i, []),
     "pkv_blocks_assign": (_i, [_p, _i64, _i, _i, _p, _ip, _p, _p, _i, _p, _p, _ip]),
     "pkv_blocks_release": (_i, [_p, _i64, _i, _i, _i, _p, _ip, _i, _p, _p, _ip]),
     "pkv_block_table_patch": (_i, [_p, _i64, _p, _p, _i, _p]),
@@ -303,6 +305,22 @@ def pkv_device_errors(clear=True, stream=None):
     flags = C.c_uint32(0)
     _check("pkv_device_errors", load().pkv_device_errors(C.byref(flags), 1 if clear else 0, _stream(stream)))
     return flags.value
+
+
+PKV_KV_READ_STREAM, PKV_KV_READ_REUSE = 1, 2
+
+
+def pkv_set_kv_read_policy(policy):
+    """Cache policy of the decode calls' K/V reads, process-wide:
+    PKV_KV_READ_STREAM (non-temporal, the default) or PKV_KV_READ_REUSE
+    (cached, for tables whose rows share blocks).  Speed only, never
+    results."""
+    _check("pkv_set_kv_read_policy", load().pkv_set_kv_read_policy(int(policy)))
+
+
+def pkv_kv_read_policy():
+    """The current K/V read policy (PKV_KV_READ_STREAM or PKV_KV_READ_REUSE)."""
+    return int(load().pkv_kv_read_policy())
 
 
 def pkv_paged_read_probe(k_pool, v_pool, block_table, slot_ids, row_lens_host, sink, stream=None):

@@ -85,6 +85,35 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   const v4u x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(x[0], x[1], x[2], x[3]);
 }
+// The same load marked non-temporal (cache policy bit nt): for data read
+// once per launch (the K/V stream of a decode call), so that it does not
+// push the small, reused data (plans, tables, queries, partial records) out
+// of the L2 and last-level caches.
+constexpr int kCpolNt = 2;
+__device__ __forceinline__ uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolNt);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+// Four 16-byte loads of one K/V block (two from each descriptor), marked
+// non-temporal when NT is set.  A compile-time choice: loads behind a
+// run-time branch make the compiler's wait counting conservative.
+template <bool NT>
+__device__ __forceinline__ void buf_load_kv4(__amdgpu_buffer_rsrc_t rk, uint32_t ka, uint32_t kb,
+                                             __amdgpu_buffer_rsrc_t rv, uint32_t va, uint32_t vb, uint4& k0,
+                                             uint4& k1, uint4& v0, uint4& v1) {
+  if constexpr (NT) {
+    k0 = buf_load16_nt(rk, ka);
+    k1 = buf_load16_nt(rk, kb);
+    v0 = buf_load16_nt(rv, va);
+    v1 = buf_load16_nt(rv, vb);
+  } else {
+    k0 = buf_load16(rk, ka);
+    k1 = buf_load16(rk, kb);
+    v0 = buf_load16(rv, va);
+    v1 = buf_load16(rv, vb);
+  }
+}
 
 // Byte permute: result byte k = byte sel[k] of the 8-byte value (hi:lo).
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {

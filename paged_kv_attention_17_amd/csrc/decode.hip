@@ -40,6 +40,7 @@
 // rotated key and the value into their pool row at the end of the kernel.
 #include "attn_block.h"
 #include "decode_api.h"
+#include "kv_policy.h"
 
 #include <algorithm>
 #include <atomic>
@@ -75,6 +76,7 @@ struct DecodeArgs {
   int max_pos;
   int batch;
   float scale_log2e;
+  int kv_nt;                   // K/V loads marked non-temporal
   // Host schedule (plan_seqs > 0), built from host-known row lengths.  Row b
   // has length plan_n[b] and is cut into partitions of plan_ps[b] * 16
   // tokens (only its last one shorter).  Items [0, full_items) are the
@@ -168,7 +170,7 @@ __device__ __forceinline__ bool decode_item(const DecodeArgs& a, Item& it) {
   return true;
 }
 
-template <int G, bool FUSED>
+template <int G, bool FUSED, bool NT>
 __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
   Item it;
   if (!decode_item(a, it)) return;
@@ -233,10 +235,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_kernel(DecodeArgs a) {
       blk = blk < 0 ? 0 : blk;
       const auto rk = buf_rsrc(kbase + (size_t)blk * block_bytes, block_bytes);
       const auto rv = buf_rsrc(vbase + (size_t)blk * block_bytes, block_bytes);
-      R.k0 = buf_load16(rk, lane_off);
-      R.k1 = buf_load16(rk, lane_off8);
-      R.v0 = buf_load16(rv, lane_off);
-      R.v1 = buf_load16(rv, lane_off8);
+      buf_load_kv4<NT>(rk, lane_off, lane_off8, rv, lane_off, lane_off8, R.k0, R.k1, R.v0, R.v1);
     };
 
     // One block: branch-free apart from the rare rescale.  Rows past the
@@ -411,12 +410,16 @@ static WsLayout ws_layout(int batch, int n_q, int n_kv, int64_t P) {
   return L;
 }
 
+template <bool FUSED, bool NT>
+static const void* pick_kernel_nt(int G) {
+  return G == 1 ? (const void*)decode_kernel<1, FUSED, NT>
+       : G == 2 ? (const void*)decode_kernel<2, FUSED, NT>
+       : G == 4 ? (const void*)decode_kernel<4, FUSED, NT>
+                : (const void*)decode_kernel<8, FUSED, NT>;
+}
 template <bool FUSED>
-static const void* pick_kernel(int G) {
-  return G == 1 ? (const void*)decode_kernel<1, FUSED>
-       : G == 2 ? (const void*)decode_kernel<2, FUSED>
-       : G == 4 ? (const void*)decode_kernel<4, FUSED>
-                : (const void*)decode_kernel<8, FUSED>;
+static const void* pick_kernel(int G, bool nt) {
+  return nt ? pick_kernel_nt<FUSED, true>(G) : pick_kernel_nt<FUSED, false>(G);
 }
 
 // Longest-first schedule from host-known row lengths.  Row b (n tokens) is
@@ -471,7 +474,7 @@ static int partition_launch(bool fused, DecodeArgs& a, int batch, int max_contex
   if (row_lens_host && batch <= kMaxPlanSeqs && a.max_blocks <= 0xffff) build_plan(a, row_lens_host, batch);
   const int64_t items = a.plan_seqs > 0 ? (int64_t)a.n_items : (int64_t)batch * a.P;
   const int64_t grid = (items + 7) / 8 * 8 * a.n_kv;
-  const void* fn = fused ? pick_kernel<true>(G) : pick_kernel<false>(G);
+  const void* fn = fused ? pick_kernel<true>(G, a.kv_nt != 0) : pick_kernel<false>(G, a.kv_nt != 0);
   void* args[] = {&a};
   const int rc = launch_status(hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kWaves * kWave), args, 0, st));
   if (rc != PKV_OK || P <= 1) return rc;
@@ -568,9 +571,26 @@ static DecodeArgs base_args(const DecodeCall& c) {
 
 namespace pkv {
 
+namespace {
+std::atomic<int> g_kv_read{PKV_KV_READ_STREAM};   // process-wide K/V read policy
+thread_local int t_kv_read = 0;                   // this thread's override, 0 = none
+}  // namespace
+
+int kv_read_policy_now() { return t_kv_read ? t_kv_read : g_kv_read.load(std::memory_order_relaxed); }
+
+int kv_read_override(int policy) {
+  const int prev = t_kv_read;
+  t_kv_read = policy;
+  return prev;
+}
+
+void kv_read_set(int policy) { g_kv_read.store(policy, std::memory_order_relaxed); }
+int kv_read_setting() { return g_kv_read.load(std::memory_order_relaxed); }
+
 int decode_prepare(const DecodeCall& c, DecodeLaunch* L) {
   L->c = c;
   L->path = 0;
+  L->kv_nt = kv_read_policy_now() == PKV_KV_READ_STREAM;
   int rc = decode_common_checks(c.out, c.q, c.k_pool, c.v_pool, c.num_blocks, c.block_table, c.bt_row_stride,
                                 c.num_slots, c.max_blocks_per_seq, c.slot_ids, c.context_lens, c.batch,
                                 c.max_context_len, c.n_q_heads, c.n_kv_heads, c.head_dim, c.scale,
@@ -617,6 +637,7 @@ int decode_prepare(const DecodeCall& c, DecodeLaunch* L) {
     sc.fixed_shape = c.fixed_shape;
     sc.plan_out = c.plan_out;
     sc.chain_plan = c.chain_plan;
+    sc.kv_nt = L->kv_nt;
     if (stream_prepare(c.fused, sc, &L->s) == PKV_OK) {
       L->path = 1;
       return PKV_OK;
@@ -646,6 +667,7 @@ int decode_enqueue(const DecodeLaunch& L, hipStream_t st, bool merge) {
   if (L.path == 0) return PKV_OK;
   if (L.path == 1) return stream_enqueue(L.s, st, merge);
   DecodeArgs a = base_args(L.c);
+  a.kv_nt = L.kv_nt ? 1 : 0;
   return partition_launch(L.c.fused, a, L.c.batch, L.c.max_context_len, L.c.partition_size, L.c.row_lens_host,
                           L.c.workspace, st);
 }
@@ -655,6 +677,14 @@ int decode_finish(const DecodeLaunch& L, hipStream_t st) {
 }
 
 }  // namespace pkv
+
+extern "C" int pkv_set_kv_read_policy(int policy) {
+  if (policy != PKV_KV_READ_STREAM && policy != PKV_KV_READ_REUSE) return PKV_ERR_INVALID_ARG;
+  pkv::kv_read_set(policy);
+  return PKV_OK;
+}
+
+extern "C" int pkv_kv_read_policy(void) { return pkv::kv_read_setting(); }
 
 extern "C" int pkv_paged_read_probe(const pkv_bf16* k_pool, const pkv_bf16* v_pool, int num_blocks,
                                     const int32_t* block_table, int64_t bt_row_stride, int num_slots,
@@ -681,6 +711,7 @@ extern "C" int pkv_paged_read_probe(const pkv_bf16* k_pool, const pkv_bf16* v_po
   c.row_lens_host = row_lens_host;
   c.batch = batch;
   c.n_kv = n_kv_heads;
+  c.kv_nt = kv_read_policy_now() == PKV_KV_READ_STREAM;
   return stream_read_probe(c, sink, static_cast<hipStream_t>(stream));
 }
 

@@ -60,6 +60,7 @@ struct DecodeCall {
 struct DecodeLaunch {
   DecodeCall c;
   int path;                    // 0: nothing to do, 1: streaming kernel, 2: per-partition kernels
+  bool kv_nt;                  // K/V loads marked non-temporal (the policy when the call was prepared)
   StreamLaunch s;
 };
 

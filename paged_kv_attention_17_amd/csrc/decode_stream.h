@@ -56,6 +56,7 @@ struct StreamCore {
   const StreamPlan* plan_dev;  // device-plan launches: the plan in device memory
   StreamPlan* plan_out;        // argument-plan launches: workgroup 0 also stores the plan here
   uint32_t* errors;            // device error flags (errors.hip), or null
+  int kv_nt;                   // K/V loads marked non-temporal
 };
 struct StreamArgs : StreamCore {
   StreamPlan plan;             // argument-plan launches: the plan itself
@@ -91,6 +92,7 @@ struct StreamCall {
                                //   captured once and replayed; the plan may change between replays)
   StreamPlan* plan_out;        // non-null: the launch also stores its plan here, in device memory
   bool chain_plan;             // shares sized for chained launches (see stream_plan_build)
+  bool kv_nt;                  // K/V loads marked non-temporal (PKV_KV_READ_STREAM)
 };
 
 struct StreamLaunch {

@@ -367,7 +367,7 @@ __device__ __forceinline__ const StreamPlan& plan_of(const ArgsOf<DEVPLAN>& a) {
     return a.plan;
 }
 
-template <int G, bool FUSED, bool PREV, bool DEVPLAN>
+template <int G, bool FUSED, bool PREV, bool DEVPLAN, bool NT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void stream_kernel(ArgsOf<DEVPLAN> a) {
   const StreamPlan& P = plan_of<DEVPLAN>(a);
@@ -461,10 +461,7 @@ void stream_kernel(ArgsOf<DEVPLAN> a) {
     const size_t base = ok ? (size_t)blk * block_bytes : 0;
     const auto rk = buf_rsrc(kbase + base, ok ? block_bytes : 0u);
     const auto rv = buf_rsrc(vbase + base, ok ? block_bytes : 0u);
-    R.k0 = buf_load16(rk, k_offA);
-    R.k1 = buf_load16(rk, k_offB);
-    R.v0 = buf_load16(rv, v_off0);
-    R.v1 = buf_load16(rv, v_off1);
+    buf_load_kv4<NT>(rk, k_offA, k_offB, rv, v_off0, v_off1, R.k0, R.k1, R.v0, R.v1);
   };
 
   // ---- start-up.  A wave's vector loads complete in order, so waiting for
@@ -849,6 +846,7 @@ __global__ __launch_bounds__(1024) void stream_merge_wide_kernel(ArgsOf<DEVPLAN>
 // wave); the data are XOR-ed into `sink` under a condition they never meet.
 // It gives the time that reading a batch's blocks in this pattern takes on
 // its own.
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void stream_read_probe_kernel(StreamArgs a, uint32_t* sink) {
   const StreamPlan& P = a.plan;
   const int B0 = blockIdx.x * P.share;
@@ -899,10 +897,7 @@ __global__ __launch_bounds__(kThreads) void stream_read_probe_kernel(StreamArgs 
     const size_t base = ok ? (size_t)blk * block_bytes : 0;
     const auto rk = buf_rsrc(kbase + base, ok ? block_bytes : 0u);
     const auto rv = buf_rsrc(vbase + base, ok ? block_bytes : 0u);
-    R.k0 = buf_load16(rk, k_offA);
-    R.k1 = buf_load16(rk, k_offB);
-    R.v0 = buf_load16(rv, v_off0);
-    R.v1 = buf_load16(rv, v_off1);
+    buf_load_kv4<NT>(rk, k_offA, k_offB, rv, v_off0, v_off1, R.k0, R.k1, R.v0, R.v1);
   };
   KVRegs R[kDepth];
 #pragma unroll
@@ -934,11 +929,15 @@ int device_cus() {
   return n;
 }
 
+template <bool FUSED, bool PREV, bool DEVPLAN, bool NT>
+const void* pick_stream_nt(int G) {
+  return G == 1 ? (const void*)stream_kernel<1, FUSED, PREV, DEVPLAN, NT>
+       : G == 2 ? (const void*)stream_kernel<2, FUSED, PREV, DEVPLAN, NT>
+                : (const void*)stream_kernel<4, FUSED, PREV, DEVPLAN, NT>;
+}
 template <bool FUSED, bool PREV, bool DEVPLAN>
-const void* pick_stream(int G) {
-  return G == 1 ? (const void*)stream_kernel<1, FUSED, PREV, DEVPLAN>
-       : G == 2 ? (const void*)stream_kernel<2, FUSED, PREV, DEVPLAN>
-                : (const void*)stream_kernel<4, FUSED, PREV, DEVPLAN>;
+const void* pick_stream(int G, bool nt) {
+  return nt ? pick_stream_nt<FUSED, PREV, DEVPLAN, true>(G) : pick_stream_nt<FUSED, PREV, DEVPLAN, false>(G);
 }
 
 template <bool DEVPLAN>
@@ -1066,6 +1065,7 @@ int stream_prepare(bool fused, const StreamCall& c, StreamLaunch* L) {
   a.batch = c.batch;
   a.scale_log2e = c.scale * kLog2e;
   a.errors = device_errors_ptr();
+  a.kv_nt = c.kv_nt ? 1 : 0;
   int merge = 0;
   const int pr = stream_plan_build(c.batch, c.row_lens_host, c.max_blocks, c.slot_ids_host, c.slot_ids != nullptr,
                                    c.num_slots, c.chain_plan, &a.plan, &merge);
@@ -1106,12 +1106,13 @@ int stream_enqueue(const StreamLaunch& L, hipStream_t st, bool merge) {
   StreamArgs a = L.a;
   StreamCore core = L.a;               // device-plan launches pass the core alone
   void* args[] = {L.devplan ? static_cast<void*>(&core) : static_cast<void*>(&a)};
+  const bool nt = L.a.kv_nt != 0;
   const void* fn;
   if (L.devplan)
-    fn = L.prev ? pick_stream<true, true, true>(L.G) : pick_stream<true, false, true>(L.G);
+    fn = L.prev ? pick_stream<true, true, true>(L.G, nt) : pick_stream<true, false, true>(L.G, nt);
   else
-    fn = L.fused ? (L.prev ? pick_stream<true, true, false>(L.G) : pick_stream<true, false, false>(L.G))
-                 : (L.prev ? pick_stream<false, true, false>(L.G) : pick_stream<false, false, false>(L.G));
+    fn = L.fused ? (L.prev ? pick_stream<true, true, false>(L.G, nt) : pick_stream<true, false, false>(L.G, nt))
+                 : (L.prev ? pick_stream<false, true, false>(L.G, nt) : pick_stream<false, false, false>(L.G, nt));
   const int rc = launch_status(hipLaunchKernel(fn, dim3(L.grid), dim3(kThreads), args, 0, st));
   if (rc != PKV_OK || !merge) return rc;
   return stream_merge_enqueue(L, st);
@@ -1132,13 +1133,15 @@ int stream_read_probe(const StreamCall& c, uint32_t* sink, hipStream_t st) {
   a.max_blocks = c.max_blocks;
   a.n_kv = c.n_kv;
   a.batch = c.batch;
+  a.kv_nt = c.kv_nt ? 1 : 0;
   int merge = 0;
   if (stream_plan_build(c.batch, c.row_lens_host, c.max_blocks, c.slot_ids_host, c.slot_ids != nullptr, c.num_slots,
                         false, &a.plan, &merge) < 0)
     return PKV_ERR_UNSUPPORTED;
   if (a.plan.share > kWin) return PKV_ERR_UNSUPPORTED;     // one table window per share
   void* args[] = {&a, &sink};
-  return launch_status(hipLaunchKernel((const void*)stream_read_probe_kernel, dim3(a.plan.grid), dim3(kThreads),
+  const void* fn = c.kv_nt ? (const void*)stream_read_probe_kernel<true> : (const void*)stream_read_probe_kernel<false>;
+  return launch_status(hipLaunchKernel(fn, dim3(a.plan.grid), dim3(kThreads),
                                        args, 0, st));
 }
 

@@ -277,6 +277,9 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
   float m = -1.0e30f;              // shared by lane and lane ^ 32 (same query)
   float thr = -INFINITY;           // raw-score level above which m must be raised
   float l = 0.f;                   // this lane's half of the sum
+  // keys below this bound are visible to this lane's query (none for a
+  // padding lane): the causal limit and the cache's end
+  const int key_lim = q_ok ? min(my_pos + 1, n_keys) : 0;
 
   // This lane's K-operand slots: row `col` of each 32-key half, dims
   // 16 ks + 8 half .. + 7, i.e. chunk 2 ks + half at slot (2 ks + half) ^ (col & 7)
@@ -319,14 +322,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4, 8
       // masks only where a key of the tile can lie past a query or the cache
       const bool need_mask = kbase + kKTile - 1 > sub_last_pos - 31 || kbase + kKTile > n_keys;
       if (need_mask) {
+        // accumulator i of half kh holds key kbase + 32 kh + 8 (i / 4) + 4 half + i % 4
+        const int r = key_lim - kbase - 4 * half;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + kh * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-            const bool ok = q_ok && key <= my_pos && key < n_keys;
-            s[kh][i] = ok ? s[kh][i] : -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i) s[kh][i] = 32 * kh + 8 * (i / 4) + (i % 4) < r ? s[kh][i] : -INFINITY;
         }
       }
       float tmax = s[0][0];

@@ -43,6 +43,7 @@
 #include <vector>
 
 #include "../../include/pagedkv.h"
+#include "kv_policy.h"
 
 namespace pkv {
 // paging.hip: write (offset, value) pairs with distinct offsets through kernel arguments
@@ -525,6 +526,16 @@ extern "C" int pkv_sched_run(const pkv_sched* s, const pkv_sched_iter* it, pkv_b
 
   int max_ctx = 0;
   for (int b = 0; b < nd; ++b) max_ctx = std::max(max_ctx, it->decode_lens[b]);
+  // decode rows that list the same prefix-cache blocks read them with cached
+  // loads (a block two requests list is its first node's, at least)
+  bool shared = false;
+  for (int b = 0; b < nd && !shared; ++b) {
+    const int sl = it->decode_slots[b];
+    if (sl < 0 || sl >= ns) continue;
+    const std::vector<int>& path = s->slot[sl].path;
+    shared = !path.empty() && s->nodes[path[0]].ref >= 2;
+  }
+  const pkv::KvReadScope kv_read(shared ? PKV_KV_READ_REUSE : 0);
   const int64_t row_stride = (int64_t)s->n_layers * s->max_blocks;
   const int64_t q_row = (int64_t)n_q_heads * head_dim, kv_row = (int64_t)n_kv_heads * head_dim;
   for (int l = 0; l < s->n_layers; ++l) {

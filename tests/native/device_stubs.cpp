@@ -7,6 +7,12 @@
 
 namespace pkv {
 int patch_distinct(int32_t*, int64_t, const int32_t*, const int32_t*, int, void*) { return PKV_OK; }
+int kv_read_override(int policy) {
+  static thread_local int current = 0;
+  const int prev = current;
+  current = policy;
+  return prev;
+}
 }  // namespace pkv
 
 extern "C" {

@@ -382,3 +382,19 @@ def test_load_shares_torch_hip_runtime():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_kv_read_policy_setting(lib):
+    """The K/V read policy: STREAM by default, REUSE settable, anything else
+    refused with nothing changed."""
+    E = _abi
+    assert lib.pkv_kv_read_policy() == E.PKV_KV_READ_STREAM
+    try:
+        assert lib.pkv_set_kv_read_policy(E.PKV_KV_READ_REUSE) == E.PKV_OK
+        assert lib.pkv_kv_read_policy() == E.PKV_KV_READ_REUSE
+        for bad in (0, 3, -1):
+            assert lib.pkv_set_kv_read_policy(bad) == E.PKV_ERR_INVALID_ARG
+            assert lib.pkv_kv_read_policy() == E.PKV_KV_READ_REUSE
+    finally:
+        assert lib.pkv_set_kv_read_policy(E.PKV_KV_READ_STREAM) == E.PKV_OK
+    assert lib.pkv_kv_read_policy() == E.PKV_KV_READ_STREAM

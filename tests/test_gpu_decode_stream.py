@@ -362,3 +362,28 @@ def test_paged_read_probe_reads_without_writing(gpu):
     assert int(sink.item()) == 5
     np.testing.assert_array_equal(bits(kpd), kp)
     np.testing.assert_array_equal(bits(vpd), vp)
+
+
+@pytest.mark.parametrize("row_lens", [True, False], ids=["stream", "partitions"])
+def test_kv_read_policy_does_not_change_results(gpu, row_lens):
+    """Both K/V read policies (non-temporal loads, and ordinary cached loads
+    for shared blocks) give the same output bit for bit, on the streaming
+    kernel (host lengths) and on the per-partition kernels, over rows that
+    share their first blocks (a shared prompt) and rows that do not."""
+    rng = np.random.default_rng(31)
+    lens = np.array([700, 1500, 33, 2048, 900, 1200], np.int32)
+    kp, vp, bt = _batch(rng, lens, 8)
+    bt[1, :20] = bt[0, :20]          # rows 0, 1 and 4 share row 0's first 20 blocks
+    bt[4, :20] = bt[0, :20]
+    q = W.randn_bf16(rng, (len(lens), 32, 64))
+    outs = []
+    try:
+        for policy in (pkv.PKV_KV_READ_REUSE, pkv.PKV_KV_READ_STREAM, pkv.PKV_KV_READ_REUSE):
+            pkv.pkv_set_kv_read_policy(policy)
+            outs.append(_decode(q, kp, vp, bt, None, lens, lens if row_lens else None))
+    finally:
+        pkv.pkv_set_kv_read_policy(pkv.PKV_KV_READ_STREAM)
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+    ref = attention.decode(q, kp, vp, bt, np.arange(len(lens)), lens, 0.125)
+    check_attention(outs[0], ref, "both read policies")
