@@ -714,7 +714,8 @@ int check_layer_args(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int in
                      const int32_t* block_table, int64_t bt_row_stride, int num_slots, int max_blocks_per_seq,
                      const int32_t* slot_ids, const int32_t* context_lens, const int32_t* row_lens_host, int batch,
                      int max_context_len, int n_q_heads, int n_kv_heads, const float* cos_sin, int max_pos,
-                     float scale, float eps, void* workspace, size_t workspace_bytes, DecodeLaunch* att) {
+                     float scale, float eps, void* workspace, size_t workspace_bytes, DecodeLaunch* att,
+                     StreamPlan* plan_out = nullptr, const StreamPlan* plan_dev = nullptr) {
   if (hidden <= 0 || intermediate <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || !(eps >= 0.f))
     return PKV_ERR_INVALID_ARG;
   if (!h || !w || !scratch || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->mlp_norm ||
@@ -755,6 +756,8 @@ int check_layer_args(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int in
   c.scale = scale;
   c.workspace = workspace;
   c.workspace_bytes = workspace_bytes;
+  c.plan_out = plan_out;
+  c.plan_dev = plan_dev;
   return decode_prepare(c, att);
 }
 
@@ -793,12 +796,22 @@ extern "C" int pkv_decode_layers(pkv_bf16* h, const pkv_layer_weights* layers, i
   if (!layers || !block_table) return PKV_ERR_NULL;
   thread_local std::vector<DecodeLaunch> att;
   att.resize(n_layers);
+  // The layers' attention calls share the rows and their lengths, hence the
+  // streaming kernel's plan: the first launch stores it in the workspace and
+  // the others read it there (small kernel arguments for them and for their
+  // merges; a launch that carries the plan in its arguments waits longer to
+  // start).
+  const size_t plan_off = decode_plan_offset(n_q_heads);
+  StreamPlan* plan_ws = n_layers > 1 && workspace && n_q_heads > 0 && workspace_bytes >= plan_off + kStreamPlanBytes
+                            ? reinterpret_cast<StreamPlan*>(static_cast<char*>(workspace) + plan_off)
+                            : nullptr;
   for (int l = 0; l < n_layers; ++l) {
+    const bool devplan = l > 0 && plan_ws && att[0].path == 1;
     const int rc = check_layer_args(h, &layers[l], hidden, intermediate, scratch, scratch_elems, k_pool, v_pool,
                                     num_blocks, block_table + bt_layer_stride * l, bt_row_stride, num_slots,
                                     max_blocks_per_seq, slot_ids, context_lens, row_lens_host, batch, max_context_len,
                                     n_q_heads, n_kv_heads, cos_sin, max_pos, scale, eps, workspace, workspace_bytes,
-                                    &att[l]);
+                                    &att[l], l == 0 ? plan_ws : nullptr, devplan ? plan_ws : nullptr);
     if (rc != PKV_OK) return rc;
   }
   for (int l = 0; l < n_layers; ++l) {
