@@ -670,7 +670,7 @@ def decode_layer_leg(torch, np, pkv, eng, ctx_now, stream, iters: int = 5):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--attn-iters", type=int, default=10, help="passes over the 16 layers for kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -724,16 +724,20 @@ def main():
     # ---- timed region: K whole decode steps --------------------------------
     kv_bytes = 0
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event after every step as well, for the spread of the step times
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         kv_bytes += (int(eng.cached.sum()) + w.batch) * KV_BYTES_PER_TOKEN * L   # lengths after this step
         eng.step(sids, q, k, v, out)
+        step_ev[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     t_step = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    per_step = np.array([(step_ev[i - 1] if i else ev0).elapsed_time(step_ev[i]) * 1e3 for i in range(args.steps)])
     value = kv_bytes / args.steps / t_step / 1e9
     log(f"step: {t_step * 1e6:.1f} us ({t_step * 1e6 / L:.2f} us/layer), KV {value:.0f} GB/s, "
         f"host wall {wall / args.steps * 1e6:.1f} us/step")
@@ -877,6 +881,7 @@ def main():
                    "partition_size": pkv.pkv_decode_partition_size(w.batch, 8, eng.max_context_len)
                    if args.partition_size == 0 else args.partition_size},
         "us_per_layer": round(t_step * 1e6 / L, 3),
+        "step_us_p10_p50_p90": [round(float(np.percentile(per_step, x)), 1) for x in (10, 50, 90)],
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
