@@ -413,7 +413,8 @@ int pkv_paged_decode_fused_noalloc(pkv_bf16* out, const pkv_bf16* q, const pkv_b
  * absolute position q_start_pos[i]; query row at position a attends keys
  * 0 .. a of table row slot_ids[i] (NULL = i). The chunk's own K/V must already
  * be in the pool (pkv_paged_kv_append). QK^T and PV run on MFMA (bf16 in,
- * float32 accumulate); out is bf16 [total_q][n_q_heads][head_dim].
+ * float32 accumulate); out is bf16 [total_q][n_q_heads][head_dim].  scale
+ * must be positive and finite (PKV_ERR_INVALID_ARG otherwise).
  * max_q_len: host bound on the longest query run (sizes the grid).
  * cu_q_lens_host, q_start_host: optional HOST copies of cu_q_lens and
  * q_start_pos (both or neither).  When given (and the call has at most 768

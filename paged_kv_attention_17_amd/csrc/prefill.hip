@@ -446,7 +446,7 @@ extern "C" int pkv_paged_attn_prefill(pkv_bf16* out, const pkv_bf16* q, const in
                                       float scale, const int32_t* cu_q_lens_host, const int32_t* q_start_host,
                                       void* stream) {
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || num_slots < 0 ||
-      max_blocks_per_seq < 0 || bt_row_stride < max_blocks_per_seq || !(scale == scale))
+      max_blocks_per_seq < 0 || bt_row_stride < max_blocks_per_seq || !(scale > 0.f && scale < 3.0e38f))
     return PKV_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads) return PKV_ERR_INVALID_ARG;
   if (head_dim != kHeadDim || !ratio_supported(n_q_heads, n_kv_heads)) return PKV_ERR_UNSUPPORTED;

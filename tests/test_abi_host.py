@@ -105,6 +105,11 @@ def test_other_entry_points_argument_errors(lib):
                                       32, 8, 48, 0.125, None, None, None) == E.PKV_ERR_UNSUPPORTED
     assert lib.pkv_paged_attn_prefill(FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 8, FAKE, 4, 1, 4, 1, 10, 10,
                                       32, 8, 64, 0.125, None, None, None) == E.PKV_ERR_NULL
+    # the masked scores are -inf: a scale of 0, below 0 or not finite would
+    # turn them into NaN or +inf, so it is refused
+    for bad in (0.0, -0.125, float("inf"), float("nan")):
+        assert lib.pkv_paged_attn_prefill(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 8, FAKE, 4, 1, 4, 1, 10, 10,
+                                          32, 8, 64, bad, None, None, None) == E.PKV_ERR_INVALID_ARG
     # fused decode: same checks plus its own inputs
     assert lib.pkv_paged_decode_fused(FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None, 1, 17,
                                       32, 8, 64, FAKE, 100, 0.125, 0, None, 0, None) == E.PKV_ERR_NULL
