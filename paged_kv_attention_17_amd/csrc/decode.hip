@@ -659,6 +659,28 @@ int decode_prepare(const DecodeCall& c, DecodeLaunch* L) {
 
 size_t decode_plan_offset(int n_q_heads) { return 2 * stream_records_bytes(n_q_heads); }
 
+int decode_retarget(const DecodeLaunch& base, const int32_t* block_table, const StreamPlan* plan_dev,
+                    DecodeLaunch* out) {
+  if (base.c.out_prev || base.c.plan_dev || base.c.fixed_shape) return PKV_ERR_INVALID_ARG;
+  if (base.path != 0 && !block_table) return PKV_ERR_NULL;
+  if (base.path != 0 && !aligned4(block_table)) return PKV_ERR_MISALIGNED;
+  if (plan_dev && (base.path != 1 || base.c.plan_out != plan_dev)) return PKV_ERR_INVALID_ARG;
+  *out = base;
+  out->c.block_table = block_table;
+  out->c.plan_out = nullptr;
+  out->c.plan_dev = plan_dev;
+  if (base.path == 1) {
+    StreamArgs& a = out->s.a;
+    a.bt = block_table;
+    a.plan_out = nullptr;
+    if (plan_dev) {
+      out->s.devplan = true;
+      a.plan_dev = plan_dev;
+    }
+  }
+  return PKV_OK;
+}
+
 bool decode_chainable(const DecodeLaunch& L) {
   return L.path == 1 && !L.s.long_rows && L.c.workspace_bytes >= decode_plan_offset(L.c.n_q_heads) + kStreamPlanBytes;
 }

@@ -73,6 +73,14 @@ size_t decode_plan_offset(int n_q_heads);
 int decode_prepare(const DecodeCall& c, DecodeLaunch* L);
 bool decode_chainable(const DecodeLaunch& L);
 
+// A prepared call for the same rows on another table view (another layer's
+// entries, same row stride): `out` = `base` with the table replaced, and
+// with plan_dev set (streaming path only) the launch reads the plan `base`
+// stored there (base.c.plan_out) instead of carrying it.  Checks only what
+// differs from `base`; PKV_OK or a status.
+int decode_retarget(const DecodeLaunch& base, const int32_t* block_table, const StreamPlan* plan_dev,
+                    DecodeLaunch* out);
+
 // Enqueue a prepared call.  merge = false leaves the streaming path's merge
 // to the next chained launch (or to decode_finish).
 int decode_enqueue(const DecodeLaunch& L, hipStream_t st, bool merge = true);

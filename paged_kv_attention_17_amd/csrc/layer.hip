@@ -715,7 +715,7 @@ int check_layer_args(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int in
                      const int32_t* slot_ids, const int32_t* context_lens, const int32_t* row_lens_host, int batch,
                      int max_context_len, int n_q_heads, int n_kv_heads, const float* cos_sin, int max_pos,
                      float scale, float eps, void* workspace, size_t workspace_bytes, DecodeLaunch* att,
-                     StreamPlan* plan_out = nullptr, const StreamPlan* plan_dev = nullptr) {
+                     StreamPlan* plan_out = nullptr) {
   if (hidden <= 0 || intermediate <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || !(eps >= 0.f))
     return PKV_ERR_INVALID_ARG;
   if (!h || !w || !scratch || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->mlp_norm ||
@@ -757,8 +757,9 @@ int check_layer_args(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int in
   c.workspace = workspace;
   c.workspace_bytes = workspace_bytes;
   c.plan_out = plan_out;
-  c.plan_dev = plan_dev;
-  return decode_prepare(c, att);
+  // att null: the weights and sizes only (the caller derives the attention
+  // call from another layer's)
+  return att ? decode_prepare(c, att) : PKV_OK;
 }
 
 }  // namespace
@@ -805,13 +806,20 @@ extern "C" int pkv_decode_layers(pkv_bf16* h, const pkv_layer_weights* layers, i
   StreamPlan* plan_ws = n_layers > 1 && workspace && n_q_heads > 0 && workspace_bytes >= plan_off + kStreamPlanBytes
                             ? reinterpret_cast<StreamPlan*>(static_cast<char*>(workspace) + plan_off)
                             : nullptr;
+  // Every layer's arguments are checked before the first launch.  The
+  // attention calls differ only in the table view, so the first layer's is
+  // planned in full and the others are the same call on their own view (the
+  // plan is built once: planning every layer before the first launch would
+  // keep the GPU waiting).
   for (int l = 0; l < n_layers; ++l) {
-    const bool devplan = l > 0 && plan_ws && att[0].path == 1;
-    const int rc = check_layer_args(h, &layers[l], hidden, intermediate, scratch, scratch_elems, k_pool, v_pool,
-                                    num_blocks, block_table + bt_layer_stride * l, bt_row_stride, num_slots,
-                                    max_blocks_per_seq, slot_ids, context_lens, row_lens_host, batch, max_context_len,
-                                    n_q_heads, n_kv_heads, cos_sin, max_pos, scale, eps, workspace, workspace_bytes,
-                                    &att[l], l == 0 ? plan_ws : nullptr, devplan ? plan_ws : nullptr);
+    int rc = check_layer_args(h, &layers[l], hidden, intermediate, scratch, scratch_elems, k_pool, v_pool,
+                              num_blocks, block_table + bt_layer_stride * l, bt_row_stride, num_slots,
+                              max_blocks_per_seq, slot_ids, context_lens, row_lens_host, batch, max_context_len,
+                              n_q_heads, n_kv_heads, cos_sin, max_pos, scale, eps, workspace, workspace_bytes,
+                              l == 0 ? &att[0] : nullptr, plan_ws);
+    if (rc == PKV_OK && l > 0)
+      rc = decode_retarget(att[0], block_table + bt_layer_stride * l, plan_ws && att[0].path == 1 ? plan_ws : nullptr,
+                           &att[l]);
     if (rc != PKV_OK) return rc;
   }
   for (int l = 0; l < n_layers; ++l) {
