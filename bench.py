@@ -114,10 +114,14 @@ def stream_read_gbs(torch, pkv, nbytes=4 << 30, iters=10):
 
 
 def unfused_layer_us(torch, np, pkv, eng, q, k, v, out, stream, iters=3):
-    """The unfused decode of one layer at the same point: RoPE kernel, append
-    kernel and attention call, each timed with HIP events (mean over the 16
-    layers x iters).  Works on copies of q/k so the step's inputs stay as they
-    are, and re-appends the tokens of the last step (the cache is unchanged)."""
+    """The unfused decode of one layer at the same point: the RoPE kernel, the
+    append kernel and the attention call, each timed over its 16 layers'
+    launches back to back (one event pair per kernel and pass, per-launch time
+    = interval / 16), queued behind a device-side wait so that the host has
+    enqueued them before the GPU starts: the figures are GPU time, not the
+    host's launch latency.  Works on copies of q/k so the step's inputs stay
+    as they are, and re-appends the tokens of the last step (the cache is
+    unchanged)."""
     L = q.shape[0]
     B = q.shape[1]
     pos = torch.from_numpy((eng.cached[:B] - 1).astype(np.int32)).cuda()
@@ -125,26 +129,28 @@ def unfused_layer_us(torch, np, pkv, eng, q, k, v, out, stream, iters=3):
     ctx_now = eng.cached.copy()
     t = {"rope": [], "append": [], "attention": []}
     for it in range(iters + 1):
+        qc, kc = q.clone(), k.clone()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(10_000_000)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(stream)
         for layer in range(L):
-            qc, kc = q[layer].clone(), k[layer].clone()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            ev[0].record(stream)
-            pkv.pkv_rope_decode(qc, kc, pos, eng.cos_sin, stream=stream)
-            ev[1].record(stream)
-            pkv.pkv_paged_kv_append(eng.k_pool, eng.v_pool, kc, v[layer], eng.bt_dev[:, layer, :], sid, pos,
+            pkv.pkv_rope_decode(qc[layer], kc[layer], pos, eng.cos_sin, stream=stream)
+        ev[1].record(stream)
+        for layer in range(L):
+            pkv.pkv_paged_kv_append(eng.k_pool, eng.v_pool, kc[layer], v[layer], eng.bt_dev[:, layer, :], sid, pos,
                                     stream=stream)
-            ev[2].record(stream)
-            pkv.pkv_paged_attn_decode(out[layer], qc, eng.k_pool, eng.v_pool, eng.bt_dev[:, layer, :], None,
+        ev[2].record(stream)
+        for layer in range(L):
+            pkv.pkv_paged_attn_decode(out[layer], qc[layer], eng.k_pool, eng.v_pool, eng.bt_dev[:, layer, :], None,
                                       eng.ctx_dev, eng.max_context_len, eng.scale, eng.partition_size,
                                       eng.workspace, stream=stream, row_lens_host=ctx_now)
-            ev[3].record(stream)
-            if it > 0:
-                t["rope"].append(ev[:2])
-                t["append"].append(ev[1:3])
-                t["attention"].append(ev[2:4])
-    torch.cuda.synchronize()
-    return {kname: round(float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3, 2)
-            for kname, pairs in t.items()}
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        if it > 0:
+            for i, kname in enumerate(("rope", "append", "attention")):
+                t[kname].append(ev[i].elapsed_time(ev[i + 1]) * 1e3 / L)
+    return {kname: round(float(np.median(v_)), 2) for kname, v_ in t.items()}
 
 
 def cpu_baseline(eng, q_host, seconds: float, threads: int):
