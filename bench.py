@@ -682,9 +682,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--partition-size", type=int, default=0)
-    ap.add_argument("--leg", choices=["prefill", "decode"], default=None,
-                    help="run one leg alone and print its JSON (for profiling it): prefill, or the "
-                         "decode step with its roofline, read probe and the plain copy used to scale counters")
+    ap.add_argument("--leg", choices=["prefill", "decode", "layer"], default=None,
+                    help="run one leg alone and print its JSON (for profiling it): prefill, the "
+                         "decode step with its roofline, read probe and the plain copy used to scale counters, "
+                         "or the whole decode layers after the warm-up steps")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -726,6 +727,9 @@ def main():
     for _ in range(args.warmup):
         eng.step(sids, q, k, v, out)
     torch.cuda.synchronize()
+    if args.leg == "layer":
+        print(json.dumps(decode_layer_leg(torch, np, pkv, eng, eng.cached.copy(), stream)), flush=True)
+        return
 
     # ---- timed region: K whole decode steps --------------------------------
     kv_bytes = 0
