@@ -314,6 +314,147 @@ __global__ __launch_bounds__(kDbWaves * kWave) void decode_gemm_kernel(DecodeGem
   }
 }
 
+// Narrow-tile variant for products whose feature tiles alone cannot fill the
+// chip (the query, key and value projections): one 4-wave workgroup per 16
+// output features and 64-row block, the waves taking the four quarters of
+// the K slices and their sums added in LDS at the end (quarter 0 + 1 + 2 +
+// 3, a fixed order), so no float32 partials leave the workgroup and no
+// reduction launch follows.  Each wave streams its 16 W rows (the A operand,
+// as in decode_gemm_kernel) and brings its own X slices (64 rows x 128 k)
+// through a private LDS tile: 16-byte loads covering four whole rows per
+// wave instruction, written to LDS and read back in the B-operand layout.
+// X is thus read once per workgroup, four times the weight bytes of a
+// 16-feature tile, from L2.  Loads past the K range, the rows or a quarter's
+// slices read zeros through the buffer descriptors (an offset with its top
+// bit set lies past every range); features past n load the last feature
+// row and are not stored.  W and X of the next two slices are in flight
+// while one is multiplied.
+constexpr int kNwWaves = 4;
+constexpr int kNwN = 16;                       // output features per workgroup
+constexpr int kNwXq = kDbRows * kDbSlice / 8 / kWave;   // 16-byte X loads per lane and slice (16)
+constexpr int kNarrowMaxK = 4096;              // X of a 64-row block at most 512 KB per workgroup
+
+struct NarrowArgs {
+  GemmSeg seg[kMaxSeg];         // tile ranges in 16-feature tiles; part unused
+  const uint16_t* x;
+  int nseg, rows, k, kq;        // kq: 128-wide slices per wave (K quarter)
+  int accumulate;
+};
+
+__global__ __launch_bounds__(kNwWaves * kWave) void decode_gemm_narrow_kernel(NarrowArgs args) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = blockIdx.x;
+  const int row0 = blockIdx.y * kDbRows;
+  int si = 0;
+  while (si + 1 < args.nseg && t >= args.seg[si].tile_end) ++si;
+  const uint16_t* __restrict__ w = args.seg[si].w;
+  const int n = args.seg[si].n;
+  const int n0 = (t - args.seg[si].tile_begin) * kNwN;
+  const int k = args.k;
+  const int rows = min(kDbRows, args.rows - row0);
+  const int nsl = (k + kDbSlice - 1) / kDbSlice;
+  const int first = wv * args.kq;                       // this wave's first slice
+  const int mine = max(0, min(args.kq, nsl - first));   // and how many it has
+  const int r16 = lane & 15;
+  const int kg = 8 * (lane >> 4);
+  const int wr = min(n0 + r16, n - 1);
+  const auto wres = buf_rsrc(w, (uint32_t)((int64_t)n * k * 2));
+  const auto xres = buf_rsrc(args.x, (uint32_t)((int64_t)args.rows * k * 2));
+  constexpr uint32_t kOut = 0x80000000u;
+  const uint32_t wbase = (uint32_t)(((int64_t)wr * k + kg) * 2);
+  // X load q of this lane: row 4 q + lane / 16 of the block, 16-byte piece lane % 16
+  const int xch = lane & 15;
+  const int xr0 = lane >> 4;
+  const uint32_t xbase = (uint32_t)(((int64_t)(row0 + xr0) * k + 8 * xch) * 2);
+  const uint32_t xrow4 = (uint32_t)(4 * k * 2);          // four rows, in bytes
+  __shared__ uint16_t xs[kNwWaves][kDbRows * kXsRow];    // one private tile per wave
+  uint16_t* xw = &xs[wv][xr0 * kXsRow + 8 * xch];        // + q x 4 rows
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load_w = [&](int it, uint4 (&wd)[kDbSteps]) {
+    const int off = (first + it) * kDbSlice;
+    const uint32_t dead = it < mine ? 0u : kOut;
+#pragma unroll
+    for (int u = 0; u < kDbSteps; ++u)
+      wd[u] = buf_load16(wres, (wbase + 2u * (off + kDbStage * u)) | dead |
+                                   (off + kDbStage * u + kg < k ? 0u : kOut));
+  };
+  auto load_x = [&](int it, uint4 (&xd)[kNwXq]) {
+    const int off = (first + it) * kDbSlice;
+    const uint32_t dead = (it < mine ? 0u : kOut) | (off + 8 * xch < k ? 0u : kOut);
+#pragma unroll
+    for (int q = 0; q < kNwXq; ++q)
+      xd[q] = buf_load16(xres, (xbase + (uint32_t)q * xrow4 + 2u * off) | dead | (4 * q + xr0 < rows ? 0u : kOut));
+  };
+  // slice it: its X (in xr) goes to the wave's LDS tile, then slice it + 2's
+  // X is requested into the same registers; after the products with its W
+  // (in wr_), slice it + 2's W is requested into those: two register sets
+  // each, used in turn
+  auto slice = [&](int it, uint4 (&wr_)[kDbSteps], uint4 (&xr)[kNwXq]) {
+    // the tile is this wave's alone: its earlier reads are done (wave-ordered
+    // LDS), so the wave overwrites it and reads it back without a barrier
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < kNwXq; ++q) *reinterpret_cast<uint4*>(xw + q * 4 * kXsRow) = xr[q];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    load_x(it + 2, xr);
+    const uint16_t* xb = &xs[wv][r16 * kXsRow + kg];
+#pragma unroll
+    for (int u = 0; u < kDbSteps; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 bv = *reinterpret_cast<const uint4*>(xb + 16 * j * kXsRow + kDbStage * u);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr_[u]),
+                                                         __builtin_bit_cast(bf16x8, bv), acc[j], 0, 0, 0);
+      }
+    load_w(it + 2, wr_);
+  };
+  if (mine > 0) {
+    uint4 w0[kDbSteps], w1[kDbSteps], x0[kNwXq], x1[kNwXq];
+    load_w(0, w0);
+    load_x(0, x0);
+    load_w(1, w1);
+    load_x(1, x1);
+    for (int it = 0;; it += 2) {
+      slice(it, w0, x0);
+      if (it + 1 >= mine) break;
+      slice(it + 1, w1, x1);
+      if (it + 2 >= mine) break;
+    }
+  }
+  __shared__ f32x4 hand[kNwWaves - 1][4][kWave];
+  if (wv > 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hand[wv - 1][j][lane] = acc[j];
+  }
+  __syncthreads();
+  if (wv > 0) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = ((acc[j] + hand[0][j][lane]) + hand[1][j][lane]) + hand[2][j][lane];
+  const int nn = n0 + 4 * (lane >> 4);      // C^T rows nn .. nn + 3 of column b
+  if (nn >= n) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = 16 * j + r16;
+    if (b >= rows) continue;
+    uint16_t* crow = args.seg[si].c + (int64_t)(row0 + b) * n + nn;
+    float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+    if (args.accumulate) {
+      const uint2 old = *reinterpret_cast<const uint2*>(crow);
+      v[0] += bf16_lo(old.x);
+      v[1] += bf16_hi(old.x);
+      v[2] += bf16_lo(old.y);
+      v[3] += bf16_hi(old.y);
+    }
+    *reinterpret_cast<uint2*>(crow) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+}
+
 struct ReduceSeg {
   uint16_t* c;
   const float* part;
@@ -540,6 +681,38 @@ int decode_gemm_glu(uint16_t* act, const uint16_t* x, const uint16_t* w, int row
                                        dim3(kDbWaves * kWave), args, 0, stream));
 }
 
+// Products sharing X [rows][k] (1 to kMaxSeg of them) on the narrow-tile
+// kernel: every output is written (rounded once, plus C when accumulating)
+// by the launch itself.  PKV_ERR_UNSUPPORTED (nothing launched) when the
+// shape does not fit (a feature count or K that is not a multiple of 8).
+int decode_gemm_narrow(int nseg, uint16_t* const* c, const uint16_t* const* w, const int* n, const uint16_t* x,
+                       int rows, int k, bool accumulate, hipStream_t stream) {
+  if (nseg < 1 || nseg > kMaxSeg) return PKV_ERR_INVALID_ARG;
+  if (rows <= 0 || k <= 0 || k % 8) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)rows * k * 2 > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;     // 31-bit buffer offsets
+  NarrowArgs a{};
+  int t0 = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (n[i] <= 0 || n[i] % 8 || n[i] > (1 << 24)) return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)n[i] * k * 2 > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+    const int nt = (n[i] + kNwN - 1) / kNwN;
+    a.seg[i] = GemmSeg{w[i], c[i], nullptr, n[i], t0, t0 + nt};
+    t0 += nt;
+  }
+  const int64_t row_blocks = (rows + kDbRows - 1) / kDbRows;
+  if (row_blocks > 65535) return PKV_ERR_INVALID_ARG;
+  const int nsl = (k + kDbSlice - 1) / kDbSlice;
+  a.x = x;
+  a.nseg = nseg;
+  a.rows = rows;
+  a.k = k;
+  a.kq = (nsl + kNwWaves - 1) / kNwWaves;
+  a.accumulate = accumulate ? 1 : 0;
+  void* args[] = {&a};
+  return launch_status(hipLaunchKernel((const void*)decode_gemm_narrow_kernel, dim3(t0, (unsigned)row_blocks),
+                                       dim3(kNwWaves * kWave), args, 0, stream));
+}
+
 // h = bf16(h + sum of the output projection's partials), m = rmsnorm(h) * w.
 int reduce_residual_norm(uint16_t* h, uint16_t* m, const float* part, const uint16_t* w, int rows, int dim,
                          int splits, float eps, hipStream_t stream) {
@@ -669,12 +842,16 @@ int decode_layer_impl(pkv_bf16* h, const pkv_layer_weights* w, int hidden, int i
   const hipStream_t st = static_cast<hipStream_t>(stream);
   int rc;
   if (!a_ready && (rc = pkv_rmsnorm(S.a, h, w->attn_norm, batch, hidden, eps, stream)) != PKV_OK) return rc;
-  // q, k and v in one launch
+  // q, k and v in one launch: on the narrow-tile kernel (no partials, no
+  // reduction launch) while X is small enough to be read once per 16
+  // features, else K split over workgroups plus a reduction
   {
     uint16_t* cs[3] = {S.q, S.k, S.v};
     const uint16_t* ws[3] = {w->wq, w->wk, w->wv};
     const int ns[3] = {qd, kvd, kvd};
-    if ((rc = decode_gemm(3, cs, ws, ns, S.a, batch, hidden, false, S.part, S.part_bytes, st)) != PKV_OK) return rc;
+    rc = hidden <= kNarrowMaxK ? decode_gemm_narrow(3, cs, ws, ns, S.a, batch, hidden, false, st)
+                               : decode_gemm(3, cs, ws, ns, S.a, batch, hidden, false, S.part, S.part_bytes, st);
+    if (rc != PKV_OK) return rc;
   }
   if ((rc = decode_enqueue(att, st)) != PKV_OK) return rc;
   // h += x W^T, then (norm_w given) y = rmsnorm(h, norm_w): with K split, the
