@@ -20,7 +20,10 @@
 // along the workgroup's K range, and where 64-wide feature tiles alone would
 // leave the chip's 256 CUs idle K is split over workgroups, whose float32
 // partials a second kernel sums in a fixed order (no atomics: the result
-// does not depend on scheduling).  Larger batches run
+// does not depend on scheduling).  The layer's query/key/value product runs
+// on a narrow-tile kernel instead (16 features per workgroup, K split over
+// its four waves and summed in LDS), which reads the activations once per
+// 16 features but needs no partials and no second launch.  Larger batches run
 // the same kernel once per 64-row block (a second grid dimension; the weights
 // are then read once per row block), and a K or feature count that is not a
 // multiple of the tiles is masked, so every shape with K and the feature
