@@ -44,6 +44,11 @@ namespace {
 constexpr int kNormThreads = 256;
 
 // out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * w, bf16 in and out, float32 math.
+// A thread keeps its first kNormKeep groups of eight features (and their
+// weights, requested with them) in registers for the second pass; wider
+// rows re-read the rest.
+constexpr int kNormKeep = 4;
+
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(uint16_t* __restrict__ out,
                                                                const uint16_t* __restrict__ x,
                                                                const uint16_t* __restrict__ w, int dim, float eps) {
@@ -53,8 +58,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(uint16_t* __restr
   uint4* o4 = reinterpret_cast<uint4*>(out + (int64_t)r * dim);
   const int n4 = dim / 8;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n4; i += kNormThreads) {
-    const uint4 v = xr[i];
+  auto square_sum = [&](uint4 v) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -62,7 +66,20 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(uint16_t* __restr
       ss = __builtin_fmaf(a, a, ss);
       ss = __builtin_fmaf(b, b, ss);
     }
+  };
+  uint4 keep[kNormKeep], wkeep[kNormKeep];
+#pragma unroll
+  for (int gi = 0; gi < kNormKeep; ++gi) {
+    const int i = threadIdx.x + gi * kNormThreads;
+    if (i < n4) {
+      keep[gi] = xr[i];
+      wkeep[gi] = w4[i];
+    }
   }
+#pragma unroll
+  for (int gi = 0; gi < kNormKeep; ++gi)
+    if (threadIdx.x + gi * kNormThreads < n4) square_sum(keep[gi]);
+  for (int i = threadIdx.x + kNormKeep * kNormThreads; i < n4; i += kNormThreads) square_sum(xr[i]);
   __shared__ float part[kNormThreads / kWave];
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) ss += shfl_xor(ss, off);
@@ -72,9 +89,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(uint16_t* __restr
 #pragma unroll
   for (int i = 0; i < kNormThreads / kWave; ++i) tot += part[i];
   const float inv = 1.0f / sqrtf(tot / (float)dim + eps);
-  for (int i = threadIdx.x; i < n4; i += kNormThreads) {
-    const uint4 v = xr[i];
-    const uint4 g = w4[i];
+  auto write = [&](int i, uint4 v, uint4 g) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
     const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
     uint32_t res[4];
@@ -82,7 +97,13 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(uint16_t* __restr
     for (int j = 0; j < 4; ++j)
       res[j] = pack_bf16x2(bf16_lo(u[j]) * inv * bf16_lo(gw[j]), bf16_hi(u[j]) * inv * bf16_hi(gw[j]));
     o4[i] = make_uint4(res[0], res[1], res[2], res[3]);
+  };
+#pragma unroll
+  for (int gi = 0; gi < kNormKeep; ++gi) {
+    const int i = threadIdx.x + gi * kNormThreads;
+    if (i < n4) write(i, keep[gi], wkeep[gi]);
   }
+  for (int i = threadIdx.x + kNormKeep * kNormThreads; i < n4; i += kNormThreads) write(i, xr[i], w4[i]);
 }
 
 // act[r][i] = silu(gu[r][i]) * gu[r][inter + i], eight outputs per thread.
@@ -506,7 +527,14 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(ReduceArgs args) {
 
 // The attention output projection's finish, one workgroup per row:
 // h[b] = bf16(h[b] + sum over splits of part[s][b]) and, from that rounded
-// h, m[b] = rmsnorm(h[b]) * w (as rmsnorm_kernel).
+// h, m[b] = rmsnorm(h[b]) * w (as rmsnorm_kernel).  A thread's eight
+// features at a time: the partials of up to eight splits, h and the norm
+// weights are all requested before the first sum (one round trip to memory
+// for a row of up to 8 x 256 x 8 features at 8 splits), and the rounded h
+// stays in registers for the second pass (up to kRrnKeep groups per thread;
+// wider rows re-read what the thread wrote).
+constexpr int kRrnKeep = 4;
+
 __global__ __launch_bounds__(kNormThreads) void reduce_residual_norm_kernel(uint16_t* __restrict__ h,
                                                                            uint16_t* __restrict__ m,
                                                                            const float* __restrict__ part,
@@ -516,18 +544,30 @@ __global__ __launch_bounds__(kNormThreads) void reduce_residual_norm_kernel(uint
   const int n8 = dim / 8;
   const int64_t plane = (int64_t)rows * dim;
   uint4* hr = reinterpret_cast<uint4*>(h + (int64_t)r * dim);
+  const uint4* w4 = reinterpret_cast<const uint4*>(nw);
   float ss = 0.f;
-  for (int g = threadIdx.x; g < n8; g += kNormThreads) {
+  // h's eight features at group g, summed, rounded, written and returned
+  auto finish_h = [&](int g) {
     const float* p = part + (int64_t)r * dim + 8 * g;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int s = 0; s < splits; ++s) {
-      const float4 a = reinterpret_cast<const float4*>(p + s * plane)[0];
-      const float4 c = reinterpret_cast<const float4*>(p + s * plane)[1];
-      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-      v[4] += c.x; v[5] += c.y; v[6] += c.z; v[7] += c.w;
-    }
     const uint4 old = hr[g];
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+      float4 pa[8], pc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (s0 + i < splits) {
+          pa[i] = reinterpret_cast<const float4*>(p + (s0 + i) * plane)[0];
+          pc[i] = reinterpret_cast<const float4*>(p + (s0 + i) * plane)[1];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (s0 + i < splits) {
+          v[0] += pa[i].x; v[1] += pa[i].y; v[2] += pa[i].z; v[3] += pa[i].w;
+          v[4] += pc[i].x; v[5] += pc[i].y; v[6] += pc[i].z; v[7] += pc[i].w;
+        }
+      }
+    }
     const uint32_t o[4] = {old.x, old.y, old.z, old.w};
     uint32_t res[4];
 #pragma unroll
@@ -537,8 +577,20 @@ __global__ __launch_bounds__(kNormThreads) void reduce_residual_norm_kernel(uint
       ss = __builtin_fmaf(x0, x0, ss);
       ss = __builtin_fmaf(x1, x1, ss);
     }
-    hr[g] = make_uint4(res[0], res[1], res[2], res[3]);
+    const uint4 hv = make_uint4(res[0], res[1], res[2], res[3]);
+    hr[g] = hv;
+    return hv;
+  };
+  uint4 keep[kRrnKeep], wkeep[kRrnKeep];
+#pragma unroll
+  for (int gi = 0; gi < kRrnKeep; ++gi) {
+    const int g = threadIdx.x + gi * kNormThreads;
+    if (g < n8) {
+      wkeep[gi] = w4[g];
+      keep[gi] = finish_h(g);
+    }
   }
+  for (int g = threadIdx.x + kRrnKeep * kNormThreads; g < n8; g += kNormThreads) finish_h(g);
   __shared__ float sh[kNormThreads / kWave];
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) ss += shfl_xor(ss, off);
@@ -548,11 +600,8 @@ __global__ __launch_bounds__(kNormThreads) void reduce_residual_norm_kernel(uint
 #pragma unroll
   for (int i = 0; i < kNormThreads / kWave; ++i) tot += sh[i];
   const float inv = 1.0f / sqrtf(tot / (float)dim + eps);
-  const uint4* w4 = reinterpret_cast<const uint4*>(nw);
   uint4* mr = reinterpret_cast<uint4*>(m + (int64_t)r * dim);
-  for (int g = threadIdx.x; g < n8; g += kNormThreads) {   // each thread re-reads what it wrote
-    const uint4 v = hr[g];
-    const uint4 gw = w4[g];
+  auto write_m = [&](int g, uint4 v, uint4 gw) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
     const uint32_t ww[4] = {gw.x, gw.y, gw.z, gw.w};
     uint32_t res[4];
@@ -560,7 +609,14 @@ __global__ __launch_bounds__(kNormThreads) void reduce_residual_norm_kernel(uint
     for (int q = 0; q < 4; ++q)
       res[q] = pack_bf16x2(bf16_lo(u[q]) * inv * bf16_lo(ww[q]), bf16_hi(u[q]) * inv * bf16_hi(ww[q]));
     mr[g] = make_uint4(res[0], res[1], res[2], res[3]);
+  };
+#pragma unroll
+  for (int gi = 0; gi < kRrnKeep; ++gi) {
+    const int g = threadIdx.x + gi * kNormThreads;
+    if (g < n8) write_m(g, keep[gi], wkeep[gi]);
   }
+  // past the kept groups: each thread re-reads what it wrote
+  for (int g = threadIdx.x + kRrnKeep * kNormThreads; g < n8; g += kNormThreads) write_m(g, hr[g], w4[g]);
 }
 
 // K splits for a launch of `tiles` 64-feature tiles over `rows` rows: the
