@@ -29,8 +29,8 @@
 // multiple of the tiles is masked, so every shape with K and the feature
 // count multiples of 8 runs here.  The residual adds are folded in, so h is
 // read, summed in float32 and rounded once.  RMSNorm is one workgroup per
-// row: 16-byte loads, a float32 sum of squares reduced across the workgroup,
-// one rounding per output.
+// row: 16-byte loads all requested at once, a float32 sum of squares reduced
+// across the workgroup, one rounding per output.
 #include "common.h"
 #include "decode_api.h"
 
