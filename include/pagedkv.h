@@ -669,15 +669,18 @@ int pkv_silu_mul(pkv_bf16* act, const pkv_bf16* gate_up, int rows, int intermedi
 
 /* Bytes of float32 partials pkv_linear needs for this shape (0: none):
  * nonzero where the product's K is split across workgroups (few output
- * tiles for the chip's 256 CUs). */
+ * tiles for the chip's 256 CUs and in_features above 4096; at most 4096,
+ * such shapes run on the narrow-tile kernel, which needs none). */
 size_t pkv_linear_workspace_bytes(int rows, int out_features, int in_features);
 
 /* out[rows][out_features] = x[rows][in_features] weight^T (+ out when
  * accumulate != 0), float32 sums, one rounding per output, on the library's
- * MFMA projection kernel (one workgroup per 64 features and 64-row block,
- * deterministic: K-split partials summed in a fixed order).  When the shape
- * splits K and `workspace` (caller-owned device memory, 16-byte aligned,
- * contents ignored and overwritten) is null or smaller than
+ * MFMA projection kernels, deterministic (every sum in a fixed order): one
+ * workgroup per 64 features and 64-row block, or, where those tiles alone
+ * would leave CUs idle and in_features <= 4096, one per 16 features whose
+ * four waves split K and add their sums in LDS.  When the 64-feature kernel
+ * splits K over workgroups and `workspace` (caller-owned device memory,
+ * 16-byte aligned, contents ignored and overwritten) is null or smaller than
  * pkv_linear_workspace_bytes(...), the product runs as one K range.
  * out_features and in_features must be multiples of 8
  * (PKV_ERR_UNSUPPORTED otherwise).  out must not overlap x or weight. */

@@ -815,8 +815,21 @@ extern "C" int pkv_silu_mul(pkv_bf16* act, const pkv_bf16* gate_up, int rows, in
                                        args, 0, (hipStream_t)stream));
 }
 
+namespace {
+
+// pkv_linear's choice: the narrow-tile kernel where the wide one would split
+// K over workgroups (its 64-feature tiles alone leave CUs idle) and X is small
+// enough to be read once per 16 features; else the wide kernel.
+bool linear_narrow(int rows, int n, int k) {
+  if (rows <= 0 || n <= 0 || k <= 0 || k % 8 || n % 8 || k > kNarrowMaxK) return false;
+  return decode_gemm_splits(rows, (n + kDbN - 1) / kDbN, k) > 1;
+}
+
+}  // namespace
+
 extern "C" size_t pkv_linear_workspace_bytes(int rows, int out_features, int in_features) {
-  return decode_gemm_workspace_bytes(rows, out_features, in_features);
+  return linear_narrow(rows, out_features, in_features) ? 0
+                                                        : decode_gemm_workspace_bytes(rows, out_features, in_features);
 }
 
 extern "C" int pkv_linear(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weight, int rows, int out_features,
@@ -830,6 +843,8 @@ extern "C" int pkv_linear(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weig
   uint16_t* cc[1] = {out};
   const uint16_t* ww[1] = {weight};
   const int nn[1] = {out_features};
+  if (linear_narrow(rows, out_features, in_features))
+    return decode_gemm_narrow(1, cc, ww, nn, x, rows, in_features, accumulate != 0, static_cast<hipStream_t>(stream));
   return decode_gemm(1, cc, ww, nn, x, rows, in_features, accumulate != 0, workspace, workspace_bytes,
                      static_cast<hipStream_t>(stream));
 }
