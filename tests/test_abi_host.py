@@ -131,10 +131,13 @@ def test_layer_sizes_and_argument_errors(lib):
     E = _abi
     # K-split partials: splits x rows x features x 4 bytes, the most splits
     # (a power of two) that keep the workgroups (tiles x 64-row blocks x
-    # splits) within 256, each split whole 128-wide slices but the last
+    # splits) within 256, each split whole 128-wide slices but the last;
+    # shapes that would split with K <= 4096 take the narrow-tile kernel,
+    # which needs no partials
     assert pkv.pkv_linear_workspace_bytes(64, 2048, 8192) == 8 * 64 * 2048 * 4
-    assert pkv.pkv_linear_workspace_bytes(64, 3072, 2048) == 4 * 64 * 3072 * 4
-    assert pkv.pkv_linear_workspace_bytes(1, 512, 2048) == 16 * 1 * 512 * 4
+    assert pkv.pkv_linear_workspace_bytes(64, 3072, 2048) == 0        # would split 4 ways: narrow tiles
+    assert pkv.pkv_linear_workspace_bytes(1, 512, 2048) == 0          # would split 16 ways: narrow tiles
+    assert pkv.pkv_linear_workspace_bytes(1, 512, 4104) == 17 * 1 * 512 * 4   # K above 4096: 256-wide ranges, 17
     assert pkv.pkv_linear_workspace_bytes(64, 16384, 2048) == 0       # 256 tiles: no split
     assert pkv.pkv_linear_workspace_bytes(65, 2048, 8192) == 4 * 65 * 2048 * 4   # two row blocks
     assert pkv.pkv_linear_workspace_bytes(64, 2048, 8008) == 8 * 64 * 2048 * 4   # last K range shorter
