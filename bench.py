@@ -663,6 +663,21 @@ def decode_layer_leg(torch, np, pkv, eng, ctx_now, stream, iters: int = 5):
 
     t_calls = timed(per_layer_calls)
     t = timed(one_call)
+
+    # the weight reads alone (pkv_weight_read_probe: the projection kernels'
+    # lane pattern, one wave per 16-row block and K part), over the 16
+    # layers' matrices back to back (2 GB, so nothing is cached)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def probe(name, parts):
+        def run():
+            for layer in range(L):
+                pkv.pkv_weight_read_probe(weights[layer][name], sink, k_parts=parts, stream=stream)
+        us = timed(run) / L * 1e6
+        return {"us": round(us, 2), "GBps": round(weights[0][name].numel() * 2 / us / 1e3, 1)}
+
+    read_probe = {"gate_up_one_part": probe("w_gate_up", 1), "gate_up_two_parts": probe("w_gate_up", 2),
+                  "down_eight_parts": probe("w_down", 8), "wq_four_parts": probe("wq", 4)}
     del weights
     torch.cuda.empty_cache()
     return {"workload": f"Llama-3.2-1B decode step, B={B}, {L} layers, hidden 2048, intermediate 8192, synthetic "
@@ -670,7 +685,7 @@ def decode_layer_leg(torch, np, pkv, eng, ctx_now, stream, iters: int = 5):
             "ms_per_step": round(t * 1e3, 4), "us_per_layer": round(t / L * 1e6, 2),
             "ms_per_step_layer_calls": round(t_calls * 1e3, 4),
             "tokens_per_s": round(B / t, 1), "weight_bytes_per_layer": wbytes,
-            "kv_bytes_per_layer": int(ctx_now.sum()) * KV_BYTES_PER_TOKEN}
+            "kv_bytes_per_layer": int(ctx_now.sum()) * KV_BYTES_PER_TOKEN, "weight_read_probe": read_probe}
 
 
 def main():

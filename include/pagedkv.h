@@ -687,6 +687,17 @@ size_t pkv_linear_workspace_bytes(int rows, int out_features, int in_features);
 int pkv_linear(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weight, int rows, int out_features,
                int in_features, int accumulate, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Diagnostic, off the layer's path: the projection kernels' weight reads
+ * alone over w [n][k] bf16 (n % 16 == 0, k a multiple of 128 x k_parts,
+ * else PKV_ERR_UNSUPPORTED; k_parts 1, 2, 4 or 8, else PKV_ERR_INVALID_ARG):
+ * one wave per 16-row block and K part, each lane 16-byte loads in the MFMA
+ * operand pattern the kernels use (row lane % 16, k 8 (lane / 16) + 32 u of
+ * each 128-wide slice), two slices in flight, no arithmetic and no output
+ * (the last slice is re-read twice at the end, from cache).  `sink` as
+ * pkv_hbm_read_probe.  It gives the rate at which a weight matrix streams in
+ * this pattern, the floor the projections are compared with. */
+int pkv_weight_read_probe(const pkv_bf16* w, int n, int k, int k_parts, uint32_t* sink, void* stream);
+
 typedef struct {
   const pkv_bf16* attn_norm;    /* [hidden] */
   const pkv_bf16* wq;           /* [n_q_heads * 64][hidden] */

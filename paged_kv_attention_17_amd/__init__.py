@@ -11,7 +11,7 @@ call does, and raises if it has not been built.
 from ._abi import (  # noqa: F401
     PagedKVError, load, header_functions, LIB_PATH,
     pkv_status_str, pkv_abi_version, pkv_rope_table_init, pkv_rope_decode, pkv_paged_kv_append,
-    pkv_paged_gather, pkv_hbm_read_probe, pkv_paged_read_probe, pkv_blocks_assign, pkv_blocks_release,
+    pkv_paged_gather, pkv_hbm_read_probe, pkv_paged_read_probe, pkv_weight_read_probe, pkv_blocks_assign, pkv_blocks_release,
     pkv_block_table_patch,
     pkv_blocks_share, pkv_blocks_assign_shared, pkv_blocks_release_shared, pkv_blocks_copy, pkv_check_block_table,
     pkv_decode_workspace_bytes, pkv_decode_partition_size, pkv_paged_attn_decode, pkv_paged_attn_prefill,

@@ -45,6 +45,7 @@ SIGNATURES = {
     "pkv_paged_kv_append": (_i, [_p, _p, _i, _p, _p, _p, _i64, _i, _i, _p, _p, _i, _i, _i, _p]),
     "pkv_paged_gather": (_i, [_p, _p, _p, _p, _i, _p, _i64, _i, _i, _i, _i, _i, _p]),
     "pkv_hbm_read_probe": (_i, [_p, _sz, _p, _p]),
+    "pkv_weight_read_probe": (_i, [_p, _i, _i, _i, _p, _p]),
     "pkv_paged_read_probe": (_i, [_p, _p, _i, _p, _i64, _i, _i, _p, _p, _i, _i, _i, _p, _p]),
     "pkv_device_errors": (_i, [C.POINTER(C.c_uint32), _i, _p]),
     "pkv_set_kv_read_policy": (_i, [_i]),
@@ -286,6 +287,16 @@ def pkv_paged_gather(k_dense, v_dense, k_pool, v_pool, block_table, slot, contex
         _dev_ptr(k_dense, "k_dense", _bf16_types()), _dev_ptr(v_dense, "v_dense", _bf16_types()),
         _dev_ptr(k_pool, "k_pool", _bf16_types()), _dev_ptr(v_pool, "v_pool", _bf16_types()), k_pool.shape[0],
         bt + 0, stride, mb, slot, context_len, k_pool.shape[2], k_pool.shape[3], _stream(stream)))
+
+
+def pkv_weight_read_probe(w, sink, k_parts=1, stream=None):
+    """Read weight matrix `w` [n][k] (bf16, contiguous) once in the projection
+    kernels' access pattern, K split over `k_parts` waves per 16-row block
+    (diagnostic weight-stream rate); `sink` as for pkv_hbm_read_probe."""
+    _contig(w, "w")
+    n, k = w.shape
+    _check("pkv_weight_read_probe", load().pkv_weight_read_probe(
+        _dev_ptr(w, "w", _bf16_types()), n, k, k_parts, _dev_ptr(sink, "sink"), _stream(stream)))
 
 
 def pkv_hbm_read_probe(buf, sink, stream=None):

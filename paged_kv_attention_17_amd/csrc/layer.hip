@@ -784,6 +784,63 @@ int reduce_residual_norm(uint16_t* h, uint16_t* m, const float* part, const uint
 
 using namespace pkv;
 
+namespace pkv {
+namespace {
+
+// Diagnostic: the projection kernels' weight reads alone.  Wave i of the grid
+// takes 16-row block i / k_parts of w [n][k] over K part i % k_parts, with the
+// projection kernels' lane pattern (row lane % 16, 16 bytes at k 8 (lane /
+// 16) + 32 u of each 128-wide slice) and two slices in flight; the data are
+// XOR-ed into `sink` under a condition they never meet.
+__global__ __launch_bounds__(256) void weight_read_probe_kernel(const uint16_t* __restrict__ w, int k, int k_parts,
+                                                                int waves, uint32_t* sink) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wave >= waves) return;
+  const int kw = k / k_parts;                  // a multiple of 128 (checked on the host)
+  const int ns = kw / kDbSlice;
+  const uint16_t* base = w + (int64_t)(16 * (wave / k_parts) + (lane & 15)) * k + (wave % k_parts) * kw +
+                         8 * (lane >> 4);
+  uint4 b0[kDbSteps], b1[kDbSteps];
+  auto load = [&](int sl, uint4 (&d)[kDbSteps]) {
+    const int s = sl < ns ? sl : ns - 1;       // past the last slice: the last one again (in bounds, cached)
+#pragma unroll
+    for (int u = 0; u < kDbSteps; ++u) d[u] = *reinterpret_cast<const uint4*>(base + s * kDbSlice + kDbStage * u);
+  };
+  uint32_t acc = 0;
+  auto eat = [&](const uint4 (&d)[kDbSteps]) {
+#pragma unroll
+    for (int u = 0; u < kDbSteps; ++u) acc ^= d[u].x ^ d[u].y ^ d[u].z ^ d[u].w;
+  };
+  load(0, b0);
+  load(1, b1);
+  for (int sl = 0; sl < ns; sl += 2) {
+    eat(b0);
+    load(sl + 2, b0);
+    if (sl + 1 < ns) eat(b1);
+    load(sl + 3, b1);
+  }
+  if (acc == 0x9e3779b9u) *sink = acc;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int pkv_weight_read_probe(const pkv_bf16* w, int n, int k, int k_parts, uint32_t* sink, void* stream) {
+  if (n <= 0 || k <= 0 || (k_parts != 1 && k_parts != 2 && k_parts != 4 && k_parts != 8)) return PKV_ERR_INVALID_ARG;
+  if (n % 16 || k % (128 * k_parts)) return PKV_ERR_UNSUPPORTED;
+  if (!w || !sink) return PKV_ERR_NULL;
+  if (!aligned16(w) || !aligned4(sink)) return PKV_ERR_MISALIGNED;
+  if ((int64_t)n / 16 * k_parts > (int64_t)4 * 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  const uint16_t* ww = w;
+  int kk = k, kp = k_parts;
+  int waves = n / 16 * k_parts;
+  uint32_t* sk = sink;
+  void* args[] = {&ww, &kk, &kp, &waves, &sk};
+  return launch_status(hipLaunchKernel((const void*)weight_read_probe_kernel, dim3((unsigned)((waves + 3) / 4)),
+                                       dim3(256), args, 0, (hipStream_t)stream));
+}
+
 extern "C" int pkv_rmsnorm(pkv_bf16* out, const pkv_bf16* x, const pkv_bf16* weight, int rows, int dim, float eps,
                            void* stream) {
   if (rows < 0 || dim <= 0 || dim % 8 || !(eps >= 0.f)) return PKV_ERR_INVALID_ARG;

@@ -369,6 +369,14 @@ def test_read_probe_argument_errors(lib):
     assert lib.pkv_hbm_read_probe(FAKE, 64, None, None) == E.PKV_ERR_NULL
     assert lib.pkv_hbm_read_probe(FAKE + 4, 64, FAKE, None) == E.PKV_ERR_MISALIGNED
     assert lib.pkv_hbm_read_probe(FAKE, 60, FAKE, None) == E.PKV_ERR_MISALIGNED
+    # the weight-stream probe: shape rules before pointers, nothing launched
+    assert lib.pkv_weight_read_probe(FAKE, 0, 2048, 1, FAKE, None) == E.PKV_ERR_INVALID_ARG
+    assert lib.pkv_weight_read_probe(FAKE, 64, 2048, 3, FAKE, None) == E.PKV_ERR_INVALID_ARG
+    assert lib.pkv_weight_read_probe(FAKE, 24, 2048, 1, FAKE, None) == E.PKV_ERR_UNSUPPORTED    # n % 16
+    assert lib.pkv_weight_read_probe(FAKE, 64, 384, 2, FAKE, None) == E.PKV_ERR_UNSUPPORTED     # k % 256
+    assert lib.pkv_weight_read_probe(None, 64, 2048, 1, FAKE, None) == E.PKV_ERR_NULL
+    assert lib.pkv_weight_read_probe(FAKE, 64, 2048, 1, None, None) == E.PKV_ERR_NULL
+    assert lib.pkv_weight_read_probe(FAKE + 4, 64, 2048, 1, FAKE, None) == E.PKV_ERR_MISALIGNED
 
 
 def test_load_shares_torch_hip_runtime():

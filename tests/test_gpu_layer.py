@@ -311,3 +311,18 @@ def test_decode_layers_match_per_layer_calls(gpu, B, short, host):
     assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
     assert torch.equal(kp1.view(torch.int16), kp2.view(torch.int16))
     assert torch.equal(vp1.view(torch.int16), vp2.view(torch.int16))
+
+
+@pytest.mark.parametrize("n,k,parts", [(64, 2048, 1), (48, 512, 2), (16, 512, 4), (32, 128, 1), (16, 2048, 8)])
+def test_weight_read_probe_reads_without_writing(gpu, n, k, parts):
+    """The diagnostic weight-stream probe reads the matrix (one to eight K
+    parts per 16-row block, one slice and several) and writes nothing: the
+    matrix is unchanged and the sink keeps its value."""
+    rng = np.random.default_rng(n + k + parts)
+    w = W.randn_bf16(rng, (n, k))
+    wd = dev_bf16(w)
+    sink = torch.full((1,), 5, dtype=torch.int32, device="cuda")
+    pkv.pkv_weight_read_probe(wd, sink, k_parts=parts)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 5
+    np.testing.assert_array_equal(bits(wd), w)
