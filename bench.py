@@ -615,7 +615,8 @@ def decode_layer_leg(torch, np, pkv, eng, ctx_now, stream, iters: int = 5):
     16 layers in one call) for the B=64 rows of the main workload, synthetic
     bf16 weights ~ N(0, 1/fan_in) on the device (121 MB per layer).  Each
     layer's attention re-writes the last token in place, like the attention
-    timing.  HIP events around each 16-layer pass; the same pass as one
+    timing.  HIP events around each 16-layer pass, queued behind a device-side
+    wait (GPU time; the host's time per pass beside it); the same pass as one
     pkv_decode_layer call per layer is timed too."""
     HID, INTER, NQ, NKV = 2048, 8192, 32, 8
     L = eng.n_layers
@@ -648,21 +649,32 @@ def decode_layer_leg(torch, np, pkv, eng, ctx_now, stream, iters: int = 5):
                               eng.max_context_len, eng.cos_sin, eng.scale, eng.workspace, row_lens_host=ctx_now,
                               stream=stream)
 
-    def timed(fn):
+    host_s = {}
+
+    def timed(fn, key=None):
+        # each pass queued behind a device-side wait, so that the host has
+        # enqueued the whole pass (and done its checks and planning) before
+        # the GPU starts: the events time the GPU's work, and the host's own
+        # time per pass is reported beside it
         fn()
         torch.cuda.synchronize()
-        times = []
+        times, walls = [], []
         for _ in range(iters):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(10_000_000)
             e0.record(stream)
+            w0 = time.perf_counter()
             fn()
+            walls.append(time.perf_counter() - w0)
             e1.record(stream)
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1) / 1e3)
+        if key:
+            host_s[key] = float(np.median(walls))
         return float(np.median(times))
 
-    t_calls = timed(per_layer_calls)
-    t = timed(one_call)
+    t_calls = timed(per_layer_calls, "calls")
+    t = timed(one_call, "one")
 
     # the weight reads alone (pkv_weight_read_probe: the projection kernels'
     # lane pattern, one wave per 16-row block and K part), over the 16
@@ -684,6 +696,8 @@ def decode_layer_leg(torch, np, pkv, eng, ctx_now, stream, iters: int = 5):
                         "bf16 weights, the main workload's paged cache (ctx U[512,4096])",
             "ms_per_step": round(t * 1e3, 4), "us_per_layer": round(t / L * 1e6, 2),
             "ms_per_step_layer_calls": round(t_calls * 1e3, 4),
+            "host_ms_per_step": round(host_s["one"] * 1e3, 4),
+            "host_ms_per_step_layer_calls": round(host_s["calls"] * 1e3, 4),
             "tokens_per_s": round(B / t, 1), "weight_bytes_per_layer": wbytes,
             "kv_bytes_per_layer": int(ctx_now.sum()) * KV_BYTES_PER_TOKEN, "weight_read_probe": read_probe}
 
